@@ -1,0 +1,377 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks one oracle function against a closed form, an independent
+construction, a library routine, brute force, or a hand-derived worked
+example under tests/golden/. The pins are chosen so that a plausible slip (a
+dropped term, a wrong sign, a wrong index, a transposed operand, a different
+bit order) fails at least one of them; tests/test_oracle_mutations.py plants
+such slips in copies of the oracle and checks that they are caught.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+import torch
+
+from oracle import cfm_oracle as O
+import synth
+
+
+def _rng(s=0):
+    return np.random.default_rng(s)
+
+
+# ----------------------------------------------------------------------------- BF16 + SiLU
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    r = _rng(1)
+    v = (r.standard_normal(200_000) * np.exp(r.uniform(-90, 90, 200_000))).astype(np.float32)
+    v = np.concatenate([v, np.float32([0.0, -0.0, 1e-40, -3e-39, 3.4e38, np.inf, -np.inf])])
+    ours = O.f64_to_bf16(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_ties_to_even_by_hand():
+    # 1 + 2^-8 lies halfway between 1 (0x3F80) and 1 + 2^-7 (0x3F81): even -> 0x3F80
+    # 1 + 3*2^-8 lies halfway between 0x3F81 and 0x3F82: even -> 0x3F82
+    # 1 + 2^-8 + 2^-40 is above the midpoint -> 0x3F81 (an fp32 detour would lose it)
+    got = O.f64_to_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, -2.5]))
+    assert [int(g) for g in got] == [0x3F80, 0x3F82, 0x3F81, 0xC020]
+
+
+def test_bf16_decode_exact():
+    assert O.bf16_to_f64(np.array([0x3F80, 0xC020, 0x0001], np.uint16)).tolist() == [1.0, -2.5, 2.0 ** -133]
+
+
+def test_silu_matches_scipy():
+    z = np.linspace(-40, 40, 4001)
+    assert np.allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+
+
+# ----------------------------------------------------------------------------- rotation
+
+def _sylvester(H):
+    m = np.array([[1.0]])
+    while m.shape[0] < H:
+        m = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), m)
+    return m
+
+
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 64, 256])
+def test_hadamard_equals_sylvester_construction(H):
+    assert np.array_equal(O.hadamard(H), _sylvester(H))
+    assert np.array_equal(O.hadamard(H), scipy.linalg.hadamard(H).astype(np.float64))
+
+
+def test_hadamard_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        O.hadamard(12)
+
+
+def test_rotation_inverse_and_inner_products():
+    H = 128
+    r = _rng(2)
+    d = np.where(r.integers(0, 2, H) == 1, -1, 1).astype(np.int8)
+    v, w = r.standard_normal((2, H))
+    # with d = 1: T(T(v)) = H v (Hadamard squared is H times identity)
+    ones = np.ones(H, np.int8)
+    assert np.allclose(O.rotate(O.rotate(v, ones), ones), H * v, rtol=1e-12, atol=1e-9)
+    # the signed rotation is sqrt(H) times an orthogonal map: inner products scale by H
+    assert np.isclose(O.rotate(v, d) @ O.rotate(w, d), H * (v @ w), rtol=1e-11)
+    assert np.isclose(np.sum(O.rotate(v, d) ** 2), H * np.sum(v ** 2), rtol=1e-12)
+    # signs act before the transform: T(v) with d equals Hadamard applied to d*v, by brute force
+    i = 5
+    brute = sum(((-1) ** bin(i & j).count("1")) * d[j] * v[j] for j in range(H))
+    assert np.isclose(O.rotate(v, d)[i], brute, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- sketch
+
+def test_twn_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "twn_worked_example.json")))
+    for case in g["cases"]:
+        w = np.array(case["w"])
+        d = np.array(case["signs"], np.int8)
+        assert np.array_equal(O.rotate(w, d), np.array(case["rotated"]))
+        bits = O.f64_to_bf16(w)[None]
+        assert np.array_equal(O.bf16_to_f64(bits)[0], w)       # the row is BF16-exact
+        codes, scale = O.sketch_rows(bits, d)
+        assert codes[0].tolist() == case["codes"]
+        assert scale[0] == np.float32(case["scale"])
+
+
+@pytest.mark.parametrize("H,seed", [(16, 0), (64, 1), (256, 2)])
+def test_sketch_round_trip_on_ternary_rows(H, seed):
+    """Rows w = d * (Hadamard . t) have T(w) = H t exactly, so the sketch must return t, scale 1."""
+    r = _rng(seed)
+    d = np.where(r.integers(0, 2, H) == 1, -1, 1).astype(np.int8)
+    t = r.integers(-1, 2, size=(40, H)).astype(np.int8)
+    t[0] = 0
+    t[0, 3] = -1                       # a single nonzero
+    t[1] = 1                           # all nonzero
+    w = d * (t.astype(np.float64) @ _sylvester(H))   # integers of magnitude <= H: BF16-exact
+    bits = O.f64_to_bf16(w)
+    assert np.array_equal(O.bf16_to_f64(bits), w)
+    codes, scale = O.sketch_rows(bits, d)
+    assert np.array_equal(codes, t[:len(codes)])
+    assert np.all(scale[1:] == 1.0) and scale[0] == 1.0
+
+
+def test_sketch_zero_row():
+    codes, scale = O.sketch_rows(np.zeros((1, 16), np.uint16), np.ones(16, np.int8))
+    assert not codes.any() and scale[0] == 0.0
+
+
+def test_twn_scale_is_least_squares_for_its_pattern():
+    r = _rng(3)
+    wt = r.standard_normal((5, 64))
+    codes, alpha = O.ternarize(wt)
+    for n in range(5):
+        t = codes[n].astype(np.float64)[:, None]
+        sol, *_ = np.linalg.lstsq(t, wt[n], rcond=None)
+        assert np.isclose(alpha[n], sol[0], rtol=1e-12)
+
+
+def test_twn_nonzero_fraction_on_gaussian_rows():
+    """For Gaussian rows, P(|z| > 0.7 E|z|) = 2(1 - Phi(0.7 sqrt(2/pi))) = 0.5764."""
+    r = _rng(4)
+    codes, _ = O.ternarize(r.standard_normal((400, 1024)))
+    expected = 2 * (1 - scipy.special.ndtr(0.7 * np.sqrt(2 / np.pi)))
+    assert abs(np.mean(codes != 0) - expected) < 0.005
+    assert abs(np.mean(codes == 1) - np.mean(codes == -1)) < 0.005
+
+
+def test_pack_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "pack_example.json")))
+    codes = np.array([g["codes"]], np.int8)
+    packed = O.pack_codes(codes)
+    assert packed[0].tolist() == g["bytes"]
+    assert int(packed[0].view("<u4")[0]) == int(g["word"], 16)
+    assert np.array_equal(O.unpack_codes(packed), codes)
+
+
+def test_pack_fp4_reading():
+    """The word masks give E2M1 codes: 0x2 = +1.0, 0xA = -1.0, 0x0 = 0 (OCP MX spec)."""
+    e2m1 = {0x0: 0.0, 0x2: 1.0, 0xA: -1.0}
+    r = _rng(5)
+    codes = r.integers(-1, 2, size=(3, 64)).astype(np.int8)
+    words = O.pack_codes(codes).view("<u4")
+    for n in range(3):
+        for b in range(4):
+            w = int(words[n, b])
+            lo, hi = w & 0xAAAAAAAA, (w << 1) & 0xAAAAAAAA
+            for q in range(8):
+                assert e2m1[(lo >> 4 * q) & 0xF] == codes[n, 16 * b + q]
+                assert e2m1[(hi >> 4 * q) & 0xF] == codes[n, 16 * b + 8 + q]
+
+
+def test_pack_round_trip_random():
+    r = _rng(6)
+    codes = r.integers(-1, 2, size=(17, 256)).astype(np.int8)
+    p = O.pack_codes(codes)
+    assert p.shape == (17, 64) and p.dtype == np.uint8
+    assert np.array_equal(O.unpack_codes(p), codes)
+
+
+# ----------------------------------------------------------------------------- selection
+
+def test_topk_brute_force_with_ties():
+    r = _rng(7)
+    for trial in range(50):
+        n = int(r.integers(1, 60))
+        s = r.integers(0, 5, n).astype(np.float64)       # many exact ties
+        k = int(r.integers(0, n + 1))
+        brute = sorted(sorted(range(n), key=lambda j: (-s[j], j))[:k])
+        assert O.topk_set(s, k).tolist() == brute
+
+
+def test_topk_nan_counts_as_zero():
+    s = np.array([np.nan, 0.5, 0.0, np.nan])
+    assert O.topk_set(s, 2).tolist() == [0, 1]      # 0.5, then the first of the zero-keyed
+
+
+def _ternary_expert(H, I, d, r):
+    t = r.integers(-1, 2, size=(I, H)).astype(np.int8)
+    w = d * (t.astype(np.float64) @ _sylvester(H))
+    return O.f64_to_bf16(w / 64.0)                   # exact: powers of two keep BF16 exactness
+
+
+def test_screen_equals_exact_on_ternary_weights():
+    """An exactly ternary rotated row has a lossless sketch: the screen gives the exact activations."""
+    H, I = 64, 48
+    r = _rng(8)
+    d = np.where(r.integers(0, 2, H) == 1, -1, 1).astype(np.int8)
+    wg, wu = _ternary_expert(H, I, d, r), _ternary_expert(H, I, d, r)
+    x = O.f64_to_bf16(r.standard_normal(H))
+    tg, sg = O.sketch_rows(wg, d)
+    tu, su = O.sketch_rows(wu, d)
+    hhat = O.screen_scores(x, O.pack_codes(tg), O.pack_codes(tu), sg, su, d)
+    xt = torch.from_numpy(O.bf16_to_f64(x))
+    ref = (torch.nn.functional.silu(torch.from_numpy(O.bf16_to_f64(wg)) @ xt)
+           * (torch.from_numpy(O.bf16_to_f64(wu)) @ xt)).numpy()
+    assert np.allclose(hhat, ref, rtol=1e-10, atol=1e-12)
+    assert np.allclose(O.exact_activations(x, wg, wu), ref, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- forward
+
+def _small_layer(E=4, I=32, H=64, T=3, K=2, seed=9):
+    shape = synth.LayerShape(E=E, K=K, I=I, H=H, chan_scale=True)
+    wg, wu, wd = synth.layer_weights(shape, seed)
+    d = synth.rotation_signs(H, seed)
+    x = synth.hidden_states(T, H, seed)
+    ids, w = synth.routing(T, E, K, seed)
+    return wg, wu, wd, d, x, ids, w
+
+
+def _torch_swiglu_out(x, ids, w, wg, wu, wd):
+    outs = []
+    for t in range(ids.shape[0]):
+        xt = torch.from_numpy(O.bf16_to_f64(x[t]))
+        acc = torch.zeros(wg.shape[2], dtype=torch.float64)
+        for q in range(ids.shape[1]):
+            e = int(ids[t, q])
+            g = torch.from_numpy(O.bf16_to_f64(wg[e])) @ xt
+            u = torch.from_numpy(O.bf16_to_f64(wu[e])) @ xt
+            h = torch.nn.functional.silu(g) * u
+            acc += float(w[t, q]) * (torch.from_numpy(O.bf16_to_f64(wd[e])).T @ h)
+        outs.append(acc.numpy())
+    return np.stack(outs)
+
+
+def test_dense_matches_torch_swiglu():
+    wg, wu, wd, d, x, ids, w = _small_layer()
+    ours = O.bf16_to_f64(O.dense_forward(x, ids, w, wg, wu, wd))
+    ref = _torch_swiglu_out(x, ids, w, wg, wu, wd)
+    assert np.allclose(ours, ref, rtol=2 ** -8, atol=1e-30)
+    assert np.array_equal(O.dense_forward(x, ids, w, wg, wu, wd), O.f64_to_bf16(ref)) or \
+        np.max(np.abs(ours - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2 ** -8
+
+
+@pytest.mark.parametrize("r", [0, 5])
+def test_all_kept_equals_dense(r):
+    """k = c = I reads every channel: the selected layer is the dense layer, bit for bit."""
+    wg, wu, wd, d, x, ids, w = _small_layer()
+    I = wg.shape[1]
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, r)
+    out, pairs = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, I, I)
+    assert np.array_equal(out, O.dense_forward(x, ids, w, wg, wu, wd))
+    assert all(len(p["S"]) == I and len(p["C"]) == I for p in pairs.values())
+
+
+def test_nothing_kept_full_rank_recovers_wdown_times_sketch_activations():
+    """k = 0 with the full-rank map: y = W_down · hhat (the sketch-activation dense layer)."""
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    I, H = wg.shape[1], wg.shape[2]
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A = np.stack([O.lowrank(wd[e], I)[0] for e in range(wd.shape[0])])
+    Bt = np.stack([O.lowrank(wd[e], I)[1] for e in range(wd.shape[0])])
+    for t in range(ids.shape[0]):
+        for q in range(ids.shape[1]):
+            e = int(ids[t, q])
+            p = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, 0)
+            ref = O.bf16_to_f64(wd[e]).T @ p["hhat"]
+            assert np.allclose(p["y"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+            assert len(p["S"]) == 0 and len(p["C"]) == 0
+
+
+def test_kept_part_and_recovery_are_separate_terms():
+    """y - (sum over S of h_j Wd_j) must equal A · Bt[skip]^T hhat[skip] with skip = complement of S."""
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 6)
+    e = int(ids[0, 0])
+    p = O.select_pair(x[0], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 11)
+    S = p["S"]
+    assert set(S) <= set(p["C"]) and len(S) == 5 and len(p["C"]) == 11
+    kept = sum(p["h_all"][j] * O.bf16_to_f64(wd[e][j]) for j in S)
+    skip = [j for j in range(32) if j not in set(S)]
+    rec = O.bf16_to_f64(A[e]) @ sum(p["hhat"][j] * O.bf16_to_f64(Bt[e][j]) for j in skip)
+    assert np.allclose(p["y"], kept + rec, rtol=1e-11, atol=1e-14)
+    # S is the top-5 of C by exact |h| (brute force), C the top-11 of all by |hhat|
+    C_b = sorted(sorted(range(32), key=lambda j: (-abs(p["hhat"][j]), j))[:11])
+    assert p["C"].tolist() == C_b
+    S_b = sorted(sorted(C_b, key=lambda j: (-abs(p["h_all"][j]), j))[:5])
+    assert S.tolist() == S_b
+
+
+def test_combine_linear_and_slot_order_free():
+    r = _rng(10)
+    ys = r.standard_normal((3, 64))
+    w = r.random(3)
+    a = O.bf16_to_f64(O.combine(ys, w))
+    b = O.bf16_to_f64(O.combine(ys[::-1], w[::-1]))
+    assert np.array_equal(a, b)
+    ref = w[0] * ys[0] + w[1] * ys[1] + w[2] * ys[2]
+    assert np.allclose(a, ref, rtol=2 ** -8)
+    assert np.array_equal(O.combine(ys[:1], np.ones(1)), O.f64_to_bf16(ys[0]))
+
+
+def test_batch_independence():
+    """Token t's sets and output do not depend on the other tokens of the batch."""
+    wg, wu, wd, d, x, ids, w = _small_layer(T=4)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 4)
+    full, pf = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 6, 12)
+    one, p1 = O.select_forward(x[2:3], ids[2:3], w[2:3], wg, wu, wd, tg, tu, sg, su, d, A, Bt, 6, 12)
+    assert np.array_equal(full[2], one[0])
+    assert all(np.array_equal(pf[(2, q)]["S"], p1[(0, q)]["S"]) for q in range(ids.shape[1]))
+
+
+# ----------------------------------------------------------------------------- low-rank map
+
+def test_lowrank_eckart_young_and_orthonormal():
+    r = _rng(11)
+    W = r.standard_normal((96, 40)) * np.exp(r.standard_normal(40))[None, :]   # H x I
+    for rank in (0, 1, 7, 40):
+        A, Bt = O.lowrank(W.T, rank)
+        resid = np.sum((W - A @ Bt.T) ** 2)
+        ev = np.sort(np.linalg.eigvalsh(W.T @ W))[::-1]       # squared singular values, another routine
+        assert np.isclose(resid, max(ev[rank:].sum(), 0.0), rtol=1e-9, atol=1e-9)
+        assert np.allclose(Bt.T @ Bt, np.eye(rank), atol=1e-12)
+
+
+def test_lowrank_known_factorisation():
+    r = _rng(12)
+    U, _ = np.linalg.qr(r.standard_normal((64, 20)))
+    V, _ = np.linalg.qr(r.standard_normal((20, 20)))
+    s = np.linspace(10, 1, 20)
+    W = U @ np.diag(s) @ V.T                                  # H x I with known SVD
+    A, Bt = O.lowrank(W.T, 5)
+    assert np.allclose(A @ Bt.T, U[:, :5] @ np.diag(s[:5]) @ V[:, :5].T, atol=1e-10)
+    for l in range(5):
+        j = int(np.argmax(np.abs(Bt[:, l])))
+        assert Bt[j, l] > 0
+
+
+def test_lowrank_exact_on_low_rank_matrix():
+    r = _rng(13)
+    W = r.standard_normal((50, 3)) @ r.standard_normal((3, 30))
+    A, Bt = O.lowrank(W.T, 3)
+    assert np.allclose(A @ Bt.T, W, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------- byte accounting
+
+def test_read_bytes_closed_form_q18():
+    """Per pair: 2*I*H/4 + 8I + 2Hr + 2Ir + 4Hc + 2Hk = 3,979,264 bytes at H 2048, I 768, k 138, c 276, r 64."""
+    ids = np.arange(8, dtype=np.int32)[None]
+    b = O.read_bytes(ids, 128, 768, 2048, 138, 276, 64)
+    assert b == 8 * 3_979_264 + 2 * 2048 + 8 * 8 + 2 * 2048
+    assert O.dense_bytes(ids, 128, 768, 2048) == 8 * 9_437_184 + 2 * 2048 + 64 + 2 * 2048
+
+
+def test_read_bytes_unions_shared_experts():
+    ids = np.array([[0, 1], [0, 2]], np.int32)
+    cs = {(0, 0): np.array([1, 2]), (1, 0): np.array([2, 3]), (0, 1): np.array([5]), (1, 1): np.array([6])}
+    ks = {(0, 0): np.array([1]), (1, 0): np.array([1]), (0, 1): np.array([5]), (1, 1): np.array([6])}
+    I, H, r = 8, 16, 2
+    per = lambda nc, nk: 2 * (I * H // 4) + 8 * I + 2 * H * r + 2 * I * r + 4 * H * nc + 2 * H * nk
+    want = per(3, 1) + per(1, 1) + per(1, 1) + 2 * 2 * H + 8 * 2 * 2 + 2 * 2 * H
+    assert O.read_bytes(ids, 3, I, H, 1, 2, r, cs, ks) == want
