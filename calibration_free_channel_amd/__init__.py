@@ -1,0 +1,11 @@
+"""Channel-selected routed-expert SwiGLU FFN for MoE decoding on MI355X (gfx950).
+
+The computation lives in libcfm.so (hand-written HIP, C ABI in include/cfm.h);
+this package is its ctypes binding. Importing it without the built library
+raises ImportError: there is no CPU fallback.
+"""
+from ._lib import (  # noqa: F401
+    CfmError, EXPORTED, STATS_BYTES, decode_stats, dense_workspace, last_error, lowrank_build,
+    lowrank_workspace, moe_dense_forward, moe_select_forward, new_workspace, select_workspace,
+    sketch_build, version,
+)

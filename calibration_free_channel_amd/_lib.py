@@ -1,0 +1,188 @@
+"""ctypes binding of libcfm.so (include/cfm.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. PyTorch supplies device memory and the current stream. BF16 arrays
+are torch.bfloat16 (or raw torch.int16 / torch.uint16) tensors.
+
+There is no fallback: if libcfm.so is missing the import raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcfm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m calibration_free_channel_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_z = ctypes.c_size_t
+
+_SIGS = {
+    "cfm_last_error": (ctypes.c_char_p, []),
+    "cfm_version": (ctypes.c_char_p, []),
+    "sketch_build": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "lowrank_workspace": (_z, [_i, _i, _i, _i]),
+    "lowrank_build": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _z, _p]),
+    "select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_select_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
+                                _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
+    "dense_workspace": (_z, [_i, _i, _i, _i, _i]),
+    "moe_dense_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _z, _p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+STATS_FIELDS = ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io",
+                "bytes_dense_equiv", "experts_used", "rows_candidates", "rows_down")
+STATS_BYTES = 6 * 8 + 4 * 4
+
+
+class CfmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.cfm_last_error().decode()
+        super().__init__(f"{where} failed ({code}): {msg}")
+        self.code = code
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise CfmError(code, where)
+
+
+def version() -> str:
+    return _lib.cfm_version().decode()
+
+
+def last_error() -> str:
+    return _lib.cfm_last_error().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libcfm must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold BF16 values (torch.bfloat16), got {t.dtype}")
+    return t
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def sketch_build(w_gate, w_up, signs, out=None):
+    """Sketch of every expert's gate and up rows. Returns (tg, tu, sg, su)."""
+    _bf16(w_gate, "w_gate"), _bf16(w_up, "w_up")
+    E, I, H = w_gate.shape
+    if w_up.shape != w_gate.shape or signs.shape != (H,) or signs.dtype != torch.int8:
+        raise ValueError("shape/dtype mismatch")
+    dev = w_gate.device
+    if out is None:
+        out = (torch.empty((E, I, H // 4), dtype=torch.uint8, device=dev),
+               torch.empty((E, I, H // 4), dtype=torch.uint8, device=dev),
+               torch.empty((E, I), dtype=torch.float32, device=dev),
+               torch.empty((E, I), dtype=torch.float32, device=dev))
+    tg, tu, sg, su = out
+    _check(_lib.sketch_build(_ptr(w_gate), _ptr(w_up), E, I, H, _ptr(signs), _ptr(tg), _ptr(tu),
+                             _ptr(sg), _ptr(su), _stream(dev)), "sketch_build")
+    return tg, tu, sg, su
+
+
+def lowrank_workspace(E, I, H, r) -> int:
+    return int(_lib.lowrank_workspace(E, I, H, r))
+
+
+def lowrank_build(w_down_t, r, ws=None, out=None):
+    """Rank-r map of every expert's down projection. Returns (A [E][H][r], Bt [E][I][r]) BF16."""
+    _bf16(w_down_t, "w_down_t")
+    E, I, H = w_down_t.shape
+    dev = w_down_t.device
+    if out is None:
+        out = (torch.empty((E, H, r), dtype=torch.bfloat16, device=dev),
+               torch.empty((E, I, r), dtype=torch.bfloat16, device=dev))
+    A, Bt = out
+    if r == 0:
+        return A, Bt
+    need = lowrank_workspace(E, I, H, r)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(_lib.lowrank_build(_ptr(w_down_t), E, I, H, r, _ptr(A), _ptr(Bt), _ptr(ws), ws.numel(),
+                              _stream(dev)), "lowrank_build")
+    return A, Bt
+
+
+def select_workspace(T, K, E, I, H, k, c, r) -> int:
+    return int(_lib.select_workspace(T, K, E, I, H, k, c, r))
+
+
+def dense_workspace(T, K, E, I, H) -> int:
+    return int(_lib.dense_workspace(T, K, E, I, H))
+
+
+def new_workspace(nbytes, device):
+    """A zero-filled workspace (the forward calls require zeroed memory on first use)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_select_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, tu, sg, su, A, Bt,
+                       k, c, r, out=None, ws=None, cand_out=None, keep_out=None, stats=None):
+    """Selected-channel MoE layer. Returns out [T][H] BF16."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = new_workspace(select_workspace(T, K, E, I, H, k, c, r), dev)
+    _check(_lib.moe_select_forward(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
+        E, I, H, _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su),
+        _ptr(A) if r > 0 else None, _ptr(Bt) if r > 0 else None, k, c, r, _ptr(out),
+        _ptr(cand_out), _ptr(keep_out), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)),
+        "moe_select_forward")
+    return out
+
+
+def moe_dense_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, out=None, ws=None):
+    """Dense routed-expert SwiGLU layer (every channel). Returns out [T][H] BF16."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = new_workspace(dense_workspace(T, K, E, I, H), dev)
+    _check(_lib.moe_dense_forward(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
+        E, I, H, _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), "moe_dense_forward")
+    return out
+
+
+def decode_stats(buf) -> dict:
+    """cfm_stats bytes (a uint8 tensor of STATS_BYTES) -> dict."""
+    import numpy as np
+    raw = buf.detach().cpu().numpy().tobytes()
+    u64 = np.frombuffer(raw[:48], dtype="<u8")
+    u32 = np.frombuffer(raw[48:64], dtype="<u4")
+    vals = list(map(int, u64)) + list(map(int, u32[:3]))
+    return dict(zip(STATS_FIELDS, vals))

@@ -1,0 +1,149 @@
+// C ABI entry points: argument validation, workspace sizing, dispatch.
+// Validation is plain host code that runs before any HIP call, so argument
+// errors are reported the same way on machines without a GPU.
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "cfm_internal.h"
+#include "cfm_launch.h"
+
+namespace cfm {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+int check_shape(int E, int I, int H, bool need_pow2_h) {
+  if (E <= 0 || I <= 0 || H <= 0) return set_error(CFM_EINVAL, "E, I and H must be positive");
+  if (H < 64 || H > kMaxH) return set_error(CFM_EUNSUPPORTED, "H must lie in [64, 8192]");
+  if (need_pow2_h && !is_pow2(H)) return set_error(CFM_EUNSUPPORTED, "H must be a power of two");
+  if (!need_pow2_h && H % 64) return set_error(CFM_EUNSUPPORTED, "H must be a multiple of 64");
+  if (I > kMaxI) return set_error(CFM_EUNSUPPORTED, "I must be at most 8192");
+  return CFM_OK;
+}
+
+int check_budget(int I, int H, int k, int c, int r) {
+  if (k < 0 || c < 0 || r < 0) return set_error(CFM_EUNSUPPORTED, "k, c and r must be nonnegative");
+  if (c > I) return set_error(CFM_EUNSUPPORTED, "c must not exceed I");
+  if (k > c) return set_error(CFM_EUNSUPPORTED, "k must not exceed c");
+  if (r > std::min(H, I)) return set_error(CFM_EUNSUPPORTED, "r must not exceed min(H, I)");
+  if (r > kMaxRank) return set_error(CFM_EUNSUPPORTED, "r must be at most 128");
+  return CFM_OK;
+}
+
+int check_tokens(int T, int K) {
+  if (T < 0) return set_error(CFM_EINVAL, "T must be nonnegative");
+  if (K <= 0) return set_error(CFM_EINVAL, "K must be positive");
+  if (K > kMaxK) return set_error(CFM_EUNSUPPORTED, "K must be at most 64");
+  if ((long)T * K > (1L << 24)) return set_error(CFM_EUNSUPPORTED, "T*K too large");
+  return CFM_OK;
+}
+
+}  // namespace
+}  // namespace cfm
+
+using namespace cfm;
+
+extern "C" {
+
+const char* cfm_last_error(void) { return g_last_error.c_str(); }
+
+const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
+
+int sketch_build(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H,
+                 const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,
+                 void* stream) {
+  clear_error();
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (!w_gate || !w_up || !signs || !tg || !tu || !sg || !su)
+    return set_error(CFM_EINVAL, "sketch_build: null pointer");
+  if ((long)E * I * 2 > 0x7FFFFFFFL) return set_error(CFM_EUNSUPPORTED, "too many rows");
+  return launch_sketch_build(w_gate, w_up, E, I, H, signs, tg, tu, sg, su,
+                             static_cast<hipStream_t>(stream));
+}
+
+size_t lowrank_workspace(int E, int I, int H, int r) {
+  if (E <= 0 || I <= 0 || H <= 0 || r < 0 || r > kMaxRank || r > std::min(H, I)) return 0;
+  return lowrank_plan(E, I, H, r).bytes;
+}
+
+int lowrank_build(const cfm_bf16* w_down_t, int E, int I, int H, int r, cfm_bf16* A,
+                  cfm_bf16* Bt, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_shape(E, I, H, false)) return rc;
+  if (r < 0) return set_error(CFM_EUNSUPPORTED, "r must be nonnegative");
+  if (r > std::min(H, I)) return set_error(CFM_EUNSUPPORTED, "r must not exceed min(H, I)");
+  if (r > kMaxRank) return set_error(CFM_EUNSUPPORTED, "r must be at most 128");
+  if (r == 0) return CFM_OK;
+  if (!w_down_t || !A || !Bt) return set_error(CFM_EINVAL, "lowrank_build: null pointer");
+  const LowrankPlan plan = lowrank_plan(E, I, H, r);
+  if (!ws || ws_bytes < plan.bytes)
+    return set_error(CFM_EWORKSPACE, "lowrank_build: workspace smaller than lowrank_workspace()");
+  return launch_lowrank_build(w_down_t, E, I, H, r, A, Bt, ws, plan,
+                              static_cast<hipStream_t>(stream));
+}
+
+size_t select_workspace(int T, int K, int E, int I, int H, int k, int c, int r) {
+  if (T < 0 || K <= 0 || K > kMaxK || E <= 0 || I <= 0 || I > kMaxI || H < 64 || H > kMaxH ||
+      k < 0 || c < k || c > I || r < 0 || r > kMaxRank || r > std::min(H, I))
+    return 0;
+  return select_plan(T, K, E, I, H, k, c, r).bytes;
+}
+
+int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                       const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                       const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                       const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, cfm_bf16* out,
+                       int32_t* cand_out, int32_t* keep_out, cfm_stats* stats, void* ws,
+                       size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (int rc = check_budget(I, H, k, c, r)) return rc;
+  if (T == 0) return CFM_OK;
+  if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down_t || !signs || !tg || !tu ||
+      !sg || !su || !out)
+    return set_error(CFM_EINVAL, "moe_select_forward: null pointer");
+  if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_select_forward: null A or Bt with r > 0");
+  const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r);
+  if (!ws || ws_bytes < plan.bytes)
+    return set_error(CFM_EWORKSPACE, "moe_select_forward: workspace smaller than select_workspace()");
+  SelectArgs a{x, w_gate, w_up, w_down_t, A, Bt, topk_ids, topk_w, signs, tg, tu, sg, su, out,
+               cand_out, keep_out, stats, static_cast<char*>(ws)};
+  return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+
+size_t dense_workspace(int T, int K, int E, int I, int H) {
+  if (T < 0 || K <= 0 || K > kMaxK || E <= 0 || I <= 0 || I > kMaxI || H < 64 || H > kMaxH ||
+      H % 64)
+    return 0;
+  return dense_plan(T, K, E, I, H).bytes;
+}
+
+int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                      int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                      const cfm_bf16* w_down_t, int E, int I, int H, cfm_bf16* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, false)) return rc;
+  if (T == 0) return CFM_OK;
+  if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down_t || !out)
+    return set_error(CFM_EINVAL, "moe_dense_forward: null pointer");
+  const ForwardPlan plan = dense_plan(T, K, E, I, H);
+  if (!ws || ws_bytes < plan.bytes)
+    return set_error(CFM_EWORKSPACE, "moe_dense_forward: workspace smaller than dense_workspace()");
+  SelectArgs a{x, w_gate, w_up, w_down_t, nullptr, nullptr, topk_ids, topk_w, nullptr, nullptr,
+               nullptr, nullptr, nullptr, out, nullptr, nullptr, nullptr, static_cast<char*>(ws)};
+  return launch_dense_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Host-side launchers of the HIP kernels (one translation unit each) and the
+// workspace layouts shared between the size queries and the launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace cfm {
+
+int launch_sketch_build(const uint16_t* w_gate, const uint16_t* w_up, int E, int I, int H,
+                        const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- low-rank map
+struct LowrankPlan {
+  int p;          // subspace block width (rank + oversampling, padded to even)
+  int iters;      // subspace iterations
+  size_t off_gram, off_q, off_y, off_v, bytes;
+};
+LowrankPlan lowrank_plan(int E, int I, int H, int r);
+int launch_lowrank_build(const uint16_t* w_down_t, int E, int I, int H, int r, uint16_t* A,
+                         uint16_t* Bt, void* ws, const LowrankPlan& plan, hipStream_t stream);
+
+// ---------------------------------------------------------------- forward passes
+struct ForwardPlan {
+  int T, K, P, E, I, H, k, c, r;
+  int nch;        // screen workgroups per pair
+  int cw;         // channels per screen workgroup
+  int nex;        // exact-score workgroups per pair
+  int per_ex;     // candidates per exact-score workgroup
+  int nhs;        // 64-column output slices per token
+  size_t off_hhat, off_zpart, off_zsum, off_cand, off_hc, off_keep, off_hk, off_z, off_ypart;
+  size_t off_ctr_screen, off_ctr_exact, off_ctr_down, bytes;
+};
+ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r);
+ForwardPlan dense_plan(int T, int K, int E, int I, int H);
+
+struct SelectArgs {
+  const uint16_t *x, *w_gate, *w_up, *w_down_t, *A, *Bt;
+  const int32_t* ids;
+  const float* topk_w;
+  const int8_t* signs;
+  const uint8_t *tg, *tu;
+  const float *sg, *su;
+  uint16_t* out;
+  int32_t *cand_out, *keep_out;
+  void* stats;
+  char* ws;
+};
+int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
+int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
+
+}  // namespace cfm

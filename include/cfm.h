@@ -1,0 +1,180 @@
+/*
+ * cfm.h - C ABI of the channel-selected routed-expert SwiGLU FFN for MI355X (gfx950).
+ *
+ * The method: arXiv:2610.37386, "Channel Selection for Mixture-of-Experts
+ * Decoding Needs No Calibration Data" (abstract), and the aimodeling.com
+ * article on it (section "A reader that needs no data at all"). Each routed
+ * (token, expert) pair screens its expert's intermediate channels with a
+ * resident rotated ternary sketch of W_gate / W_up, keeps the top-k channels by
+ * exact BF16 gate/up activations (top-k, no calibrated threshold), runs the down
+ * projection over those k channels only, and adds back the skipped channels
+ * through a rank-r map of W_down built offline from the weights.
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers, allocated and owned by the
+ *     caller; the library keeps no device state and allocates no memory,
+ *     except where an entry point says otherwise.
+ *   - BF16 values are passed as raw 16-bit patterns (cfm_bf16).
+ *   - Layouts are row-major and dense. E experts, I intermediate channels per
+ *     expert, H hidden width, T tokens, K experts per token, P = T*K pairs.
+ *     Expert weights are [E][I][H]; the down projection is passed
+ *     channel-major (w_down_t[e][j][:] is column j of W_down), so every
+ *     channel's weights are one contiguous H-row.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call except
+ *     lowrank_build only enqueues work and returns without waiting.
+ *   - Return value: CFM_OK or a negative status; cfm_last_error() gives a
+ *     message (thread-local). Argument errors are detected on the host before
+ *     anything is enqueued. Asynchronous device faults surface at the next
+ *     synchronisation, as with any HIP call.
+ *   - Not checked (preconditions): router ids in [0, E) and distinct within a
+ *     token; finite inputs; buffers of the documented sizes.
+ */
+#ifndef CFM_H_
+#define CFM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t cfm_bf16;
+
+enum {
+  CFM_OK = 0,
+  CFM_EINVAL = -1,        /* null pointer where one is required, negative or zero sizes */
+  CFM_EUNSUPPORTED = -2,  /* shape or budget outside the supported range (see each call) */
+  CFM_EWORKSPACE = -3,    /* workspace missing or smaller than the size query returns */
+  CFM_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* cfm_last_error(void);
+
+/* Library version string. */
+const char* cfm_version(void);
+
+/*
+ * sketch_build - rotated ternary sketch of every expert's gate and up rows.
+ * (article section "A reader that needs no data at all": a rotated ternary
+ * sketch of each expert's gate and up projections, resident on the GPU,
+ * used to screen candidate channels.)
+ *
+ * For every row w (one channel of W_gate or W_up):
+ *   w~ = Hadamard_H * (signs (.) w)     unnormalised Sylvester-Hadamard, float64
+ *   delta = 0.7 * mean_i |w~_i|          Ternary Weight Networks threshold
+ *   t_i = +1 if w~_i > delta, -1 if w~_i < -delta, else 0
+ *   scale = float32( mean_{t_i != 0} |w~_i| / H )   (0 if no t_i is nonzero)
+ *
+ *   w_gate, w_up : [E][I][H] BF16.
+ *   signs        : [H] int8, each +1 or -1; the layer's rotation; the same
+ *                  vector must be passed to moe_select_forward.
+ *   tg, tu       : out [E][I][H/4] bytes, 2 bits per value. Per row, value
+ *                  16b+q and value 16b+8+q (q < 8) share nibble q of the
+ *                  little-endian 32-bit word b: bit 4q+0 = (t[16b+8+q] != 0),
+ *                  bit 4q+1 = (t[16b+q] != 0), bit 4q+2 = (t[16b+8+q] < 0),
+ *                  bit 4q+3 = (t[16b+q] < 0). (word & 0xAAAAAAAA) is then the
+ *                  FP4 E2M1 encoding of values 16b..16b+7, and
+ *                  ((word << 1) & 0xAAAAAAAA) that of values 16b+8..16b+15.
+ *   sg, su       : out [E][I] float32 scales.
+ * Supported: H a power of two, 64 <= H <= 8192; E, I >= 1.
+ * Sizes: tg/tu E*I*H/4 bytes each (H/4 bytes per row).
+ */
+int sketch_build(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H,
+                 const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,
+                 void* stream);
+
+/*
+ * lowrank_build - rank-r map of every expert's down projection.
+ * (article section "A reader that needs no data at all": the skipped
+ * channels are recovered through a low-rank map of the down projections,
+ * built from the weights alone.)
+ *
+ * Computes the rank-r truncated SVD W_down ~ A * Bt^T per expert, with
+ * A = W_down V_r = U_r diag(s_r) and Bt = V_r (orthonormal columns), both
+ * rounded to BF16. Computed on the device in float64: Gram matrix
+ * W_down^T W_down, block subspace iteration with oversampling and a
+ * Rayleigh-Ritz step. Each column of V_r is signed so that its
+ * largest-magnitude entry is positive.
+ *
+ *   w_down_t : [E][I][H] BF16 (channel-major W_down).
+ *   A        : out [E][H][r] BF16.   Bt : out [E][I][r] BF16.
+ *   ws       : device workspace of at least lowrank_workspace(E, I, H, r) bytes.
+ * Supported: 0 <= r <= min(H, I), r <= 128, H <= 8192, I <= 8192.
+ * Synchronises `stream` before returning (offline call).
+ */
+size_t lowrank_workspace(int E, int I, int H, int r);
+int lowrank_build(const cfm_bf16* w_down_t, int E, int I, int H, int r, cfm_bf16* A,
+                  cfm_bf16* Bt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_select_forward - the selected-channel MoE layer for a decode batch.
+ * (abstract: top-k keeps each token's k highest-scoring channels and reads
+ * only their weights; article section "A reader that needs no data at all":
+ * sketch screen, exact top-k from the BF16 weights, low-rank recovery.)
+ *
+ * For each pair (t, q) with e = topk_ids[t][q]:
+ *   x~ = Hadamard_H (signs (.) x[t]); ghat_j = sg[e][j] (t^g_j . x~),
+ *   uhat_j = su[e][j] (t^u_j . x~), hhat_j = SiLU(ghat_j) uhat_j  (all j < I)
+ *   C = the c channels with largest |hhat_j| (ties: lower j)
+ *   h_j = SiLU(Wg[e][j] . x[t]) (Wu[e][j] . x[t]) for j in C (BF16 weights,
+ *         float32 accumulation)
+ *   S = the k channels of C with largest |h_j| (ties: lower j)
+ *   y = sum_{j in S} h_j Wd_t[e][j] + A[e] (sum_{j not in S} hhat_j Bt[e][j])
+ * out[t] = BF16( sum_q topk_w[t][q] y_(t,q) )  (weights used as given).
+ *
+ *   x        : [T][H] BF16 hidden states.
+ *   topk_ids : [T][K] int32 router choices. topk_w : [T][K] float32.
+ *   w_gate, w_up, w_down_t : [E][I][H] BF16.
+ *   signs, tg, tu, sg, su  : the layer's sketch from sketch_build.
+ *   A [E][H][r], Bt [E][I][r] : the map from lowrank_build (ignored if r = 0).
+ *   out      : out [T][H] BF16.
+ *   cand_out : optional out [T*K][c] int32, C of each pair in ascending order.
+ *   keep_out : optional out [T*K][k] int32, S of each pair in ascending order.
+ *   stats    : optional out, device cfm_stats (bytes the call reads).
+ *   ws       : device workspace of at least select_workspace(...) bytes. It
+ *              must be zero-filled once after allocation; every call leaves it
+ *              ready for the next. Calls sharing a workspace must not overlap.
+ * Supported: H a power of two, 64 <= H <= 8192; 1 <= I <= 8192;
+ *            0 <= k <= c <= I; 0 <= r <= min(H, I), r <= 128; K <= 64.
+ *            T = 0 is a no-op.
+ */
+typedef struct {
+  uint64_t bytes_sketch;       /* packed sketch + scales of the routed experts */
+  uint64_t bytes_candidates;   /* BF16 gate + up rows of the candidates */
+  uint64_t bytes_down;         /* BF16 down rows of the kept channels */
+  uint64_t bytes_recovery;     /* A and Bt of the routed experts */
+  uint64_t bytes_io;           /* x, router output, out */
+  uint64_t bytes_dense_equiv;  /* what the dense layer reads for the same routing */
+  uint32_t experts_used, rows_candidates, rows_down, pad;
+} cfm_stats;
+
+size_t select_workspace(int T, int K, int E, int I, int H, int k, int c, int r);
+int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                       const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                       const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                       const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, cfm_bf16* out,
+                       int32_t* cand_out, int32_t* keep_out, cfm_stats* stats, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moe_dense_forward - the same routed-expert SwiGLU layer reading every channel
+ * (the comparator the method is measured against: abstract, "MoE blocks ...
+ * faster than optimized vLLM").
+ *   out[t] = BF16( sum_q w[t][q] sum_j SiLU(Wg[e][j].x) (Wu[e][j].x) Wd_t[e][j] )
+ * Arguments as in moe_select_forward. Same workspace rules.
+ * Supported: 64 <= H <= 8192 (multiple of 64), 1 <= I <= 8192, K <= 64.
+ */
+size_t dense_workspace(int T, int K, int E, int I, int H);
+int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                      int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                      const cfm_bf16* w_down_t, int E, int I, int H, cfm_bf16* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFM_H_ */

@@ -1,0 +1,319 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bars (see tests/parity.py): packed sketches and scales bit-exact; candidate and
+kept index sets equal to the oracle's up to near-ties at the boundary; BF16
+outputs within 2e-2 relative L2 per token. The forward tests give the library
+the oracle's low-rank map, so the forward kernels are checked in isolation;
+the library's own map is checked by Eckart-Young optimality and end to end.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cfm_oracle as O
+from gpu_util import (custom_workload, dev, down_bf16, log, oracle_map, up, up_bf16, upload)
+from parity import OUT_TOL, check_topset, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cfm():
+    import calibration_free_channel_amd as m
+    return m
+
+
+def gpu_sketch(cfm, L):
+    tg, tu, sg, su = cfm.sketch_build(L.wg, L.wu, L.signs)
+    torch.cuda.synchronize()
+    return tg, tu, sg, su
+
+
+def run_select(cfm, L, sk, A, Bt, k, c, r, stats=False):
+    T, K = L.host.ids.shape
+    cand = torch.empty((max(T * K, 1), max(c, 1)), dtype=torch.int32, device=dev())
+    keep = torch.empty((max(T * K, 1), max(k, 1)), dtype=torch.int32, device=dev())
+    st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device=dev()) if stats else None
+    out = cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, k, c, r,
+                                 cand_out=cand if c > 0 else None, keep_out=keep if k > 0 else None,
+                                 stats=st)
+    torch.cuda.synchronize()
+    res = (down_bf16(out), cand.cpu().numpy()[:, :c], keep.cpu().numpy()[:, :k])
+    return res + ((cfm.decode_stats(st),) if stats else ())
+
+
+def compare_forward(L, A_bits, Bt_bits, got, cand, keep, k, c, tokens=None, what=""):
+    """Oracle run on the host inputs (its own sketch) vs the library's results."""
+    h = L.host
+    T, K = h.ids.shape
+    tokens = list(range(T)) if tokens is None else list(tokens)
+    used = sorted(set(int(e) for t in tokens for e in h.ids[t]))
+    E, I, H = h.w_gate.shape
+    tg, tu, sg, su = O.sketch_build(h.w_gate[used], h.w_up[used], h.signs)
+    # scatter back to full-E arrays (only the used experts are read)
+    def full(a):
+        z = np.zeros((E,) + a.shape[1:], a.dtype)
+        z[used] = a
+        return z
+    tg, tu, sg, su = full(tg), full(tu), full(sg), full(su)
+    out, pairs = O.select_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su,
+                                  h.signs, A_bits, Bt_bits, k, c, tokens=tokens)
+    exact_tokens, errs = 0, []
+    for n, t in enumerate(tokens):
+        same = True
+        for q in range(K):
+            pr = pairs[(t, q)]
+            p = t * K + q
+            s1 = check_topset(cand[p], np.arange(I), np.abs(pr["hhat"]), c, f"{what} C(t={t},q={q})")
+            s2 = check_topset(keep[p], cand[p], np.abs(pr["h_all"][cand[p]]), k, f"{what} S(t={t},q={q})")
+            same &= s1 and s2
+        if same:
+            exact_tokens += 1
+            err = rel_l2(got[t], out[n])
+            errs.append(err)
+            assert err <= OUT_TOL, f"{what}: token {t} relative L2 {err:.3e}"
+    log(f"{what}: {exact_tokens}/{len(tokens)} tokens with identical sets; max rel L2 "
+        f"{max(errs) if errs else float('nan'):.3e}")
+    assert exact_tokens >= max(1, int(0.8 * len(tokens)))
+    return max(errs) if errs else 0.0
+
+
+# ----------------------------------------------------------------------------- sketch
+
+SKETCH_SHAPES = [
+    custom_workload("tinyish", 8, 2, 128, 256, 1, 23, 46, 8, 0, chan_scale=False),
+    custom_workload("ragged", 6, 3, 101, 128, 5, 17, 33, 6, 5),
+    custom_workload("h64", 3, 2, 40, 64, 3, 4, 9, 3, 6),
+    custom_workload("hmax", 2, 2, 24, 8192, 2, 3, 6, 2, 7),
+]
+
+
+@pytest.mark.parametrize("wl", SKETCH_SHAPES, ids=lambda w: w.name)
+def test_sketch_bitwise(cfm, wl):
+    log(f"sketch {wl.name}")
+    L = upload(wl)
+    tg, tu, sg, su = gpu_sketch(cfm, L)
+    otg, otu, osg, osu = O.sketch_build(L.host.w_gate, L.host.w_up, L.host.signs)
+    assert np.array_equal(tg.cpu().numpy(), otg)
+    assert np.array_equal(tu.cpu().numpy(), otu)
+    assert np.array_equal(sg.cpu().numpy().view(np.uint32), osg.view(np.uint32))
+    assert np.array_equal(su.cpu().numpy().view(np.uint32), osu.view(np.uint32))
+
+
+def test_sketch_round_trip_gpu(cfm):
+    """Exactly ternary rotated rows: the library's sketch returns the ternary pattern, scale 1."""
+    H, I = 256, 64
+    r = np.random.default_rng(21)
+    d = np.where(r.integers(0, 2, H) == 1, -1, 1).astype(np.int8)
+    t = r.integers(-1, 2, size=(2, I, H)).astype(np.int8)
+    hm = O.hadamard(H)
+    w = d * (t.astype(np.float64) @ hm)          # integers |.| <= H: BF16-exact
+    bits = O.f64_to_bf16(w)
+    tg, tu, sg, su = cfm.sketch_build(up_bf16(bits[:1]), up_bf16(bits[1:]), up(d))
+    torch.cuda.synchronize()
+    assert np.array_equal(O.unpack_codes(tg.cpu().numpy()[0]), t[0])
+    assert np.array_equal(O.unpack_codes(tu.cpu().numpy()[0]), t[1])
+    assert np.all(sg.cpu().numpy() == 1.0) and np.all(su.cpu().numpy() == 1.0)
+
+
+# ----------------------------------------------------------------------------- forward, small
+
+SMALL = [
+    synth.WORKLOADS["tiny"],
+    custom_workload("ragged", 6, 3, 101, 128, 5, 17, 33, 6, 5),
+    custom_workload("batch7", 8, 2, 128, 256, 7, 23, 46, 8, 8),
+    custom_workload("h64", 3, 2, 40, 64, 3, 4, 9, 3, 6),
+    custom_workload("hmax", 2, 2, 24, 8192, 2, 3, 6, 2, 7),
+    custom_workload("imax", 1, 1, 8192, 64, 1, 1474, 2948, 8, 9, rmsnorm=False),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_select_parity_small(cfm, wl):
+    log(f"select {wl.name}")
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, sorted(set(L.host.ids.reshape(-1).tolist())), E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, what=wl.name)
+
+
+@pytest.mark.parametrize("kc", [(0, 0), (0, 40), (128, 128), (5, 128), (46, 46), (1, 1)])
+@pytest.mark.parametrize("r", [0, 8])
+def test_select_budget_edges(cfm, kc, r):
+    k, c = kc
+    wl = custom_workload(f"edge_k{k}_c{c}_r{r}", 8, 2, 128, 256, 3, k, c, r, 11)
+    log(f"select {wl.name}")
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, r, range(E), E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), k, c, r)
+    compare_forward(L, A, Bt, got, cand, keep, k, c, what=wl.name)
+
+
+def test_select_full_rank_recovery_only(cfm):
+    """k = 0 and r = min(H, I): every channel enters through the map (y = W_down hhat)."""
+    wl = custom_workload("fullrank", 4, 2, 64, 128, 2, 0, 0, 64, 12)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, 64, range(4), 4, 64, 128)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), 0, 0, 64)
+    compare_forward(L, A, Bt, got, cand, keep, 0, 0, what="fullrank")
+
+
+def test_empty_batch_is_noop(cfm):
+    wl = custom_workload("empty", 4, 2, 64, 128, 0, 5, 10, 4, 13)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A = torch.zeros((4, 128, 4), dtype=torch.bfloat16, device=dev())
+    Bt = torch.zeros((4, 64, 4), dtype=torch.bfloat16, device=dev())
+    out = cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, 5, 10, 4)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+
+
+def test_all_kept_equals_dense_on_gpu(cfm):
+    """k = c = I, r = 0: the selected layer reads every channel and must equal the dense kernel bit for bit."""
+    wl = custom_workload("allkept", 8, 2, 128, 256, 4, 128, 128, 0, 14)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    got, _, _ = run_select(cfm, L, sk, None, None, 128, 128, 0)
+    dense = down_bf16(cfm.moe_dense_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd))
+    assert np.array_equal(got, dense)
+
+
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], custom_workload("ragged", 6, 3, 101, 128, 5, 17, 33, 6, 5),
+                                custom_workload("hmax", 2, 2, 24, 8192, 2, 3, 6, 2, 7)], ids=lambda w: w.name)
+def test_dense_parity(cfm, wl):
+    L = upload(wl)
+    got = down_bf16(cfm.moe_dense_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd))
+    h = L.host
+    want = O.dense_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t)
+    for t in range(h.ids.shape[0]):
+        assert rel_l2(got[t], want[t]) <= OUT_TOL
+
+
+def test_determinism_and_batch_invariance(cfm):
+    wl = custom_workload("inv", 8, 2, 128, 256, 8, 23, 46, 8, 15)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, 8, range(8), 8, 128, 256)
+    A, Bt = up_bf16(A), up_bf16(Bt)
+    a = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
+    b = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    # token 3 alone
+    one = cfm.moe_select_forward(L.x[3:4].contiguous(), L.ids[3:4].contiguous(), L.w[3:4].contiguous(),
+                                 L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, 23, 46, 8)
+    assert np.array_equal(down_bf16(one)[0], a[0][3])
+
+
+def test_stats_counts(cfm):
+    wl = synth.WORKLOADS["tiny"]
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A = torch.zeros((8, 256, 8), dtype=torch.bfloat16, device=dev())
+    Bt = torch.zeros((8, 128, 8), dtype=torch.bfloat16, device=dev())
+    *_, st = run_select(cfm, L, sk, A, Bt, 23, 46, 8, stats=True)
+    total = sum(st[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
+    assert total == O.read_bytes(L.host.ids, 8, 128, 256, 23, 46, 8)
+    assert st["bytes_dense_equiv"] == O.dense_bytes(L.host.ids, 8, 128, 256)
+
+
+# ----------------------------------------------------------------------------- low-rank map
+
+def _eckart_young_excess(wd_bits, A_bits, Bt_bits, r):
+    W = O.bf16_to_f64(wd_bits).T                      # H x I
+    A, Bt = O.bf16_to_f64(A_bits), O.bf16_to_f64(Bt_bits)
+    ev = np.sort(np.linalg.eigvalsh(W.T @ W))[::-1]
+    opt = max(ev[r:].sum(), 0.0)
+    resid = np.sum((W - A @ Bt.T) ** 2)
+    return (resid - opt) / max(ev.sum(), 1e-300), Bt
+
+
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], custom_workload("ragged", 6, 3, 101, 128, 5, 17, 33, 6, 5),
+                                custom_workload("rfull", 3, 2, 64, 128, 1, 4, 8, 64, 16)], ids=lambda w: w.name)
+def test_lowrank_optimality(cfm, wl):
+    L = upload(wl)
+    A, Bt = cfm.lowrank_build(L.wd, wl.r)
+    torch.cuda.synchronize()
+    A, Bt = down_bf16(A), down_bf16(Bt)
+    for e in range(wl.shape.E):
+        excess, B = _eckart_young_excess(L.host.w_down_t[e], A[e], Bt[e], wl.r)
+        assert excess <= 1e-2, f"expert {e}: residual above the optimum by {excess:.2e} of ||W||^2"
+        assert np.allclose(B.T @ B, np.eye(wl.r), atol=2e-2)
+
+
+def test_lowrank_end_to_end_tiny(cfm):
+    """The library's own map in the forward pass, against the oracle with the oracle's map."""
+    wl = synth.WORKLOADS["tiny"]
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A, Bt = cfm.lowrank_build(L.wd, wl.r)
+    got, cand, keep = run_select(cfm, L, sk, A, Bt, wl.k, wl.c, wl.r)
+    Ao, Bo = oracle_map(L.host.w_down_t, wl.r, range(8), 8, 128, 256)
+    compare_forward(L, Ao, Bo, got, cand, keep, wl.k, wl.c, what="tiny/own-map")
+
+
+# ----------------------------------------------------------------------------- full-size configurations
+
+@pytest.fixture(scope="module")
+def q18_layer():
+    wl = synth.WORKLOADS["q18_b1"]
+    log("generating the Qwen3-30B-A3B-shaped layer")
+    return upload(wl)
+
+
+def test_q18_b1_full_size(cfm, q18_layer):
+    """Qwen3-30B-A3B-shaped layer (H 2048, E 128, K 8, I 768), batch 1, k 138, c 276, r 64."""
+    L, wl = q18_layer, q18_layer.wl
+    E, I, H = L.host.w_gate.shape
+    used = sorted(set(L.host.ids.reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    # sketch of the routed experts: bit-exact
+    otg, otu, osg, osu = O.sketch_build(L.host.w_gate[used], L.host.w_up[used], L.host.signs)
+    assert np.array_equal(sk[0].cpu().numpy()[used], otg)
+    assert np.array_equal(sk[1].cpu().numpy()[used], otu)
+    assert np.array_equal(sk[2].cpu().numpy()[used].view(np.uint32), osg.view(np.uint32))
+    assert np.array_equal(sk[3].cpu().numpy()[used].view(np.uint32), osu.view(np.uint32))
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, what="q18_b1")
+    # the library's own map on the routed experts: near-optimal
+    Ag, Bg = cfm.lowrank_build(L.wd, wl.r)
+    torch.cuda.synchronize()
+    Ag, Bg = down_bf16(Ag), down_bf16(Bg)
+    for e in used[:3]:
+        excess, _ = _eckart_young_excess(L.host.w_down_t[e], Ag[e], Bg[e], wl.r)
+        assert excess <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["q13_b8", "q13_b16", "q18_b16"])
+def test_batched_full_size(cfm, name):
+    wl = synth.WORKLOADS[name]
+    log(f"generating {name}")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    tokens = [0, wl.T // 2, wl.T - 1]
+    used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=name)
+
+
+def test_olmoe_b64_full_size(cfm):
+    wl = synth.WORKLOADS["olmoe_b64"]
+    log("generating the OLMoE-shaped layer")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    tokens = [0, 31, 63]
+    used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what="olmoe_b64")
