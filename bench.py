@@ -1,0 +1,289 @@
+"""Benchmark of the selected-channel routed-expert SwiGLU layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
+
+Workload: a Qwen3-30B-A3B-shaped MoE layer (H 2048, 128 experts, top-8,
+SwiGLU intermediate 768, BF16 weights ~N(0, 0.02) times a per-channel
+LogNormal(0, 0.5) factor), decode batch 1, read budget k = 138 (18 % of I),
+c = 276 candidates, rank r = 64. One step is one call of moe_select_forward
+(the whole hot path: screen, exact top-k, down over kept channels, low-rank
+recovery, combine) for one fresh token. Steps cycle over a ring of L
+independently drawn layers, so every step streams weights that are not
+resident in the 256 MiB last-level cache, as in a real decode step through a
+48-layer model. Inputs are resident in HBM before the timed region; the K
+timed steps are one replay of a HIP graph holding K distinct calls.
+
+Prints one JSON line on stdout (logs go to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer µs/token + achieved HBM GB/s at 18% read budget, batch 1/8/16"
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8, help="ring of independently drawn layers")
+    ap.add_argument("--batches", default="1,8,16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--seed", type=int, default=1)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- inputs on the device
+
+def make_layer(torch, seed, layer, E, I, H, sigma=0.02, chan_scale=True):
+    """Synthetic BF16 expert weights drawn on the device (same recipe as synth/)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed * 100003 + layer)
+    mats = []
+    for _ in range(3):
+        w = torch.randn((E, I, H), generator=g, device="cuda", dtype=torch.float32).mul_(sigma)
+        if chan_scale:
+            s = torch.randn((E, I, 1), generator=g, device="cuda", dtype=torch.float32).mul_(0.5).exp_()
+            w.mul_(s)
+        mats.append(w.to(torch.bfloat16))
+        del w
+    bits = torch.randint(0, 2, (H,), generator=g, device="cuda", dtype=torch.int8)
+    signs = (1 - 2 * bits).to(torch.int8)
+    return mats[0], mats[1], mats[2], signs
+
+
+def make_tokens(torch, seed, n, T, E, K, H):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed * 7919 + 17)
+    z = torch.randn((n, T, H), generator=g, device="cuda", dtype=torch.float32)
+    z = z * torch.rsqrt(z.pow(2).mean(-1, keepdim=True) + 1e-6)
+    x = z.to(torch.bfloat16)
+    logits = torch.randn((n, T, E), generator=g, device="cuda", dtype=torch.float32)
+    p = torch.softmax(logits, dim=-1)
+    w, ids = torch.topk(p, K, dim=-1)
+    return x.contiguous(), ids.to(torch.int32).contiguous(), w.contiguous()
+
+
+# ----------------------------------------------------------------------------- GPU measurement
+
+def timed_graph(torch, fn, n_steps):
+    """Capture fn(i) for i < n_steps in one graph; return (ms for one replay, wall ms)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_steps):
+            fn(i)
+    g.replay()                      # first replay: untimed (graph upload)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return e0.elapsed_time(e1), wall
+
+
+def kernel_times(torch, cfm, fn, n_steps):
+    """Average duration of each library kernel (HIP events around every launch,
+    host kept ahead of the GPU so the events bracket only device work)."""
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    cfm.timing_enable(True)
+    for i in range(n_steps):
+        fn(i)
+    cfm.timing_enable(False)
+    rep = cfm.timing_report()
+    return {k: v[1] / v[0] for k, v in rep.items()}
+
+
+def cpu_baseline(wl_name="q18_b1", target_s=10.0):
+    """The CPU oracle on a bounded sample of the same workload (per-token forward)."""
+    import numpy as np
+    import threadpoolctl
+
+    import synth
+    from oracle import cfm_oracle as O
+
+    wl = synth.WORKLOADS[wl_name]
+    s = wl.shape
+    ids, w = synth.routing(2, s.E, s.K, wl.seed + 101, 0)
+    x = synth.hidden_states(2, s.H, wl.seed + 101, 0, rmsnorm=True)
+    used = sorted(set(int(e) for e in ids.reshape(-1)))
+    local = {e: n for n, e in enumerate(used)}
+    ids_l = np.vectorize(local.get)(ids).astype(np.int32)
+    wg, wu, wd = synth.layer_weights(s, wl.seed, 0, experts=used)
+    signs = synth.rotation_signs(s.H, wl.seed, 0)
+    tg, tu, sg, su = O.sketch_build(wg, wu, signs)          # offline steps: not timed
+    A, Bt = O.lowrank_build(wd, wl.r)
+    info = threadpoolctl.threadpool_info()
+    cores = max([d.get("num_threads", 1) for d in info] + [1])
+    n_tok, t0 = 0, time.perf_counter()
+    while True:
+        O.select_forward(x, ids_l, w, wg, wu, wd, tg, tu, sg, su, signs, A, Bt, wl.k, wl.c)
+        n_tok += x.shape[0]
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    us_sel = el / n_tok * 1e6
+    t0 = time.perf_counter()
+    O.dense_forward(x, ids_l, w, wg, wu, wd)
+    us_dense = (time.perf_counter() - t0) / x.shape[0] * 1e6
+    return {"value": round(us_sel, 1), "unit": "us/token", "cores": int(cores), "kind": "oracle",
+            "sample": f"{wl_name}: 2 tokens x {n_tok // 2} repeats of the float64 numpy oracle forward "
+                      f"(screen, exact top-k, down, recovery, combine) over the tokens' "
+                      f"{len(used)} routed experts; sketch and low-rank map prepared untimed",
+            "dense_us_per_token": round(us_dense, 1)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is described in DESIGN.md but not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import calibration_free_channel_amd as cfm
+
+    torch.manual_seed(args.seed)
+    E, K, I, H = 128, 8, 768, 2048
+    k, c, r = 138, 276, 64
+    L = args.layers
+    log(f"building {L} Qwen3-30B-A3B-shaped layers on the device ...")
+    layers, t_sketch, t_lr = [], 0.0, 0.0
+    lr_ws = torch.empty(cfm.lowrank_workspace(E, I, H, r), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sk = cfm.sketch_build(wg, wu, signs)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        A, Bt = cfm.lowrank_build(wd, r, ws=lr_ws)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        t_sketch += t1 - t0
+        t_lr += t2 - t1
+        layers.append((wg, wu, wd, signs, sk, A, Bt))
+    del lr_ws
+    log(f"offline: sketch_build {t_sketch / L * 1e3:.1f} ms/layer, lowrank_build {t_lr / L * 1e3:.1f} ms/layer")
+
+    results = {}
+    batches = [int(b) for b in args.batches.split(",") if b]
+    for T in batches:
+        steps = args.steps if T == 1 else max(10, args.steps // 4)
+        n_tok = args.warmup + 2 * steps
+        x, ids, w = make_tokens(torch, args.seed + T, n_tok, T, E, K, H)
+        ws_s = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+        ws_d = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+        out = torch.empty((n_tok, T, H), dtype=torch.bfloat16, device="cuda")
+
+        def sel(i):
+            wg, wu, wd, signs, sk, A, Bt = layers[i % L]
+            cfm.moe_select_forward(x[i], ids[i], w[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
+                                   out=out[i], ws=ws_s)
+
+        def dense(i):
+            wg, wu, wd, *_ = layers[i % L]
+            cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=out[i], ws=ws_d)
+
+        for i in range(args.warmup):            # untimed warmup steps
+            sel(i)
+            dense(i)
+        torch.cuda.synchronize()
+        off = args.warmup
+        ms_sel, wall_sel = timed_graph(torch, lambda i: sel(off + i), steps)
+        ms_den, wall_den = timed_graph(torch, lambda i: dense(off + steps + i), steps)
+        kt_sel = kernel_times(torch, cfm, lambda i: sel(off + i), steps)
+        kt_den = kernel_times(torch, cfm, lambda i: dense(off + steps + i), steps)
+        st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+        wg, wu, wd, signs, sk, A, Bt = layers[0]
+        cfm.moe_select_forward(x[0], ids[0], w[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
+                               out=out[0], ws=ws_s, stats=st)
+        torch.cuda.synchronize()
+        stats = cfm.decode_stats(st)
+        bytes_sel = sum(stats[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down",
+                                           "bytes_recovery", "bytes_io"))
+        bytes_den = stats["bytes_dense_equiv"]
+        us_step = ms_sel / steps * 1e3
+        us_step_d = ms_den / steps * 1e3
+        results[T] = dict(steps=steps, us_per_step=us_step, us_per_token=us_step / T,
+                          gbps=bytes_sel / (us_step * 1e-6) / 1e9, bytes=bytes_sel,
+                          dense_us_per_token=us_step_d / T,
+                          dense_gbps=bytes_den / (us_step_d * 1e-6) / 1e9, dense_bytes=bytes_den,
+                          speedup=us_step_d / us_step, kernels_us={n: v * 1e3 for n, v in kt_sel.items()},
+                          dense_kernels_us={n: v * 1e3 for n, v in kt_den.items()},
+                          wall_ms=wall_sel, stats=stats)
+        log(f"B={T}: selected {us_step:.2f} us/step ({us_step / T:.2f} us/token, "
+            f"{results[T]['gbps']:.0f} GB/s on {bytes_sel / 1e6:.1f} MB), dense {us_step_d:.2f} us/step "
+            f"({results[T]['dense_gbps']:.0f} GB/s), speedup {results[T]['speedup']:.2f}x; kernels "
+            f"{ {n: round(v * 1e3, 2) for n, v in kt_sel.items()} }")
+        del ws_s, ws_d, out, x, ids, w
+
+    r1 = results[1]
+    # the whole hot path is one kernel: its algorithmic bytes per launch are the call's bytes
+    k_us = r1["kernels_us"].get("k_select_fused")
+    roof = None
+    if k_us:
+        ach = r1["bytes"] / (k_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_select_fused", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                "traffic": None, "bytes_per_launch": r1["bytes"], "avg_launch_us": round(k_us, 3)}
+    line = {
+        "metric": METRIC,
+        "value": round(r1["us_per_token"], 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": r1["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(r1["us_per_step"] / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped MoE layer, batch-1 decode (H 2048, E 128, "
+                               "top-8, I 768), 18% budget k=138 c=276 r=64",
+                   "global_batch": 1, "layers_in_ring": L, "seed": args.seed},
+        "hbm_GBps": round(r1["gbps"], 1),
+        "hbm_frac": round(r1["gbps"] / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": r1["bytes"],
+        "dense": {"us_per_token": round(r1["dense_us_per_token"], 3),
+                  "GBps": round(r1["dense_gbps"], 1), "bytes_per_step": r1["dense_bytes"]},
+        "speedup_vs_dense": round(r1["speedup"], 3),
+        "roofline": roof,
+        "kernels_us": {n: round(v, 3) for n, v in r1["kernels_us"].items()},
+        "dense_kernels_us": {n: round(v, 3) for n, v in r1["dense_kernels_us"].items()},
+        "batches": {str(T): {"us_per_token": round(v["us_per_token"], 3), "GBps": round(v["gbps"], 1),
+                             "dense_us_per_token": round(v["dense_us_per_token"], 3),
+                             "speedup_vs_dense": round(v["speedup"], 3), "bytes_per_step": v["bytes"]}
+                    for T, v in results.items()},
+        "offline_ms_per_layer": {"sketch_build": round(t_sketch / L * 1e3, 2),
+                                 "lowrank_build": round(t_lr / L * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

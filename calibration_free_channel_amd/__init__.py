@@ -7,5 +7,5 @@ raises ImportError: there is no CPU fallback.
 from ._lib import (  # noqa: F401
     CfmError, EXPORTED, STATS_BYTES, decode_stats, dense_workspace, last_error, lowrank_build,
     lowrank_workspace, moe_dense_forward, moe_select_forward, new_workspace, select_workspace,
-    sketch_build, version,
+    sketch_build, timing_enable, timing_report, version,
 )

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcfm.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m calibration_free_channel_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python calibration_free_channel_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _p = ctypes.c_void_p
@@ -35,6 +35,8 @@ _SIGS = {
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
     "dense_workspace": (_z, [_i, _i, _i, _i, _i]),
     "moe_dense_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _z, _p]),
+    "cfm_timing_enable": (_i, [_i]),
+    "cfm_timing_report": (_i, [ctypes.c_char_p, _z]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -175,6 +177,24 @@ def moe_dense_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, out=None, ws=
     _check(_lib.moe_dense_forward(
         _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
         E, I, H, _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), "moe_dense_forward")
+    return out
+
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events (instrumentation)."""
+    _lib.cfm_timing_enable(1 if on else 0)
+
+
+def timing_report() -> dict:
+    """{kernel name: (launches, total_ms)} since the last report; synchronises the events."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = _lib.cfm_timing_report(buf, len(buf))
+    if n < 0:
+        raise CfmError(n, "cfm_timing_report")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
     return out
 
 

@@ -1,6 +1,6 @@
 """Build libcfm.so (the HIP library behind include/cfm.h) in-tree for gfx950.
 
-    python -m calibration_free_channel_amd.build [-j N]
+    python calibration_free_channel_amd/build.py [-j N]
 
 Compiles every csrc/*.hip translation unit with hipcc and links them into
 calibration_free_channel_amd/libcfm.so. Always recompiles.

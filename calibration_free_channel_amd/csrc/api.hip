@@ -3,7 +3,10 @@
 // errors are reported the same way on machines without a GPU.
 #include <algorithm>
 #include <cstdio>
+#include <cstring>
+#include <map>
 #include <string>
+#include <vector>
 
 #include "cfm_internal.h"
 #include "cfm_launch.h"
@@ -17,6 +20,41 @@ int set_error(int code, const std::string& msg) {
   return code;
 }
 void clear_error() { g_last_error.clear(); }
+
+// ---------------------------------------------------------------- event timing
+namespace {
+struct Pending { std::string name; hipEvent_t a, b; };
+bool g_timing = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+std::string g_open;
+hipEvent_t g_open_ev = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) { hipEvent_t e = g_pool.back(); g_pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+bool timing_on() { return g_timing; }
+
+void timing_begin(const char* name, hipStream_t s) {
+  if (!g_timing) return;
+  g_open = name;
+  g_open_ev = take_event();
+  if (g_open_ev) hipEventRecord(g_open_ev, s);
+}
+
+void timing_end(hipStream_t s) {
+  if (!g_timing || !g_open_ev) return;
+  hipEvent_t b = take_event();
+  if (!b) return;
+  hipEventRecord(b, s);
+  g_pending.push_back({g_open, g_open_ev, b});
+  g_open_ev = nullptr;
+}
 
 namespace {
 
@@ -56,6 +94,38 @@ extern "C" {
 const char* cfm_last_error(void) { return g_last_error.c_str(); }
 
 const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
+
+int cfm_timing_enable(int on) {
+  g_timing = on != 0;
+  return CFM_OK;
+}
+
+int cfm_timing_report(char* buf, size_t len) {
+  std::map<std::string, std::pair<long, double>> acc;
+  for (auto& p : g_pending) {
+    if (hipEventSynchronize(p.b) != hipSuccess) return set_error(CFM_EHIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) return set_error(CFM_EHIP, "elapsed time failed");
+    auto& v = acc[p.name];
+    v.first += 1;
+    v.second += ms;
+    g_pool.push_back(p.a);
+    g_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  std::string out;
+  char line[256];
+  for (auto& kv : acc) {
+    snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (buf && len) {
+    const size_t n = std::min(len - 1, out.size());
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return (int)acc.size();
+}
 
 int sketch_build(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H,
                  const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,

@@ -16,6 +16,11 @@ namespace cfm {
 int set_error(int code, const std::string& msg);
 void clear_error();
 
+// Optional per-kernel event timing (cfm_timing_enable); no-ops while disabled.
+bool timing_on();
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
 #define CFM_HIP_TRY(expr)                                                             \
   do {                                                                                \
     hipError_t e_ = (expr);                                                           \

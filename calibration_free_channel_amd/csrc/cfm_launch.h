@@ -25,13 +25,13 @@ int launch_lowrank_build(const uint16_t* w_down_t, int E, int I, int H, int r, u
 // ---------------------------------------------------------------- forward passes
 struct ForwardPlan {
   int T, K, P, E, I, H, k, c, r;
-  int nch;        // screen workgroups per pair
-  int cw;         // channels per screen workgroup
-  int nex;        // exact-score workgroups per pair
-  int per_ex;     // candidates per exact-score workgroup
+  int nw;         // workgroups per routed pair
+  int G;          // grid size (<= one workgroup per compute unit)
+  int cw;         // channels screened per workgroup
+  int cpw;        // candidates (selected) or channels (dense) per workgroup in the exact phase
   int nhs;        // 64-column output slices per token
-  size_t off_hhat, off_zpart, off_zsum, off_cand, off_hc, off_keep, off_hk, off_z, off_ypart;
-  size_t off_ctr_screen, off_ctr_exact, off_ctr_down, bytes;
+  size_t lds;     // dynamic LDS bytes per workgroup
+  size_t off_hhat, off_zpart, off_hc, off_ypart, off_ctr, off_err, bytes;
 };
 ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r);
 ForwardPlan dense_plan(int T, int K, int E, int I, int H);

@@ -173,6 +173,17 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
                       const cfm_bf16* w_down_t, int E, int I, int H, cfm_bf16* out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Instrumentation (not part of the method). While enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the
+ * launch stream. cfm_timing_report synchronises those events, writes one line
+ * per kernel name, "<name> <launches> <total_ms>\n", into buf (NUL-terminated,
+ * truncated to len), clears the record and returns the number of kernel names
+ * (or a negative status). Host-side state only; not thread-safe.
+ */
+int cfm_timing_enable(int on);
+int cfm_timing_report(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

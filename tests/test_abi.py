@@ -23,7 +23,7 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def lib():
-    assert os.path.exists(LIB), "libcfm.so not built (python -m calibration_free_channel_amd.build)"
+    assert os.path.exists(LIB), "libcfm.so not built (python calibration_free_channel_amd/build.py)"
     return ctypes.CDLL(LIB)
 
 
