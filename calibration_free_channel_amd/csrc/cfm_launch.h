@@ -23,6 +23,10 @@ int launch_lowrank_build(const uint16_t* w_down_t, int E, int I, int H, int r, u
                          uint16_t* Bt, void* ws, const LowrankPlan& plan, hipStream_t stream);
 
 // ---------------------------------------------------------------- forward passes
+// Workspace of a forward pass. The first three regions sit at the same offsets
+// in the selected and the dense layouts, so one zeroed buffer can serve both:
+// per-workgroup launch sequence numbers (the tag of exchanged values), the
+// failed-launch word and the combine counters. Then the exchange buffers.
 struct ForwardPlan {
   int T, K, P, E, I, H, k, c, r;
   int nw;         // workgroups per routed pair
@@ -31,7 +35,10 @@ struct ForwardPlan {
   int cpw;        // candidates (selected) or channels (dense) per workgroup in the exact phase
   int nhs;        // 64-column output slices per token
   size_t lds;     // dynamic LDS bytes per workgroup
-  size_t off_hhat, off_zpart, off_hc, off_ypart, off_ctr, off_err, bytes;
+  size_t off_seq, off_err, off_ctr;      // u32 [256], u32, u32 [T][nhs]
+  size_t off_xh, off_xz, off_xc;         // tagged u64 [P][I], [P][nw][r], [P][c]
+  size_t off_ypart;                      // f32 [P][H]
+  size_t bytes;
 };
 ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r);
 ForwardPlan dense_plan(int T, int K, int E, int I, int H);

@@ -1,29 +1,33 @@
 // Forward passes as single persistent kernels (gfx950): the selected-channel
 // routed-expert SwiGLU layer and the dense comparator.
 //
-// Selected layer, per routed (token, expert) pair (arXiv:2610.37386 abstract;
+// Selected layer, per routed (token, expert) pair (arXiv:2610.37386, abstract;
 // aimodeling.com article, section "A reader that needs no data at all"):
-//   phase A  screen: x~ = Hadamard (signs . x) exactly in float64, fixed point,
-//            FP8 base-16 digits; sketch activations hhat_j of this workgroup's
-//            channels from FP4 ternary rows x FP8 digits on MFMA (exact integer
-//            dot products); partial recovery sums over its channels;
-//   phase B  top-c candidates (every workgroup of the pair, identically), exact
-//            BF16 gate / up dot products over its share of the candidates;
+//   phase A  screen: x~ = Hadamard(d . x) exactly in fixed point, split into
+//            base-16 digit planes (FP8 operands); sketch activations hhat_j of
+//            this workgroup's channels from the FP4 ternary rows on the matrix
+//            cores (exact integer dot products); partial recovery sums over
+//            this workgroup's channels;
+//   phase B  top-c candidates (every workgroup of the pair, identically) and
+//            the exact BF16 gate / up dot products of this workgroup's share;
 //   phase C  top-k kept set, recovery coefficients z, down projection over the
-//            kept rows of its 64-column output slice plus A z, and the token's
-//            router-weighted combine by the last of its K pairs to arrive.
+//            kept rows of this workgroup's 64-column output slices plus A z,
+//            and the token's router-weighted combine by the last of its K
+//            pairs to finish a slice.
 //
-// A pair is served by nw workgroups. They exchange hhat, partial recovery sums
-// and h through global memory with agent-coherent loads and stores (these
-// bypass the per-XCD L2, so no cache flush or invalidation is needed), and
-// meet at two per-pair phase counters (epoch in the high 16 bits, arrivals in
-// the low 16; the last arrival advances the epoch, so the counters reset
-// themselves). The grid never exceeds one workgroup per compute unit, so all
-// workgroups are co-resident; waits are bounded and raise an error flag.
-// Workgroup g serves pair g % P: with P a multiple of 8 all workgroups of a pair
+// A pair is served by nw workgroups, all resident at once (the grid never
+// exceeds one workgroup per compute unit). They exchange values through global
+// memory as 64-bit words (float, launch tag): the writer stores each value with
+// this launch's tag; a reader polls the word itself until the tag matches. No
+// counter, fence or cache flush is involved, and a value is read in one round
+// trip once it is there. Every wait is bounded: on expiry the launch records
+// its tag in the failure word and its outputs become NaN.
+//
+// The launch tag is one more than the sequence number in the workspace; each
+// workgroup reads its own slot at the start and every slot is rewritten at the
+// end, so all workgroups of a launch agree and tags never repeat (2^32 launches).
+// Workgroup g serves pair g % P: with P a multiple of 8 the workgroups of a pair
 // share an XCD (workgroups are dispatched round-robin over the 8 XCDs).
-// Everything a workgroup can fetch without knowing the selections (x, its
-// sketch rows, its Bt rows, its A slice) is requested at the start.
 //
 // The dense layer uses the same skeleton without the screen and selections.
 #include <algorithm>
@@ -36,37 +40,116 @@ namespace cfm {
 namespace {
 
 constexpr int NT = 256;                       // threads per workgroup
-constexpr int kSubChunk = 32;                 // channels per phase-A sub-chunk
-constexpr unsigned kSpinLimit = 1u << 22;     // bounded waits (seconds); then an error flag
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr int kSubChunk = 32;                 // channels per screen sub-chunk (4 MFMA tiles of 16 rows)
+constexpr int kPlanes = 6;                    // base-16 digit planes of the 24-bit fixed-point x~
+constexpr int kOnes = kPlanes;                // MFMA column of constant ones (row sums of the codes)
+constexpr int kDShift = 7;                    // x~ in units of 2^(7 - F0) before the digit split
+constexpr unsigned kSpinLimit = 1u << 20;     // polls of one exchanged value before the launch fails
+constexpr int kSeqSlots = 256;                // launch sequence slots (one per possible workgroup)
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ memory helpers
 
-__device__ __forceinline__ uint4 ld16(const void* p) {       // streamed weights
+__device__ __forceinline__ uint4 ld16(const void* p) {        // streamed weights
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint4 ld16c(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Cross-workgroup exchange: agent-coherent (L2-bypassing) scalar loads / stores.
-__device__ __forceinline__ void st_x(float* p, float v) {
+// Agent-coherent float stores / loads (bypass the non-coherent caches).
+__device__ __forceinline__ void st_f(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_x(const float* p) {
+__device__ __forceinline__ float ld_f(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned ld_ctr(unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t ld_u(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ tagged exchange
+
+__device__ __forceinline__ void put_tagged(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The value of *p once it carries `tag` (v: its first load). On expiry of the
+// bounded wait the launch is marked failed and 0 is returned.
+__device__ __forceinline__ float await_tagged(const uint64_t* p, uint64_t v, uint32_t tag, uint32_t* fail) {
+  for (unsigned it = 0; (uint32_t)(v >> 32) != tag; ++it) {
+    if (it >= kSpinLimit) {
+      st_u(fail, tag);
+      return 0.f;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = ld_tagged(p);
+  }
+  return __uint_as_float((uint32_t)v);
+}
+
 // Completes this wave's outstanding memory operations, then joins the workgroup.
 __device__ __forceinline__ void drain_and_join() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
+}
+
+// True in the workgroup that arrives last of `total` at *ctr (which it resets).
+__device__ __forceinline__ bool last_of(unsigned* ctr, unsigned total, int* s_flag) {
+  drain_and_join();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (old == total - 1);
+    if (old == total - 1) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// ------------------------------------------------------------------ wavefront primitives
+
+// Value of lane (lane ^ M): DPP quad permutes for 1 and 2, bank-masked row
+// shifts for 4, a row rotation for 8, and the gfx950 row / half swaps for 16
+// and 32; all are VALU operations (no LDS traffic).
+template <int M>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (M == 4) {
+    const int a = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
+    return __builtin_amdgcn_update_dpp(a, v, 0x114, 0xF, 0xA, false);
+  } else if constexpr (M == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+  else if constexpr (M == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? (int)s[0] : (int)s[1];
+  } else {
+    static_assert(M == 32, "lane masks 1..32");
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? (int)s[0] : (int)s[1];
+  }
+}
+
+// Sum over the 64 lanes (DPP row shifts and broadcasts), in every lane.
+__device__ __forceinline__ float wave_sum_f(float x) {
+  float v = x;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
@@ -90,48 +173,7 @@ __device__ __forceinline__ float dot8_f(const uint4& w, const float* z) {
          bf16lo(w.z) * z[4] + bf16hi(w.z) * z[5] + bf16lo(w.w) * z[6] + bf16hi(w.w) * z[7];
 }
 
-// ------------------------------------------------------------------ phase counters
-
-// Epoch of a phase counter; read by thread 0 before this workgroup arrives.
-__device__ __forceinline__ unsigned counter_epoch(unsigned* ctr) { return ld_ctr(ctr) >> 16; }
-
-__device__ __forceinline__ void arrive(unsigned* ctr, unsigned epoch, unsigned n) {
-  drain_and_join();
-  if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((old & 0xFFFFu) == n - 1)
-      __hip_atomic_store(ctr, ((epoch + 1) & 0xFFFFu) << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-__device__ __forceinline__ void wait_all(unsigned* ctr, unsigned epoch, unsigned n, int* err) {
-  if (threadIdx.x == 0) {
-    unsigned it = 0;
-    for (;;) {
-      const unsigned v = ld_ctr(ctr);
-      if ((v >> 16) != epoch || (v & 0xFFFFu) >= n) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++it > kSpinLimit) { atomicOr(err, 1); break; }
-    }
-  }
-  __syncthreads();
-}
-
-// True in the workgroup that arrives last of `total` at *ctr (which it resets).
-__device__ __forceinline__ bool last_of(unsigned* ctr, unsigned total, int* s_flag) {
-  drain_and_join();
-  if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = (old == total - 1);
-    if (old == total - 1) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// e4m3 encodings of the integers -8..7 (index d + 8)
-__constant__ uint8_t kE4M3Digit[16] = {0xD0, 0xCE, 0xCC, 0xCA, 0xC8, 0xC4, 0xC0, 0xB8,
-                                       0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E};
+// ------------------------------------------------------------------ arguments and LDS
 
 struct FusedArgs {
   const uint16_t* x; const int32_t* ids; const float* topk_w;
@@ -139,243 +181,260 @@ struct FusedArgs {
   const int8_t* signs; const uint8_t *tg, *tu; const float *sg, *su;
   const uint16_t *A, *Bt;
   uint16_t* out; int32_t *cand_out, *keep_out;
-  float* hhat;      // [P][I]  sketch activations (selected) / exact activations (dense)
-  float* zpart;     // [P][nw][r]
-  float* hc;        // [P][c]  exact activations of the candidates
-  float* ypart;     // [P][H]
-  unsigned* ctr;    // [P][2] phase counters, [T][nhs] combine counters
-  int* err;
+  uint32_t* seq;     // [256] launch sequence numbers
+  uint32_t* fail;    // tag of the last launch whose wait expired
+  unsigned* ctr;     // [T][nhs] combine counters
+  uint64_t* xh;      // [P][I]  sketch activations (selected) / exact activations (dense)
+  uint64_t* xz;      // [P][nw][r] partial recovery sums
+  uint64_t* xc;      // [P][c]  exact activations of the candidates
+  float* ypart;      // [P][H]
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
 };
 
-// ------------------------------------------------------------------ LDS layout (host and device)
-
 struct Lds {
-  double* xs;        // [H] x~ (float64) transpose buffer
-  uint8_t* limb;     // [6][Hp] FP8 digits of the fixed-point x~
-  float* hloc;       // [sub-chunk] sketch activations of the current channels
-  float* dsum;       // [ntile][16][8] digit partial dots
-  float* btc;        // [sub-chunk][r] Bt rows of the current channels (float)
-  float* hh;         // [I] hhat of the pair
-  uint32_t* keys;    // [max(I, c)]
-  int32_t* candp;    // [c] candidate channel ids
-  int32_t* sel;      // [max(c, k)]
-  int32_t* keep;     // [k] kept channel ids
-  float* hk;         // [k] kept activations
+  int32_t* xs;       // [max(H, 256)] rotation exchange
+  uint8_t* limb;     // [kPlanes][Hp] FP8 digit planes of x~
+  float* dsum;       // [64][8] per-row digit dots of a sub-chunk
+  float* hloc;       // [kSubChunk] sketch activations of the current sub-chunk
+  float* hh;         // [I] sketch (selected) / exact (dense) activations of the pair
+  int32_t* candp;    // [c] candidate channels
+  int32_t* sel;      // [k] positions of the kept channels among the candidates
+  int32_t* keep;     // [k] kept channels
+  float* hk;         // [k] their exact activations
   float* hcl;        // [c] exact activations of the candidates
-  float* zsum;       // [r]
+  float* zsum;       // [r] sum of the partial recovery sums
   float* zv;         // [r] recovery coefficients
-  float* red;        // [max(32*64+64, 32 r)] reduction scratch
-  float* gu;         // [2][cpw]
-  uint8_t* tks;      // top-k scratch
+  float* red;        // reduction scratch
+  float* gu;         // [2][cpw] gate / up dots of the exact phase
+  uint32_t* tks;     // top-k scratch
 };
 
-__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cw, int cpw,
-                                             size_t* off) {
+__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cpw, size_t* off) {
   size_t o = 0;
   int n = 0;
   auto take = [&](size_t b) { off[n++] = o; o = (o + b + 15) & ~size_t(15); };
   const int Hp = H > 256 ? H : 256;
-  cw = cw < kSubChunk ? cw : kSubChunk;       // phase A works in sub-chunks of channels
-  const int ntile = (2 * cw + 15) / 16;
-  const int ic = I > c ? I : c;
-  const int ck = c > k ? c : k;
-  const int r1 = r > 1 ? r : 1;
-  take(8 * (size_t)H);
-  take(6 * (size_t)Hp);
-  take(4 * (size_t)cw);
-  take(4 * (size_t)ntile * 128);
-  take(4 * (size_t)cw * r1);
+  const int c1 = c > 1 ? c : 1, k1 = k > 1 ? k : 1, r1 = r > 1 ? r : 1;
+  take(4 * (size_t)Hp);
+  take((size_t)kPlanes * Hp);
+  take(4 * 64 * 8);
+  take(4 * (size_t)kSubChunk);
   take(4 * (size_t)I);
-  take(4 * (size_t)ic);
-  take(4 * (size_t)(c > 1 ? c : 1));
-  take(4 * (size_t)(ck > 1 ? ck : 1));
-  take(4 * (size_t)(k > 1 ? k : 1));
-  take(4 * (size_t)(k > 1 ? k : 1));
-  take(4 * (size_t)(c > 1 ? c : 1));
+  take(4 * (size_t)c1);
+  take(4 * (size_t)k1);
+  take(4 * (size_t)k1);
+  take(4 * (size_t)k1);
+  take(4 * (size_t)c1);
   take(4 * (size_t)r1);
   take(4 * (size_t)r1);
-  const int nred = 32 * r1 > 32 * 64 + 64 ? 32 * r1 : 32 * 64 + 64;     // >= 8 NT, >= nw r
-  take(4 * (size_t)nred);
+  take(4 * (size_t)(32 * 64 + 64 > 2 * NT ? 32 * 64 + 64 : 2 * NT));   // >= 8 NT, >= groups r
   take(8 * (size_t)(cpw > 1 ? cpw : 1));
-  take(topk_scratch_bytes(ic, NT));
+  take(4 * (size_t)kTopkScratchWords);
   return o;
 }
 
-__device__ Lds carve(unsigned char* smem, const FusedArgs& a, TopkScratch* ts) {
-  size_t off[20];
-  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cw, a.cpw, off);
+__device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
+  size_t off[16];
+  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, off);
   Lds L;
-  L.xs = reinterpret_cast<double*>(smem + off[0]);
+  L.xs = reinterpret_cast<int32_t*>(smem + off[0]);
   L.limb = smem + off[1];
-  L.hloc = reinterpret_cast<float*>(smem + off[2]);
-  L.dsum = reinterpret_cast<float*>(smem + off[3]);
-  L.btc = reinterpret_cast<float*>(smem + off[4]);
-  L.hh = reinterpret_cast<float*>(smem + off[5]);
-  L.keys = reinterpret_cast<uint32_t*>(smem + off[6]);
-  L.candp = reinterpret_cast<int32_t*>(smem + off[7]);
-  L.sel = reinterpret_cast<int32_t*>(smem + off[8]);
-  L.keep = reinterpret_cast<int32_t*>(smem + off[9]);
-  L.hk = reinterpret_cast<float*>(smem + off[10]);
-  L.hcl = reinterpret_cast<float*>(smem + off[11]);
-  L.zsum = reinterpret_cast<float*>(smem + off[12]);
-  L.zv = reinterpret_cast<float*>(smem + off[13]);
-  L.red = reinterpret_cast<float*>(smem + off[14]);
-  L.gu = reinterpret_cast<float*>(smem + off[15]);
-  L.tks = smem + off[16];
-  const int ic = a.I > a.c ? a.I : a.c;
-  ts->hist = reinterpret_cast<uint32_t*>(L.tks);
-  ts->flag = L.tks + 4 * kHistBins;
-  ts->lkey = reinterpret_cast<uint32_t*>(ts->flag + ((ic + 15) & ~15));
-  ts->lidx = reinterpret_cast<int32_t*>(ts->lkey + kListMax);
-  ts->misc = reinterpret_cast<uint32_t*>(ts->lidx + kListMax);
+  L.dsum = reinterpret_cast<float*>(smem + off[2]);
+  L.hloc = reinterpret_cast<float*>(smem + off[3]);
+  L.hh = reinterpret_cast<float*>(smem + off[4]);
+  L.candp = reinterpret_cast<int32_t*>(smem + off[5]);
+  L.sel = reinterpret_cast<int32_t*>(smem + off[6]);
+  L.keep = reinterpret_cast<int32_t*>(smem + off[7]);
+  L.hk = reinterpret_cast<float*>(smem + off[8]);
+  L.hcl = reinterpret_cast<float*>(smem + off[9]);
+  L.zsum = reinterpret_cast<float*>(smem + off[10]);
+  L.zv = reinterpret_cast<float*>(smem + off[11]);
+  L.red = reinterpret_cast<float*>(smem + off[12]);
+  L.gu = reinterpret_cast<float*>(smem + off[13]);
+  L.tks = reinterpret_cast<uint32_t*>(smem + off[14]);
   return L;
 }
 
 // ------------------------------------------------------------------ phase A: rotation and digits
+//
+// x~ = Hadamard(d . x) in fixed point: X_i = rint(d_i x_i 2^F0) as int32 with
+// F0 = 30 - log2 H - E (max |x| < 2^E), so |X~| <= 2^30 and the transform of
+// the integers is exact. The digit planes hold the six base-16 digits of
+// Y = floor(X~ / 2^7) + 2^23 (0 <= Y < 2^24); the MFMA column of ones gives the
+// row sums of the codes, which remove the offset: t . floor(X~ / 2^7) =
+// sum_l 16^l D_l - 2^23 D_ones.
 
-// Writes the six FP8 digits of X = rint(x~ 2^F) for element i.
-__device__ __forceinline__ void put_digits(const Lds& L, int Hp, int i, double v, int F) {
-  int X = (int32_t)rint(ldexp(v, F));
-#pragma unroll
-  for (int l = 0; l < 6; ++l) {
-    const int d = ((X + 8) & 15) - 8;
-    L.limb[l * Hp + i] = kE4M3Digit[d + 8];
-    X = (X - d) >> 4;
-  }
-}
-
-__device__ __forceinline__ int scale_exponent(double m, double* dred) {
+// The exponent F0 from the bf16 bit patterns of this thread's values (mx: the
+// largest |x| pattern it holds); one barrier.
+__device__ __forceinline__ int fixed_exponent(uint32_t mx, int log2H, uint32_t* wred) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
-  if (lane == 0) dred[wv] = m;
+  mx = wave_max_u32(mx);
+  if (lane == 0) wred[wv] = mx;
   __syncthreads();
-  m = dred[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) m = fmax(m, dred[w]);
-  int F = 0;
-  if (m > 0.0) { int ex; frexp(m, &ex); F = 22 - ex; }   // max |x~| 2^F in [2^21, 2^22)
-  return F;
+  const uint4 m4 = *reinterpret_cast<const uint4*>(wred);
+  mx = max(max(m4.x, m4.y), max(m4.z, m4.w));
+  if (mx == 0) return 0;
+  const int E = (int)((mx >> 7) & 0xFF) - 126;          // max |x| < 2^E
+  return 30 - log2H - E;
 }
 
-// x~ for H = 256 EPT with EPT >= 4. Layout A (thread t holds i = EPT t + q):
-// in-register stages for the low bits, wavefront shuffles for the next six; one
-// LDS transpose to layout B (i = t + 256 q) for the two bits that cross
-// wavefronts. xv: the thread's EPT BF16 values of x (prefetched).
+__device__ __forceinline__ int32_t fix_value(uint32_t xb, int8_t s, int F0) {
+  const float f = ldexpf(__uint_as_float(xb << 16), F0);   // exact scaling; |f| < 2^(30 - log2 H)
+  const int32_t q = (int32_t)rintf(f);
+  return s < 0 ? -q : q;
+}
+
+// Writes the digit bytes of Y for EPT consecutive elements starting at i0.
 template <int EPT>
-__device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint4* xv, double* dred) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  double v[EPT];
-  const int8_t* sg = a.signs + EPT * tid;
-  if constexpr (EPT >= 8) {
+__device__ __forceinline__ void put_digit_planes(const Lds& L, int Hp, int i0, const int32_t* v) {
+  uint32_t y[EPT];
 #pragma unroll
-    for (int u = 0; u < EPT / 8; ++u) {
-      const uint4 w = xv[u];
-      const uint2 s8 = *reinterpret_cast<const uint2*>(sg + 8 * u);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      const uint32_t ss[2] = {s8.x, s8.y};
+  for (int q = 0; q < EPT; ++q) y[q] = (uint32_t)((v[q] >> kDShift) + (1 << 23));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float f = (q & 1) ? bf16hi(ww[q >> 1]) : bf16lo(ww[q >> 1]);
-        const int s = (int8_t)((ss[q >> 2] >> (8 * (q & 3))) & 0xFF);
-        v[8 * u + q] = (double)f * (double)s;
-      }
+  for (int l = 0; l < kPlanes; ++l) {
+    uint32_t w[(EPT + 3) / 4];
+#pragma unroll
+    for (int g = 0; g < (EPT + 3) / 4; ++g) {
+      float f[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) f[h] = 4 * g + h < EPT ? (float)((y[4 * g + h] >> (4 * l)) & 15u) : 0.f;
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
+      w[g] = (uint32_t)pk;
     }
-  } else {
-    const uint4 w = xv[0];                 // EPT == 4: the first 8 bytes
-    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(sg);
-    const uint32_t ww[2] = {w.x, w.y};
+    uint8_t* dst = L.limb + (size_t)l * Hp + i0;
+    if constexpr (EPT == 4) *reinterpret_cast<uint32_t*>(dst) = w[0];
+    else if constexpr (EPT == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float f = (q & 1) ? bf16hi(ww[q >> 1]) : bf16lo(ww[q >> 1]);
-      v[q] = (double)f * (double)(int8_t)((s4 >> (8 * q)) & 0xFF);
+      for (int g = 0; g < EPT / 16; ++g)
+        reinterpret_cast<uint4*>(dst)[g] = make_uint4(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]);
     }
   }
+}
+
+// Butterfly of one lane stage: partner p, this lane upper (bit set) or lower.
+__device__ __forceinline__ int32_t bfly(int32_t v, int32_t p, bool upper) { return upper ? p - v : v + p; }
+
+// x~ for H = 256 EPT with EPT >= 4 (H >= 1024). Thread t holds i = EPT t + q:
+// in-register stages for the low log2 EPT bits, VALU lane exchanges for the
+// next six, one LDS exchange among the four wavefronts for the top two. xb:
+// this thread's EPT BF16 patterns; sg: its EPT signs. Returns F0.
+template <int EPT>
+__device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint32_t* xb, const int8_t* sg,
+                           uint32_t* wred) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) mx = max(mx, xb[q] & 0x7FFFu);
+  const int F0 = fixed_exponent(mx, a.log2H, wred);
+  int32_t v[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = fix_value(xb[q], sg[q], F0);
 #pragma unroll
   for (int h = 1; h < EPT; h <<= 1)
 #pragma unroll
     for (int q = 0; q < EPT; ++q)
-      if (!(q & h)) { const double x0 = v[q], x1 = v[q + h]; v[q] = x0 + x1; v[q + h] = x0 - x1; }
+      if (!(q & h)) { const int32_t x0 = v[q], x1 = v[q + h]; v[q] = x0 + x1; v[q + h] = x0 - x1; }
 #pragma unroll
-  for (int s = 0; s < 6; ++s) {
-    const int m = 1 << s;
-    const bool upper = lane & m;
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<1>(v[q]), lane & 1);
 #pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-      const double o = __shfl_xor(v[q], m, 64);
-      v[q] = upper ? o - v[q] : v[q] + o;
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<2>(v[q]), lane & 2);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<4>(v[q]), lane & 4);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<8>(v[q]), lane & 8);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<16>(v[q]), lane & 16);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = bfly(v[q], lane_xor<32>(v[q]), lane & 32);
+  // the two wavefront bits: a 4-point Hadamard across the wavefronts
+  int32_t* mine = L.xs + EPT * tid;
+#pragma unroll
+  for (int g = 0; g < EPT / 4; ++g)
+    reinterpret_cast<int4*>(mine)[g] = make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+  __syncthreads();
+  int32_t acc[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) acc[q] = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const int32_t* src = L.xs + EPT * (64 * w2 + lane);
+    const bool neg = __builtin_popcount(w2 & wv) & 1;
+#pragma unroll
+    for (int g = 0; g < EPT / 4; ++g) {
+      const int4 u = reinterpret_cast<const int4*>(src)[g];
+      acc[4 * g] += neg ? -u.x : u.x;
+      acc[4 * g + 1] += neg ? -u.y : u.y;
+      acc[4 * g + 2] += neg ? -u.z : u.z;
+      acc[4 * g + 3] += neg ? -u.w : u.w;
     }
   }
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) L.xs[EPT * tid + q] = v[q];
+  put_digit_planes<EPT>(L, a.H, EPT * tid, acc);
   __syncthreads();
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) v[q] = L.xs[tid + NT * q];
-#pragma unroll
-  for (int h = EPT / 4; h < EPT; h <<= 1)
-#pragma unroll
-    for (int q = 0; q < EPT; ++q)
-      if (!(q & h)) { const double x0 = v[q], x1 = v[q + h]; v[q] = x0 + x1; v[q + h] = x0 - x1; }
-  double m = 0.0;
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) m = fmax(m, fabs(v[q]));
-  const int F = scale_exponent(m, dred);
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) put_digits(L, a.H, tid + NT * q, v[q], F);
-  __syncthreads();
-  return F;
+  return F0;
 }
 
-// x~ for small H (< 1024): LDS butterflies.
-__device__ int rotate_small(const FusedArgs& a, const Lds& L, int t, double* dred) {
+// x~ for small H (< 1024): LDS butterflies. Digits for i >= H (up to 256) are
+// written too; the sketch codes there are zero, so their value does not matter.
+__device__ int rotate_small(const FusedArgs& a, const Lds& L, int t, uint32_t* wred) {
   const int tid = threadIdx.x, H = a.H;
   const uint16_t* xt = a.x + (size_t)t * H;
-  for (int i = tid; i < H; i += NT) L.xs[i] = (double)bf16_to_f32(xt[i]) * (double)a.signs[i];
+  uint32_t mx = 0;
+  for (int i = tid; i < H; i += NT) mx = max(mx, (uint32_t)xt[i] & 0x7FFFu);
+  const int F0 = fixed_exponent(mx, a.log2H, wred);
+  for (int i = tid; i < H; i += NT) L.xs[i] = fix_value(xt[i], a.signs[i], F0);
   __syncthreads();
   for (int s = 0; s < a.log2H; ++s) {
     const int h = 1 << s;
     for (int b = tid; b < H / 2; b += NT) {
       const int i = ((b >> s) << (s + 1)) | (b & (h - 1));
-      const double u = L.xs[i], w = L.xs[i + h];
+      const int32_t u = L.xs[i], w = L.xs[i + h];
       L.xs[i] = u + w;
       L.xs[i + h] = u - w;
     }
     __syncthreads();
   }
-  double m = 0.0;
-  for (int i = tid; i < H; i += NT) m = fmax(m, fabs(L.xs[i]));
-  const int F = scale_exponent(m, dred);
   const int Hp = max(H, 256);
-  for (int i = tid; i < Hp; i += NT) put_digits(L, Hp, i, i < H ? L.xs[i] : 0.0, F);
+  for (int i0 = 4 * tid; i0 < Hp; i0 += 4 * NT) {
+    int32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = i0 + q < H ? L.xs[i0 + q] : 0;
+    put_digit_planes<4>(L, Hp, i0, v);
+  }
   __syncthreads();
-  return F;
+  return F0;
 }
 
 // ------------------------------------------------------------------ phase A: screen
 
-// B operand: FP8 digit l of x~ in column l < 6 (zero in columns 6..15), for
-// super-block sb (256 hidden indices) and half m; it matches the FP4 A operand
-// layout where lane group g holds hidden indices sb*256 + 64 g + 32 m + (0..31).
+// B operand for super-block sb (256 hidden indices) and half m: column col < 6
+// is digit plane col, column 6 is all ones, columns 7..15 are zero. It matches
+// the FP4 A operand, where lane group g holds hidden indices
+// sb*256 + 64 g + 32 m + (0..31).
 __device__ __forceinline__ v8i digit_operand(const Lds& L, int Hp, int sb, int m) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, gB = lane >> 4;
-  const uint8_t* row = L.limb + (size_t)min(col, 5) * Hp;
+  const uint8_t* row = L.limb + (size_t)min(col, kPlanes - 1) * Hp;
   const int i0 = sb * 256 + 64 * (gB >> 1) + 32 * m + 16 * (gB & 1);
   const uint4 lo = *reinterpret_cast<const uint4*>(row + i0);
   const uint4 hi = *reinterpret_cast<const uint4*>(row + i0 + 128);
-  const unsigned keep = col < 6 ? 0xFFFFFFFFu : 0u;
+  const unsigned keep = col < kPlanes ? 0xFFFFFFFFu : 0u;
+  const unsigned one = col == kOnes ? 0x38383838u : 0u;       // FP8 E4M3 1.0
   v8i b;
-  b[0] = lo.x & keep; b[1] = lo.y & keep; b[2] = lo.z & keep; b[3] = lo.w & keep;
-  b[4] = hi.x & keep; b[5] = hi.y & keep; b[6] = hi.z & keep; b[7] = hi.w & keep;
+  b[0] = (lo.x & keep) | one; b[1] = (lo.y & keep) | one; b[2] = (lo.z & keep) | one; b[3] = (lo.w & keep) | one;
+  b[4] = (hi.x & keep) | one; b[5] = (hi.y & keep) | one; b[6] = (hi.z & keep) | one; b[7] = (hi.w & keep) | one;
   return b;
 }
 
-// The products are formed with the unscaled FP8/FP6/FP4 MFMA (v_mfma_f32_16x16x128_f8f6f4):
-// the builtin selects it when both block-scale operands are 0. (The block-scaled
-// encoding with an explicit 2^0 scale gave wrong accumulator rows in this kernel.)
+// A operand: sixteen 2-bit codes per 32-bit word become FP4 E2M1 +1 / -1 / 0 by
+// masking (the packing puts the nonzero and sign flags of each value at the
+// mantissa and sign bits of its nibble). The products use the unscaled
+// FP8/FP6/FP4 MFMA (v_mfma_f32_16x16x128_f8f6f4), which the builtin selects when
+// both block-scale operands are 0. (The block-scaled form with an explicit 2^0
+// scale gave wrong accumulator rows in this kernel.)
 __device__ __forceinline__ v8i trit_operand(uint32_t w0, uint32_t w1) {
-  constexpr uint32_t M = 0xAAAAAAAAu;   // flag pairs -> FP4 E2M1 codes of +1 / -1 / 0
+  constexpr uint32_t M = 0xAAAAAAAAu;
   v8i a;
   a[0] = (int)(w0 & M); a[1] = (int)((w0 << 1) & M);
   a[2] = (int)(w1 & M); a[3] = (int)((w1 << 1) & M);
@@ -383,110 +442,88 @@ __device__ __forceinline__ v8i trit_operand(uint32_t w0, uint32_t w1) {
   return a;
 }
 
-// Screen items of a wavefront: (tile u, super-block sb = wave + 4 s); item it = u * nsbw + s.
-constexpr int kScreenBatch = 8;
-
-struct ScreenGeom {
-  int cwk, nrows, ntile, nsb, nsbw, nitems;
-};
-__device__ __forceinline__ ScreenGeom screen_geom(const FusedArgs& a, int j0, int j1) {
-  ScreenGeom g;
-  const int wv = threadIdx.x >> 6;
-  g.cwk = j1 - j0;
-  g.nrows = 2 * g.cwk;
-  g.ntile = (g.nrows + 15) / 16;
-  g.nsb = (a.H + 255) / 256;
-  g.nsbw = g.nsb > wv ? (g.nsb - wv + 3) / 4 : 0;
-  g.nitems = g.ntile * g.nsbw;
-  return g;
-}
-
-__device__ __forceinline__ uint4 screen_load(const FusedArgs& a, const ScreenGeom& g, int e,
-                                             int j0, int it) {
+// The sketch rows of a sub-chunk of cwk channels: rows 0..cwk-1 are the gate
+// rows, rows cwk..2cwk-1 the up rows; tile u = rows 16u..16u+15. Wavefront w
+// computes tile w over all super-blocks. Its loads: item s = super-block s,
+// lane (row = lane & 15, g = lane >> 4) takes 16 bytes of its row at byte
+// 64 s + 16 g.
+__device__ __forceinline__ uint4 sketch_item(const FusedArgs& a, int e, int j0, int cwk, int s) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (it >= g.nitems) return make_uint4(0, 0, 0, 0);
-  const int u = it / g.nsbw, s = it % g.nsbw;
-  const int sb = wv + 4 * s;
-  const int rho = u * 16 + (lane & 15);
+  const int rho = 16 * wv + (lane & 15);
   const int rowb = a.H / 4;
-  const int off = sb * 64 + (lane >> 4) * 16;
-  if (rho < g.nrows && off < rowb) {
-    const int j = j0 + (rho < g.cwk ? rho : rho - g.cwk);
-    return ld16((rho < g.cwk ? a.tg : a.tu) + ((size_t)e * a.I + j) * rowb + off);
+  const int off = 64 * s + 16 * (lane >> 4);
+  if (rho < 2 * cwk && off < rowb) {
+    const int j = j0 + (rho < cwk ? rho : rho - cwk);
+    return ld16((rho < cwk ? a.tg : a.tu) + ((size_t)e * a.I + j) * rowb + off);
   }
   return make_uint4(0, 0, 0, 0);
 }
 
-// Sketch activations of channels [j0, j1) of expert e into L.hloc and hhat[p][.].
-// pre[]: the first batch of this wave's screen items, prefetched (if use_pre).
-__device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int j0, int j1,
-                             int F, const uint4* pre, bool use_pre) {
-  const int tid = threadIdx.x, lane = tid & 63;
+constexpr int kSketchPre = 8;   // super-blocks of the first sub-chunk requested up front
+
+// Sketch activations of channels [j0, j0 + cwk) into hloc (LDS) and the
+// exchange. pre: the first kSketchPre items of this wavefront (if use_pre);
+// sgu: this thread's prefetched scale (thread c < 2 cwk: gate scale of channel
+// c, or up scale of channel c - cwk).
+__device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int j0, int cwk, int F0,
+                             const uint4* pre, bool use_pre, float sgu, uint32_t tag) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Hp = max(a.H, 256);
-  const ScreenGeom g = screen_geom(a, j0, j1);
-  const int wv = tid >> 6;
-  for (int o = tid; o < g.ntile * 128; o += NT) L.dsum[o] = 0.f;
-  __syncthreads();
-  for (int b0 = 0; b0 < g.nitems; b0 += kScreenBatch) {
-    uint4 w[kScreenBatch];
+  const int nsb = (a.H + 255) / 256;
+  if (16 * wv < 2 * cwk) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsb; s0 += kSketchPre) {
+      uint4 w[kSketchPre];
 #pragma unroll
-    for (int u = 0; u < kScreenBatch; ++u)
-      w[u] = (use_pre && b0 == 0) ? pre[u] : screen_load(a, g, e, j0, b0 + u);
-    v4f acc[kScreenBatch];
-#pragma unroll
-    for (int u = 0; u < kScreenBatch; ++u) {
-      acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-      const int it = b0 + u;
-      if (it < g.nitems) {
-        const int sb = wv + 4 * (it % g.nsbw);
-        const v8i d0 = digit_operand(L, Hp, sb, 0);
-        const v8i d1 = digit_operand(L, Hp, sb, 1);
-        acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].x, w[u].y), d0, acc[u], 4, 0, 0, 0, 0, 0);
-        acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].z, w[u].w), d1, acc[u], 4, 0, 0, 0, 0, 0);
+      for (int u = 0; u < kSketchPre; ++u) {
+        const int s = s0 + u;
+        w[u] = (use_pre && s0 == 0) ? pre[u] : (s < nsb ? sketch_item(a, e, j0, cwk, s) : make_uint4(0, 0, 0, 0));
       }
-    }
-    // lane holds D[4 (lane / 16) + v][lane % 16]: (row within tile, digit column);
-    // partial dots of each item are integers, so the LDS sums are exact in any order
-    const int col = lane & 15;
-    if (col < 6) {
 #pragma unroll
-      for (int u = 0; u < kScreenBatch; ++u) {
-        const int it = b0 + u;
-        if (it < g.nitems) {
-          const int tile = it / g.nsbw;
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            atomicAdd(&L.dsum[(tile * 16 + 4 * (lane >> 4) + v) * 8 + col], acc[u][v]);
+      for (int u = 0; u < kSketchPre; ++u) {
+        const int s = s0 + u;
+        if (s < nsb) {
+          const v8i d0 = digit_operand(L, Hp, s, 0);
+          const v8i d1 = digit_operand(L, Hp, s, 1);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].x, w[u].y), d0, acc, 4, 0, 0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].z, w[u].w), d1, acc, 4, 0, 0, 0, 0, 0);
         }
       }
     }
+    // lane holds D[4 (lane / 16) + v][lane % 16]: (row within the tile, column)
+    const int col = lane & 15;
+    if (col < 8) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) L.dsum[(16 * wv + 4 * (lane >> 4) + v) * 8 + col] = acc[v];
+    }
+  }
+  // per-row scale times the exact integer dot: sum_l 16^l D_l - 2^23 D_ones, in units of 2^(7 - F0)
+  __syncthreads();
+  if (tid < 2 * cwk) {
+    const float4 d0 = *reinterpret_cast<const float4*>(L.dsum + tid * 8);
+    const float4 d1 = *reinterpret_cast<const float4*>(L.dsum + tid * 8 + 4);
+    const long long S = (long long)(int)d0.x + ((long long)(int)d0.y << 4) + ((long long)(int)d0.z << 8) +
+                        ((long long)(int)d0.w << 12) + ((long long)(int)d1.x << 16) +
+                        ((long long)(int)d1.y << 20) - ((long long)(int)d1.z << 23);
+    L.red[NT + tid] = (float)((double)sgu * ldexp((double)S, kDShift - F0));
   }
   __syncthreads();
-  // exact integer dot per row: sum_l 16^l D_l (each D_l an integer below 8 H)
-  for (int jj = tid; jj < g.cwk; jj += NT) {
-    long long dg = 0, du = 0;
-#pragma unroll
-    for (int l = 0; l < 6; ++l) {
-      dg += (long long)(int)L.dsum[jj * 8 + l] << (4 * l);
-      du += (long long)(int)L.dsum[(g.cwk + jj) * 8 + l] << (4 * l);
-    }
-    const int j = j0 + jj;
-    const float gh = (float)((double)a.sg[(size_t)e * a.I + j] * ldexp((double)dg, -F));
-    const float uh = (float)((double)a.su[(size_t)e * a.I + j] * ldexp((double)du, -F));
+  if (tid < cwk) {
+    const float gh = L.red[NT + tid], uh = L.red[NT + cwk + tid];
     const float hv = silu_f32(gh) * uh;
-    L.hloc[jj] = hv;
-    st_x(a.hhat + (size_t)p * a.I + j, hv);
+    L.hloc[tid] = hv;
+    put_tagged(a.xh + (size_t)p * a.I + j0 + tid, hv, tag);
   }
   __syncthreads();
 }
 
 // ------------------------------------------------------------------ phase B: exact gate / up
 
-// h for items [q0, q1) of `chan` (null: channel = position) into out[q0..q1)
-// (exchange stores). One wavefront per (row, matrix).
+// h for items [q0, q1) of `chan` (null: channel = position), published as
+// out[q0 .. q1) with the tag. One wavefront per (row, matrix).
 template <int CH>
-__device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_t* chan, int q0,
-                           int q1, const uint4* xr, float* out) {
+__device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_t* chan, int q0, int q1,
+                           const uint4* xr, uint64_t* out, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
   const int nchunk = H / 8;
   const int nitems = 2 * (q1 - q0);
@@ -509,17 +546,15 @@ __device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int it = it0 + u;
-      if (it < nitems) {
-        float acc = 0.f;
+      float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < CH; ++m) acc = dot8_bf16(wr[u][m], xr[m], acc);
-        acc = wave_sum(acc);
-        if (lane == 0) L.gu[(it & 1) * a.cpw + (it >> 1)] = acc;
-      }
+      for (int m = 0; m < CH; ++m) acc = dot8_bf16(wr[u][m], xr[m], acc);
+      acc = wave_sum_f(acc);
+      if (lane == 0 && it < nitems) L.gu[(it & 1) * a.cpw + (it >> 1)] = acc;
     }
   }
   __syncthreads();
-  for (int i = tid; i < q1 - q0; i += NT) st_x(out + q0 + i, silu_f32(L.gu[i]) * L.gu[a.cpw + i]);
+  for (int i = tid; i < q1 - q0; i += NT) put_tagged(out + q0 + i, silu_f32(L.gu[i]) * L.gu[a.cpw + i], tag);
 }
 
 // ------------------------------------------------------------------ phase C: down + combine
@@ -531,7 +566,7 @@ __device__ void recovery_slice(const FusedArgs& a, const Lds& L, int e, int hs, 
   const int tid = threadIdx.x, r = a.r;
   const int c0 = hs * 64;
   if (r % 8 == 0) {
-    const int cpr = r / 8;                 // 16-byte chunks per row
+    const int cpr = r / 8;                 // 16-byte chunks per row (<= 16)
     const int nchunk = 64 * cpr;           // <= 1024
     float* part = L.red;
 #pragma unroll
@@ -564,7 +599,8 @@ __device__ void recovery_slice(const FusedArgs& a, const Lds& L, int e, int hs, 
 // L.red[32*64 ..]), published for the combine; the last of the token's K pairs
 // writes out[t][c0 .. c0+64).
 __device__ void down_slice(const FusedArgs& a, const Lds& L, int p, int t, int e, int hs,
-                           const int32_t* rows, const float* hv, int n, bool add_rec, int* s_flag) {
+                           const int32_t* rows, const float* hv, int n, bool add_rec, int* s_flag,
+                           uint32_t tag) {
   const int tid = threadIdx.x, l8 = tid & 7, g = tid >> 3;
   const int c0 = hs * 64;
   float acc[8];
@@ -593,41 +629,57 @@ __device__ void down_slice(const FusedArgs& a, const Lds& L, int p, int t, int e
     float y = 0.f;
     for (int gg = 0; gg < 32; ++gg) y += L.red[gg * 64 + tid];
     if (add_rec) y += L.red[32 * 64 + tid];
-    st_x(a.ypart + (size_t)p * a.H + c0 + tid, y);
+    st_f(a.ypart + (size_t)p * a.H + c0 + tid, y);
   }
-  unsigned* cc = a.ctr + 2 * (size_t)a.P + (size_t)t * a.nhs + hs;
+  unsigned* cc = a.ctr + (size_t)t * a.nhs + hs;
   if (last_of(cc, (unsigned)a.K, s_flag)) {
     if (tid < 64) {
       float o = 0.f;
       for (int q = 0; q < a.K; ++q)
-        o += a.topk_w[(size_t)t * a.K + q] * ld_x(a.ypart + (size_t)(t * a.K + q) * a.H + c0 + tid);
-      const bool bad = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + c0 + tid);
+      const bool bad = ld_u(a.fail) == tag;
       a.out[(size_t)t * a.H + c0 + tid] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
     }
   }
   __syncthreads();
 }
 
-// Loads n exchange values src[0..n) into dst (LDS), batched; optionally keys too.
-__device__ void fetch_exchange(const float* src, int n, float* dst, uint32_t* keys) {
-  constexpr int HB = 8;
-  const int tid = threadIdx.x;
-  for (int i0 = tid; i0 < n; i0 += NT * HB) {
-    float hv[HB];
+// ------------------------------------------------------------------ exchange reads
+
+// Partial recovery sums of all nw workgroups of pair p: thread (zl, zg) adds
+// those of workgroups zg, zg + groups, ... into L.red[NT + zg r + zl]. All its
+// loads are issued before the first wait.
+__device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int p, int zl, int zg,
+                                           int groups, uint32_t tag) {
+  constexpr int kMaxPer = 16;                      // nw <= 32 and groups >= 2 (r <= 128)
+  if (zg >= groups) return;
+  const uint64_t* zp = a.xz + (size_t)p * a.nw * a.r + zl;
+  uint64_t raw[kMaxPer];
 #pragma unroll
-    for (int u = 0; u < HB; ++u) {
-      const int i = i0 + NT * u;
-      hv[u] = i < n ? ld_x(src + i) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < HB; ++u) {
-      const int i = i0 + NT * u;
-      if (i < n) {
-        dst[i] = hv[u];
-        if (keys) keys[i] = score_key(hv[u]);
-      }
-    }
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int q = zg + groups * u;
+    raw[u] = q < a.nw ? ld_tagged(zp + (size_t)q * a.r) : 0;
   }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int q = zg + groups * u;
+    if (q < a.nw) s += await_tagged(zp + (size_t)q * a.r, raw[u], tag, a.fail);
+  }
+  L.red[NT + zg * a.r + zl] = s;
+}
+
+// ------------------------------------------------------------------ launch tag
+
+__device__ __forceinline__ uint32_t launch_tag(const FusedArgs& a, uint32_t* s_tag) {
+  if (threadIdx.x == 0) *s_tag = ld_u(a.seq + blockIdx.x) + 1u;
+  __syncthreads();
+  return *s_tag;
+}
+// Every sequence slot is rewritten by exactly one workgroup of the launch.
+__device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) {
+  if (threadIdx.x == 0)
+    for (int b = blockIdx.x; b < kSeqSlots; b += a.G) st_u(a.seq + b, tag);
 }
 
 // ------------------------------------------------------------------ kernels
@@ -635,49 +687,62 @@ __device__ void fetch_exchange(const float* src, int n, float* dst, uint32_t* ke
 template <int EPT>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ double dred[NT / 64];
+  __shared__ __align__(16) uint32_t wred[NT / 64];
   __shared__ int s_flag;
-  __shared__ unsigned s_epoch[2];
-  __shared__ uint32_t radix_scratch[256 + NT / 64 + 8];
-  TopkScratch ts;
-  const Lds L = carve(smem, a, &ts);
+  __shared__ uint32_t s_tag;
+  const Lds L = carve(smem, a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int nw = a.nw, H = a.H, r = a.r;
   constexpr int CH = EPT >= 2 ? EPT / 2 : 1;        // 16-byte chunks of x per lane (H / 512)
-  constexpr int XV = EPT >= 8 ? EPT / 8 : 1;
+  const uint32_t tag = launch_tag(a, &s_tag);
+  const int groups = r > 0 ? NT / r : 1;             // recovery partial sums: thread (l, g)
+  const int zl = r > 0 ? tid % r : 0, zg = r > 0 ? tid / r : groups;
 
   for (int slot = blockIdx.x; slot < a.P * nw; slot += a.G) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
     const int e = a.ids[p];
-    unsigned* ctrA = a.ctr + 2 * (size_t)p;
-    unsigned* ctrB = ctrA + 1;
     const int j0 = min(a.I, w * a.cw), j1 = min(a.I, j0 + a.cw);
     const int hs0 = w;                              // first output slice of this workgroup
     const bool one_slice = hs0 < a.nhs && hs0 + nw >= a.nhs;
 
-    // ---- requests that need no selection: x, sketch rows, Bt rows, A slice
-    uint4 xv[XV];
+    // ---- requests that need no selection: x and signs first, then the sketch
+    //      rows, scales and Bt rows of the first sub-chunk, and the A slice
+    uint32_t xb[EPT >= 4 ? EPT : 1];
+    int8_t sgn[EPT >= 4 ? EPT : 1];
     if constexpr (EPT >= 4) {
       const uint16_t* xt = a.x + (size_t)t * H + EPT * tid;
 #pragma unroll
-      for (int u = 0; u < XV; ++u) {
-        if constexpr (EPT >= 8) xv[u] = ld16c(xt + 8 * u);
-        else { const uint2 h2 = *reinterpret_cast<const uint2*>(xt); xv[u] = make_uint4(h2.x, h2.y, 0, 0); }
+      for (int g = 0; g < EPT / 8; ++g) {
+        const uint4 u = ld16c(xt + 8 * g);
+        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xb[8 * g + q] = (q & 1) ? ww[q >> 1] >> 16 : ww[q >> 1] & 0xFFFFu;
+      }
+      if constexpr (EPT == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(xt);
+        xb[0] = u.x & 0xFFFFu; xb[1] = u.x >> 16; xb[2] = u.y & 0xFFFFu; xb[3] = u.y >> 16;
+      }
+#pragma unroll
+      for (int g = 0; g < EPT / 4; ++g) {
+        const uint32_t s4 = *reinterpret_cast<const uint32_t*>(a.signs + EPT * tid + 4 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sgn[4 * g + q] = (int8_t)(s4 >> (8 * q));
       }
     }
-    const int sj1f = min(j1, j0 + kSubChunk);       // first sub-chunk
-    const ScreenGeom sgm = screen_geom(a, j0, sj1f);
-    uint4 spre[kScreenBatch];
+    const int cwk0 = min(j1 - j0, kSubChunk);
+    uint4 spre[kSketchPre];
 #pragma unroll
-    for (int u = 0; u < kScreenBatch; ++u) spre[u] = screen_load(a, sgm, e, j0, u);
-    constexpr int BTP = 8;                          // Bt rows of the first sub-chunk: flat bf16
-    uint16_t btp[BTP];
-    const uint16_t* btbase = a.Bt + ((size_t)e * a.I + j0) * r;
+    for (int u = 0; u < kSketchPre; ++u)
+      spre[u] = u < (H + 255) / 256 ? sketch_item(a, e, j0, cwk0, u) : make_uint4(0, 0, 0, 0);
+    float sgu = 0.f;
+    if (tid < 2 * cwk0) sgu = tid < cwk0 ? a.sg[(size_t)e * a.I + j0 + tid] : a.su[(size_t)e * a.I + j0 + tid - cwk0];
+    constexpr int kBtPer = kMaxRank * kSubChunk / NT;   // Bt values per thread and sub-chunk (<= 16)
+    uint16_t btv[kBtPer];
 #pragma unroll
-    for (int u = 0; u < BTP; ++u) {
-      const int f = tid + NT * u;
-      btp[u] = f < (sj1f - j0) * r ? btbase[f] : (uint16_t)0;
+    for (int u = 0; u < kBtPer; ++u) {
+      const int jj = zg + groups * u;
+      btv[u] = (r > 0 && zg < groups && jj < cwk0) ? a.Bt[((size_t)e * a.I + j0 + jj) * r + zl] : (uint16_t)0;
     }
     uint4 apre[4];
     const bool have_apre = one_slice && r > 0 && r % 8 == 0 && 8 * r <= 4 * NT;
@@ -687,48 +752,83 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       apre[u] = (have_apre && f < 8 * r) ? ld16(a.A + ((size_t)e * H + hs0 * 64) * r + 8 * (size_t)f)
                                          : make_uint4(0, 0, 0, 0);
     }
-    if (tid == 0) { s_epoch[0] = counter_epoch(ctrA); s_epoch[1] = counter_epoch(ctrB); }
 
     // ---- phase A: screen this workgroup's channels, sub-chunk by sub-chunk
-    int F;
-    if constexpr (EPT >= 4) F = rotate_fast<EPT>(a, L, xv, dred);
-    else F = rotate_small(a, L, t, dred);
-    float zacc = 0.f;                               // partial recovery sum for l = tid
+    int F0;
+    if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(a, L, xb, sgn, wred);
+    else F0 = rotate_small(a, L, t, wred);
+    float zacc = 0.f;                               // partial recovery sum for (zl, zg)
     for (int sj0 = j0; sj0 < j1; sj0 += kSubChunk) {
-      const int sj1 = min(j1, sj0 + kSubChunk);
+      const int cwk = min(j1 - sj0, kSubChunk);
       const bool first = sj0 == j0;
-      screen_chunk(a, L, p, e, sj0, sj1, F, spre, first);
-      if (r > 0) {
-        const int nbt = (sj1 - sj0) * r;
-        const uint16_t* bb = a.Bt + ((size_t)e * a.I + sj0) * r;
-        if (first) {
+      if (!first) {
+        if (tid < 2 * cwk) sgu = tid < cwk ? a.sg[(size_t)e * a.I + sj0 + tid] : a.su[(size_t)e * a.I + sj0 + tid - cwk];
 #pragma unroll
-          for (int u = 0; u < BTP; ++u) {
-            const int f = tid + NT * u;
-            if (f < nbt) L.btc[f] = bf16_to_f32(btp[u]);
-          }
+        for (int u = 0; u < kBtPer; ++u) {
+          const int jj = zg + groups * u;
+          btv[u] = (r > 0 && zg < groups && jj < cwk) ? a.Bt[((size_t)e * a.I + sj0 + jj) * r + zl] : (uint16_t)0;
         }
-        for (int f = tid + (first ? NT * BTP : 0); f < nbt; f += NT) L.btc[f] = bf16_to_f32(bb[f]);
-        __syncthreads();
-        if (tid < r)
-          for (int jj = 0; jj < sj1 - sj0; ++jj) zacc += L.hloc[jj] * L.btc[jj * r + tid];
-        __syncthreads();
+      }
+      screen_chunk(a, L, p, e, sj0, cwk, F0, spre, first, sgu, tag);
+      if (r > 0 && zg < groups) {
+#pragma unroll
+        for (int u = 0; u < kBtPer; ++u) {
+          const int jj = zg + groups * u;
+          if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32(btv[u]);
+        }
+      }
+      __syncthreads();
+    }
+    if (r > 0) {
+      if (zg < groups) L.red[zg * r + zl] = zacc;
+      __syncthreads();
+      for (int l = tid; l < r; l += NT) {
+        float s = 0.f;
+        for (int g = 0; g < groups; ++g) s += L.red[g * r + l];
+        put_tagged(a.xz + ((size_t)p * nw + w) * r + l, s, tag);
       }
     }
-    if (tid < r) st_x(a.zpart + ((size_t)p * nw + w) * r + tid, zacc);
-    arrive(ctrA, s_epoch[0], (unsigned)nw);
-    wait_all(ctrA, s_epoch[0], (unsigned)nw, a.err);
 
     // ---- top-c candidates (identical in every workgroup of the pair)
-    fetch_exchange(a.hhat + (size_t)p * a.I, a.I, L.hh, L.keys);
-    if (r > 0) fetch_exchange(a.zpart + (size_t)p * nw * r, nw * r, L.red, nullptr);
-    __syncthreads();
+    {
+      int cnt;
+      const int i0 = topk_range<NT>(a.I, &cnt);
+      const uint64_t* src = a.xh + (size_t)p * a.I + i0;
+      uint64_t raw[32];
+      uint32_t kr[32];
+      const int per = (a.I + NT - 1) / NT;
+      if (per <= 4) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
+          if (j < cnt) L.hh[i0 + j] = hv;
+          k4[j] = score_key(hv);
+        }
+        // recovery sums of all workgroups of the pair
+        if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
+        block_topk<NT, 4>(k4, i0, cnt, a.I, a.c, L.candp, L.tks);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
+          if (j < cnt) L.hh[i0 + j] = hv;
+          kr[j] = score_key(hv);
+        }
+        if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
+        block_topk<NT, 32>(kr, i0, cnt, a.I, a.c, L.candp, L.tks);
+      }
+      if (a.c >= a.I || a.c <= 0) __syncthreads();   // block_topk's early exits skip its barrier
+    }
     for (int l = tid; l < r; l += NT) {
       float s = 0.f;
-      for (int q = 0; q < nw; ++q) s += L.red[q * r + l];
+      for (int g = 0; g < groups; ++g) s += L.red[NT + g * r + l];
       L.zsum[l] = s;
     }
-    block_topk<NT>(L.keys, a.I, a.c, L.candp, ts, radix_scratch);
     if (w == 0 && a.cand_out)
       for (int i = tid; i < a.c; i += NT) a.cand_out[(size_t)p * a.c + i] = L.candp[i];
 
@@ -742,16 +842,41 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         const int ci = lane + 64 * m;
         xr[m] = ci < H / 8 ? ld16c(xg + ci) : make_uint4(0, 0, 0, 0);
       }
-      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.hc + (size_t)p * a.c);
+      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag);
     }
-    arrive(ctrB, s_epoch[1], (unsigned)nw);
-    wait_all(ctrB, s_epoch[1], (unsigned)nw, a.err);
 
     // ---- top-k kept set and recovery coefficients
     if (a.k > 0) {
-      fetch_exchange(a.hc + (size_t)p * a.c, a.c, L.hcl, L.keys);
-      __syncthreads();
-      block_topk<NT>(L.keys, a.c, a.k, L.sel, ts, radix_scratch);
+      int cnt;
+      const int i0 = topk_range<NT>(a.c, &cnt);
+      const uint64_t* src = a.xc + (size_t)p * a.c + i0;
+      const int per = (a.c + NT - 1) / NT;
+      if (per <= 4) {
+        uint64_t raw[4];
+        uint32_t k4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
+          if (j < cnt) L.hcl[i0 + j] = hv;
+          k4[j] = score_key(hv);
+        }
+        block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
+      } else {
+        uint64_t raw[32];
+        uint32_t kr[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
+          if (j < cnt) L.hcl[i0 + j] = hv;
+          kr[j] = score_key(hv);
+        }
+        block_topk<NT, 32>(kr, i0, cnt, a.c, a.k, L.sel, L.tks);
+      }
+      if (a.k >= a.c) __syncthreads();
       for (int i = tid; i < a.k; i += NT) {
         L.keep[i] = L.candp[L.sel[i]];
         L.hk[i] = L.hcl[L.sel[i]];
@@ -759,22 +884,24 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       __syncthreads();
       if (w == 0 && a.keep_out)
         for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = L.keep[i];
+    } else {
+      __syncthreads();
     }
     if (r > 0) {
       // z = zsum - sum_{j in S} hhat_j Bt[e][j]
       if (r % 8 == 0) {
-        const int cpr = r / 8, groups = NT / cpr;   // r <= 128: cpr <= 16, groups >= 16
+        const int cpr = r / 8, ng = NT / cpr;       // r <= 128: cpr <= 16, ng >= 16
         const int cc = tid % cpr, g = tid / cpr;
         float acc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
         constexpr int ZB = 8;
-        for (int i0 = g; i0 < a.k; i0 += groups * ZB) {
+        for (int i0 = g; i0 < a.k; i0 += ng * ZB) {
           uint4 bw[ZB];
           float hv[ZB];
 #pragma unroll
           for (int u = 0; u < ZB; ++u) {
-            const int i = i0 + groups * u;
+            const int i = i0 + ng * u;
             const bool ok = i < a.k;
             const int j = ok ? L.keep[i] : 0;
             hv[u] = ok ? L.hh[j] : 0.f;
@@ -784,11 +911,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           for (int u = 0; u < ZB; ++u) fma8(acc, hv[u], bw[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) L.red[g * r + 8 * cc + u] = acc[u];    // groups * r = 8 NT
+        for (int u = 0; u < 8; ++u) L.red[g * r + 8 * cc + u] = acc[u];    // ng * r = 8 NT
         __syncthreads();
         for (int l = tid; l < r; l += NT) {
           float s = 0.f;
-          for (int gg = 0; gg < groups; ++gg) s += L.red[gg * r + l];
+          for (int gg = 0; gg < ng; ++gg) s += L.red[gg * r + l];
           L.zv[l] = L.zsum[l] - s;
         }
       } else {
@@ -807,27 +934,26 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     // ---- phase C: down projection over kept rows for this workgroup's output slices
     for (int hs = hs0; hs < a.nhs; hs += nw) {
       if (r > 0) recovery_slice(a, L, e, hs, apre, have_apre && hs == hs0);
-      down_slice(a, L, p, t, e, hs, L.keep, L.hk, a.k, r > 0, &s_flag);
+      down_slice(a, L, p, t, e, hs, L.keep, L.hk, a.k, r > 0, &s_flag, tag);
     }
   }
+  finish_launch(a, tag);
 }
 
 template <int EPT>
 __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_flag;
-  __shared__ unsigned s_epoch;
-  TopkScratch ts;
-  const Lds L = carve(smem, a, &ts);
+  __shared__ uint32_t s_tag;
+  const Lds L = carve(smem, a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int nw = a.nw, H = a.H;
   constexpr int CH = EPT >= 2 ? EPT / 2 : 1;
+  const uint32_t tag = launch_tag(a, &s_tag);
   for (int slot = blockIdx.x; slot < a.P * nw; slot += a.G) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
     const int e = a.ids[p];
-    unsigned* ctrB = a.ctr + 2 * (size_t)p + 1;
-    if (tid == 0) s_epoch = counter_epoch(ctrB);
     const int q0 = min(a.I, w * a.cpw), q1 = min(a.I, q0 + a.cpw);
     if (q0 < q1) {
       uint4 xr[CH];
@@ -837,15 +963,28 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
         const int ci = lane + 64 * m;
         xr[m] = ci < H / 8 ? ld16c(xg + ci) : make_uint4(0, 0, 0, 0);
       }
-      exact_rows<CH>(a, L, e, nullptr, q0, q1, xr, a.hhat + (size_t)p * a.I);
+      exact_rows<CH>(a, L, e, nullptr, q0, q1, xr, a.xh + (size_t)p * a.I, tag);
     }
-    arrive(ctrB, s_epoch, (unsigned)nw);
-    wait_all(ctrB, s_epoch, (unsigned)nw, a.err);
-    fetch_exchange(a.hhat + (size_t)p * a.I, a.I, L.hh, nullptr);
+    // all activations of the pair
+    {
+      const uint64_t* src = a.xh + (size_t)p * a.I;
+      constexpr int HB = 8;
+      for (int i0 = tid; i0 < a.I; i0 += NT * HB) {
+        uint64_t raw[HB];
+#pragma unroll
+        for (int u = 0; u < HB; ++u) raw[u] = i0 + NT * u < a.I ? ld_tagged(src + i0 + NT * u) : 0;
+#pragma unroll
+        for (int u = 0; u < HB; ++u) {
+          const int i = i0 + NT * u;
+          if (i < a.I) L.hh[i] = await_tagged(src + i, raw[u], tag, a.fail);
+        }
+      }
+    }
     __syncthreads();
     for (int hs = w; hs < a.nhs; hs += nw)
-      down_slice(a, L, p, t, e, hs, nullptr, L.hh, a.I, false, &s_flag);
+      down_slice(a, L, p, t, e, hs, nullptr, L.hh, a.I, false, &s_flag, tag);
   }
+  finish_launch(a, tag);
 }
 
 // ------------------------------------------------------------------ stats
@@ -924,22 +1063,27 @@ static void fused_geometry(ForwardPlan& p, int G_max) {
   p.nhs = p.H / 64;
 }
 
+static void common_regions(ForwardPlan& p, Carve& cv) {
+  p.off_seq = cv.take(4 * (size_t)kSeqSlots);
+  p.off_err = cv.take(4);
+  p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * std::max(p.nhs, 1));
+}
+
 ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) {
   ForwardPlan p{};
   p.T = T; p.K = K; p.P = T * K; p.E = E; p.I = I; p.H = H; p.k = k; p.c = c; p.r = r;
   fused_geometry(p, 256);
   p.cw = (I + p.nw - 1) / p.nw;
   p.cpw = std::max(1, (c + p.nw - 1) / p.nw);
-  size_t off[20];
-  p.lds = lds_layout(H, I, c, k, r, p.cw, p.cpw, off);
+  size_t off[16];
+  p.lds = lds_layout(H, I, c, k, r, p.cpw, off);
   Carve cv;
+  common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
-  p.off_hhat = cv.take(Pz * I * 4);
-  p.off_zpart = cv.take(Pz * p.nw * std::max(r, 1) * 4);
-  p.off_hc = cv.take(Pz * std::max(c, 1) * 4);
+  p.off_xh = cv.take(Pz * I * 8);
+  p.off_xz = cv.take(Pz * p.nw * std::max(r, 1) * 8);
+  p.off_xc = cv.take(Pz * std::max(c, 1) * 8);
   p.off_ypart = cv.take(Pz * H * 4);
-  p.off_ctr = cv.take((2 * Pz + (size_t)T * p.nhs) * 4);
-  p.off_err = cv.take(64);
   p.bytes = cv.off;
   return p;
 }
@@ -950,14 +1094,15 @@ ForwardPlan dense_plan(int T, int K, int E, int I, int H) {
   fused_geometry(p, 256);
   p.cw = 1;
   p.cpw = std::max(1, (I + p.nw - 1) / p.nw);
-  size_t off[20];
-  p.lds = lds_layout(H, I, 0, 0, 0, p.cw, p.cpw, off);
+  size_t off[16];
+  p.lds = lds_layout(H, I, 0, 0, 0, p.cpw, off);
   Carve cv;
+  common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
-  p.off_hhat = cv.take(Pz * I * 4);
+  p.off_xh = cv.take(Pz * I * 8);
+  p.off_xz = p.off_xh;
+  p.off_xc = p.off_xh;
   p.off_ypart = cv.take(Pz * H * 4);
-  p.off_ctr = cv.take((2 * Pz + (size_t)T * p.nhs) * 4);
-  p.off_err = cv.take(64);
   p.bytes = cv.off;
   return p;
 }
@@ -971,12 +1116,13 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.signs = s.signs; a.tg = s.tg; a.tu = s.tu; a.sg = s.sg; a.su = s.su;
   a.A = s.A; a.Bt = s.Bt;
   a.out = s.out; a.cand_out = s.cand_out; a.keep_out = s.keep_out;
-  a.hhat = reinterpret_cast<float*>(s.ws + p.off_hhat);
-  a.zpart = reinterpret_cast<float*>(s.ws + p.off_zpart);
-  a.hc = reinterpret_cast<float*>(s.ws + p.off_hc);
-  a.ypart = reinterpret_cast<float*>(s.ws + p.off_ypart);
+  a.seq = reinterpret_cast<uint32_t*>(s.ws + p.off_seq);
+  a.fail = reinterpret_cast<uint32_t*>(s.ws + p.off_err);
   a.ctr = reinterpret_cast<unsigned*>(s.ws + p.off_ctr);
-  a.err = reinterpret_cast<int*>(s.ws + p.off_err);
+  a.xh = reinterpret_cast<uint64_t*>(s.ws + p.off_xh);
+  a.xz = reinterpret_cast<uint64_t*>(s.ws + p.off_xz);
+  a.xc = reinterpret_cast<uint64_t*>(s.ws + p.off_xc);
+  a.ypart = reinterpret_cast<float*>(s.ws + p.off_ypart);
   a.T = p.T; a.K = p.K; a.P = p.P; a.E = p.E; a.I = p.I; a.H = p.H;
   int log2H = 0;
   while ((1 << log2H) < p.H) ++log2H;

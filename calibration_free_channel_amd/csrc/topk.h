@@ -1,142 +1,195 @@
 // Block-wide top-k selection with ties to the lower index (gfx950).
 //
 // Top-k keeps each token's k highest-scoring channels (arXiv:2610.37386,
-// abstract). Keys are the IEEE bit patterns of nonnegative float scores, so
+// abstract; aimodeling.com article, section "Swapping the threshold for
+// top-k"). Keys are the IEEE bit patterns of nonnegative float scores, so
 // unsigned order is score order. Every workgroup that selects from the same
-// keys returns the same set.
+// keys returns the same set, in ascending index order.
 //
-// Method: a 2048-bin histogram of the top 12 key bits (sign, exponent and three
-// mantissa bits) finds the bin that holds the k-th largest key; keys above it
-// are taken, keys below it dropped, and the keys inside it (few, since scores
-// spread over many bins) are ranked exactly by (key desc, index asc). If that
-// bin holds more than kListMax keys, a 4-pass 8-bit radix select settles it.
-// The selected indices are written in ascending order.
+// Method: radix select. Each thread holds its keys in registers (a contiguous
+// index range). The first digit is cut from the keys' own range: the smallest
+// shift s with (max >> s) - (min >> s) < 256, so the first histogram spreads
+// the keys over all 256 bins instead of piling them into the few bins of their
+// float exponent (LDS atomics to one address serialise). Each later pass takes
+// the next 8 bits below the settled ones and stops as soon as the boundary bin
+// is taken whole, or after the last bit; keys equal to the final prefix are
+// then taken lowest index first. Three rotating histograms let each pass clear
+// the next one, so a pass costs one barrier; every wavefront locates the
+// boundary bin itself with one DPP prefix scan, so no second barrier is needed.
+// An ordered compaction (one barrier) writes the result.
 #pragma once
 
-#include "cfm_internal.h"
+#include <stdint.h>
+#include <hip/hip_runtime.h>
 
 namespace cfm {
 
-constexpr int kHistBins = 2048;
-constexpr int kListMax = 256;
+constexpr int kTopkScratchWords = 4 * 256 + 32;    // three histograms, a dummy row, per-wave words
 
-struct TopkScratch {
-  uint32_t* hist;      // [kHistBins]
-  uint8_t* flag;       // [n] selected flags
-  uint32_t* lkey;      // [kListMax]
-  int32_t* lidx;       // [kListMax]
-  uint32_t* misc;      // [16 + NT/64]
-};
-
-__host__ __device__ constexpr size_t topk_scratch_bytes(int n, int nt) {
-  return 4ull * kHistBins + ((size_t(n) + 15) & ~size_t(15)) + 8ull * kListMax + 4ull * (16 + nt / 64) + 64;
+// Inclusive prefix sum over the 64 lanes of a wavefront: row shifts by 1..3
+// build sums of four, shifts by 4 and 8 (bank-masked) extend them over a row of
+// 16, and the row broadcasts of lanes 15 and 31 carry across rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int xi = (int)x;
+  int v = xi + __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, xi, 0x113, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xE, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xC, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return (uint32_t)v;
 }
 
-// Block exclusive scan of one uint32 per thread; returns the exclusive prefix
-// and writes the block total to *total. Two barriers.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const uint32_t s = wsum[w];
-    if (w < wv) base += s;
-    tot += s;
-  }
-  *total = tot;
-  __syncthreads();
-  return base + incl - v;
+// Maximum / minimum over the 64 lanes of a wavefront (the same DPP pattern
+// as the scan; lanes outside a shift keep the identity), returned in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  int v = (int)x;
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));
+  v = max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  int v = (int)x;
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x111, 0xF, 0xF, false));
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x112, 0xF, 0xF, false));
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x114, 0xF, 0xF, false));
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x118, 0xF, 0xF, false));
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x142, 0xA, 0xF, false));
+  v = min((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(-1, v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
+// The boundary bin of one pass, found by every lane of a wavefront: h[0..256)
+// holds the counts of the keys still in play (a higher bin = larger keys).
+// Returns the bin; need becomes the number still to take inside it and *m its
+// count.
+__device__ __forceinline__ uint32_t boundary_digit(const uint32_t* h, uint32_t& need, uint32_t* m) {
+  const int lane = threadIdx.x & 63;
+  const uint4 q4 = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);   // bins 252-4l .. 255-4l
+  const uint32_t s = q4.x + q4.y + q4.z + q4.w;
+  const uint32_t incl = wave_incl_scan(s);
+  const unsigned long long hit = __ballot(incl >= need);
+  const int L = __builtin_ffsll((long long)hit) - 1;
+  uint32_t run = __builtin_amdgcn_readlane(incl - s, L);      // keys in higher bins
+  const uint32_t c0 = __builtin_amdgcn_readlane(q4.w, L);     // bin 255 - 4L
+  const uint32_t c1 = __builtin_amdgcn_readlane(q4.z, L);
+  const uint32_t c2 = __builtin_amdgcn_readlane(q4.y, L);
+  const uint32_t c3 = __builtin_amdgcn_readlane(q4.x, L);
+  const uint32_t r1 = run + c0, r2 = r1 + c1, r3 = r2 + c2;
+  const uint32_t q = (r1 < need) + (r2 < need) + (r3 < need);   // r1 <= r2 <= r3
+  *m = q == 0 ? c0 : q == 1 ? c1 : q == 2 ? c2 : c3;
+  run = q == 0 ? run : q == 1 ? r1 : q == 2 ? r2 : r3;
+  need -= run;
+  return (uint32_t)(255 - 4 * L) - q;
+}
+
+// Per-thread key range of an n-key selection: thread t holds indices
+// [t per, t per + cnt) with per = ceil(n / NT).
 template <int NT>
-__device__ void block_topk(const uint32_t* key, int n, int k, int32_t* out_idx, const TopkScratch& s,
-                           uint32_t* radix_scratch) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ int topk_range(int n, int* cnt) {
+  const int per = (n + NT - 1) / NT;
+  const int i0 = min(n, (int)threadIdx.x * per);
+  *cnt = min(n, i0 + per) - i0;
+  return i0;
+}
+
+// Selects the k largest of n keys by (key desc, index asc) and writes their
+// indices in ascending order to out_idx[0..k) (LDS). kr[0..cnt) are this
+// thread's keys for indices [i0, i0 + cnt) as given by topk_range (requires
+// ceil(n / NT) <= KPT and n < 65536). scratch: kTopkScratchWords words of LDS,
+// 16-byte aligned. Called by the whole workgroup; ends with a barrier.
+template <int NT, int KPT>
+__device__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
+                           uint32_t* scratch) {
+  static_assert(NT == 256, "four wavefronts");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (k <= 0) return;
   if (k >= n) {
     for (int i = tid; i < n; i += NT) out_idx[i] = i;
     __syncthreads();
     return;
   }
-  uint32_t* wsum = s.misc + 16;
-  // 1. histogram of the top 12 bits
-  for (int b = tid; b < kHistBins; b += NT) s.hist[b] = 0;
-  if (tid == 0) s.misc[2] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) atomicAdd(&s.hist[key[i] >> 20], 1u);
-  __syncthreads();
-  // 2. the bin of the k-th largest key: thread t owns bins counted from the top
-  constexpr int BPT = kHistBins / NT;
-  uint32_t cnt = 0;
+  uint32_t* hist = scratch;
+  uint32_t* dummy = scratch + 3 * 256;     // sink for the stores of keys not taken
+  uint32_t* red = scratch + 4 * 256;       // [0, 8): per-wave min / max; [8, 12): per-wave totals
+  // keys beyond this thread's range become a sentinel above every real key
+  // (real keys are nonnegative floats, below 2^31), which no pass counts
+  uint32_t kk[KPT];
+  uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
-  for (int u = 0; u < BPT; ++u) cnt += s.hist[kHistBins - 1 - (tid * BPT + u)];
-  uint32_t total;
-  const uint32_t before = block_excl_scan<NT>(cnt, wsum, &total);
-  if (before < (uint32_t)k && before + cnt >= (uint32_t)k) {
-    uint32_t run = before;
-    for (int u = 0; u < BPT; ++u) {
-      const int b = kHistBins - 1 - (tid * BPT + u);
-      const uint32_t h = s.hist[b];
-      if (run + h >= (uint32_t)k) { s.misc[0] = (uint32_t)b; s.misc[1] = run; break; }
-      run += h;
-    }
+  for (int j = 0; j < KPT; ++j) {
+    kk[j] = j < cnt ? kr[j] : ~0u;
+    kmin = min(kmin, kk[j]);
+    kmax = max(kmax, j < cnt ? kk[j] : 0u);
   }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { red[2 * wv] = kmin; red[2 * wv + 1] = kmax; }
+  hist[tid] = 0;
   __syncthreads();
-  const uint32_t bstar = s.misc[0];
-  const uint32_t need = (uint32_t)k - s.misc[1];
-  const uint32_t m = s.hist[bstar];
-  if (m > (uint32_t)kListMax && need != m) {
-    block_topk_ascending<NT>(key, n, k, out_idx, radix_scratch);
-    return;
+  {
+    const uint4 a = *reinterpret_cast<const uint4*>(red);
+    const uint4 b = *reinterpret_cast<const uint4*>(red + 4);
+    kmin = min(min(a.x, a.z), min(b.x, b.z));
+    kmax = max(max(a.y, a.w), max(b.y, b.w));
   }
-  // 3. flags: above the bin -> taken; inside it -> taken when all of it is needed,
-  //    otherwise collected for exact ranking
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t b = key[i] >> 20;
-    uint8_t f = b > bstar ? 1 : 0;
-    if (b == bstar) {
-      if (need == m) {
-        f = 1;
-      } else {
-        const uint32_t slot = atomicAdd(&s.misc[2], 1u);
-        s.lkey[slot] = key[i];
-        s.lidx[slot] = i;
-      }
+  int s = kmax == kmin ? 0 : max(0, 24 - __builtin_clz(kmax - kmin));
+  if ((kmax >> s) - (kmin >> s) > 255u) ++s;
+  uint32_t base = kmin >> s;       // digit = (key >> s) - base
+  uint32_t lim = (kmax >> s) - base;   // digits in play: 0 .. lim
+  int S = 32;                      // settled: (key >> S) == V (nothing settled yet)
+  uint32_t V = 0, need = (uint32_t)k, m = 0;
+  for (int pass = 0;; ++pass) {
+    uint32_t* h = hist + 256 * (pass % 3);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      // a key is in play iff its digit lies in 0..lim (keys with other settled
+      // digits, and the sentinel, fall outside); keys out of play add 0 to a
+      // bin of their own lane, so they cause no conflicts
+      const uint32_t d = (kk[j] >> s) - base;
+      const bool in = d <= lim;
+      atomicAdd(&h[in ? d : (uint32_t)lane], in ? 1u : 0u);
     }
-    s.flag[i] = f;
-  }
-  __syncthreads();
-  if (need != m) {
-    for (int j = tid; j < (int)m; j += NT) {
-      const uint32_t kj = s.lkey[j];
-      const int ij = s.lidx[j];
-      uint32_t rank = 0;
-      for (int q = 0; q < (int)m; ++q) {
-        const uint32_t kq = s.lkey[q];
-        rank += (kq > kj) || (kq == kj && s.lidx[q] < ij);
-      }
-      if (rank < need) s.flag[ij] = 1;
-    }
+    hist[256 * ((pass + 1) % 3) + tid] = 0;      // the next pass's histogram
     __syncthreads();
+    V = base + boundary_digit(h, need, &m);
+    S = s;
+    if (m == need || S == 0) break;
+    s = max(S - 8, 0);
+    base = V << (S - s);
+    lim = (1u << (S - s)) - 1u;
   }
-  // 4. ordered compaction over contiguous index ranges
-  const int per = (n + NT - 1) / NT;
-  const int i0 = tid * per, i1 = min(n, i0 + per);
-  uint32_t c = 0;
-  for (int i = i0; i < i1; ++i) c += s.flag[i];
-  uint32_t tot;
-  uint32_t pos = block_excl_scan<NT>(c, wsum, &tot);
-  for (int i = i0; i < i1; ++i)
-    if (s.flag[i]) out_idx[pos++] = i;
+  uint32_t nd = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t v = kk[j] >> S;       // the sentinel is above V: count it, never write it
+    nd += v > V;
+    ne += v == V;
+  }
+  nd -= (uint32_t)(KPT - cnt);
+  const uint32_t packed = (nd << 16) | ne;
+  const uint32_t incl = wave_incl_scan(packed);
+  if (lane == 63) red[8 + wv] = incl;
+  __syncthreads();
+  const uint4 wt = *reinterpret_cast<const uint4*>(red + 8);
+  const uint32_t basew = (wv > 0 ? wt.x : 0u) + (wv > 1 ? wt.y : 0u) + (wv > 2 ? wt.z : 0u);
+  const uint32_t ex = basew + incl - packed;
+  uint32_t d = ex >> 16, e = ex & 0xFFFFu;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t v = kk[j] >> S;
+    const bool gt = j < cnt && v > V, eq = v == V;
+    const bool take = gt || (eq && e < need);
+    const uint32_t pos = gt ? d + min(e, need) : d + e;
+    *(take ? reinterpret_cast<uint32_t*>(out_idx) + pos : dummy + tid) = (uint32_t)(i0 + j);
+    d += gt;
+    e += eq;
+  }
   __syncthreads();
 }
 
