@@ -35,6 +35,7 @@ struct ForwardPlan {
   int cpw;        // candidates (selected) or channels (dense) per workgroup in the exact phase
   int nhs;        // 64-column output slices per token
   size_t lds;     // dynamic LDS bytes per workgroup
+  int pre;        // candidate rows prefetched into LDS (selected pass)
   size_t off_seq, off_err, off_ctr;      // u32 [256], u32, u32 [T][nhs]
   size_t off_xh, off_xz, off_xc;         // tagged u64 [P][I], [P][nw][r], [P][c]
   size_t off_ypart;                      // f32 [P][H]

@@ -46,6 +46,7 @@ constexpr int kOnes = kPlanes;                // MFMA column of constant ones (r
 constexpr int kDShift = 7;                    // x~ in units of 2^(7 - F0) before the digit split
 constexpr unsigned kSpinLimit = 1u << 20;     // polls of one exchanged value before the launch fails
 constexpr int kSeqSlots = 256;                // launch sequence slots (one per possible workgroup)
+constexpr int kZeroExp = 255;                 // fixed-point exponent of an all-zero block (any value works)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -73,6 +74,13 @@ __device__ __forceinline__ uint32_t ld_u(const uint32_t* p) {
 __device__ __forceinline__ void st_u(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Loads of values that no workgroup changes during the launch, through the
+// scalar data cache (which is invalidated at each dispatch): the router ids,
+// and this workgroup's sequence slot (read before the workgroup rewrites it at
+// its end; no other workgroup touches it).
+typedef __attribute__((address_space(4))) const uint32_t* const_u32_p;
+__device__ __forceinline__ uint32_t ld_scalar(const void* p) { return *(const_u32_p)p; }
 
 // ------------------------------------------------------------------ tagged exchange
 
@@ -189,6 +197,7 @@ struct FusedArgs {
   uint64_t* xc;      // [P][c]  exact activations of the candidates
   float* ypart;      // [P][H]
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
+  int pre;           // candidate Bt rows and down rows of the slice prefetched into LDS
 };
 
 struct Lds {
@@ -207,9 +216,11 @@ struct Lds {
   float* red;        // reduction scratch
   float* gu;         // [2][cpw] gate / up dots of the exact phase
   uint32_t* tks;     // top-k scratch
+  uint8_t* btc;      // [c][r] Bt rows of the candidates (BF16), when prefetched
+  uint8_t* dnc;      // [c][64] down rows of the candidates for this workgroup's slice, when prefetched
 };
 
-__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cpw, size_t* off) {
+__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cpw, int pre, size_t* off) {
   size_t o = 0;
   int n = 0;
   auto take = [&](size_t b) { off[n++] = o; o = (o + b + 15) & ~size_t(15); };
@@ -230,12 +241,16 @@ __host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, 
   take(4 * (size_t)(32 * 64 + 64 > 2 * NT ? 32 * 64 + 64 : 2 * NT));   // >= 8 NT, >= groups r
   take(8 * (size_t)(cpw > 1 ? cpw : 1));
   take(4 * (size_t)kTopkScratchWords);
+  // prefetch buffers, in whole 1 KB wavefront transfers
+  const size_t nbt = pre ? (size_t)c * (r / 8) : 0, ndn = pre ? (size_t)c * 8 : 0;
+  take(16 * ((nbt + 63) / 64 * 64));
+  take(16 * ((ndn + 63) / 64 * 64));
   return o;
 }
 
 __device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
-  size_t off[16];
-  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, off);
+  size_t off[20];
+  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, a.pre, off);
   Lds L;
   L.xs = reinterpret_cast<int32_t*>(smem + off[0]);
   L.limb = smem + off[1];
@@ -252,6 +267,8 @@ __device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
   L.red = reinterpret_cast<float*>(smem + off[12]);
   L.gu = reinterpret_cast<float*>(smem + off[13]);
   L.tks = reinterpret_cast<uint32_t*>(smem + off[14]);
+  L.btc = smem + off[15];
+  L.dnc = smem + off[16];
   return L;
 }
 
@@ -264,20 +281,21 @@ __device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
 // row sums of the codes, which remove the offset: t . floor(X~ / 2^7) =
 // sum_l 16^l D_l - 2^23 D_ones.
 
-// The exponent F0 from the bf16 bit patterns of this thread's values (mx: the
-// largest |x| pattern it holds); one barrier.
+// F0 from the largest |x| bit pattern mx of the token (0 for an all-zero row).
+__device__ __forceinline__ int exponent_from_max(uint32_t mx, int log2H) {
+  if (mx == 0) return kZeroExp;
+  const int E = (int)((mx >> 7) & 0xFF) - 126;          // max |x| < 2^E
+  return 30 - log2H - E;
+}
+// The same from this thread's values, over the workgroup (one barrier).
 __device__ __forceinline__ int fixed_exponent(uint32_t mx, int log2H, uint32_t* wred) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   mx = wave_max_u32(mx);
   if (lane == 0) wred[wv] = mx;
   __syncthreads();
   const uint4 m4 = *reinterpret_cast<const uint4*>(wred);
-  mx = max(max(m4.x, m4.y), max(m4.z, m4.w));
-  if (mx == 0) return 0;
-  const int E = (int)((mx >> 7) & 0xFF) - 126;          // max |x| < 2^E
-  return 30 - log2H - E;
+  return exponent_from_max(max(max(m4.x, m4.y), max(m4.z, m4.w)), log2H);
 }
-
 __device__ __forceinline__ int32_t fix_value(uint32_t xb, int8_t s, int F0) {
   const float f = ldexpf(__uint_as_float(xb << 16), F0);   // exact scaling; |f| < 2^(30 - log2 H)
   const int32_t q = (int32_t)rintf(f);
@@ -314,23 +332,44 @@ __device__ __forceinline__ void put_digit_planes(const Lds& L, int Hp, int i0, c
 }
 
 // Butterfly of one lane stage: partner p, this lane upper (bit set) or lower.
-__device__ __forceinline__ int32_t bfly(int32_t v, int32_t p, bool upper) { return upper ? p - v : v + p; }
+__device__ __forceinline__ int32_t bfly(int32_t v, int32_t p, bool upper) {
+  const int32_t m = upper ? -1 : 0;               // p + v (lower lane) or p - v (upper lane)
+  return p + (v ^ m) + (m & 1);
+}
 
 // x~ for H = 256 EPT with EPT >= 4 (H >= 1024). Thread t holds i = EPT t + q:
 // in-register stages for the low log2 EPT bits, VALU lane exchanges for the
-// next six, one LDS exchange among the four wavefronts for the top two. xb:
-// this thread's EPT BF16 patterns; sg: its EPT signs. Returns F0.
+// next six, one LDS exchange among the four wavefronts for the top two. Each
+// wavefront scales its quarter by its own F0 (no barrier for the scale); at the
+// exchange the quarters are brought to the smallest F0 of the four by an exact
+// right shift (floor), so the result is X~ for that F0 with each input rounded
+// once to its own grid and once more to the common one. xq: this thread's EPT
+// BF16 values as loaded (16-byte words; 8 bytes for EPT 4), sq: its EPT signs
+// as loaded. Returns the common F0.
 template <int EPT>
-__device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint32_t* xb, const int8_t* sg,
-                           uint32_t* wred) {
+__device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint4* xq, const uint32_t* sq,
+                           int* wf0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t xb[EPT];
+  int8_t sg[EPT];
+#pragma unroll
+  for (int g = 0; g < (EPT + 7) / 8; ++g) {
+    const uint32_t ww[4] = {xq[g].x, xq[g].y, xq[g].z, xq[g].w};
+#pragma unroll
+    for (int q = 0; q < 8 && 8 * g + q < EPT; ++q) xb[8 * g + q] = (q & 1) ? ww[q >> 1] >> 16 : ww[q >> 1] & 0xFFFFu;
+  }
+#pragma unroll
+  for (int g = 0; g < EPT / 4; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sg[4 * g + q] = (int8_t)(sq[g] >> (8 * q));
   uint32_t mx = 0;
 #pragma unroll
   for (int q = 0; q < EPT; ++q) mx = max(mx, xb[q] & 0x7FFFu);
-  const int F0 = fixed_exponent(mx, a.log2H, wred);
+  // |partial sums of a quarter| <= 2^(30 - log2 H) H / 4 = 2^28
+  const int F0w = exponent_from_max(wave_max_u32(mx), a.log2H);
   int32_t v[EPT];
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) v[q] = fix_value(xb[q], sg[q], F0);
+  for (int q = 0; q < EPT; ++q) v[q] = fix_value(xb[q], sg[q], F0w);
 #pragma unroll
   for (int h = 1; h < EPT; h <<= 1)
 #pragma unroll
@@ -353,7 +392,11 @@ __device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint32_t* xb,
 #pragma unroll
   for (int g = 0; g < EPT / 4; ++g)
     reinterpret_cast<int4*>(mine)[g] = make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+  if (lane == 0) wf0[wv] = F0w;
   __syncthreads();
+  const int4 f4 = *reinterpret_cast<const int4*>(wf0);
+  const int F0 = min(min(f4.x, f4.y), min(f4.z, f4.w));
+  const int fw[4] = {f4.x, f4.y, f4.z, f4.w};
   int32_t acc[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) acc[q] = 0;
@@ -361,13 +404,13 @@ __device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint32_t* xb,
   for (int w2 = 0; w2 < 4; ++w2) {
     const int32_t* src = L.xs + EPT * (64 * w2 + lane);
     const bool neg = __builtin_popcount(w2 & wv) & 1;
+    const int sh = min(fw[w2] - F0, 31);
 #pragma unroll
     for (int g = 0; g < EPT / 4; ++g) {
       const int4 u = reinterpret_cast<const int4*>(src)[g];
-      acc[4 * g] += neg ? -u.x : u.x;
-      acc[4 * g + 1] += neg ? -u.y : u.y;
-      acc[4 * g + 2] += neg ? -u.z : u.z;
-      acc[4 * g + 3] += neg ? -u.w : u.w;
+      const int32_t u4[4] = {u.x >> sh, u.y >> sh, u.z >> sh, u.w >> sh};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[4 * g + q] += neg ? -u4[q] : u4[q];
     }
   }
   put_digit_planes<EPT>(L, a.H, EPT * tid, acc);
@@ -452,11 +495,36 @@ __device__ __forceinline__ uint4 sketch_item(const FusedArgs& a, int e, int j0, 
   const int rho = 16 * wv + (lane & 15);
   const int rowb = a.H / 4;
   const int off = 64 * s + 16 * (lane >> 4);
-  if (rho < 2 * cwk && off < rowb) {
-    const int j = j0 + (rho < cwk ? rho : rho - cwk);
-    return ld16((rho < cwk ? a.tg : a.tu) + ((size_t)e * a.I + j) * rowb + off);
+  // every lane loads from a valid address (no branch around the load, so the
+  // request is not held back); rows past the sub-chunk only reach D rows that
+  // are never read, and bytes past H / 4 are masked where the operand is built
+  const int rr = rho < 2 * cwk ? rho : 0;
+  const int j = j0 + (rr < cwk ? rr : rr - cwk);
+  return ld16((rr < cwk ? a.tg : a.tu) + ((size_t)e * a.I + j) * rowb + (off < rowb ? off : 0));
+}
+
+// This thread's row scale for a sub-chunk: thread c < 2 cwk takes the gate scale
+// of channel c (c < cwk) or the up scale of channel c - cwk (other threads: a
+// value that is not used).
+__device__ __forceinline__ float load_scale(const FusedArgs& a, int e, int j0, int cwk) {
+  const int tid = threadIdx.x;
+  const int c = min(tid, 2 * cwk - 1);
+  return c < cwk ? a.sg[(size_t)e * a.I + j0 + c] : a.su[(size_t)e * a.I + j0 + c - cwk];
+}
+// Bt values of a sub-chunk for thread (zl, zg): channels zg, zg + groups, ...
+// (entries past the sub-chunk, and threads beyond the groups, load a value the
+// consumer skips).
+template <int N>
+__device__ __forceinline__ void load_bt(const FusedArgs& a, int e, int j0, int cwk, int zl, int zg, int groups,
+                                        uint32_t (&btv)[N]) {
+  const bool gok = zg < groups;
+  const uint16_t* src = a.r > 0 ? a.Bt : a.x;        // rank 0: nothing to read, a valid address
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int jj = zg + groups * u;
+    const bool ok = a.r > 0 && gok && jj < cwk;
+    btv[u] = src[ok ? ((size_t)e * a.I + j0 + jj) * a.r + zl : 0];
   }
-  return make_uint4(0, 0, 0, 0);
 }
 
 constexpr int kSketchPre = 8;   // super-blocks of the first sub-chunk requested up front
@@ -483,10 +551,12 @@ __device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int
       for (int u = 0; u < kSketchPre; ++u) {
         const int s = s0 + u;
         if (s < nsb) {
+          // codes past the row end (H < 256 only) were loaded from a clamped address
+          const uint32_t km = 64 * s + 16 * (lane >> 4) < a.H / 4 ? ~0u : 0u;
           const v8i d0 = digit_operand(L, Hp, s, 0);
           const v8i d1 = digit_operand(L, Hp, s, 1);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].x, w[u].y), d0, acc, 4, 0, 0, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].z, w[u].w), d1, acc, 4, 0, 0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].x & km, w[u].y & km), d0, acc, 4, 0, 0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(w[u].z & km, w[u].w & km), d1, acc, 4, 0, 0, 0, 0, 0);
         }
       }
     }
@@ -521,13 +591,14 @@ __device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int
 
 // h for items [q0, q1) of `chan` (null: channel = position), published as
 // out[q0 .. q1) with the tag. One wavefront per (row, matrix).
-template <int CH>
+template <int CH, typename Hook>
 __device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_t* chan, int q0, int q1,
-                           const uint4* xr, uint64_t* out, uint32_t tag) {
+                           const uint4* xr, uint64_t* out, uint32_t tag, Hook hook) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
   const int nchunk = H / 8;
   const int nitems = 2 * (q1 - q0);
   constexpr int RB = CH >= 16 ? 1 : (CH >= 8 ? 2 : 20 / CH);
+  bool hooked = false;
   for (int it0 = wv * RB; it0 < nitems; it0 += (NT / 64) * RB) {
     uint4 wr[RB][CH];
 #pragma unroll
@@ -543,6 +614,8 @@ __device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_
         wr[u][m] = (it < nitems && ci < nchunk) ? ld16(row + ci) : make_uint4(0, 0, 0, 0);
       }
     }
+    // requests issued after these rows do not delay them (loads complete in order)
+    if (!hooked) { hook(); hooked = true; }
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int it = it0 + u;
@@ -553,11 +626,81 @@ __device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_
       if (lane == 0 && it < nitems) L.gu[(it & 1) * a.cpw + (it >> 1)] = acc;
     }
   }
+  if (!hooked) hook();
   __syncthreads();
   for (int i = tid; i < q1 - q0; i += NT) put_tagged(out + q0 + i, silu_f32(L.gu[i]) * L.gu[a.cpw + i], tag);
 }
 
+// ------------------------------------------------------------------ prefetch of the candidates' rows
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+// 16 bytes per lane straight into LDS: lane l's bytes land at lds_base + 16 l
+// (lds_base uniform over the wavefront); counted like any other load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// Requests the Bt rows of all candidates ([c][r] BF16 into L.btc) and their
+// down rows for output columns [64 hs, 64 hs + 64) ([c][64] BF16 into L.dnc).
+// Lanes past the end repeat the last row (their bytes land in the padding).
+__device__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e, int hs) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int cpr = a.r / 8, nb = a.c * cpr;
+  for (int q = wv; q * 64 < nb; q += NT / 64) {
+    const int f = q * 64 + lane;
+    const int i = min(f / cpr, a.c - 1), cc = f % cpr;
+    lds_dma16(a.Bt + ((size_t)e * a.I + L.candp[i]) * a.r + 8 * cc, L.btc + (size_t)q * 1024);
+  }
+  const int nd = a.c * 8;
+  for (int q = wv; q * 64 < nd; q += NT / 64) {
+    const int f = q * 64 + lane;
+    const int i = min(f / 8, a.c - 1), l8 = f % 8;
+    lds_dma16(a.wd + ((size_t)e * a.I + L.candp[i]) * a.H + 64 * hs + 8 * l8, L.dnc + (size_t)q * 1024);
+  }
+}
+
+// Sum over the lanes of a wavefront that share (lane mod span): lane bits
+// log2(span) .. 5 (span a power of two, <= 64).
+__device__ __forceinline__ float sum_over_high_lanes(float v, int span) {
+  if (span < 2) v += __int_as_float(lane_xor<1>(__float_as_int(v)));
+  if (span < 4) v += __int_as_float(lane_xor<2>(__float_as_int(v)));
+  if (span < 8) v += __int_as_float(lane_xor<4>(__float_as_int(v)));
+  if (span < 16) v += __int_as_float(lane_xor<8>(__float_as_int(v)));
+  if (span < 32) v += __int_as_float(lane_xor<16>(__float_as_int(v)));
+  if (span < 64) v += __int_as_float(lane_xor<32>(__float_as_int(v)));
+  return v;
+}
+// Sum over aligned groups of `span` consecutive lanes (lane bits 0 .. log2(span)-1).
+__device__ __forceinline__ float sum_over_low_lanes(float v, int span) {
+  if (span > 1) v += __int_as_float(lane_xor<1>(__float_as_int(v)));
+  if (span > 2) v += __int_as_float(lane_xor<2>(__float_as_int(v)));
+  if (span > 4) v += __int_as_float(lane_xor<4>(__float_as_int(v)));
+  if (span > 8) v += __int_as_float(lane_xor<8>(__float_as_int(v)));
+  if (span > 16) v += __int_as_float(lane_xor<16>(__float_as_int(v)));
+  if (span > 32) v += __int_as_float(lane_xor<32>(__float_as_int(v)));
+  return v;
+}
+
 // ------------------------------------------------------------------ phase C: down + combine
+
+// After this workgroup's y slice is stored: the last of the token's K pairs to
+// arrive writes out[t][64 hs .. 64 hs + 64) = sum_q w_q y_q, in BF16.
+__device__ void combine_slice(const FusedArgs& a, int t, int hs, int* s_flag, uint32_t tag) {
+  const int tid = threadIdx.x, c0 = hs * 64;
+  unsigned* cc = a.ctr + (size_t)t * a.nhs + hs;
+  if (last_of(cc, (unsigned)a.K, s_flag)) {
+    if (tid < 64) {
+      float o = 0.f;
+      for (int q = 0; q < a.K; ++q)
+        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + c0 + tid);
+      const bool bad = ld_u(a.fail) == tag;
+      a.out[(size_t)t * a.H + c0 + tid] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
+    }
+  }
+  __syncthreads();
+}
 
 // Recovery term of a 64-column slice into L.red[32*64 + 0..64): A[e][c0 + hh][:] . z.
 // apre: the slice prefetched as 16-byte chunks f = tid + NT u (valid when r % 8 == 0).
@@ -631,17 +774,7 @@ __device__ void down_slice(const FusedArgs& a, const Lds& L, int p, int t, int e
     if (add_rec) y += L.red[32 * 64 + tid];
     st_f(a.ypart + (size_t)p * a.H + c0 + tid, y);
   }
-  unsigned* cc = a.ctr + (size_t)t * a.nhs + hs;
-  if (last_of(cc, (unsigned)a.K, s_flag)) {
-    if (tid < 64) {
-      float o = 0.f;
-      for (int q = 0; q < a.K; ++q)
-        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + c0 + tid);
-      const bool bad = ld_u(a.fail) == tag;
-      a.out[(size_t)t * a.H + c0 + tid] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
-    }
-  }
-  __syncthreads();
+  combine_slice(a, t, hs, s_flag, tag);
 }
 
 // ------------------------------------------------------------------ exchange reads
@@ -671,11 +804,9 @@ __device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int
 
 // ------------------------------------------------------------------ launch tag
 
-__device__ __forceinline__ uint32_t launch_tag(const FusedArgs& a, uint32_t* s_tag) {
-  if (threadIdx.x == 0) *s_tag = ld_u(a.seq + blockIdx.x) + 1u;
-  __syncthreads();
-  return *s_tag;
-}
+// Every thread reads the tag itself (no barrier); it is first needed when this
+// workgroup publishes a value.
+__device__ __forceinline__ uint32_t launch_tag(const FusedArgs& a) { return ld_scalar(a.seq + blockIdx.x) + 1u; }
 // Every sequence slot is rewritten by exactly one workgroup of the launch.
 __device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) {
   if (threadIdx.x == 0)
@@ -688,93 +819,71 @@ template <int EPT>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) uint32_t wred[NT / 64];
+  __shared__ __align__(16) int wf0[NT / 64];
   __shared__ int s_flag;
-  __shared__ uint32_t s_tag;
   const Lds L = carve(smem, a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int nw = a.nw, H = a.H, r = a.r;
   constexpr int CH = EPT >= 2 ? EPT / 2 : 1;        // 16-byte chunks of x per lane (H / 512)
-  const uint32_t tag = launch_tag(a, &s_tag);
+  const uint32_t tag = launch_tag(a);
   const int groups = r > 0 ? NT / r : 1;             // recovery partial sums: thread (l, g)
   const int zl = r > 0 ? tid % r : 0, zg = r > 0 ? tid / r : groups;
 
   for (int slot = blockIdx.x; slot < a.P * nw; slot += a.G) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
-    const int e = a.ids[p];
     const int j0 = min(a.I, w * a.cw), j1 = min(a.I, j0 + a.cw);
     const int hs0 = w;                              // first output slice of this workgroup
     const bool one_slice = hs0 < a.nhs && hs0 + nw >= a.nhs;
 
-    // ---- requests that need no selection: x and signs first, then the sketch
-    //      rows, scales and Bt rows of the first sub-chunk, and the A slice
-    uint32_t xb[EPT >= 4 ? EPT : 1];
-    int8_t sgn[EPT >= 4 ? EPT : 1];
+    // ---- requests that need no selection, issued before anything waits on
+    //      them: x (this thread's elements and the whole row) and signs first,
+    //      then the sketch rows, scales and Bt rows of the first sub-chunk, and
+    //      the A slice
+    uint4 xq[EPT >= 8 ? EPT / 8 : 1];
+    uint32_t sq[EPT >= 4 ? EPT / 4 : 1];
     if constexpr (EPT >= 4) {
       const uint16_t* xt = a.x + (size_t)t * H + EPT * tid;
+      if constexpr (EPT >= 8) {
 #pragma unroll
-      for (int g = 0; g < EPT / 8; ++g) {
-        const uint4 u = ld16c(xt + 8 * g);
-        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xb[8 * g + q] = (q & 1) ? ww[q >> 1] >> 16 : ww[q >> 1] & 0xFFFFu;
-      }
-      if constexpr (EPT == 4) {
+        for (int g = 0; g < EPT / 8; ++g) xq[g] = ld16c(xt + 8 * g);
+      } else {
         const uint2 u = *reinterpret_cast<const uint2*>(xt);
-        xb[0] = u.x & 0xFFFFu; xb[1] = u.x >> 16; xb[2] = u.y & 0xFFFFu; xb[3] = u.y >> 16;
+        xq[0] = make_uint4(u.x, u.y, 0, 0);
       }
 #pragma unroll
-      for (int g = 0; g < EPT / 4; ++g) {
-        const uint32_t s4 = *reinterpret_cast<const uint32_t*>(a.signs + EPT * tid + 4 * g);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sgn[4 * g + q] = (int8_t)(s4 >> (8 * q));
-      }
+      for (int g = 0; g < EPT / 4; ++g) sq[g] = *reinterpret_cast<const uint32_t*>(a.signs + EPT * tid + 4 * g);
     }
+    const int e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
     const int cwk0 = min(j1 - j0, kSubChunk);
+    // (every prefetch below is issued on every path, so no later wait has to
+    //  assume that some of them were skipped; unused ones read valid addresses)
     uint4 spre[kSketchPre];
 #pragma unroll
-    for (int u = 0; u < kSketchPre; ++u)
-      spre[u] = u < (H + 255) / 256 ? sketch_item(a, e, j0, cwk0, u) : make_uint4(0, 0, 0, 0);
-    float sgu = 0.f;
-    if (tid < 2 * cwk0) sgu = tid < cwk0 ? a.sg[(size_t)e * a.I + j0 + tid] : a.su[(size_t)e * a.I + j0 + tid - cwk0];
+    for (int u = 0; u < kSketchPre; ++u) spre[u] = sketch_item(a, e, j0, cwk0, min(u, (H + 255) / 256 - 1));
+    // (loads below are unconditional at clamped addresses, masked afterwards)
+    float sgu = load_scale(a, e, j0, cwk0);
     constexpr int kBtPer = kMaxRank * kSubChunk / NT;   // Bt values per thread and sub-chunk (<= 16)
-    uint16_t btv[kBtPer];
-#pragma unroll
-    for (int u = 0; u < kBtPer; ++u) {
-      const int jj = zg + groups * u;
-      btv[u] = (r > 0 && zg < groups && jj < cwk0) ? a.Bt[((size_t)e * a.I + j0 + jj) * r + zl] : (uint16_t)0;
-    }
-    uint4 apre[4];
-    const bool have_apre = one_slice && r > 0 && r % 8 == 0 && 8 * r <= 4 * NT;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = tid + NT * u;
-      apre[u] = (have_apre && f < 8 * r) ? ld16(a.A + ((size_t)e * H + hs0 * 64) * r + 8 * (size_t)f)
-                                         : make_uint4(0, 0, 0, 0);
-    }
-
+    uint32_t btv[kBtPer];
+    load_bt(a, e, j0, cwk0, zl, zg, groups, btv);
     // ---- phase A: screen this workgroup's channels, sub-chunk by sub-chunk
     int F0;
-    if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(a, L, xb, sgn, wred);
+    if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(a, L, xq, sq, wf0);
     else F0 = rotate_small(a, L, t, wred);
     float zacc = 0.f;                               // partial recovery sum for (zl, zg)
     for (int sj0 = j0; sj0 < j1; sj0 += kSubChunk) {
       const int cwk = min(j1 - sj0, kSubChunk);
       const bool first = sj0 == j0;
       if (!first) {
-        if (tid < 2 * cwk) sgu = tid < cwk ? a.sg[(size_t)e * a.I + sj0 + tid] : a.su[(size_t)e * a.I + sj0 + tid - cwk];
-#pragma unroll
-        for (int u = 0; u < kBtPer; ++u) {
-          const int jj = zg + groups * u;
-          btv[u] = (r > 0 && zg < groups && jj < cwk) ? a.Bt[((size_t)e * a.I + sj0 + jj) * r + zl] : (uint16_t)0;
-        }
+        sgu = load_scale(a, e, sj0, cwk);
+        load_bt(a, e, sj0, cwk, zl, zg, groups, btv);
       }
       screen_chunk(a, L, p, e, sj0, cwk, F0, spre, first, sgu, tag);
       if (r > 0 && zg < groups) {
 #pragma unroll
         for (int u = 0; u < kBtPer; ++u) {
           const int jj = zg + groups * u;
-          if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32(btv[u]);
+          if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32((uint16_t)btv[u]);
         }
       }
       __syncthreads();
@@ -787,6 +896,16 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         for (int g = 0; g < groups; ++g) s += L.red[g * r + l];
         put_tagged(a.xz + ((size_t)p * nw + w) * r + l, s, tag);
       }
+    }
+
+    // the A slice of the recovery term: requested now, used at the end
+    uint4 apre[4];
+    const bool have_apre = one_slice && r > 0 && r % 8 == 0 && 8 * r <= 4 * NT;
+    {
+      const uint16_t* abase = have_apre ? a.A + ((size_t)e * H + hs0 * 64) * r : a.x;
+      const int nA = have_apre ? 8 * r : 1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) apre[u] = ld16(abase + 8 * (size_t)min(tid + NT * u, nA - 1));   // past 8 r: unused
     }
 
     // ---- top-c candidates (identical in every workgroup of the pair)
@@ -838,11 +957,12 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       uint4 xr[CH];
       const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
-      for (int m = 0; m < CH; ++m) {
-        const int ci = lane + 64 * m;
-        xr[m] = ci < H / 8 ? ld16c(xg + ci) : make_uint4(0, 0, 0, 0);
-      }
-      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag);
+      for (int m = 0; m < CH; ++m) xr[m] = ld16c(xg + min(lane + 64 * m, H / 8 - 1));   // past H / 8: times zero rows
+      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag, [&] {
+        if (a.pre && hs0 < a.nhs) prefetch_candidate_rows(a, L, e, hs0);
+      });
+    } else if (a.pre && hs0 < a.nhs) {
+      prefetch_candidate_rows(a, L, e, hs0);
     }
 
     // ---- top-k kept set and recovery coefficients
@@ -886,6 +1006,61 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = L.keep[i];
     } else {
       __syncthreads();
+    }
+    if (a.pre) {
+      // candidate rows are in LDS: z, the recovery term and the down projection
+      // of this workgroup's slice need no further memory reads
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (r > 0) {
+        const int cpr = r / 8, ng = NT / cpr;
+        const int cc = tid % cpr, g = tid / cpr;
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+        for (int m = g; m < a.k; m += ng)
+          fma8(acc, L.hh[L.keep[m]], *reinterpret_cast<const uint4*>(L.btc + (size_t)L.sel[m] * 2 * r + 16 * cc));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], cpr);
+        if (lane < cpr)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) L.red[(tid >> 6) * r + 8 * lane + u] = acc[u];
+        __syncthreads();
+        for (int l = tid; l < r; l += NT) L.zv[l] = L.zsum[l] - (L.red[l] + L.red[r + l] + L.red[2 * r + l] + L.red[3 * r + l]);
+        __syncthreads();
+      }
+      if (hs0 < a.nhs) {
+        float* rec = L.red + 4 * 128;                     // [64] recovery term of the slice
+        float* part = L.red + 4 * 128 + 64;               // [4][64] per-wavefront down partials
+        if (r > 0) {
+          const int cpr = r / 8;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int f = tid + NT * u;
+            float d = f < 64 * cpr ? dot8_f(apre[u], L.zv + 8 * (f % cpr)) : 0.f;
+            d = sum_over_low_lanes(d, cpr);
+            if (f < 64 * cpr && f % cpr == 0) rec[f / cpr] = d;
+          }
+        }
+        const int l8 = tid & 7, g = tid >> 3;
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+        for (int m = g; m < a.k; m += NT / 8)
+          fma8(acc, L.hk[m], *reinterpret_cast<const uint4*>(L.dnc + (size_t)L.sel[m] * 128 + 16 * l8));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], 8);
+        if (lane < 8)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) part[(tid >> 6) * 64 + 8 * lane + u] = acc[u];
+        __syncthreads();
+        if (tid < 64) {
+          const float y = part[tid] + part[64 + tid] + part[128 + tid] + part[192 + tid] + (r > 0 ? rec[tid] : 0.f);
+          st_f(a.ypart + (size_t)p * H + hs0 * 64 + tid, y);
+        }
+        combine_slice(a, t, hs0, &s_flag, tag);
+      }
+      continue;
     }
     if (r > 0) {
       // z = zsum - sum_{j in S} hhat_j Bt[e][j]
@@ -944,16 +1119,15 @@ template <int EPT>
 __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_flag;
-  __shared__ uint32_t s_tag;
   const Lds L = carve(smem, a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int nw = a.nw, H = a.H;
   constexpr int CH = EPT >= 2 ? EPT / 2 : 1;
-  const uint32_t tag = launch_tag(a, &s_tag);
+  const uint32_t tag = launch_tag(a);
   for (int slot = blockIdx.x; slot < a.P * nw; slot += a.G) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
-    const int e = a.ids[p];
+    const int e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
     const int q0 = min(a.I, w * a.cpw), q1 = min(a.I, q0 + a.cpw);
     if (q0 < q1) {
       uint4 xr[CH];
@@ -963,7 +1137,7 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
         const int ci = lane + 64 * m;
         xr[m] = ci < H / 8 ? ld16c(xg + ci) : make_uint4(0, 0, 0, 0);
       }
-      exact_rows<CH>(a, L, e, nullptr, q0, q1, xr, a.xh + (size_t)p * a.I, tag);
+      exact_rows<CH>(a, L, e, nullptr, q0, q1, xr, a.xh + (size_t)p * a.I, tag, [] {});
     }
     // all activations of the pair
     {
@@ -1075,8 +1249,12 @@ ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) 
   fused_geometry(p, 256);
   p.cw = (I + p.nw - 1) / p.nw;
   p.cpw = std::max(1, (c + p.nw - 1) / p.nw);
-  size_t off[16];
-  p.lds = lds_layout(H, I, c, k, r, p.cpw, off);
+  size_t off[20];
+  // prefetch of the candidates' rows when every workgroup has at most one output
+  // slice and the buffers fit
+  const bool pre_ok = p.nw >= p.nhs && k > 0 && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0));
+  p.pre = pre_ok && lds_layout(H, I, c, k, r, p.cpw, 1, off) <= 160 * 1024 ? 1 : 0;
+  p.lds = lds_layout(H, I, c, k, r, p.cpw, p.pre, off);
   Carve cv;
   common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
@@ -1094,8 +1272,8 @@ ForwardPlan dense_plan(int T, int K, int E, int I, int H) {
   fused_geometry(p, 256);
   p.cw = 1;
   p.cpw = std::max(1, (I + p.nw - 1) / p.nw);
-  size_t off[16];
-  p.lds = lds_layout(H, I, 0, 0, 0, p.cpw, off);
+  size_t off[20];
+  p.lds = lds_layout(H, I, 0, 0, 0, p.cpw, 0, off);
   Carve cv;
   common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
@@ -1128,6 +1306,7 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   while ((1 << log2H) < p.H) ++log2H;
   a.log2H = log2H;
   a.k = p.k; a.c = p.c; a.r = p.r; a.nw = p.nw; a.cw = p.cw; a.cpw = p.cpw; a.nhs = p.nhs; a.G = p.G;
+  a.pre = p.pre;
   return a;
 }
 
