@@ -46,6 +46,7 @@ constexpr int kOnes = kPlanes;                // MFMA column of constant ones (r
 constexpr int kDShift = 7;                    // x~ in units of 2^(7 - F0) before the digit split
 constexpr unsigned kSpinLimit = 1u << 20;     // polls of one exchanged value before the launch fails
 constexpr int kSeqSlots = 256;                // launch sequence slots (one per possible workgroup)
+constexpr int kMaxNw = 32;                    // workgroups per pair (power of two)
 constexpr int kZeroExp = 255;                 // fixed-point exponent of an all-zero block (any value works)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -191,13 +192,13 @@ struct FusedArgs {
   uint16_t* out; int32_t *cand_out, *keep_out;
   uint32_t* seq;     // [256] launch sequence numbers
   uint32_t* fail;    // tag of the last launch whose wait expired
-  unsigned* ctr;     // [T][nhs] combine counters
+  unsigned* ctr;     // [T][32] combine counters (token, workgroup of the pair)
   uint64_t* xh;      // [P][I]  sketch activations (selected) / exact activations (dense)
   uint64_t* xz;      // [P][nw][r] partial recovery sums
   uint64_t* xc;      // [P][c]  exact activations of the candidates
   float* ypart;      // [P][H]
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
-  int pre;           // candidate Bt rows and down rows of the slice prefetched into LDS
+  int pre;           // column chunks per workgroup when the candidates' rows are prefetched into LDS, else 0
 };
 
 struct Lds {
@@ -215,6 +216,7 @@ struct Lds {
   float* zv;         // [r] recovery coefficients
   float* red;        // reduction scratch
   float* gu;         // [2][cpw] gate / up dots of the exact phase
+  float* part;       // [NT][8] phase C partial sums
   uint32_t* tks;     // top-k scratch
   uint8_t* btc;      // [c][r] Bt rows of the candidates (BF16), when prefetched
   uint8_t* dnc;      // [c][64] down rows of the candidates for this workgroup's slice, when prefetched
@@ -238,17 +240,18 @@ __host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, 
   take(4 * (size_t)c1);
   take(4 * (size_t)r1);
   take(4 * (size_t)r1);
-  take(4 * (size_t)(32 * 64 + 64 > 2 * NT ? 32 * 64 + 64 : 2 * NT));   // >= 8 NT, >= groups r
+  take(4 * (size_t)(32 * 64 + 64 > 8 * NT ? 32 * 64 + 64 : 8 * NT));   // >= 8 NT, >= groups r
   take(8 * (size_t)(cpw > 1 ? cpw : 1));
+  take(4 * (size_t)NT * 8);
   take(4 * (size_t)kTopkScratchWords);
   // prefetch buffers, in whole 1 KB wavefront transfers
-  const size_t nbt = pre ? (size_t)c * (r / 8) : 0, ndn = pre ? (size_t)c * 8 : 0;
+  const size_t nbt = pre ? (size_t)c * (r / 8) : 0, ndn = pre ? (size_t)c * pre : 0;   // pre: column chunks
   take(16 * ((nbt + 63) / 64 * 64));
   take(16 * ((ndn + 63) / 64 * 64));
   return o;
 }
 
-__device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
+__device__ __forceinline__ Lds carve(unsigned char* smem, const FusedArgs& a) {
   size_t off[20];
   lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, a.pre, off);
   Lds L;
@@ -266,9 +269,10 @@ __device__ Lds carve(unsigned char* smem, const FusedArgs& a) {
   L.zv = reinterpret_cast<float*>(smem + off[11]);
   L.red = reinterpret_cast<float*>(smem + off[12]);
   L.gu = reinterpret_cast<float*>(smem + off[13]);
-  L.tks = reinterpret_cast<uint32_t*>(smem + off[14]);
-  L.btc = smem + off[15];
-  L.dnc = smem + off[16];
+  L.part = reinterpret_cast<float*>(smem + off[14]);
+  L.tks = reinterpret_cast<uint32_t*>(smem + off[15]);
+  L.btc = smem + off[16];
+  L.dnc = smem + off[17];
   return L;
 }
 
@@ -347,7 +351,7 @@ __device__ __forceinline__ int32_t bfly(int32_t v, int32_t p, bool upper) {
 // BF16 values as loaded (16-byte words; 8 bytes for EPT 4), sq: its EPT signs
 // as loaded. Returns the common F0.
 template <int EPT>
-__device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint4* xq, const uint32_t* sq,
+__device__ __forceinline__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint4* xq, const uint32_t* sq,
                            int* wf0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t xb[EPT];
@@ -420,7 +424,7 @@ __device__ int rotate_fast(const FusedArgs& a, const Lds& L, const uint4* xq, co
 
 // x~ for small H (< 1024): LDS butterflies. Digits for i >= H (up to 256) are
 // written too; the sketch codes there are zero, so their value does not matter.
-__device__ int rotate_small(const FusedArgs& a, const Lds& L, int t, uint32_t* wred) {
+__device__ __forceinline__ int rotate_small(const FusedArgs& a, const Lds& L, int t, uint32_t* wred) {
   const int tid = threadIdx.x, H = a.H;
   const uint16_t* xt = a.x + (size_t)t * H;
   uint32_t mx = 0;
@@ -533,8 +537,11 @@ constexpr int kSketchPre = 8;   // super-blocks of the first sub-chunk requested
 // exchange. pre: the first kSketchPre items of this wavefront (if use_pre);
 // sgu: this thread's prefetched scale (thread c < 2 cwk: gate scale of channel
 // c, or up scale of channel c - cwk).
-__device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int j0, int cwk, int F0,
-                             const uint4* pre, bool use_pre, float sgu, uint32_t tag) {
+// ALLPRE: every super-block is among the prefetched items (H <= 256 kSketchPre),
+// so the loop below issues no loads (and no wait for later requests is forced).
+template <bool ALLPRE>
+__device__ __forceinline__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int j0, int cwk, int F0,
+                                             const uint4 (&pre)[kSketchPre], bool use_pre, float sgu, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Hp = max(a.H, 256);
   const int nsb = (a.H + 255) / 256;
@@ -545,7 +552,8 @@ __device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int
 #pragma unroll
       for (int u = 0; u < kSketchPre; ++u) {
         const int s = s0 + u;
-        w[u] = (use_pre && s0 == 0) ? pre[u] : (s < nsb ? sketch_item(a, e, j0, cwk, s) : make_uint4(0, 0, 0, 0));
+        if constexpr (ALLPRE) w[u] = pre[u];
+        else w[u] = (use_pre && s0 == 0) ? pre[u] : (s < nsb ? sketch_item(a, e, j0, cwk, s) : make_uint4(0, 0, 0, 0));
       }
 #pragma unroll
       for (int u = 0; u < kSketchPre; ++u) {
@@ -592,7 +600,7 @@ __device__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int
 // h for items [q0, q1) of `chan` (null: channel = position), published as
 // out[q0 .. q1) with the tag. One wavefront per (row, matrix).
 template <int CH, typename Hook>
-__device__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_t* chan, int q0, int q1,
+__device__ __forceinline__ void exact_rows(const FusedArgs& a, const Lds& L, int e, const int32_t* chan, int q0, int q1,
                            const uint4* xr, uint64_t* out, uint32_t tag, Hook hook) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
   const int nchunk = H / 8;
@@ -643,9 +651,10 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
 }
 
 // Requests the Bt rows of all candidates ([c][r] BF16 into L.btc) and their
-// down rows for output columns [64 hs, 64 hs + 64) ([c][64] BF16 into L.dnc).
-// Lanes past the end repeat the last row (their bytes land in the padding).
-__device__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e, int hs) {
+// down rows for output chunks [ck0, ck0 + nck) ([c][nck] 16-byte pieces into
+// L.dnc). Lanes past the end repeat the last row (their bytes land in the
+// padding).
+__device__ __forceinline__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e, int ck0, int nck) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int cpr = a.r / 8, nb = a.c * cpr;
   for (int q = wv; q * 64 < nb; q += NT / 64) {
@@ -653,11 +662,11 @@ __device__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e,
     const int i = min(f / cpr, a.c - 1), cc = f % cpr;
     lds_dma16(a.Bt + ((size_t)e * a.I + L.candp[i]) * a.r + 8 * cc, L.btc + (size_t)q * 1024);
   }
-  const int nd = a.c * 8;
+  const int nd = a.c * nck;
   for (int q = wv; q * 64 < nd; q += NT / 64) {
     const int f = q * 64 + lane;
-    const int i = min(f / 8, a.c - 1), l8 = f % 8;
-    lds_dma16(a.wd + ((size_t)e * a.I + L.candp[i]) * a.H + 64 * hs + 8 * l8, L.dnc + (size_t)q * 1024);
+    const int i = min(f / nck, a.c - 1), cc = f % nck;
+    lds_dma16(a.wd + ((size_t)e * a.I + L.candp[i]) * a.H + 8 * (ck0 + cc), L.dnc + (size_t)q * 1024);
   }
 }
 
@@ -683,98 +692,117 @@ __device__ __forceinline__ float sum_over_low_lanes(float v, int span) {
   return v;
 }
 
-// ------------------------------------------------------------------ phase C: down + combine
+// ------------------------------------------------------------------ phase C over a column range
+//
+// Output columns are split into 16-byte chunks (8 columns); workgroup w of a
+// pair owns chunks [w nck, (w + 1) nck), nck = max(1, H / 8 / nw) (a power of
+// two). The down projection reads each kept row's segment of those columns as
+// contiguous 16-byte pieces; the combine of the K pairs of a token happens once
+// per (token, w).
 
-// After this workgroup's y slice is stored: the last of the token's K pairs to
-// arrive writes out[t][64 hs .. 64 hs + 64) = sum_q w_q y_q, in BF16.
-__device__ void combine_slice(const FusedArgs& a, int t, int hs, int* s_flag, uint32_t tag) {
-  const int tid = threadIdx.x, c0 = hs * 64;
-  unsigned* cc = a.ctr + (size_t)t * a.nhs + hs;
-  if (last_of(cc, (unsigned)a.K, s_flag)) {
-    if (tid < 64) {
-      float o = 0.f;
-      for (int q = 0; q < a.K; ++q)
-        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + c0 + tid);
-      const bool bad = ld_u(a.fail) == tag;
-      a.out[(size_t)t * a.H + c0 + tid] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
+__device__ __forceinline__ int col_chunks(const FusedArgs& a) { return max(1, (a.H / 8) / a.nw); }
+
+// y[8 ck0 .. 8 (ck0 + ncb)) of pair p into the exchange buffer: the down
+// projection over rows[0..n) with coefficients hv, plus (use_rec) A z.
+// ncb: a power of two <= NT. Ends with a barrier.
+__device__ __forceinline__ void cols_block(const FusedArgs& a, const Lds& L, int p, int e, int ck0, int ncb,
+                           const int32_t* rows, const float* hv, int n, bool use_rec) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H;
+  float* rec = L.red;                      // [8 ncb] recovery term
+  float* part = L.part;                    // [NT][8] partial sums
+  if (use_rec && !(a.r % 8 == 0 && 64 % (a.r / 8) == 0)) {
+    // any other rank: one thread per column
+    for (int col = tid; col < 8 * ncb; col += NT) {
+      const uint16_t* arow = a.A + ((size_t)e * H + 8 * ck0 + col) * a.r;
+      float sacc = 0.f;
+      for (int l = 0; l < a.r; ++l) sacc += bf16_to_f32(arow[l]) * L.zv[l];
+      rec[col] = sacc;
     }
-  }
-  __syncthreads();
-}
-
-// Recovery term of a 64-column slice into L.red[32*64 + 0..64): A[e][c0 + hh][:] . z.
-// apre: the slice prefetched as 16-byte chunks f = tid + NT u (valid when r % 8 == 0).
-__device__ void recovery_slice(const FusedArgs& a, const Lds& L, int e, int hs, const uint4* apre,
-                               bool have_pre) {
-  const int tid = threadIdx.x, r = a.r;
-  const int c0 = hs * 64;
-  if (r % 8 == 0) {
-    const int cpr = r / 8;                 // 16-byte chunks per row (<= 16)
-    const int nchunk = 64 * cpr;           // <= 1024
-    float* part = L.red;
+  } else if (use_rec) {
+    // item f = col cpr + lc: 16 bytes of A's row for column col, rank chunk lc
+    const int cpr = a.r / 8, nitem = 8 * ncb * cpr;
+    const uint16_t* abase = a.A + ((size_t)e * H + 8 * ck0) * a.r;
+    constexpr int AB = 8;
+    for (int f0 = 0; f0 < nitem; f0 += NT * AB) {
+      uint4 w[AB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = tid + NT * u;
-      if (f < nchunk) {
-        const uint4 w = have_pre ? apre[u] : ld16(a.A + ((size_t)e * a.H + c0) * r + 8 * (size_t)f);
-        part[f] = dot8_f(w, L.zv + 8 * (f % cpr));
+      for (int u = 0; u < AB; ++u) w[u] = ld16(abase + 8 * (size_t)min(f0 + tid + NT * u, nitem - 1));
+#pragma unroll
+      for (int u = 0; u < AB; ++u) {
+        const int f = f0 + tid + NT * u;
+        float d = f < nitem ? dot8_f(w[u], L.zv + 8 * (f % cpr)) : 0.f;
+        d = sum_over_low_lanes(d, cpr);
+        if (f < nitem && f % cpr == 0) rec[f / cpr] = d;
       }
     }
-    __syncthreads();
-    float s = 0.f;
-    if (tid < 64)
-      for (int q = 0; q < cpr; ++q) s += part[tid * cpr + q];
-    __syncthreads();
-    if (tid < 64) L.red[32 * 64 + tid] = s;
-  } else {
-    float s = 0.f;
-    if (tid < 64) {
-      const uint16_t* arow = a.A + ((size_t)e * a.H + c0 + tid) * r;
-      for (int l = 0; l < r; ++l) s += bf16_to_f32(arow[l]) * L.zv[l];
-    }
-    __syncthreads();
-    if (tid < 64) L.red[32 * 64 + tid] = s;
   }
-  __syncthreads();
-}
-
-// y[c0 .. c0+64) = sum_i h_i Wd_t[e][row_i][c0..] (+ the recovery term already in
-// L.red[32*64 ..]), published for the combine; the last of the token's K pairs
-// writes out[t][c0 .. c0+64).
-__device__ void down_slice(const FusedArgs& a, const Lds& L, int p, int t, int e, int hs,
-                           const int32_t* rows, const float* hv, int n, bool add_rec, int* s_flag,
-                           uint32_t tag) {
-  const int tid = threadIdx.x, l8 = tid & 7, g = tid >> 3;
-  const int c0 = hs * 64;
+  const int cc = tid % ncb, g = tid / ncb, ng = NT / ncb;
   float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const uint16_t* base = a.wd + (size_t)e * a.I * a.H + c0 + 8 * l8;
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  const uint16_t* base = a.wd + (size_t)e * a.I * H + 8 * (ck0 + cc);
   constexpr int DB = 8;
-  for (int i0 = g; i0 < n; i0 += 32 * DB) {
+  for (int m0 = g; m0 < n; m0 += ng * DB) {
     uint4 w[DB];
     float h[DB];
 #pragma unroll
     for (int u = 0; u < DB; ++u) {
-      const int i = i0 + 32 * u;
-      const bool ok = i < n;
-      const int row = ok ? (rows ? rows[i] : i) : 0;
-      h[u] = ok ? hv[i] : 0.f;
-      w[u] = ok ? ld16(base + (size_t)row * a.H) : make_uint4(0, 0, 0, 0);
+      const int m = min(m0 + ng * u, n - 1);
+      w[u] = ld16(base + (size_t)(rows ? rows[m] : m) * H);
+      h[u] = m0 + ng * u < n ? hv[m] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < DB; ++u) fma8(acc, h[u], w[u]);
   }
+  // sum over the threads that share a chunk: lane bits above log2 ncb in the
+  // wavefront, then the wavefronts (ncb < 64); groups g < ng (ncb >= 64)
+  int slot;
+  if (ncb < 64) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) L.red[g * 64 + 8 * l8 + i] = acc[i];
-  __syncthreads();
-  if (tid < 64) {
-    float y = 0.f;
-    for (int gg = 0; gg < 32; ++gg) y += L.red[gg * 64 + tid];
-    if (add_rec) y += L.red[32 * 64 + tid];
-    st_f(a.ypart + (size_t)p * a.H + c0 + tid, y);
+    for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], ncb);
+    slot = lane < ncb ? wv * ncb + lane : -1;
+  } else {
+    slot = tid;
   }
-  combine_slice(a, t, hs, s_flag, tag);
+  if (slot >= 0) {
+    reinterpret_cast<float4*>(part)[2 * slot] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(part)[2 * slot + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  __syncthreads();
+  const int nsrc = ncb < 64 ? NT / 64 : ng;   // partial sums per chunk
+  for (int col = tid; col < 8 * ncb; col += NT) {
+    const int c8 = col / 8, j = col % 8;
+    float y = use_rec ? rec[col] : 0.f;
+    for (int q = 0; q < nsrc; ++q) y += part[(q * ncb + c8) * 8 + j];
+    st_f(a.ypart + (size_t)p * H + 8 * ck0 + col, y);
+  }
+  __syncthreads();
+}
+
+// After this workgroup's y columns of pair p are stored: the last of the
+// token's K pairs to arrive writes out[t][8 ck0 .. 8 (ck0 + nck)) in BF16.
+__device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, int ck0, int nck, int* s_flag, uint32_t tag) {
+  const int tid = threadIdx.x;
+  unsigned* cc = a.ctr + (size_t)t * kMaxNw + w;
+  if (last_of(cc, (unsigned)a.K, s_flag)) {
+    const bool bad = ld_u(a.fail) == tag;
+    for (int col = 8 * ck0 + tid; col < 8 * (ck0 + nck); col += NT) {
+      float o = 0.f;
+      for (int q = 0; q < a.K; ++q)
+        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + col);
+      a.out[(size_t)t * a.H + col] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
+    }
+  }
+  __syncthreads();
+}
+
+// Phase C of a workgroup: its columns in blocks of at most NT chunks, then the combine.
+__device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p, int t, int e, int w,
+                        const int32_t* rows, const float* hv, int n, bool use_rec, int* s_flag, uint32_t tag) {
+  const int nck = col_chunks(a), ck0 = w * nck;
+  if (ck0 >= a.H / 8) return;
+  for (int cb = 0; cb < nck; cb += NT) cols_block(a, L, p, e, ck0 + cb, min(NT, nck - cb), rows, hv, n, use_rec);
+  combine_cols(a, t, w, ck0, nck, s_flag, tag);
 }
 
 // ------------------------------------------------------------------ exchange reads
@@ -800,6 +828,23 @@ __device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int
     if (q < a.nw) s += await_tagged(zp + (size_t)q * a.r, raw[u], tag, a.fail);
   }
   L.red[NT + zg * a.r + zl] = s;
+}
+
+// One sub-chunk of phase A: the screen, then this thread's partial recovery sum.
+template <int EPT, int NBT>
+__device__ __forceinline__ void screen_and_sum(const FusedArgs& a, const Lds& L, int p, int e, int sj0, int cwk,
+                                               int F0, const uint4 (&pre)[kSketchPre], float sc,
+                                               const uint32_t (&bt)[NBT], int zg, int groups, float& zacc,
+                                               uint32_t tag) {
+  screen_chunk<(EPT <= kSketchPre)>(a, L, p, e, sj0, cwk, F0, pre, true, sc, tag);
+  if (a.r > 0 && zg < groups) {
+#pragma unroll
+    for (int u = 0; u < NBT; ++u) {
+      const int jj = zg + groups * u;
+      if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32((uint16_t)bt[u]);
+    }
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ launch tag
@@ -833,8 +878,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
     const int j0 = min(a.I, w * a.cw), j1 = min(a.I, j0 + a.cw);
-    const int hs0 = w;                              // first output slice of this workgroup
-    const bool one_slice = hs0 < a.nhs && hs0 + nw >= a.nhs;
+    const int nck = col_chunks(a), ck0 = w * nck;   // this workgroup's output columns: 16-byte chunks
 
     // ---- requests that need no selection, issued before anything waits on
     //      them: x (this thread's elements and the whole row) and signs first,
@@ -871,22 +915,29 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(a, L, xq, sq, wf0);
     else F0 = rotate_small(a, L, t, wred);
     float zacc = 0.f;                               // partial recovery sum for (zl, zg)
-    for (int sj0 = j0; sj0 < j1; sj0 += kSubChunk) {
-      const int cwk = min(j1 - sj0, kSubChunk);
-      const bool first = sj0 == j0;
-      if (!first) {
-        sgu = load_scale(a, e, sj0, cwk);
-        load_bt(a, e, sj0, cwk, zl, zg, groups, btv);
-      }
-      screen_chunk(a, L, p, e, sj0, cwk, F0, spre, first, sgu, tag);
-      if (r > 0 && zg < groups) {
+    if (j1 - j0 <= kSubChunk) {
+      if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
+    } else {
+      // several sub-chunks: the next one's rows are requested before this one is
+      // screened (unconditionally inside the loop; the last one is peeled)
+      const int nsb = (H + 255) / 256;
+      int sj0 = j0;
+      for (; sj0 + kSubChunk < j1; sj0 += kSubChunk) {
+        const int nj0 = sj0 + kSubChunk, ncwk = min(j1 - nj0, kSubChunk);
+        uint4 snext[kSketchPre];
 #pragma unroll
-        for (int u = 0; u < kBtPer; ++u) {
-          const int jj = zg + groups * u;
-          if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32((uint16_t)btv[u]);
-        }
+        for (int u = 0; u < kSketchPre; ++u) snext[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
+        const float nsgu = load_scale(a, e, nj0, ncwk);
+        uint32_t nbtv[kBtPer];
+        load_bt(a, e, nj0, ncwk, zl, zg, groups, nbtv);
+        screen_and_sum<EPT>(a, L, p, e, sj0, kSubChunk, F0, spre, sgu, btv, zg, groups, zacc, tag);
+#pragma unroll
+        for (int u = 0; u < kSketchPre; ++u) spre[u] = snext[u];
+        sgu = nsgu;
+#pragma unroll
+        for (int u = 0; u < kBtPer; ++u) btv[u] = nbtv[u];
       }
-      __syncthreads();
+      screen_and_sum<EPT>(a, L, p, e, sj0, j1 - sj0, F0, spre, sgu, btv, zg, groups, zacc, tag);
     }
     if (r > 0) {
       if (zg < groups) L.red[zg * r + zl] = zacc;
@@ -898,14 +949,14 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       }
     }
 
-    // the A slice of the recovery term: requested now, used at the end
+    // the A rows of this workgroup's columns (prefetched path): requested now, used at the end
     uint4 apre[4];
-    const bool have_apre = one_slice && r > 0 && r % 8 == 0 && 8 * r <= 4 * NT;
+    const bool have_apre = a.pre && r > 0 && ck0 < H / 8;
     {
-      const uint16_t* abase = have_apre ? a.A + ((size_t)e * H + hs0 * 64) * r : a.x;
-      const int nA = have_apre ? 8 * r : 1;
+      const uint16_t* abase = have_apre ? a.A + ((size_t)e * H + 8 * ck0) * r : a.x;
+      const int nA = have_apre ? nck * r : 1;          // 16-byte pieces (<= 1024)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) apre[u] = ld16(abase + 8 * (size_t)min(tid + NT * u, nA - 1));   // past 8 r: unused
+      for (int u = 0; u < 4; ++u) apre[u] = ld16(abase + 8 * (size_t)min(tid + NT * u, nA - 1));   // past nA: unused
     }
 
     // ---- top-c candidates (identical in every workgroup of the pair)
@@ -958,12 +1009,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
       for (int m = 0; m < CH; ++m) xr[m] = ld16c(xg + min(lane + 64 * m, H / 8 - 1));   // past H / 8: times zero rows
-      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag, [&] {
-        if (a.pre && hs0 < a.nhs) prefetch_candidate_rows(a, L, e, hs0);
-      });
-    } else if (a.pre && hs0 < a.nhs) {
-      prefetch_candidate_rows(a, L, e, hs0);
+      exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag, [] {});
     }
+    // candidate rows for z and the down projection: requested once the exact
+    // rows are in (so they do not share bandwidth with them), used after top-k
+    if (a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck);
 
     // ---- top-k kept set and recovery coefficients
     if (a.k > 0) {
@@ -1029,36 +1079,37 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         for (int l = tid; l < r; l += NT) L.zv[l] = L.zsum[l] - (L.red[l] + L.red[r + l] + L.red[2 * r + l] + L.red[3 * r + l]);
         __syncthreads();
       }
-      if (hs0 < a.nhs) {
-        float* rec = L.red + 4 * 128;                     // [64] recovery term of the slice
-        float* part = L.red + 4 * 128 + 64;               // [4][64] per-wavefront down partials
+      if (ck0 < H / 8) {
+        float* rec = L.red + 4 * 128;                     // [8 nck] recovery term (nck <= 8)
+        float* part = L.red + 4 * 128 + 64;               // [4][8 nck] per-wavefront down partials
         if (r > 0) {
           const int cpr = r / 8;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int f = tid + NT * u;
-            float d = f < 64 * cpr ? dot8_f(apre[u], L.zv + 8 * (f % cpr)) : 0.f;
+            float d = f < nck * r ? dot8_f(apre[u], L.zv + 8 * (f % cpr)) : 0.f;
             d = sum_over_low_lanes(d, cpr);
-            if (f < 64 * cpr && f % cpr == 0) rec[f / cpr] = d;
+            if (f < nck * r && f % cpr == 0) rec[f / cpr] = d;
           }
         }
-        const int l8 = tid & 7, g = tid >> 3;
+        const int cc = tid % nck, g = tid / nck;
         float acc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-        for (int m = g; m < a.k; m += NT / 8)
-          fma8(acc, L.hk[m], *reinterpret_cast<const uint4*>(L.dnc + (size_t)L.sel[m] * 128 + 16 * l8));
+        for (int m = g; m < a.k; m += NT / nck)
+          fma8(acc, L.hk[m], *reinterpret_cast<const uint4*>(L.dnc + ((size_t)L.sel[m] * nck + cc) * 16));
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], 8);
-        if (lane < 8)
+        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], nck);
+        if (lane < nck)
 #pragma unroll
-          for (int u = 0; u < 8; ++u) part[(tid >> 6) * 64 + 8 * lane + u] = acc[u];
+          for (int u = 0; u < 8; ++u) part[(tid >> 6) * 8 * nck + 8 * lane + u] = acc[u];
         __syncthreads();
-        if (tid < 64) {
-          const float y = part[tid] + part[64 + tid] + part[128 + tid] + part[192 + tid] + (r > 0 ? rec[tid] : 0.f);
-          st_f(a.ypart + (size_t)p * H + hs0 * 64 + tid, y);
+        for (int col = tid; col < 8 * nck; col += NT) {
+          const float y = part[col] + part[8 * nck + col] + part[16 * nck + col] + part[24 * nck + col] +
+                          (r > 0 ? rec[col] : 0.f);
+          st_f(a.ypart + (size_t)p * H + 8 * ck0 + col, y);
         }
-        combine_slice(a, t, hs0, &s_flag, tag);
+        combine_cols(a, t, w, ck0, nck, &s_flag, tag);
       }
       continue;
     }
@@ -1107,10 +1158,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     }
 
     // ---- phase C: down projection over kept rows for this workgroup's output slices
-    for (int hs = hs0; hs < a.nhs; hs += nw) {
-      if (r > 0) recovery_slice(a, L, e, hs, apre, have_apre && hs == hs0);
-      down_slice(a, L, p, t, e, hs, L.keep, L.hk, a.k, r > 0, &s_flag, tag);
-    }
+    phase_c(a, L, p, t, e, w, L.keep, L.hk, a.k, r > 0, &s_flag, tag);
   }
   finish_launch(a, tag);
 }
@@ -1155,8 +1203,7 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
       }
     }
     __syncthreads();
-    for (int hs = w; hs < a.nhs; hs += nw)
-      down_slice(a, L, p, t, e, hs, nullptr, L.hh, a.I, false, &s_flag, tag);
+    phase_c(a, L, p, t, e, w, nullptr, L.hh, a.I, false, &s_flag, tag);
   }
   finish_launch(a, tag);
 }
@@ -1240,7 +1287,7 @@ static void fused_geometry(ForwardPlan& p, int G_max) {
 static void common_regions(ForwardPlan& p, Carve& cv) {
   p.off_seq = cv.take(4 * (size_t)kSeqSlots);
   p.off_err = cv.take(4);
-  p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * std::max(p.nhs, 1));
+  p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * kMaxNw);
 }
 
 ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) {
@@ -1252,8 +1299,9 @@ ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) 
   size_t off[20];
   // prefetch of the candidates' rows when every workgroup has at most one output
   // slice and the buffers fit
-  const bool pre_ok = p.nw >= p.nhs && k > 0 && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0));
-  p.pre = pre_ok && lds_layout(H, I, c, k, r, p.cpw, 1, off) <= 160 * 1024 ? 1 : 0;
+  const int nck = std::max(1, (H / 8) / p.nw);
+  const bool pre_ok = nck <= 8 && k > 0 && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0));
+  p.pre = pre_ok && lds_layout(H, I, c, k, r, p.cpw, nck, off) <= 160 * 1024 ? nck : 0;
   p.lds = lds_layout(H, I, c, k, r, p.cpw, p.pre, off);
   Carve cv;
   common_regions(p, cv);

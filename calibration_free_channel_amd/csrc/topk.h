@@ -104,7 +104,7 @@ __device__ __forceinline__ int topk_range(int n, int* cnt) {
 // ceil(n / NT) <= KPT and n < 65536). scratch: kTopkScratchWords words of LDS,
 // 16-byte aligned. Called by the whole workgroup; ends with a barrier.
 template <int NT, int KPT>
-__device__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
+__device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
                            uint32_t* scratch) {
   static_assert(NT == 256, "four wavefronts");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
