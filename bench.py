@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--batches", default="1,8,16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -112,6 +114,23 @@ def kernel_times(torch, cfm, fn, n_steps):
     return {k: v[1] / v[0] for k, v in rep.items()}
 
 
+def measured_traffic():
+    """HBM bytes per launch of k_select_fused from the committed rocprofv3 --pmc
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
+    None when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_select_fused_q18_b1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
 def cpu_baseline(wl_name="q18_b1", target_s=10.0):
     """The CPU oracle on a bounded sample of the same workload (per-token forward)."""
     import numpy as np
@@ -160,6 +179,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return
+
     import calibration_free_channel_amd as cfm
 
     torch.manual_seed(args.seed)
@@ -245,7 +275,7 @@ def main():
         ach = r1["bytes"] / (k_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": "k_select_fused", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-                "traffic": None, "bytes_per_launch": r1["bytes"], "avg_launch_us": round(k_us, 3)}
+                "traffic": measured_traffic(), "bytes_per_launch": r1["bytes"], "avg_launch_us": round(k_us, 3)}
     line = {
         "metric": METRIC,
         "value": round(r1["us_per_token"], 3),
