@@ -35,6 +35,7 @@ _SIGS = {
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
     "dense_workspace": (_z, [_i, _i, _i, _i, _i]),
     "moe_dense_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _z, _p]),
+    "cfm_set_forward_path": (_i, [_i]),
     "cfm_timing_enable": (_i, [_i]),
     "cfm_timing_report": (_i, [ctypes.c_char_p, _z]),
 }
@@ -178,6 +179,32 @@ def moe_dense_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, out=None, ws=
         _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
         E, I, H, _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), "moe_dense_forward")
     return out
+
+
+FORWARD_AUTO, FORWARD_PER_PAIR, FORWARD_GROUPED = 0, 1, 2
+
+
+def set_forward_path(path: int) -> int:
+    """Select the forward kernels (0 automatic, 1 per-pair, 2 expert-grouped); returns the previous setting."""
+    prev = _lib.cfm_set_forward_path(int(path))
+    if prev < 0:
+        raise CfmError(prev, "cfm_set_forward_path")
+    return prev
+
+
+class forward_path:
+    """Context manager: run the enclosed forward calls on the given path."""
+
+    def __init__(self, path: int):
+        self.path = path
+
+    def __enter__(self):
+        self.prev = set_forward_path(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        set_forward_path(self.prev)
+        return False
 
 
 def timing_enable(on: bool = True):

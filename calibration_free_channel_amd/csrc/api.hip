@@ -76,6 +76,18 @@ int check_budget(int I, int H, int k, int c, int r) {
   return CFM_OK;
 }
 
+// Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped.
+int g_path = 0;
+constexpr int kGroupedMinTokens = 8;     // automatic choice: grouped from this batch size on
+
+// Whether a forward call uses the grouped pass (or an error status).
+int pick_grouped(int T, int K, int E, int I, int H, int r, bool dense, bool* grouped) {
+  const bool ok = grouped_supported(T, K, E, I, H, r, dense);
+  if (g_path == 2 && !ok) return set_error(CFM_EUNSUPPORTED, "expert-grouped pass: shape not supported");
+  *grouped = g_path == 2 || (g_path == 0 && ok && T >= kGroupedMinTokens);
+  return CFM_OK;
+}
+
 int check_tokens(int T, int K) {
   if (T < 0) return set_error(CFM_EINVAL, "T must be nonnegative");
   if (K <= 0) return set_error(CFM_EINVAL, "K must be positive");
@@ -94,6 +106,13 @@ extern "C" {
 const char* cfm_last_error(void) { return g_last_error.c_str(); }
 
 const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
+
+int cfm_set_forward_path(int path) {
+  if (path < 0 || path > 2) return set_error(CFM_EINVAL, "path must be 0, 1 or 2");
+  const int prev = g_path;
+  g_path = path;
+  return prev;
+}
 
 int cfm_timing_enable(int on) {
   g_timing = on != 0;
@@ -164,7 +183,9 @@ size_t select_workspace(int T, int K, int E, int I, int H, int k, int c, int r) 
   if (T < 0 || K <= 0 || K > kMaxK || E <= 0 || I <= 0 || I > kMaxI || H < 64 || H > kMaxH ||
       k < 0 || c < k || c > I || r < 0 || r > kMaxRank || r > std::min(H, I))
     return 0;
-  return select_plan(T, K, E, I, H, k, c, r).bytes;
+  const size_t base = select_plan(T, K, E, I, H, k, c, r).bytes;
+  if (!grouped_supported(T, K, E, I, H, r, false)) return base;
+  return group_plan(T, K, E, I, H, k, c, r, false, base).bytes;
 }
 
 int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
@@ -183,11 +204,17 @@ int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* 
       !sg || !su || !out)
     return set_error(CFM_EINVAL, "moe_select_forward: null pointer");
   if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_select_forward: null A or Bt with r > 0");
+  bool grouped = false;
+  if (int rc = pick_grouped(T, K, E, I, H, r, false, &grouped)) return rc;
   const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r);
-  if (!ws || ws_bytes < plan.bytes)
+  const size_t need = grouped ? group_plan(T, K, E, I, H, k, c, r, false, plan.bytes).bytes : plan.bytes;
+  if (!ws || ws_bytes < need)
     return set_error(CFM_EWORKSPACE, "moe_select_forward: workspace smaller than select_workspace()");
   SelectArgs a{x, w_gate, w_up, w_down_t, A, Bt, topk_ids, topk_w, signs, tg, tu, sg, su, out,
                cand_out, keep_out, stats, static_cast<char*>(ws)};
+  if (grouped)
+    return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
+                                  static_cast<hipStream_t>(stream));
   return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
 }
 
@@ -195,7 +222,9 @@ size_t dense_workspace(int T, int K, int E, int I, int H) {
   if (T < 0 || K <= 0 || K > kMaxK || E <= 0 || I <= 0 || I > kMaxI || H < 64 || H > kMaxH ||
       H % 64)
     return 0;
-  return dense_plan(T, K, E, I, H).bytes;
+  const size_t base = dense_plan(T, K, E, I, H).bytes;
+  if (!grouped_supported(T, K, E, I, H, 0, true)) return base;
+  return group_plan(T, K, E, I, H, I, I, 0, true, base).bytes;
 }
 
 int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
@@ -208,11 +237,17 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
   if (T == 0) return CFM_OK;
   if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down_t || !out)
     return set_error(CFM_EINVAL, "moe_dense_forward: null pointer");
+  bool grouped = false;
+  if (int rc = pick_grouped(T, K, E, I, H, 0, true, &grouped)) return rc;
   const ForwardPlan plan = dense_plan(T, K, E, I, H);
-  if (!ws || ws_bytes < plan.bytes)
+  const size_t need = grouped ? group_plan(T, K, E, I, H, I, I, 0, true, plan.bytes).bytes : plan.bytes;
+  if (!ws || ws_bytes < need)
     return set_error(CFM_EWORKSPACE, "moe_dense_forward: workspace smaller than dense_workspace()");
   SelectArgs a{x, w_gate, w_up, w_down_t, nullptr, nullptr, topk_ids, topk_w, nullptr, nullptr,
                nullptr, nullptr, nullptr, out, nullptr, nullptr, nullptr, static_cast<char*>(ws)};
+  if (grouped)
+    return launch_grouped_forward(a, group_plan(T, K, E, I, H, I, I, 0, true, plan.bytes),
+                                  static_cast<hipStream_t>(stream));
   return launch_dense_forward(a, plan, static_cast<hipStream_t>(stream));
 }
 

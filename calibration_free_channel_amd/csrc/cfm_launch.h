@@ -59,4 +59,20 @@ struct SelectArgs {
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 
+// ---------------------------------------------------------------- expert-grouped forward pass
+// Workspace of the grouped pass: its regions start at `base` (the end of the
+// per-pair layout, so the per-pair pass's persistent words are never touched).
+struct GroupPlan {
+  int T, K, P, E, I, H, k, c, r;
+  bool dense;
+  int ntile, IW;          // 64-channel screen tiles, 32-bit words of a channel bitmap
+  int maxu, maxwork;      // bounds on used experts and screen work items (grid sizes)
+  size_t off_meta, off_goff, off_gpl, off_gue, off_gwork, off_xf0, off_xd, off_hs, off_zp, off_cm, off_cl,
+      off_hx, off_km, off_hk, off_zf, off_yp, off_ucnt, off_dcnt;
+  size_t bytes;           // end of the layout (including base)
+};
+bool grouped_supported(int T, int K, int E, int I, int H, int r, bool dense);
+GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool dense, size_t base);
+int launch_grouped_forward(const SelectArgs& a, const GroupPlan& p, hipStream_t stream);
+
 }  // namespace cfm

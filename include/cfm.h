@@ -174,6 +174,24 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
                       size_t ws_bytes, void* stream);
 
 /*
+ * cfm_set_forward_path - which kernels serve moe_select_forward and
+ * moe_dense_forward (process-wide; returns the previous setting, or CFM_EINVAL).
+ *   0 automatic (default): the expert-grouped pass from 8 tokens on where the
+ *     shape allows it, the per-pair pass below that;
+ *   1 the per-pair pass (one persistent launch; lowest latency at batch 1);
+ *   2 the expert-grouped pass (pairs grouped by expert; each weight row an
+ *     expert needs is read once for all of its tokens: the article's batch
+ *     8 / 16 regime, aimodeling.com article, batch-size table). Calls whose
+ *     shape it does not cover return CFM_EUNSUPPORTED: it needs T K <= 65535,
+ *     E <= 4096, and for the selected layer r a multiple of 8.
+ * Both passes compute the same selections (identical sketch activations, so
+ * identical candidate sets; exact activations and outputs agree to float
+ * rounding). The workspace sizes returned by select_workspace and
+ * dense_workspace cover both.
+ */
+int cfm_set_forward_path(int path);
+
+/*
  * Instrumentation (not part of the method). While enabled, every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the
  * launch stream. cfm_timing_report synchronises those events, writes one line

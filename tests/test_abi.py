@@ -119,3 +119,34 @@ def test_dense_forward_rejects(lib):
     assert f(P, P, P, 1, 2, P, P, P, 8, 128, 100, P, P, ctypes.c_size_t(1 << 40), None) == EUNSUP
     assert f(P, P, P, 1, 2, P, P, P, 8, 128, 256, P, None, ctypes.c_size_t(0), None) == EWS
     assert f(None, P, P, 1, 2, P, P, P, 8, 128, 256, P, P, ctypes.c_size_t(1 << 40), None) == EINVAL
+
+
+def test_forward_path_switch(lib):
+    f = lib.cfm_set_forward_path
+    f.restype = ctypes.c_int
+    assert f(3) == EINVAL and f(-1) == EINVAL
+    prev = f(2)
+    try:
+        assert f(2) == 2
+        # the grouped pass needs r to be a multiple of 8: refused before any HIP call
+        assert _sel(lib, r=6) == EUNSUP
+        assert _sel(lib, r=8, wsb=16) == EWS
+        # dense: H a multiple of 64 suffices
+        d = lib.moe_dense_forward
+        d.restype = ctypes.c_int
+        assert d(FAKE, FAKE, FAKE, 1, 2, FAKE, FAKE, FAKE, 8, 128, 192, FAKE, FAKE, ctypes.c_size_t(16), None) == EWS
+        assert f(1) == 2
+        assert _sel(lib, r=6, wsb=16) == EWS
+    finally:
+        f(prev)
+
+
+def test_workspace_covers_both_passes(lib):
+    lib.select_workspace.restype = ctypes.c_size_t
+    lib.dense_workspace.restype = ctypes.c_size_t
+    # grouped regions follow the per-pair layout, so a batch of 16 needs more than the per-pair pass alone
+    one = lib.select_workspace(1, 8, 128, 768, 2048, 100, 200, 64)
+    many = lib.select_workspace(16, 8, 128, 768, 2048, 100, 200, 64)
+    assert many > 16 * 8 * 768 * (8 + 4 + 4 + 2)      # per-pair exchange words plus grouped activations
+    assert many > one
+    assert lib.dense_workspace(16, 8, 128, 768, 2048) > 16 * 8 * 768 * 8

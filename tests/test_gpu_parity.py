@@ -197,18 +197,19 @@ def test_dense_parity(cfm, wl):
 
 
 def test_determinism_and_batch_invariance(cfm):
+    """Per-pair pass: two runs agree bit for bit, and token 3 alone gives the bits it gets inside the batch."""
     wl = custom_workload("inv", 8, 2, 128, 256, 8, 23, 46, 8, 15)
     L = upload(wl)
     sk = gpu_sketch(cfm, L)
     A, Bt = oracle_map(L.host.w_down_t, 8, range(8), 8, 128, 256)
     A, Bt = up_bf16(A), up_bf16(Bt)
-    a = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
-    b = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        a = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
+        b = run_select(cfm, L, sk, A, Bt, 23, 46, 8)
+        one = cfm.moe_select_forward(L.x[3:4].contiguous(), L.ids[3:4].contiguous(), L.w[3:4].contiguous(),
+                                     L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, 23, 46, 8)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
-    # token 3 alone
-    one = cfm.moe_select_forward(L.x[3:4].contiguous(), L.ids[3:4].contiguous(), L.w[3:4].contiguous(),
-                                 L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, 23, 46, 8)
     assert np.array_equal(down_bf16(one)[0], a[0][3])
 
 
@@ -294,6 +295,7 @@ def test_q18_b1_full_size(cfm, q18_layer):
 
 @pytest.mark.parametrize("name", ["q13_b8", "q13_b16", "q18_b16"])
 def test_batched_full_size(cfm, name):
+    """Batches of 8 and 16 tokens through both passes (grouped: the automatic choice; per-pair forced)."""
     wl = synth.WORKLOADS[name]
     log(f"generating {name}")
     L = upload(wl)
@@ -302,11 +304,14 @@ def test_batched_full_size(cfm, name):
     used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
     sk = gpu_sketch(cfm, L)
     A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
-    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
-    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=name)
+    for path in (cfm.FORWARD_AUTO, cfm.FORWARD_PER_PAIR):
+        with cfm.forward_path(path):
+            got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+        compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=f"{name} path {path}")
 
 
 def test_olmoe_b64_full_size(cfm):
+    """OLMoE-shaped layer, 64 tokens with Zipf-skewed experts (hot experts serve most tokens): both passes."""
     wl = synth.WORKLOADS["olmoe_b64"]
     log("generating the OLMoE-shaped layer")
     L = upload(wl)
@@ -315,5 +320,7 @@ def test_olmoe_b64_full_size(cfm):
     used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
     sk = gpu_sketch(cfm, L)
     A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
-    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
-    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what="olmoe_b64")
+    for path in (cfm.FORWARD_AUTO, cfm.FORWARD_PER_PAIR):
+        with cfm.forward_path(path):
+            got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+        compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=f"olmoe_b64 path {path}")
