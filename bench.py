@@ -243,6 +243,19 @@ def main():
         ms_den, wall_den = timed_graph(torch, lambda i: dense(off + steps + i), steps)
         kt_sel = kernel_times(torch, cfm, lambda i: sel(off + i), steps)
         kt_den = kernel_times(torch, cfm, lambda i: dense(off + steps + i), steps)
+        pp = None
+        if T >= 8:
+            # both passes forced on the same steps (the automatic choice is timed above)
+            pp = {}
+            for name, path in (("per_pair", cfm.FORWARD_PER_PAIR), ("grouped", cfm.FORWARD_GROUPED)):
+                with cfm.forward_path(path):
+                    for i in range(2):
+                        sel(i)
+                        dense(i)
+                    ms_p, _ = timed_graph(torch, lambda i: sel(off + i), steps)
+                    ms_pd, _ = timed_graph(torch, lambda i: dense(off + steps + i), steps)
+                pp[name] = {"us_per_token": round(ms_p / steps * 1e3 / T, 3),
+                            "dense_us_per_token": round(ms_pd / steps * 1e3 / T, 3)}
         st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
         wg, wu, wd, signs, sk, A, Bt = layers[0]
         cfm.moe_select_forward(x[0], ids[0], w[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
@@ -260,14 +273,15 @@ def main():
                           dense_gbps=bytes_den / (us_step_d * 1e-6) / 1e9, dense_bytes=bytes_den,
                           speedup=us_step_d / us_step, kernels_us={n: v * 1e3 for n, v in kt_sel.items()},
                           dense_kernels_us={n: v * 1e3 for n, v in kt_den.items()},
-                          wall_ms=wall_sel, stats=stats)
+                          wall_ms=wall_sel, stats=stats, per_pair=pp)
         log(f"B={T}: selected {us_step:.2f} us/step ({us_step / T:.2f} us/token, "
             f"{results[T]['gbps']:.0f} GB/s on {bytes_sel / 1e6:.1f} MB), dense {us_step_d:.2f} us/step "
             f"({results[T]['dense_gbps']:.0f} GB/s), speedup {results[T]['speedup']:.2f}x; kernels "
-            f"{ {n: round(v * 1e3, 2) for n, v in kt_sel.items()} }")
+            f"{ {n: round(v * 1e3, 2) for n, v in kt_sel.items()} }; dense kernels "
+            f"{ {n: round(v * 1e3, 2) for n, v in kt_den.items()} }; passes {pp}")
         del ws_s, ws_d, out, x, ids, w
 
-    r1 = results[1]
+    r1 = results[1] if 1 in results else results[batches[0]]     # (profiling runs may skip batch 1)
     # the whole hot path is one kernel: its algorithmic bytes per launch are the call's bytes
     k_us = r1["kernels_us"].get("k_select_fused")
     roof = None
@@ -303,7 +317,9 @@ def main():
         "dense_kernels_us": {n: round(v, 3) for n, v in r1["dense_kernels_us"].items()},
         "batches": {str(T): {"us_per_token": round(v["us_per_token"], 3), "GBps": round(v["gbps"], 1),
                              "dense_us_per_token": round(v["dense_us_per_token"], 3),
-                             "speedup_vs_dense": round(v["speedup"], 3), "bytes_per_step": v["bytes"]}
+                             "speedup_vs_dense": round(v["speedup"], 3), "bytes_per_step": v["bytes"],
+                             "kernels_us": {n: round(x, 3) for n, x in v["kernels_us"].items()},
+                             "passes": v["per_pair"]}
                     for T, v in results.items()},
         "offline_ms_per_layer": {"sketch_build": round(t_sketch / L * 1e3, 2),
                                  "lowrank_build": round(t_lr / L * 1e3, 2)},

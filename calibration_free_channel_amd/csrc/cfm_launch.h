@@ -65,10 +65,12 @@ int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t 
 struct GroupPlan {
   int T, K, P, E, I, H, k, c, r;
   bool dense;
-  int ntile, IW;          // 64-channel screen tiles, 32-bit words of a channel bitmap
+  int ntile, IW, nrb;     // 64-channel screen tiles, words of a channel bitmap, 16-row exact blocks
+  int IP;                 // row pitch of the union row lists (I rounded up to 8)
   int maxu, maxwork;      // bounds on used experts and screen work items (grid sizes)
-  size_t off_meta, off_goff, off_gpl, off_gue, off_gwork, off_xf0, off_xd, off_hs, off_zp, off_cm, off_cl,
-      off_hx, off_km, off_hk, off_zf, off_yp, off_ucnt, off_dcnt;
+  size_t off_uctr, off_kctr, off_octr;   // arrival counters (zero between calls)
+  size_t off_meta, off_goff, off_gpl, off_gue, off_gux, off_gwork, off_gexw, off_xf0, off_xd, off_hs, off_zp,
+      off_cm, off_cl, off_hx, off_km, off_hk, off_zf, off_yp, off_ucnt, off_dcnt, off_urows, off_drows;
   size_t bytes;           // end of the layout (including base)
 };
 bool grouped_supported(int T, int K, int E, int I, int H, int r, bool dense);

@@ -21,18 +21,24 @@
 // same; exact activations and outputs differ from it by float rounding only.
 //
 // Unlike the per-pair kernel this is a short sequence of ordinary launches
-// (no inter-workgroup waits): each stage is a streaming kernel with many
-// workgroups per compute unit, which is what hides memory latency once there
-// is enough work in flight.
+// with no inter-workgroup waits. Each stage is a streaming kernel with many
+// workgroups per compute unit; every global load of a stage is issued in one
+// batch before its first use, so a workgroup pays about one memory latency per
+// step. Where a stage needs a per-expert or per-token result that several
+// workgroups contribute to, the last contributor (release fence, counter,
+// acquire fence) computes it; the counters are reset by that workgroup.
 //
 //   k_g_prep    rotation and digit planes of every token; grouping of the
 //               pairs by expert (one workgroup)
 //   k_g_screen  (64-channel tile, expert and token group) work items
-//   k_g_topc    top-c candidates per pair, candidate bitmaps
+//   k_g_topc    top-c candidates per pair; the last pair of an expert lists
+//               the expert's candidate union and queues its exact work items
 //   k_g_exact   (16 union rows, expert) work items: gate / up / h
-//   k_g_topk    top-k per pair, masked BF16 activations, recovery coefficients
-//   k_g_down    (64 output columns, expert) work items: down rows and A z
-//   k_g_combine router-weighted sum per token, BF16 output
+//   k_g_topk    top-k per pair, masked BF16 activations, recovery
+//               coefficients; the last pair of an expert lists its kept union
+//   k_g_down    (64 output columns, expert) work items: down rows and A z; the
+//               last contribution to a (token, column tile) combines the
+//               token's K pairs into the BF16 output
 #include <algorithm>
 
 #include "cfm_internal.h"
@@ -48,11 +54,10 @@ constexpr int kTile = 64;          // channels per screen work item (128 sketch 
 constexpr int kTokGroup = 16;      // tokens per screen work item
 constexpr int kSbReg = 8;          // super-blocks of sketch rows held in registers (H <= 2048)
 constexpr int kRowBlk = 16;        // union rows per exact work item (one MFMA row tile)
-constexpr int kKc = 8;             // 32-element steps of one exact load batch
+constexpr int kKc = 8;             // 32-element steps of one exact load batch (two batches in flight; fewer for H < 256)
 constexpr int kColTile = 64;       // output columns per down work item (16 per wavefront)
-constexpr int kDnRows = 128;       // union rows per down step
-constexpr int kDnPitch = kDnRows + 8;   // LDS row pitch (BF16) of the down operands
 constexpr int kRPad = 128;         // recovery rank padded to whole 32-element steps (r <= 128)
+constexpr int kExactGrid = 512;    // workgroups of the exact stage (wavefronts loop over its work list)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -71,6 +76,29 @@ __device__ __forceinline__ v4f mfma_bf16(const uint4& a, const uint4& b, v4f c) 
                                                  0, 0, 0);
 }
 
+// Values read by another workgroup of the same launch go through agent-scope
+// atomic stores and loads (coherent across the XCDs' L2 caches without a cache
+// flush); a drained store queue then orders them before a counter update.
+__device__ __forceinline__ void st_f(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_f(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_u(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Completes this wave's outstanding memory operations, then joins the workgroup.
+__device__ __forceinline__ void drain_and_join() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
@@ -81,15 +109,17 @@ struct GArgs {
   const int8_t* signs; const uint8_t *tg, *tu; const float *sg, *su;
   const uint16_t *A, *Bt;
   uint16_t* out; int32_t *cand_out, *keep_out;
-  uint32_t* meta;     // [0] experts used, [1] screen work items
+  uint32_t* meta;     // [0] experts used, [1] screen work items, [2] exact work items
   int32_t* goff;      // [E + 1] first position of each expert's pairs in gpl
   int32_t* gpl;       // [P] pairs sorted by expert
   int32_t* gue;       // [E] used experts, ascending
-  int32_t* gwork;     // [nwork] screen work items: used expert << 16 | token group
+  int32_t* gux;       // [E] used index of each expert (-1: not routed)
+  int32_t* gwork;     // [maxwork] screen work items: used expert << 16 | token group
+  int32_t* gexw;      // [maxu nrb] exact work items: used expert << 16 | row block
   uint8_t* xd;        // [T][kPlanes][Hp] digit planes of x~
   int32_t* xf0;       // [T] fixed-point exponents
   float* hs;          // [P][I] sketch activations
-  float* zp;          // [P][ntile][r] sketch-activation recovery sums per channel tile
+  float* zp;          // [P][nz][r] sketch-activation recovery sums per 16 channels
   uint32_t* cm;       // [P][IW] candidate bitmaps
   int32_t* cl;        // [P][c] candidates, ascending
   float* hx;          // [P][I] exact activations (meaningful at the pair's candidates)
@@ -97,9 +127,14 @@ struct GArgs {
   uint16_t* hk;       // [P][I] BF16 exact activations at the kept channels, 0 elsewhere
   float* zf;          // [P][r] recovery coefficients
   float* yp;          // [P][H] pair outputs
-  uint32_t* ucnt;     // [E] candidate-union rows per used expert
-  uint32_t* dcnt;     // [E] kept-union rows per used expert
-  int T, K, P, E, I, H, log2H, k, c, r, ntile, IW, dense;
+  uint32_t* ucnt;     // [maxu] candidate-union rows per used expert
+  uint32_t* dcnt;     // [maxu] kept-union rows per used expert
+  uint16_t* urows;    // [maxu][IP] candidate-union rows, ascending
+  uint16_t* drows;    // [maxu][IP] kept-union rows, ascending
+  uint32_t* uctr;     // [E] top-c arrivals per expert (zero between calls)
+  uint32_t* kctr;     // [E] top-k arrivals per expert (zero between calls)
+  uint32_t* octr;     // [T][H / 64] pair outputs arrived per (token, column tile) (zero between calls)
+  int T, K, P, E, I, H, log2H, k, c, r, ntile, nz, IW, nrb, IP, dense;
 };
 
 // ------------------------------------------------------------------ block helpers
@@ -128,39 +163,53 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t* v, int n, uint32_t* w
   return total;
 }
 
-// Union of the bitmaps of pairs pl[0..n) (or all channels when dense) into
-// U[0..IW) with exclusive prefix popcounts pc[0..IW); returns the union size.
-__device__ __forceinline__ uint32_t union_rows(const uint32_t* bm, const int32_t* pl, int n, int IW, int I,
-                                               bool dense, uint32_t* U, uint32_t* pc, uint32_t* wtot) {
+// Arrival of this workgroup at *ctr once its agent-scope stores are complete;
+// true in the workgroup that completes `total` arrivals, which resets the
+// counter (its agent-scope loads then see every arrival's stores).
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t total, int* s_flag) {
+  drain_and_join();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1;
+    if (last) st_u(ctr, 0u);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Union of the channel bitmaps bm[p][IW] of expert e's pairs: its channels in
+// ascending order into rows_out (global), count returned. U, pc: IW words of
+// LDS each. Called by the whole workgroup.
+__device__ __forceinline__ uint32_t expert_union(const GArgs& a, const uint32_t* bm, int e, uint16_t* rows_out,
+                                                 uint32_t* U, uint32_t* pc, uint32_t* wtot) {
+  const int p0 = a.goff[e], n = a.goff[e + 1] - p0, IW = a.IW;
   for (int w = threadIdx.x; w < IW; w += GT) {
     uint32_t u = 0;
-    if (dense) {
-      const int left = I - 32 * w;
-      u = left >= 32 ? ~0u : ((1u << left) - 1u);
-    } else {
-      for (int s = 0; s < n; ++s) u |= bm[(size_t)pl[s] * IW + w];
+    for (int s0 = 0; s0 < n; s0 += 8) {
+      int pp[8];
+      uint32_t x[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) pp[v] = a.gpl[p0 + min(s0 + v, n - 1)];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) x[v] = ld_u(bm + (size_t)pp[v] * IW + w);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) u |= s0 + v < n ? x[v] : 0u;
     }
     U[w] = u;
     pc[w] = __builtin_popcount(u);
   }
   __syncthreads();
-  return block_exscan(pc, IW, wtot);
-}
-
-// rows[q - lo] = the channel of union rank q, for lo <= q < hi.
-__device__ __forceinline__ void union_list(const uint32_t* U, const uint32_t* pc, int IW, uint32_t lo, uint32_t hi,
-                                           uint16_t* rows) {
+  const uint32_t nU = block_exscan(pc, IW, wtot);
   for (int w = threadIdx.x; w < IW; w += GT) {
     uint32_t u = U[w], q = pc[w];
-    if (q >= hi || q + __builtin_popcount(u) <= lo) continue;
     while (u) {
       const int b = __builtin_ctz(u);
       u &= u - 1;
-      if (q >= lo && q < hi) rows[q - lo] = (uint16_t)(32 * w + b);
-      ++q;
+      rows_out[q++] = (uint16_t)(32 * w + b);
     }
   }
-  __syncthreads();
+  return nU;
 }
 
 // ------------------------------------------------------------------ stage 1: rotation and grouping
@@ -223,6 +272,7 @@ __global__ __launch_bounds__(GT) void k_g_prep(GArgs a) {
   for (int e = tid; e < E; e += GT) {
     a.goff[e] = (int)off[e];
     const uint32_t n = cnt[e];
+    a.gux[e] = n > 0 ? (int)uix[e] : -1;
     if (n > 0) {
       a.gue[uix[e]] = e;
       const uint32_t ng = (n + kTokGroup - 1) / kTokGroup;
@@ -233,6 +283,7 @@ __global__ __launch_bounds__(GT) void k_g_prep(GArgs a) {
     a.goff[E] = P;
     a.meta[0] = nue;
     a.meta[1] = nwork;
+    a.meta[2] = 0;
   }
   __syncthreads();
   // pairs into their expert's segment (the order inside a segment does not
@@ -245,17 +296,23 @@ __global__ __launch_bounds__(GT) void k_g_prep(GArgs a) {
 
 // ------------------------------------------------------------------ stage 2: screen
 
-// B operand of two tokens for super-block sb and half m: columns 0..5 are the
-// digit planes of the first token (LDS rows 0..5), 6..11 those of the second
-// (rows 6..11), column 12 all ones, 13..15 zero; the hidden-index order matches
-// the FP4 A operand of the sketch rows (as in the per-pair screen).
-__device__ __forceinline__ v8i digit_operand2(const uint8_t* limb2, int Hp, int sb, int m) {
+// B operand of two tokens for super-block sb and half m, read from the digit
+// planes in global memory (they are L2-resident: T kPlanes Hp bytes in all):
+// columns 0..5 are the planes of token a, 6..11 those of token b, column 12
+// all ones, 13..15 zero. The hidden-index order matches the FP4 A operand of
+// the sketch rows (as in the per-pair screen). Returns (lo, hi) 16-byte halves.
+__device__ __forceinline__ void digit_load2(const uint8_t* xa, const uint8_t* xb, int Hp, int sb, int m, uint4& lo,
+                                            uint4& hi) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, gB = lane >> 4;
-  const uint8_t* row = limb2 + (size_t)min(col, 2 * kPlanes - 1) * Hp;
+  const int pl = min(col, 2 * kPlanes - 1);
+  const uint8_t* row = (pl < kPlanes ? xa + (size_t)pl * Hp : xb + (size_t)(pl - kPlanes) * Hp);
   const int i0 = sb * 256 + 64 * (gB >> 1) + 32 * m + 16 * (gB & 1);
-  const uint4 lo = *reinterpret_cast<const uint4*>(row + i0);
-  const uint4 hi = *reinterpret_cast<const uint4*>(row + i0 + 128);
+  lo = ld16c(row + i0);
+  hi = ld16c(row + i0 + 128);
+}
+__device__ __forceinline__ v8i digit_operand2(const uint4& lo, const uint4& hi) {
+  const int col = threadIdx.x & 15;
   const unsigned keep = col < 2 * kPlanes ? 0xFFFFFFFFu : 0u;
   const unsigned one = col == 2 * kPlanes ? 0x38383838u : 0u;       // FP8 E4M3 1.0
   v8i b;
@@ -264,26 +321,29 @@ __device__ __forceinline__ v8i digit_operand2(const uint8_t* limb2, int Hp, int 
   return b;
 }
 
-// Sketch item of row tile q (rows 16 (wv + 4 q) .. +16 of the 128 rows of a
-// 64-channel tile: rows 0..63 gate, 64..127 up) and super-block s: lane
-// (row = lane & 15, g = lane >> 4) takes the 16 bytes at 64 s + 16 g of its row.
-__device__ __forceinline__ uint4 sketch_item2(const GArgs& a, int e, int j0, int cw, int q, int s) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int rho = 16 * (wv + 4 * q) + (lane & 15);
+// Sketch item of row tile q of wavefront wv (q = 0: gate rows of channels
+// jw + 0..15, q = 1: their up rows) and super-block s: lane (row = lane & 15,
+// g = lane >> 4) takes the 16 bytes at 64 s + 16 g of its row.
+__device__ __forceinline__ uint4 sketch_item2(const GArgs& a, int e, int jw, int cwv, int q, int s) {
+  const int lane = threadIdx.x & 63;
   const int rowb = a.H / 4;
   const int off = 64 * s + 16 * (lane >> 4);
-  const int jj = min(rho & 63, cw - 1);              // rows past the tile repeat a valid row (never read)
-  const uint8_t* base = rho < 64 ? a.tg : a.tu;
-  return ld16(base + ((size_t)e * a.I + j0 + jj) * rowb + (off < rowb ? off : 0));
+  const int jj = min(lane & 15, cwv - 1);            // rows past the channels repeat a valid row (never read)
+  return ld16((q ? a.tu : a.tg) + ((size_t)e * a.I + jw + jj) * rowb + (off < rowb ? off : 0));
 }
 
-// Work item (tile, screen item): the sketch rows of channels [j0, j0 + 64) of
-// expert e against up to 16 of its tokens, two per pass.
+// Work item (tile, screen item): channels [j0, j0 + 64) of expert e against up
+// to 16 of its tokens, two per pass. Wavefront w owns channels j0 + 16 w ..
+// + 15 (its gate and up sketch rows are two MFMA row tiles), so it computes
+// their sketch activations and its share of the recovery sums by itself; the
+// wavefronts never wait for each other.
 template <bool REG>
-__global__ __launch_bounds__(GT) void k_g_screen(GArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
+__global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
+  __shared__ __align__(16) float dsw[4][32 * 16];        // per wavefront: D of its two row tiles
+  __shared__ __align__(16) float hw[4][2 * 16];          // per wavefront: its activations, two tokens
+  __shared__ __align__(16) uint16_t btw[4][16 * kRPad];  // per wavefront: Bt rows of its channels
   if ((uint32_t)blockIdx.y >= a.meta[1]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, r = a.r;
   const int Hp = max(H, 256);
   const int nsb = (H + 255) / 256;
@@ -291,61 +351,65 @@ __global__ __launch_bounds__(GT) void k_g_screen(GArgs a) {
   const int e = a.gue[item >> 16];
   const int g0 = (item & 0xFFFF) * kTokGroup;
   const int p0 = a.goff[e], n = min(a.goff[e + 1] - p0 - g0, kTokGroup);
-  const int tile = blockIdx.x, j0 = tile * kTile, cw = min(kTile, I - j0);
-  uint8_t* limb2 = smem;                                                   // [12][Hp]
-  float* dsum = reinterpret_cast<float*>(smem + 2 * kPlanes * (size_t)Hp);  // [128][16]
-  float* gu = dsum + 128 * 16;                                             // [2][128]
-  float* hl = gu + 2 * 128;                                                // [2][64]
-  float* scl = hl + 2 * 64;                                                // [128]
-  uint16_t* bts = reinterpret_cast<uint16_t*>(scl + 128);                  // [64][r]
+  const int jw = blockIdx.x * kTile + 16 * wv;             // this wavefront's first channel
+  const int cwv = min(16, I - jw);
+  if (cwv <= 0) return;
+  const int zslot = jw / 16;                               // its recovery-sum slot
+  const int row = lane & 15, qe = (lane >> 4) & 1, tk = lane >> 5;   // epilogue: row, gate / up, token
+  float* myD = dsw[wv];
+  float* myH = hw[wv];
+  uint16_t* myB = btw[wv];
 
+  // requests that do not depend on the tokens
   uint4 wa[2][kSbReg];
   if constexpr (REG) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int s = 0; s < kSbReg; ++s) wa[q][s] = sketch_item2(a, e, j0, cw, q, min(s, nsb - 1));
+      for (int s = 0; s < kSbReg; ++s) wa[q][s] = sketch_item2(a, e, jw, cwv, q, min(s, nsb - 1));
   }
-  if (tid < 128) {
-    const int jj = min(tid & 63, cw - 1);
-    scl[tid] = (tid < 64 ? a.sg : a.su)[(size_t)e * I + j0 + jj];
-  }
+  const float sc = (qe ? a.su : a.sg)[(size_t)e * I + jw + min(row, cwv - 1)];
   if (r > 0) {
-    const uint16_t* src = a.Bt + ((size_t)e * I + j0) * r;
-    for (int i = tid; i < kTile * r; i += GT) bts[i] = i < cw * r ? src[i] : (uint16_t)0;
+    // Bt rows jw .. jw + cwv - 1 (contiguous): 2 r pieces of 16 bytes at most
+    const uint4* src4 = reinterpret_cast<const uint4*>(a.Bt + ((size_t)e * I + jw) * r);
+    const int npc = cwv * r / 8;
+    uint4 bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = ld16c(src4 + min(lane + 64 * i, npc - 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < 2 * r) reinterpret_cast<uint4*>(myB)[idx] = idx < npc ? bv[i] : make_uint4(0, 0, 0, 0);
+    }
   }
   for (int q2 = 0; q2 < n; q2 += 2) {
-    const int pa = a.gpl[p0 + g0 + q2];
-    const int pb = a.gpl[p0 + g0 + min(q2 + 1, n - 1)];
+    const int pa = a.gpl[p0 + g0 + q2], pb = a.gpl[p0 + g0 + min(q2 + 1, n - 1)];
     const int ta = pa / a.K, tb = pb / a.K;
-    // digit planes of the two tokens
-    {
-      const uint4* sa = reinterpret_cast<const uint4*>(a.xd + (size_t)ta * kPlanes * Hp);
-      const uint4* sb = reinterpret_cast<const uint4*>(a.xd + (size_t)tb * kPlanes * Hp);
-      uint4* d = reinterpret_cast<uint4*>(limb2);
-      const int half = kPlanes * Hp / 16;
-      for (int i = tid; i < 2 * half; i += GT) d[i] = i < half ? sa[i] : sb[i - half];
-    }
-    __syncthreads();
+    const uint8_t* xa = a.xd + (size_t)ta * kPlanes * Hp;
+    const uint8_t* xb = a.xd + (size_t)tb * kPlanes * Hp;
+    const int F0 = a.xf0[tk ? tb : ta];
     v4f acc[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[q] = (v4f){0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsb; s0 += kSbReg) {
-      uint4 wl[2][kSbReg];
+      uint4 wl[2][kSbReg], dlo[kSbReg][2], dhi[kSbReg][2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int u = 0; u < kSbReg; ++u) {
 #pragma unroll
-        for (int u = 0; u < kSbReg; ++u) {
+        for (int q = 0; q < 2; ++q) {
           if constexpr (REG) wl[q][u] = wa[q][u];
-          else wl[q][u] = sketch_item2(a, e, j0, cw, q, min(s0 + u, nsb - 1));
+          else wl[q][u] = sketch_item2(a, e, jw, cwv, q, min(s0 + u, nsb - 1));
         }
+        digit_load2(xa, xb, Hp, min(s0 + u, nsb - 1), 0, dlo[u][0], dhi[u][0]);
+        digit_load2(xa, xb, Hp, min(s0 + u, nsb - 1), 1, dlo[u][1], dhi[u][1]);
+      }
 #pragma unroll
       for (int u = 0; u < kSbReg; ++u) {
         const int s = s0 + u;
         if (s < nsb) {
           const uint32_t km = 64 * s + 16 * (lane >> 4) < H / 4 ? ~0u : 0u;   // codes past the row end (H < 256)
-          const v8i d0 = digit_operand2(limb2, Hp, s, 0);
-          const v8i d1 = digit_operand2(limb2, Hp, s, 1);
+          const v8i d0 = digit_operand2(dlo[u][0], dhi[u][0]);
+          const v8i d1 = digit_operand2(dlo[u][1], dhi[u][1]);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -356,46 +420,49 @@ __global__ __launch_bounds__(GT) void k_g_screen(GArgs a) {
         }
       }
     }
-    // lane holds D[4 (lane / 16) + v][lane % 16] of each of its two row tiles
+    // lane holds D[4 (lane / 16) + v][lane % 16] of each tile; to this wavefront's LDS
     {
       const int col = lane & 15;
       if (col <= 2 * kPlanes) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) dsum[(16 * (wv + 4 * q) + 4 * (lane >> 4) + v) * 16 + col] = acc[q][v];
+          for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * 16 + col] = acc[q][v];
       }
     }
-    __syncthreads();
-    // per-row scale times the exact integer dot (as in the per-pair screen)
-    {
-      const int tk = tid >> 7, rho = tid & 127;
-      const float* d = dsum + rho * 16 + kPlanes * tk;
-      const long long S = (long long)(int)d[0] + ((long long)(int)d[1] << 4) + ((long long)(int)d[2] << 8) +
-                          ((long long)(int)d[3] << 12) + ((long long)(int)d[4] << 16) +
-                          ((long long)(int)d[5] << 20) - ((long long)(int)dsum[rho * 16 + 2 * kPlanes] << 23);
-      const int F0 = a.xf0[tk ? tb : ta];
-      gu[tk * 128 + rho] = (float)((double)scl[rho] * ldexp((double)S, kDShift - F0));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane (row, qe, tk): the row's scale times its exact integer dot for token
+    // tk (as in the per-pair screen); gate lanes pair with the up lane 16 above
+    const float* d = myD + (16 * qe + row) * 16 + kPlanes * tk;
+    const long long S = (long long)(int)d[0] + ((long long)(int)d[1] << 4) + ((long long)(int)d[2] << 8) +
+                        ((long long)(int)d[3] << 12) + ((long long)(int)d[4] << 16) + ((long long)(int)d[5] << 20) -
+                        ((long long)(int)myD[(16 * qe + row) * 16 + 2 * kPlanes] << 23);
+    const float val = (float)((double)sc * ldexp((double)S, kDShift - F0));
+    const float other = __int_as_float(lane_xor<16>(__float_as_int(val)));
+    const bool ok = row < cwv && q2 + tk < n;
+    if (qe == 0) {
+      const float hv = silu_f32(val) * other;
+      myH[tk * 16 + row] = ok ? hv : 0.f;
+      if (ok) a.hs[(size_t)(tk ? pb : pa) * I + jw + row] = hv;
     }
-    __syncthreads();
-    if (tid < 128) {
-      const int tk = tid >> 6, jj = tid & 63;
-      const bool ok = jj < cw && q2 + tk < n;
-      const float hv = silu_f32(gu[tk * 128 + jj]) * gu[tk * 128 + 64 + jj];
-      hl[tk * 64 + jj] = ok ? hv : 0.f;
-      if (ok) a.hs[(size_t)(tk ? pb : pa) * I + j0 + jj] = hv;
-    }
-    __syncthreads();
-    // this tile's share of the recovery sums: sum_j hhat_j Bt[j][:]
-    if (r > 0) {
-      const int tk = tid >> 7, l = tid & 127;
-      if (l < r && q2 + tk < n) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // this wavefront's share of the recovery sums: sum_j hhat_j Bt[j][:]
+    for (int idx = lane; idx < 2 * r; idx += 64) {
+      const int t2 = idx / r, l = idx % r;
+      if (q2 + t2 < n) {
         float z = 0.f;
-        for (int jj = 0; jj < cw; ++jj) z += hl[tk * 64 + jj] * bf16_to_f32(bts[jj * r + l]);
-        a.zp[((size_t)(tk ? pb : pa) * a.ntile + tile) * r + l] = z;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) z += myH[t2 * 16 + jj] * bf16_to_f32(myB[jj * r + l]);
+        a.zp[((size_t)(t2 ? pb : pa) * a.nz + zslot) * r + l] = z;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -405,9 +472,14 @@ template <int KPT>
 __global__ __launch_bounds__(GT) void k_g_topc(GArgs a) {
   __shared__ __align__(16) uint32_t tks[kTopkScratchWords];
   __shared__ __align__(16) int32_t cand[kMaxI];
-  __shared__ uint32_t bm[kMaxI / 32];
+  __shared__ __align__(16) uint32_t bm[kMaxI / 32];
+  __shared__ __align__(16) uint32_t pc[kMaxI / 32];
+  __shared__ uint32_t wtot[4];
+  __shared__ int s_flag;
+  __shared__ uint32_t s_base;
   const int p = blockIdx.x, tid = threadIdx.x;
   const int I = a.I, c = a.c;
+  const int e = min(max(a.ids[p], 0), a.E - 1);
   int cnt;
   const int i0 = topk_range<GT>(I, &cnt);
   uint32_t kr[KPT];
@@ -424,99 +496,102 @@ __global__ __launch_bounds__(GT) void k_g_topc(GArgs a) {
     atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  for (int w = tid; w < a.IW; w += GT) a.cm[(size_t)p * a.IW + w] = bm[w];
+  for (int w = tid; w < a.IW; w += GT) st_u(a.cm + (size_t)p * a.IW + w, bm[w]);
+  // the last pair of the expert lists the candidate union and queues its exact work
+  if (!arrive_last(a.uctr + e, (uint32_t)(a.goff[e + 1] - a.goff[e]), &s_flag)) return;
+  const int u = a.gux[e];
+  const uint32_t nU = expert_union(a, a.cm, e, a.urows + (size_t)u * a.IP, bm, pc, wtot);
+  const uint32_t nb = (nU + kRowBlk - 1) / kRowBlk;
+  if (tid == 0) {
+    a.ucnt[u] = nU;
+    s_base = atomicAdd(a.meta + 2, nb);
+  }
+  __syncthreads();
+  for (uint32_t b = tid; b < nb; b += GT) a.gexw[s_base + b] = (int)(((uint32_t)u << 16) | b);
 }
 
 // ------------------------------------------------------------------ stage 4: exact gate / up
 
-// Work item (row block, used expert): union rows [16 b, 16 b + 16) of the
-// expert's candidate union, against all of its tokens. Wavefront w takes a
-// contiguous quarter of the 32-element k steps; the quarters are summed in LDS.
-__global__ __launch_bounds__(GT) void k_g_exact(GArgs a) {
-  __shared__ __align__(16) uint32_t U[kMaxI / 32];
-  __shared__ __align__(16) uint32_t pc[kMaxI / 32];
-  __shared__ uint32_t wtot[4];
-  __shared__ uint16_t rows[kRowBlk];
-  __shared__ __align__(16) float red[4 * 2 * 4 * 256];     // [wave][gate, up][token tile][D]
-  const int u = blockIdx.y;
-  if ((uint32_t)u >= a.meta[0]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// One load batch of an exact work item: KC 32-element steps from kc on of the
+// lane's gate and up rows and of its token's x. KC divides the step count, so a
+// batch is either whole or past the end (then it repeats the last batch, which
+// is not multiplied); the loads of a batch share one address.
+template <int KC>
+struct ExactBatch {
+  uint4 g[KC], u[KC], x[KC];
+};
+template <int KC>
+__device__ __forceinline__ void exact_load(ExactBatch<KC>& b, const uint16_t* wgr, const uint16_t* wur,
+                                           const uint16_t* xr, int kc, int nks) {
+  const int k0 = 32 * min(kc, nks - KC);
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    b.g[i] = ld16(wgr + k0 + 32 * i);
+    b.u[i] = ld16(wur + k0 + 32 * i);
+    b.x[i] = ld16c(xr + k0 + 32 * i);
+  }
+}
+template <int KC>
+__device__ __forceinline__ void exact_mul(const ExactBatch<KC>& b, v4f& ag, v4f& au) {
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    ag = mfma_bf16(b.g[i], b.x[i], ag);
+    au = mfma_bf16(b.u[i], b.x[i], au);
+  }
+}
+
+// One wavefront per work item (row block, used expert): union rows
+// [16 b, 16 b + 16) of the expert's candidate union (every channel when dense)
+// over the whole hidden width, against its tokens, 16 per pass (one MFMA
+// column tile). The rows stream in batches of kKc steps, each batch requested
+// before the previous one is multiplied; the wavefronts of a workgroup run
+// independently (no barriers).
+template <int KC>
+__global__ __launch_bounds__(GT, 2) void k_g_exact(GArgs a) {
+  const int lane = threadIdx.x & 63;
   const int H = a.H, I = a.I;
-  const int e = a.gue[u];
-  const int p0 = a.goff[e], n = a.goff[e + 1] - p0;
-  const int32_t* pl = a.gpl + p0;
-  const uint32_t nU = union_rows(a.cm, pl, n, a.IW, I, a.dense != 0, U, pc, wtot);
-  if (blockIdx.x == 0 && tid == 0) a.ucnt[u] = nU;
-  const uint32_t lo = kRowBlk * blockIdx.x;
-  if (lo >= nU) return;
-  const int nrow = (int)min((uint32_t)kRowBlk, nU - lo);
-  union_list(U, pc, a.IW, lo, lo + nrow, rows);
+  const uint32_t nwork = a.dense ? a.meta[0] * (uint32_t)a.nrb : a.meta[2];
   const int row = lane & 15, g = lane >> 4;
-  const int j = rows[min(row, nrow - 1)];
-  const uint16_t* wgr = a.wg + ((size_t)e * I + j) * H + 8 * g;
-  const uint16_t* wur = a.wu + ((size_t)e * I + j) * H + 8 * g;
-  const int nks = H / 32, per = (nks + 3) / 4;
-  const int ks0 = min(nks, wv * per), ks1 = min(nks, ks0 + per);
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int ngrp = min(4, (n - s0 + 15) / 16);
-    const uint16_t* xr[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int s = min(s0 + 16 * q + row, n - 1);
-      xr[q] = a.x + (size_t)(pl[s] / a.K) * H + 8 * g;
-    }
-    v4f ag[4], au[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { ag[q] = (v4f){0.f, 0.f, 0.f, 0.f}; au[q] = ag[q]; }
-    for (int kc = ks0; kc < ks1; kc += kKc) {
-      uint4 wgv[kKc], wuv[kKc];
-#pragma unroll
-      for (int i = 0; i < kKc; ++i) {
-        const int ks = min(kc + i, ks1 - 1);
-        wgv[i] = ld16(wgr + 32 * ks);
-        wuv[i] = ld16(wur + 32 * ks);
+  const int nks = H / 32;
+  const uint32_t nwave = gridDim.x * (GT / 64);
+  for (uint32_t wi = blockIdx.x * (GT / 64) + (threadIdx.x >> 6); wi < nwork; wi += nwave) {
+    int u, b;
+    if (a.dense) { u = (int)(wi / a.nrb); b = (int)(wi % a.nrb); }
+    else { const int it = a.gexw[wi]; u = it >> 16; b = it & 0xFFFF; }
+    const int e = a.gue[u];
+    const int p0 = a.goff[e], n = a.goff[e + 1] - p0;
+    const int nU = a.dense ? I : (int)a.ucnt[u];
+    const int nrow = min(kRowBlk, nU - kRowBlk * b);
+    const int q = kRowBlk * b + min(row, nrow - 1);
+    const int j = a.dense ? q : a.urows[(size_t)u * a.IP + q];
+    const uint16_t* wgr = a.wg + ((size_t)e * I + j) * H + 8 * g;
+    const uint16_t* wur = a.wu + ((size_t)e * I + j) * H + 8 * g;
+    const int32_t* pl = a.gpl + p0;
+    for (int s0 = 0; s0 < n; s0 += 16) {
+      const int s = s0 + row;                  // this lane's token slot (B operand column)
+      const int pp = pl[min(s, n - 1)];
+      const uint16_t* xr = a.x + (size_t)(pp / a.K) * H + 8 * g;
+      v4f ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+      ExactBatch<KC> A, B;
+      exact_load(A, wgr, wur, xr, 0, nks);
+      for (int kc = 0; kc < nks; kc += 2 * KC) {
+        exact_load(B, wgr, wur, xr, kc + KC, nks);
+        exact_mul(A, ag, au);
+        exact_load(A, wgr, wur, xr, kc + 2 * KC, nks);
+        if (kc + KC < nks) exact_mul(B, ag, au);
       }
+      // lane holds D[4 g + v][lane % 16]: union rows 4 g + v, token slot s
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q < ngrp) {
-#pragma unroll
-          for (int i = 0; i < kKc; ++i) {
-            if (kc + i < ks1) {
-              const uint4 xb = ld16c(xr[q] + 32 * (kc + i));
-              ag[q] = mfma_bf16(wgv[i], xb, ag[q]);
-              au[q] = mfma_bf16(wuv[i], xb, au[q]);
-            }
-          }
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 4 * g + v;
+        const int jr = __shfl(j, rr, 64);
+        if (rr < nrow && s < n) {
+          const float h = silu_f32(ag[v]) * au[v];
+          if (a.dense) a.hk[(size_t)pp * I + jr] = f32_to_bf16(h);
+          else a.hx[(size_t)pp * I + jr] = h;
         }
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<float4*>(red + ((wv * 2 + 0) * 4 + q) * 256 + 4 * lane) =
-          make_float4(ag[q][0], ag[q][1], ag[q][2], ag[q][3]);
-      *reinterpret_cast<float4*>(red + ((wv * 2 + 1) * 4 + q) * 256 + 4 * lane) =
-          make_float4(au[q][0], au[q][1], au[q][2], au[q][3]);
-    }
-    __syncthreads();
-    // element tid of a tile: D[4 (l / 16) + v][l % 16] with l = tid / 4, v = tid % 4
-    const int rho = 4 * (tid >> 6) + (tid & 3), col = (tid >> 2) & 15;
-    for (int q = 0; q < ngrp; ++q) {
-      const int s = s0 + 16 * q + col;
-      float gs = 0.f, us = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        gs += red[((w * 2 + 0) * 4 + q) * 256 + tid];
-        us += red[((w * 2 + 1) * 4 + q) * 256 + tid];
-      }
-      if (rho < nrow && s < n) {
-        const int pp = pl[s];
-        const int jr = rows[rho];
-        const float h = silu_f32(gs) * us;
-        if (a.dense) a.hk[(size_t)pp * I + jr] = f32_to_bf16(h);
-        else a.hx[(size_t)pp * I + jr] = h;
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -527,8 +602,11 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
   __shared__ __align__(16) uint32_t tks[kTopkScratchWords];
   __shared__ __align__(16) int32_t sel[kMaxI];
   __shared__ __align__(16) uint16_t hrow[kMaxI];
-  __shared__ uint32_t bm[kMaxI / 32];
-  __shared__ float zred[GT];
+  __shared__ __align__(16) uint32_t bm[kMaxI / 32];
+  __shared__ __align__(16) uint32_t pc[kMaxI / 32];
+  __shared__ __align__(16) float zpart[GT * 8];
+  __shared__ uint32_t wtot[4];
+  __shared__ int s_flag;
   const int p = blockIdx.x, tid = threadIdx.x;
   const int I = a.I, c = a.c, k = a.k, r = a.r;
   const int e = min(max(a.ids[p], 0), a.E - 1);
@@ -536,9 +614,14 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
   if (k > 0) {
     int cnt;
     const int i0 = topk_range<GT>(c, &cnt);
+    int jc[KPT];
     uint32_t kr[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) kr[j] = j < cnt ? score_key(a.hx[(size_t)p * I + cl[i0 + j]]) : 0u;
+    for (int j = 0; j < KPT; ++j) jc[j] = cl[min(i0 + j, c - 1)];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = score_key(a.hx[(size_t)p * I + jc[j]]);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = j < cnt ? kr[j] : 0u;
     block_topk<GT, KPT>(kr, i0, cnt, c, k, sel, tks);
   }
   for (int i = tid; i < I; i += GT) hrow[i] = 0;
@@ -561,138 +644,260 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
       for (int i = tid; i < I; i += GT) hdst[i] = hrow[i];
     }
   }
-  for (int w = tid; w < a.IW; w += GT) a.km[(size_t)p * a.IW + w] = bm[w];
-  // z = sum over all channels of hhat_j Bt[j] (the screen's tile sums) minus the kept ones
+  for (int w = tid; w < a.IW; w += GT) st_u(a.km + (size_t)p * a.IW + w, bm[w]);
+  // z = sum over all channels of hhat_j Bt[j] (the screen's tile sums) minus the
+  // kept channels' terms. Thread (cc, gi): 8 columns 8 cc .. 8 cc + 7, rows and
+  // tiles gi, gi + groups, ... (loads in batches of four)
   if (r > 0) {
-    const int groups = GT / r, l = tid % r, gi = tid / r;
-    float z = 0.f;
+    const int npr = r / 8, groups = GT / npr;
+    const int cc = tid % npr, gi = tid / npr;
+    float acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
     if (gi < groups) {
-      const float* zs = a.zp + (size_t)p * a.ntile * r;
-      for (int t = gi; t < a.ntile; t += groups) z += zs[(size_t)t * r + l];
+      const float* zs = a.zp + (size_t)p * a.nz * r + 8 * cc;
+      for (int t0 = gi; t0 < a.nz; t0 += 4 * groups) {
+        float4 z4[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = min(t0 + u * groups, a.nz - 1);
+          z4[u][0] = *reinterpret_cast<const float4*>(zs + (size_t)t * r);
+          z4[u][1] = *reinterpret_cast<const float4*>(zs + (size_t)t * r + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (t0 + u * groups < a.nz) {
+            acc[0] += z4[u][0].x; acc[1] += z4[u][0].y; acc[2] += z4[u][0].z; acc[3] += z4[u][0].w;
+            acc[4] += z4[u][1].x; acc[5] += z4[u][1].y; acc[6] += z4[u][1].z; acc[7] += z4[u][1].w;
+          }
+        }
+      }
       const float* hsp = a.hs + (size_t)p * I;
-      for (int i = gi; i < k; i += groups) {
-        const int j = sel[i];
-        z -= hsp[j] * bf16_to_f32(a.Bt[((size_t)e * I + j) * r + l]);
+      for (int i0 = gi; i0 < k; i0 += 4 * groups) {
+        uint4 bw[4];
+        float hv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = sel[min(i0 + u * groups, k - 1)];
+          bw[u] = ld16c(a.Bt + ((size_t)e * I + j) * r + 8 * cc);
+          hv[u] = hsp[j];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float h = i0 + u * groups < k ? -hv[u] : 0.f;
+          acc[0] += h * bf16lo(bw[u].x); acc[1] += h * bf16hi(bw[u].x);
+          acc[2] += h * bf16lo(bw[u].y); acc[3] += h * bf16hi(bw[u].y);
+          acc[4] += h * bf16lo(bw[u].z); acc[5] += h * bf16hi(bw[u].z);
+          acc[6] += h * bf16lo(bw[u].w); acc[7] += h * bf16hi(bw[u].w);
+        }
       }
     }
-    zred[tid] = z;
+    if (gi < groups) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) zpart[gi * r + 8 * cc + v] = acc[v];
+    }
     __syncthreads();
     if (tid < r) {
       float s = 0.f;
-      for (int q = 0; q < groups; ++q) s += zred[q * r + tid];
+      for (int q = 0; q < groups; ++q) s += zpart[q * r + tid];
       a.zf[(size_t)p * r + tid] = s;
     }
   }
+  // the last pair of the expert lists the kept union
+  if (!arrive_last(a.kctr + e, (uint32_t)(a.goff[e + 1] - a.goff[e]), &s_flag)) return;
+  const int u = a.gux[e];
+  const uint32_t nU = expert_union(a, a.km, e, a.drows + (size_t)u * a.IP, bm, pc, wtot);
+  if (tid == 0) a.dcnt[u] = nU;
 }
 
-// ------------------------------------------------------------------ stage 6: down projection and A z
+// ------------------------------------------------------------------ stage 6: down projection, A z, combine
 
 // Work item (column tile, used expert): output columns [64 b, 64 b + 64) of all
-// of the expert's tokens, 16 tokens at a time. Wavefront w owns columns
-// 16 w .. 16 w + 15. D = tokens x columns: the A operand is the token's masked
-// activations (or its recovery coefficients), the B operand the down rows (or
-// the rows of A), staged column-major in LDS so that each lane reads eight
-// consecutive contraction indices.
-__global__ __launch_bounds__(GT) void k_g_down(GArgs a) {
-  __shared__ __align__(16) uint32_t U[kMaxI / 32];
-  __shared__ __align__(16) uint32_t pc[kMaxI / 32];
-  __shared__ uint32_t wtot[4];
-  __shared__ __align__(16) uint16_t rows[kMaxI];
-  __shared__ __align__(16) uint16_t hA[16 * kDnPitch];        // [token][row]
-  __shared__ __align__(16) uint16_t wT[kColTile * kDnPitch];  // [column][row]
-  const int u = blockIdx.y;
-  if ((uint32_t)u >= a.meta[0]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.H, I = a.I, r = a.r;
-  const int e = a.gue[u];
-  const int p0 = a.goff[e], n = a.goff[e + 1] - p0;
-  const int32_t* pl = a.gpl + p0;
-  const int c0 = kColTile * blockIdx.x;
-  const uint32_t nU = union_rows(a.km, pl, n, a.IW, I, a.dense != 0, U, pc, wtot);
-  if (blockIdx.x == 0 && tid == 0) a.dcnt[u] = nU;
-  union_list(U, pc, a.IW, 0, nU, rows);
-  const int m16 = lane & 15, g = lane >> 4;
-  const int col = c0 + 16 * wv + m16;            // this lane's output column (B operand and D)
-  for (int s0 = 0; s0 < n; s0 += 16) {
-    const int nt = min(16, n - s0);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    // recovery: D += z (tokens x r) A[e]^T (r x columns); z staged in hA
-    if (r > 0 && !a.dense) {
-      for (int i = tid; i < 16 * kRPad; i += GT) {
-        const int m = i / kRPad, l = i % kRPad;
-        const float z = (m < nt && l < r) ? a.zf[(size_t)pl[s0 + m] * r + l] : 0.f;
-        hA[m * kDnPitch + l] = f32_to_bf16(z);
-      }
-      __syncthreads();
-      const uint16_t* arow = a.A + ((size_t)e * H + col) * r;
-      for (int ks = 0; ks < (r + 31) / 32; ++ks) {
-        const int l0 = 32 * ks + 8 * g;
-        const uint4 bv = l0 < r ? ld16c(arow + l0) : make_uint4(0, 0, 0, 0);
-        const uint4 av = *reinterpret_cast<const uint4*>(hA + m16 * kDnPitch + l0);
-        acc = mfma_bf16(av, bv, acc);
-      }
-      __syncthreads();
-    }
-    for (uint32_t q0 = 0; q0 < nU; q0 += kDnRows) {
-      const int nr = (int)min((uint32_t)kDnRows, nU - q0);
-      // down rows: 16-byte pieces (row rho, columns 8 cc .. 8 cc + 7)
-      uint4 wv4[kDnRows * 8 / GT];
+// of the expert's tokens, 16 tokens at a time. D = tokens x columns, one MFMA
+// column tile per 16 output columns. Wavefront w takes the 32-row chunks
+// w, w + 4, ... of the expert's kept-union rows (every row when dense): it
+// requests the next chunk, transposes the current one into its own LDS
+// (column-major, so that each lane reads eight consecutive contraction indices)
+// and multiplies, with no barrier; the four partial tiles are summed at the
+// end. The recovery term z A^T of column tile w is computed by wavefront w.
+constexpr int kDnP = 40;           // LDS pitch (BF16) of a wavefront's transposed 32-row chunk
+
+struct DownChunk {
+  uint4 w[4];        // down-row pieces: row (lane >> 3) + 8 i, columns 8 (lane & 7) .. + 7
+  uint16_t h[8];     // masked activations: token (lane + 64 i) >> 5, row (lane + 64 i) & 31
+};
+
+__device__ __forceinline__ void down_load(DownChunk& d, const GArgs& a, int e, int c0, const uint16_t* rows,
+                                          const int* pls, int q0, int nr) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int qq = 0; qq < kDnRows * 8 / GT; ++qq) {
-        const int idx = tid + GT * qq, rho = idx >> 3, cc = idx & 7;
-        const int jr = rows[q0 + min(rho, nr - 1)];
-        wv4[qq] = ld16(a.wd + ((size_t)e * I + jr) * H + c0 + 8 * cc);
-      }
-      // masked activations of the tokens at these rows
-      for (int i = tid; i < 16 * kDnRows; i += GT) {
-        const int m = i / kDnRows, rho = i % kDnRows;
-        hA[m * kDnPitch + rho] = (m < nt && rho < nr) ? a.hk[(size_t)pl[s0 + m] * I + rows[q0 + rho]] : (uint16_t)0;
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int q = q0 + min((lane >> 3) + 8 * i, nr - 1);
+    const int jr = a.dense ? q : rows[q];
+    d.w[i] = ld16(a.wd + ((size_t)e * a.I + jr) * a.H + c0 + 8 * (lane & 7));
+  }
 #pragma unroll
-      for (int qq = 0; qq < kDnRows * 8 / GT; ++qq) {
-        const int idx = tid + GT * qq, rho = idx >> 3, cc = idx & 7;
-        const bool ok = rho < nr;
-        const uint32_t w4[4] = {ok ? wv4[qq].x : 0u, ok ? wv4[qq].y : 0u, ok ? wv4[qq].z : 0u, ok ? wv4[qq].w : 0u};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          wT[(8 * cc + 2 * h) * kDnPitch + rho] = (uint16_t)(w4[h] & 0xFFFFu);
-          wT[(8 * cc + 2 * h + 1) * kDnPitch + rho] = (uint16_t)(w4[h] >> 16);
-        }
-      }
-      __syncthreads();
-      for (int ks = 0; ks < (nr + 31) / 32; ++ks) {
-        const uint4 av = *reinterpret_cast<const uint4*>(hA + m16 * kDnPitch + 32 * ks + 8 * g);
-        const uint4 bv = *reinterpret_cast<const uint4*>(wT + (16 * wv + m16) * kDnPitch + 32 * ks + 8 * g);
-        acc = mfma_bf16(av, bv, acc);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
-      if (m < nt) a.yp[(size_t)pl[s0 + m] * H + col] = acc[v];
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int idx = lane + 64 * i, m = idx >> 5;
+    const int q = q0 + min(idx & 31, nr - 1);
+    d.h[i] = a.hk[(size_t)pls[m] * a.I + (a.dense ? q : rows[q])];
   }
 }
 
-// ------------------------------------------------------------------ stage 7: combine
-
-__global__ __launch_bounds__(GT) void k_g_combine(GArgs a) {
-  const int t = blockIdx.x, H = a.H, K = a.K;
-  for (int h0 = 8 * threadIdx.x; h0 < H; h0 += 8 * GT) {
-    float acc[8];
+__global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
+  __shared__ __align__(16) uint16_t rows[kMaxI];
+  __shared__ __align__(16) uint16_t wT[4][kColTile * kDnP];   // per wavefront: [column][row]
+  __shared__ __align__(16) uint16_t hA[4][16 * kDnP];         // per wavefront: [token][row]
+  __shared__ __align__(16) float red[4][16 * kColTile];       // per wavefront: [token][column]
+  __shared__ int pls[16];
+  __shared__ int lastt[16];
+  const int u = blockIdx.y;
+  if ((uint32_t)u >= a.meta[0]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, I = a.I, r = a.r, K = a.K;
+  const int e = a.gue[u];
+  const int p0 = a.goff[e], n = a.goff[e + 1] - p0;
+  const int c0 = kColTile * blockIdx.x;
+  const int nct = H / kColTile;
+  const int nU = a.dense ? I : (int)a.dcnt[u];
+  if (!a.dense) {
+    // the kept-union rows of the expert, staged once
+    const uint4* src = reinterpret_cast<const uint4*>(a.drows + (size_t)u * a.IP);
+    const int n8 = (nU + 7) / 8;
+    for (int b0 = 0; b0 < n8; b0 += 4 * GT) {
+      uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int q = 0; q < K; ++q) {
-      const float w = a.topk_w[(size_t)t * K + q];
-      const float4* y = reinterpret_cast<const float4*>(a.yp + ((size_t)t * K + q) * H + h0);
-      const float4 y0 = y[0], y1 = y[1];
-      acc[0] += w * y0.x; acc[1] += w * y0.y; acc[2] += w * y0.z; acc[3] += w * y0.w;
-      acc[4] += w * y1.x; acc[5] += w * y1.y; acc[6] += w * y1.z; acc[7] += w * y1.w;
+      for (int q = 0; q < 4; ++q) v[q] = src[min(b0 + tid + GT * q, max(n8 - 1, 0))];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (b0 + tid + GT * q < n8) reinterpret_cast<uint4*>(rows)[b0 + tid + GT * q] = v[q];
     }
-    *reinterpret_cast<uint4*>(a.out + (size_t)t * H + h0) =
-        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                   pack_bf16x2(acc[6], acc[7]));
+  }
+  const int m16 = lane & 15, g = lane >> 4;
+  const int nch = (nU + 31) / 32;
+  uint16_t* myT = wT[wv];
+  uint16_t* myA = hA[wv];
+  for (int s0 = 0; s0 < n; s0 += 16) {
+    const int nt = min(16, n - s0);
+    if (tid < 16) pls[tid] = a.gpl[p0 + s0 + min(tid, nt - 1)];
+    __syncthreads();
+    v4f acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // recovery, column tile wv: D += z (tokens x r) A[e]^T (r x columns)
+    v4f accr = {0.f, 0.f, 0.f, 0.f};
+    if (r > 0 && !a.dense) {
+      const uint16_t* arow = a.A + ((size_t)e * H + c0 + 16 * wv + m16) * r;
+      const float* zrow = a.zf + (size_t)pls[m16] * r;
+      for (int ks = 0; ks < (r + 31) / 32; ++ks) {
+        const int l0 = 32 * ks + 8 * g;
+        const bool ok = l0 < r && m16 < nt;
+        const int lc = min(l0, r - 8);
+        const uint4 bq = ld16c(arow + lc);
+        const float4 z0 = *reinterpret_cast<const float4*>(zrow + lc);
+        const float4 z1 = *reinterpret_cast<const float4*>(zrow + lc + 4);
+        const uint4 av = ok ? make_uint4(pack_bf16x2(z0.x, z0.y), pack_bf16x2(z0.z, z0.w), pack_bf16x2(z1.x, z1.y),
+                                         pack_bf16x2(z1.z, z1.w))
+                            : make_uint4(0, 0, 0, 0);
+        accr = mfma_bf16(av, l0 < r ? bq : make_uint4(0, 0, 0, 0), accr);
+      }
+    }
+    if (wv < nch) {
+      DownChunk cur, nxt;
+      down_load(cur, a, e, c0, rows, pls, 32 * wv, min(32, nU - 32 * wv));
+      for (int ch = wv; ch < nch; ch += 4) {
+        const int nr = min(32, nU - 32 * ch);
+        const int cn = ch + 4 < nch ? ch + 4 : ch;          // (past the end: a repeat, not used)
+        down_load(nxt, a, e, c0, rows, pls, 32 * cn, min(32, nU - 32 * cn));
+        // transpose the current chunk into this wavefront's LDS (rows past nr: zeros)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rho = (lane >> 3) + 8 * i, cc = lane & 7;
+          const bool ok = rho < nr;
+          const uint32_t w4[4] = {ok ? cur.w[i].x : 0u, ok ? cur.w[i].y : 0u, ok ? cur.w[i].z : 0u,
+                                  ok ? cur.w[i].w : 0u};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            myT[(8 * cc + 2 * h) * kDnP + rho] = (uint16_t)(w4[h] & 0xFFFFu);
+            myT[(8 * cc + 2 * h + 1) * kDnP + rho] = (uint16_t)(w4[h] >> 16);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = lane + 64 * i, m = idx >> 5, rho = idx & 31;
+          myA[m * kDnP + rho] = (m < nt && rho < nr) ? cur.h[i] : (uint16_t)0;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint4 av = *reinterpret_cast<const uint4*>(myA + m16 * kDnP + 8 * g);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const uint4 bq = *reinterpret_cast<const uint4*>(myT + (16 * ct + m16) * kDnP + 8 * g);
+          acc[ct] = mfma_bf16(av, bq, acc[ct]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        cur = nxt;
+      }
+    }
+    // partial tiles of the four wavefronts: lane holds D[4 g + v][m16] of column tile ct
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const v4f d = ct == wv ? acc[ct] + accr : acc[ct];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wv][(4 * g + v) * kColTile + 16 * ct + m16] = d[v];
+    }
+    __syncthreads();
+    {
+      const int m = tid >> 4, cq = 4 * (tid & 15);
+      if (m < nt) {
+        float4 y = *reinterpret_cast<const float4*>(&red[0][m * kColTile + cq]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const float4 t4 = *reinterpret_cast<const float4*>(&red[w][m * kColTile + cq]);
+          y.x += t4.x; y.y += t4.y; y.z += t4.z; y.w += t4.w;
+        }
+        float* dst = a.yp + (size_t)pls[m] * H + c0 + cq;
+        st_f(dst, y.x); st_f(dst + 1, y.y); st_f(dst + 2, y.z); st_f(dst + 3, y.w);
+      }
+    }
+    // arrivals per (token, column tile); the last of a token's K pairs combines it
+    drain_and_join();
+    if (tid < 16) {
+      int last = 0;
+      if (tid < nt) {
+        const int t = pls[tid] / K;
+        uint32_t* ctr = a.octr + (size_t)t * nct + blockIdx.x;
+        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (uint32_t)K - 1;
+        if (last) st_u(ctr, 0u);
+      }
+      lastt[tid] = last;
+    }
+    __syncthreads();
+    for (int m = 0; m < nt; ++m) {
+      if (!lastt[m]) continue;
+      const int t = pls[m] / K;
+      if (tid < kColTile) {
+        float sum = 0.f;
+        for (int q0 = 0; q0 < K; q0 += 8) {
+          float yv[8], wq[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int qc = min(q0 + q, K - 1);
+            yv[q] = ld_f(a.yp + ((size_t)t * K + qc) * H + c0 + tid);
+            wq[q] = a.topk_w[(size_t)t * K + qc];
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q0 + q < K) sum += wq[q] * yv[q];
+        }
+        a.out[(size_t)t * H + c0 + tid] = f32_to_bf16(sum);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -702,12 +907,15 @@ __global__ void k_g_stats(GArgs a, cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   const uint32_t nue = a.meta[0];
   uint64_t uc = 0, dc = 0;
-  for (uint32_t u = 0; u < nue; ++u) {
-    if (!a.dense) uc += a.ucnt[u];
-    dc += a.dcnt[u];
+  if (!a.dense) {
+    for (uint32_t u = 0; u < nue; ++u) {
+      uc += a.ucnt[u];
+      dc += a.dcnt[u];
+    }
+    if (a.k == 0) uc = 0;                       // no exact phase ran
+  } else {
+    uc = dc = (uint64_t)nue * a.I;
   }
-  if (a.dense) uc = dc;
-  else if (a.k == 0) uc = 0;                     // no exact phase ran
   const uint64_t I = a.I, H = a.H, r = a.r;
   cfm_stats s;
   s.bytes_io = 2ull * a.T * H + 8ull * a.T * a.K + 2ull * a.T * H;
@@ -729,11 +937,6 @@ size_t prep_lds(int H, int E) {
   const size_t Hp = std::max(H, 256);
   return std::max(10 * Hp, (size_t)16 * E);
 }
-size_t screen_lds(int H, int r) {
-  const size_t Hp = std::max(H, 256);
-  return 2 * kPlanes * Hp + 4 * (128 * 16 + 2 * 128 + 2 * 64 + 128) + 2 * (size_t)kTile * std::max(r, 1);
-}
-
 int launch_k(const char* name, const void* fn, dim3 grid, size_t lds, const GArgs& ga, hipStream_t stream) {
   if (grid.x == 0 || grid.y == 0) return CFM_OK;
   if (lds > 65536) CFM_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -761,20 +964,28 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   g.T = T; g.K = K; g.P = T * K; g.E = E; g.I = I; g.H = H; g.k = k; g.c = c; g.r = r; g.dense = dense;
   g.ntile = (I + kTile - 1) / kTile;
   g.IW = (I + 31) / 32;
+  g.nrb = (I + kRowBlk - 1) / kRowBlk;
+  g.IP = (I + 7) / 8 * 8;
   g.maxu = std::min(E, g.P);
   g.maxwork = g.maxu + (g.P + kTokGroup - 1) / kTokGroup;
-  const size_t P = (size_t)g.P, Hp = std::max(H, 256);
+  const size_t P = (size_t)g.P, Hp = std::max(H, 256), U = (size_t)g.maxu;
   Carve cv;
   cv.off = base;
+  // counters that must read zero between calls come first
+  g.off_uctr = cv.take(4 * (size_t)E);
+  g.off_kctr = cv.take(4 * (size_t)E);
+  g.off_octr = cv.take(4 * (size_t)T * (H / kColTile));
   g.off_meta = cv.take(16);
   g.off_goff = cv.take(4 * ((size_t)E + 1));
   g.off_gpl = cv.take(4 * P);
   g.off_gue = cv.take(4 * (size_t)E);
+  g.off_gux = cv.take(4 * (size_t)E);
   g.off_gwork = cv.take(4 * (size_t)g.maxwork);
+  g.off_gexw = cv.take(dense ? 16 : 4 * U * g.nrb);
   g.off_xf0 = cv.take(4 * (size_t)T);
   g.off_xd = cv.take(dense ? 16 : (size_t)T * kPlanes * Hp);
   g.off_hs = cv.take(dense ? 16 : P * I * 4);
-  g.off_zp = cv.take(dense || r == 0 ? 16 : P * g.ntile * r * 4);
+  g.off_zp = cv.take(dense || r == 0 ? 16 : P * (size_t)((I + 15) / 16) * r * 4);
   g.off_cm = cv.take(dense ? 16 : P * g.IW * 4);
   g.off_cl = cv.take(dense ? 16 : P * std::max(c, 1) * 4);
   g.off_hx = cv.take(dense ? 16 : P * I * 4);
@@ -782,8 +993,10 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   g.off_hk = cv.take(P * I * 2);
   g.off_zf = cv.take(dense || r == 0 ? 16 : P * r * 4);
   g.off_yp = cv.take(P * H * 4);
-  g.off_ucnt = cv.take(4 * (size_t)E);
-  g.off_dcnt = cv.take(4 * (size_t)E);
+  g.off_ucnt = cv.take(4 * U);
+  g.off_dcnt = cv.take(4 * U);
+  g.off_urows = cv.take(2 * U * g.IP);
+  g.off_drows = cv.take(2 * U * g.IP);
   g.bytes = cv.off;
   return g;
 }
@@ -800,7 +1013,9 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.goff = reinterpret_cast<int32_t*>(ws + g.off_goff);
   a.gpl = reinterpret_cast<int32_t*>(ws + g.off_gpl);
   a.gue = reinterpret_cast<int32_t*>(ws + g.off_gue);
+  a.gux = reinterpret_cast<int32_t*>(ws + g.off_gux);
   a.gwork = reinterpret_cast<int32_t*>(ws + g.off_gwork);
+  a.gexw = reinterpret_cast<int32_t*>(ws + g.off_gexw);
   a.xd = reinterpret_cast<uint8_t*>(ws + g.off_xd);
   a.xf0 = reinterpret_cast<int32_t*>(ws + g.off_xf0);
   a.hs = reinterpret_cast<float*>(ws + g.off_hs);
@@ -814,12 +1029,17 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.yp = reinterpret_cast<float*>(ws + g.off_yp);
   a.ucnt = reinterpret_cast<uint32_t*>(ws + g.off_ucnt);
   a.dcnt = reinterpret_cast<uint32_t*>(ws + g.off_dcnt);
+  a.urows = reinterpret_cast<uint16_t*>(ws + g.off_urows);
+  a.drows = reinterpret_cast<uint16_t*>(ws + g.off_drows);
+  a.uctr = reinterpret_cast<uint32_t*>(ws + g.off_uctr);
+  a.kctr = reinterpret_cast<uint32_t*>(ws + g.off_kctr);
+  a.octr = reinterpret_cast<uint32_t*>(ws + g.off_octr);
   a.T = g.T; a.K = g.K; a.P = g.P; a.E = g.E; a.I = g.I; a.H = g.H;
   int log2H = 0;
   while ((1 << log2H) < g.H) ++log2H;
   a.log2H = log2H;
   a.k = g.dense ? g.I : g.k; a.c = g.dense ? g.I : g.c; a.r = g.dense ? 0 : g.r;
-  a.ntile = g.ntile; a.IW = g.IW; a.dense = g.dense ? 1 : 0;
+  a.ntile = g.ntile; a.nz = (g.I + 15) / 16; a.IW = g.IW; a.nrb = g.nrb; a.IP = g.IP; a.dense = g.dense ? 1 : 0;
   const int H = g.H;
 
   // 1. rotation + grouping
@@ -842,9 +1062,9 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
       const bool reg = (H + 255) / 256 <= kSbReg;
       const void* fn = reg ? reinterpret_cast<const void*>(&k_g_screen<true>)
                            : reinterpret_cast<const void*>(&k_g_screen<false>);
-      if (int rc = launch_k("k_g_screen", fn, dim3(g.ntile, g.maxwork), screen_lds(H, g.r), a, stream)) return rc;
+      if (int rc = launch_k("k_g_screen", fn, dim3(g.ntile, g.maxwork), 0, a, stream)) return rc;
     }
-    // 3. top-c
+    // 3. top-c, candidate unions, exact work list
     {
       const int per = (g.I + GT - 1) / GT;
       const void* fn = per <= 4 ? reinterpret_cast<const void*>(&k_g_topc<4>)
@@ -854,22 +1074,23 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   }
   // 4. exact gate / up over the candidate unions (all channels when dense)
   if (g.dense || g.k > 0) {
-    if (int rc = launch_k("k_g_exact", reinterpret_cast<const void*>(&k_g_exact),
-                          dim3((g.I + kRowBlk - 1) / kRowBlk, g.maxu), 0, a, stream))
-      return rc;
+    const int grid = std::min(kExactGrid, (g.maxu * g.nrb + 3) / 4);
+    const int kc = std::min(kKc, H / 32);
+    const void* fn = kc == 8 ? reinterpret_cast<const void*>(&k_g_exact<8>)
+                   : kc == 4 ? reinterpret_cast<const void*>(&k_g_exact<4>)
+                             : reinterpret_cast<const void*>(&k_g_exact<2>);
+    if (int rc = launch_k("k_g_exact", fn, dim3(grid), 0, a, stream)) return rc;
   }
   if (!g.dense) {
-    // 5. top-k, masked activations, recovery coefficients
+    // 5. top-k, masked activations, recovery coefficients, kept unions
     const int per = (std::max(g.c, 1) + GT - 1) / GT;
     const void* fn = per <= 4 ? reinterpret_cast<const void*>(&k_g_topk<4>)
                               : reinterpret_cast<const void*>(&k_g_topk<32>);
     if (int rc = launch_k("k_g_topk", fn, dim3(g.P), 0, a, stream)) return rc;
   }
-  // 6. down + recovery, 7. combine
+  // 6. down + recovery + combine
   if (int rc = launch_k("k_g_down", reinterpret_cast<const void*>(&k_g_down), dim3(H / kColTile, g.maxu), 0, a,
                         stream))
-    return rc;
-  if (int rc = launch_k("k_g_combine", reinterpret_cast<const void*>(&k_g_combine), dim3(g.T), 0, a, stream))
     return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_g_stats, dim3(1), dim3(64), 0, stream, a, static_cast<cfm_stats*>(s.stats));

@@ -176,8 +176,9 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
 /*
  * cfm_set_forward_path - which kernels serve moe_select_forward and
  * moe_dense_forward (process-wide; returns the previous setting, or CFM_EINVAL).
- *   0 automatic (default): the expert-grouped pass from 8 tokens on where the
- *     shape allows it, the per-pair pass below that;
+ *   0 automatic (default): the expert-grouped pass where the shape allows it
+ *     and the batch is large (selected layer: 48 tokens or more; dense layer:
+ *     32 or more), the per-pair pass otherwise;
  *   1 the per-pair pass (one persistent launch; lowest latency at batch 1);
  *   2 the expert-grouped pass (pairs grouped by expert; each weight row an
  *     expert needs is read once for all of its tokens: the article's batch

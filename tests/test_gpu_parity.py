@@ -295,7 +295,7 @@ def test_q18_b1_full_size(cfm, q18_layer):
 
 @pytest.mark.parametrize("name", ["q13_b8", "q13_b16", "q18_b16"])
 def test_batched_full_size(cfm, name):
-    """Batches of 8 and 16 tokens through both passes (grouped: the automatic choice; per-pair forced)."""
+    """Batches of 8 and 16 tokens through both passes (each forced)."""
     wl = synth.WORKLOADS[name]
     log(f"generating {name}")
     L = upload(wl)
@@ -304,14 +304,15 @@ def test_batched_full_size(cfm, name):
     used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
     sk = gpu_sketch(cfm, L)
     A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
-    for path in (cfm.FORWARD_AUTO, cfm.FORWARD_PER_PAIR):
+    for path in (cfm.FORWARD_GROUPED, cfm.FORWARD_PER_PAIR):
         with cfm.forward_path(path):
             got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
         compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=f"{name} path {path}")
 
 
 def test_olmoe_b64_full_size(cfm):
-    """OLMoE-shaped layer, 64 tokens with Zipf-skewed experts (hot experts serve most tokens): both passes."""
+    """OLMoE-shaped layer, 64 tokens with Zipf-skewed experts (hot experts serve most tokens): both passes
+    (the automatic choice here is the grouped pass)."""
     wl = synth.WORKLOADS["olmoe_b64"]
     log("generating the OLMoE-shaped layer")
     L = upload(wl)
