@@ -154,6 +154,27 @@ def test_select_budget_edges(cfm, kc, r):
     compare_forward(L, A, Bt, got, cand, keep, k, c, what=wl.name)
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_select_candidates_concentrated(cfm, T):
+    """Gate and up rows 0..c-1 of every expert scaled by 8 (exact in BF16, gate signs set so
+    that token 0's gate is positive): the candidates crowd into the lowest channels, so the
+    candidate list is far from evenly spread over the workgroups that screened it."""
+    wl = custom_workload(f"conc_t{T}", 4, 1, 256, 256, T, 20, 40, 8, 24, chan_scale=False)
+    h = synth.make_inputs(wl)
+    x0 = O.bf16_to_f64(h.x[0])
+    for wm in (h.w_gate, h.w_up):
+        v = O.bf16_to_f64(wm[:, :40, :]) * 8.0
+        if wm is h.w_gate:                     # positive gate for token 0, so SiLU keeps the scale
+            v *= np.where(v @ x0 < 0, -1.0, 1.0)[:, :, None]
+        wm[:, :40, :] = O.f64_to_bf16(v)
+    L = upload(wl, h)
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(h.w_down_t, 8, range(4), 4, 256, 256)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), 20, 40, 8)
+    assert np.sum(cand[0] < 40) >= 30, "the scaled rows should dominate the candidates"
+    compare_forward(L, A, Bt, got, cand, keep, 20, 40, what=wl.name)
+
+
 def test_select_full_rank_recovery_only(cfm):
     """k = 0 and r = min(H, I): every channel enters through the map (y = W_down hhat)."""
     wl = custom_workload("fullrank", 4, 2, 64, 128, 2, 0, 0, 64, 12)
