@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--batches", default="1,8,16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--stack", action="store_true",
+                    help="instead of the default line: a 48-layer stack of independently drawn layers, "
+                         "batches 1/4/8/16/32, budgets 10.8/13/18/53/67 %%")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -170,6 +173,72 @@ def cpu_baseline(wl_name="q18_b1", target_s=10.0):
             "dense_us_per_token": round(us_dense, 1)}
 
 
+def stack(torch, cfm, args):
+    """A decode step's routed-expert work through 48 independently drawn Qwen3-30B-A3B-shaped
+    layers (58 GB of BF16 weights, resident in HBM), one call per layer in one HIP graph."""
+    E, K, I, H, r = 128, 8, 768, 2048, 64
+    NL = 48
+    layers = []
+    lr_ws = torch.empty(cfm.lowrank_workspace(E, I, H, r), dtype=torch.uint8, device="cuda")
+    t0 = time.perf_counter()
+    for l in range(NL):
+        wg, wu, wd, signs = make_layer(torch, args.seed + 1000, l, E, I, H)
+        sk = cfm.sketch_build(wg, wu, signs)
+        A, Bt = cfm.lowrank_build(wd, r, ws=lr_ws)
+        layers.append((wg, wu, wd, signs, sk, A, Bt))
+        if l % 8 == 7:
+            log(f"  {l + 1} layers built ({time.perf_counter() - t0:.0f} s)")
+    del lr_ws
+    torch.cuda.synchronize()
+    fracs = [0.108, 0.13, 0.18, 0.53, 0.67]
+    rows = []
+    for T in (1, 4, 8, 16, 32):
+        x, ids, w = make_tokens(torch, args.seed + 77 + T, NL, T, E, K, H)
+        out = torch.empty((NL, T, H), dtype=torch.bfloat16, device="cuda")
+        wsd = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+
+        def dense(i):
+            wg, wu, wd, *_ = layers[i % NL]
+            cfm.moe_dense_forward(x[i % NL], ids[i % NL], w[i % NL], wg, wu, wd, out=out[i % NL], ws=wsd)
+
+        for i in range(NL):
+            dense(i)
+        ms_d, _ = timed_graph(torch, dense, NL)
+        for f in fracs:
+            k = int(round(f * I))
+            c = min(2 * k, I)
+            wss = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+
+            def sel(i):
+                wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
+                cfm.moe_select_forward(x[i % NL], ids[i % NL], w[i % NL], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
+                                       out=out[i % NL], ws=wss)
+
+            for i in range(NL):
+                sel(i)
+            ms_s, _ = timed_graph(torch, sel, NL)
+            st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+            wg, wu, wd, signs, sk, A, Bt = layers[0]
+            cfm.moe_select_forward(x[0], ids[0], w[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out[0], ws=wss,
+                                   stats=st)
+            torch.cuda.synchronize()
+            sd = cfm.decode_stats(st)
+            nbytes = sum(sd[q] for q in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery",
+                                          "bytes_io"))
+            row = {"T": T, "budget": f, "k": k, "c": c,
+                   "us_per_token_per_layer": round(ms_s * 1e3 / (NL * T), 3),
+                   "dense_us_per_token_per_layer": round(ms_d * 1e3 / (NL * T), 3),
+                   "speedup_vs_dense": round(ms_d / ms_s, 3),
+                   "read_fraction_of_dense": round(nbytes / sd["bytes_dense_equiv"], 3)}
+            rows.append(row)
+            log(f"T={T} f={f}: {row}")
+            del wss
+        del wsd, out, x, ids, w
+    print(json.dumps({"workload": "48-layer stack of Qwen3-30B-A3B-shaped MoE layers (H 2048, E 128, top-8, "
+                                  "I 768), r 64, one decode step per graph replay", "data": "synthetic",
+                      "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -193,6 +262,9 @@ def main():
     import calibration_free_channel_amd as cfm
 
     torch.manual_seed(args.seed)
+    if args.stack:
+        stack(torch, cfm, args)
+        return
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64
     L = args.layers
