@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--stack", action="store_true",
                     help="instead of the default line: a 48-layer stack of independently drawn layers, "
                          "batches 1/4/8/16/32, budgets 10.8/13/18/53/67 %%")
+    ap.add_argument("--olmoe", action="store_true",
+                    help="instead of the default line: the OLMoE-1B-7B-shaped layer, 64 tokens, Zipf(1.1) experts")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -239,6 +241,72 @@ def stack(torch, cfm, args):
                       "rows": rows}), flush=True)
 
 
+def olmoe(torch, cfm, args):
+    """OLMoE-1B-7B-shaped layer (H 2048, E 64, top-8, I 1024, no per-channel scale), 64 tokens routed
+    with Zipf(1.1) expert popularity, k 184, c 368, r 64: both passes and both dense kernels."""
+    import numpy as np
+    import synth
+    E, K, I, H, r, T = 64, 8, 1024, 2048, 64, 64
+    k, c = 184, 368
+    L = 4
+    layers = []
+    for l in range(L):
+        wg, wu, wd, signs = make_layer(torch, args.seed + 2000, l, E, I, H, chan_scale=False)
+        sk = cfm.sketch_build(wg, wu, signs)
+        A, Bt = cfm.lowrank_build(wd, r)
+        layers.append((wg, wu, wd, signs, sk, A, Bt))
+    n = args.warmup + 2 * max(10, args.steps // 4)
+    xs, idss, ws_ = [], [], []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed * 31 + 5)
+    for i in range(n):
+        ids, w = synth.routing(T, E, K, 3 + i, 0, zipf=1.1)
+        idss.append(torch.from_numpy(ids).cuda())
+        ws_.append(torch.from_numpy(w).cuda())
+        z = torch.randn((T, H), generator=g, device="cuda")
+        xs.append(z.to(torch.bfloat16))
+    experts_used = [len(set(t.cpu().numpy().reshape(-1).tolist())) for t in idss[:8]]
+    steps = max(10, args.steps // 4)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    wss = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+    wsd = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+
+    def sel(i):
+        wg, wu, wd, signs, sk, A, Bt = layers[i % L]
+        cfm.moe_select_forward(xs[i], idss[i], ws_[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out, ws=wss)
+
+    def dense(i):
+        wg, wu, wd, *_ = layers[i % L]
+        cfm.moe_dense_forward(xs[i], idss[i], ws_[i], wg, wu, wd, out=out, ws=wsd)
+
+    res = {}
+    for name, path in (("grouped", cfm.FORWARD_GROUPED), ("per_pair", cfm.FORWARD_PER_PAIR)):
+        with cfm.forward_path(path):
+            for i in range(args.warmup):
+                sel(i)
+                dense(i)
+            ms_s, _ = timed_graph(torch, lambda i: sel(args.warmup + i), steps)
+            ms_d, _ = timed_graph(torch, lambda i: dense(args.warmup + steps + i), steps)
+            kt = kernel_times(torch, cfm, lambda i: sel(args.warmup + i), steps)
+        res[name] = {"us_per_token": round(ms_s * 1e3 / (steps * T), 3),
+                     "dense_us_per_token": round(ms_d * 1e3 / (steps * T), 3),
+                     "kernels_us": {kn: round(v * 1e3, 2) for kn, v in kt.items()}}
+        log(f"{name}: {res[name]}")
+    st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+    with cfm.forward_path(cfm.FORWARD_GROUPED):
+        wg, wu, wd, signs, sk, A, Bt = layers[0]
+        cfm.moe_select_forward(xs[0], idss[0], ws_[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out, ws=wss,
+                               stats=st)
+    torch.cuda.synchronize()
+    sd = cfm.decode_stats(st)
+    nbytes = sum(sd[q] for q in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
+    print(json.dumps({"workload": "OLMoE-1B-7B-shaped MoE layer (H 2048, E 64, top-8, I 1024), 64 tokens, "
+                                  "Zipf(1.1) experts, k 184 c 368 r 64", "data": "synthetic",
+                      "experts_used": experts_used, "grouped_bytes_per_step": nbytes,
+                      "grouped_read_fraction_of_dense": round(nbytes / sd["bytes_dense_equiv"], 3),
+                      "passes": res}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -264,6 +332,9 @@ def main():
     torch.manual_seed(args.seed)
     if args.stack:
         stack(torch, cfm, args)
+        return
+    if args.olmoe:
+        olmoe(torch, cfm, args)
         return
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64

@@ -290,13 +290,11 @@ __device__ __forceinline__ uint4 sketch_item(const FusedArgs& a, int e, int j0, 
   return ld16((rr < cwk ? a.tg : a.tu) + ((size_t)e * a.I + j) * rowb + (off < rowb ? off : 0));
 }
 
-// This thread's row scale for a sub-chunk: thread c < 2 cwk takes the gate scale
-// of channel c (c < cwk) or the up scale of channel c - cwk (other threads: a
-// value that is not used).
-__device__ __forceinline__ float load_scale(const FusedArgs& a, int e, int j0, int cwk) {
-  const int tid = threadIdx.x;
-  const int c = min(tid, 2 * cwk - 1);
-  return c < cwk ? a.sg[(size_t)e * a.I + j0 + c] : a.su[(size_t)e * a.I + j0 + c - cwk];
+// This thread's row scales for a sub-chunk: thread c < cwk takes the gate and
+// up scales of channel c (other threads: values that are not used).
+__device__ __forceinline__ float2 load_scale(const FusedArgs& a, int e, int j0, int cwk) {
+  const size_t o = (size_t)e * a.I + j0 + min((int)threadIdx.x, cwk - 1);
+  return make_float2(a.sg[o], a.su[o]);
 }
 // Bt values of a sub-chunk for thread (zl, zg): channels zg, zg + groups, ...
 // (entries past the sub-chunk, and threads beyond the groups, load a value the
@@ -318,13 +316,13 @@ constexpr int kSketchPre = 8;   // super-blocks of the first sub-chunk requested
 
 // Sketch activations of channels [j0, j0 + cwk) into hloc (LDS) and the
 // exchange. pre: the first kSketchPre items of this wavefront (if use_pre);
-// sgu: this thread's prefetched scale (thread c < 2 cwk: gate scale of channel
-// c, or up scale of channel c - cwk).
+// sgu: this thread's prefetched scales (thread c < cwk: gate and up scales of
+// channel c).
 // ALLPRE: every super-block is among the prefetched items (H <= 256 kSketchPre),
 // so the loop below issues no loads (and no wait for later requests is forced).
 template <bool ALLPRE>
 __device__ __forceinline__ void screen_chunk(const FusedArgs& a, const Lds& L, int p, int e, int j0, int cwk, int F0,
-                                             const uint4 (&pre)[kSketchPre], bool use_pre, float sgu, uint32_t tag) {
+                                             const uint4 (&pre)[kSketchPre], bool use_pre, float2 sgu, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Hp = max(a.H, 256);
   const int nsb = (a.H + 255) / 256;
@@ -358,20 +356,22 @@ __device__ __forceinline__ void screen_chunk(const FusedArgs& a, const Lds& L, i
       for (int v = 0; v < 4; ++v) L.dsum[(16 * wv + 4 * (lane >> 4) + v) * 8 + col] = acc[v];
     }
   }
-  // per-row scale times the exact integer dot: sum_l 16^l D_l - 2^23 D_ones, in units of 2^(7 - F0)
-  __syncthreads();
-  if (tid < 2 * cwk) {
-    const float4 d0 = *reinterpret_cast<const float4*>(L.dsum + tid * 8);
-    const float4 d1 = *reinterpret_cast<const float4*>(L.dsum + tid * 8 + 4);
-    const long long S = (long long)(int)d0.x + ((long long)(int)d0.y << 4) + ((long long)(int)d0.z << 8) +
-                        ((long long)(int)d0.w << 12) + ((long long)(int)d1.x << 16) +
-                        ((long long)(int)d1.y << 20) - ((long long)(int)d1.z << 23);
-    L.red[NT + tid] = (float)((double)sgu * ldexp((double)S, kDShift - F0));
-  }
+  // per-row scale times the exact integer dot: sum_l 16^l D_l - 2^23 D_ones, in
+  // units of 2^(7 - F0); thread c < cwk forms the gate row c and the up row cwk + c
   __syncthreads();
   if (tid < cwk) {
-    const float gh = L.red[NT + tid], uh = L.red[NT + cwk + tid];
-    const float hv = silu_f32(gh) * uh;
+    float gu2[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float* d = L.dsum + (m * cwk + tid) * 8;
+      const float4 d0 = *reinterpret_cast<const float4*>(d);
+      const float4 d1 = *reinterpret_cast<const float4*>(d + 4);
+      const long long S = (long long)(int)d0.x + ((long long)(int)d0.y << 4) + ((long long)(int)d0.z << 8) +
+                          ((long long)(int)d0.w << 12) + ((long long)(int)d1.x << 16) +
+                          ((long long)(int)d1.y << 20) - ((long long)(int)d1.z << 23);
+      gu2[m] = (float)((double)(m ? sgu.y : sgu.x) * ldexp((double)S, kDShift - F0));
+    }
+    const float hv = silu_f32(gu2[0]) * gu2[1];
     L.hloc[tid] = hv;
     put_tagged(a.xh + (size_t)p * a.I + j0 + tid, hv, tag);
   }
@@ -616,16 +616,17 @@ __device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int
 // One sub-chunk of phase A: the screen, then this thread's partial recovery sum.
 template <int EPT, int NBT>
 __device__ __forceinline__ void screen_and_sum(const FusedArgs& a, const Lds& L, int p, int e, int sj0, int cwk,
-                                               int F0, const uint4 (&pre)[kSketchPre], float sc,
+                                               int F0, const uint4 (&pre)[kSketchPre], float2 sc,
                                                const uint32_t (&bt)[NBT], int zg, int groups, float& zacc,
                                                uint32_t tag) {
   screen_chunk<(EPT <= kSketchPre)>(a, L, p, e, sj0, cwk, F0, pre, true, sc, tag);
   if (a.r > 0 && zg < groups) {
+    // branch-free: every entry is read (clamped) and the ones past the sub-chunk add zero
+    float hv[NBT];
 #pragma unroll
-    for (int u = 0; u < NBT; ++u) {
-      const int jj = zg + groups * u;
-      if (jj < cwk) zacc += L.hloc[jj] * bf16_to_f32((uint16_t)bt[u]);
-    }
+    for (int u = 0; u < NBT; ++u) hv[u] = L.hloc[min(zg + groups * u, kSubChunk - 1)];
+#pragma unroll
+    for (int u = 0; u < NBT; ++u) zacc += (zg + groups * u < cwk ? hv[u] : 0.f) * bf16_to_f32((uint16_t)bt[u]);
   }
   __syncthreads();
 }
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
     for (int u = 0; u < kSketchPre; ++u) spre[u] = sketch_item(a, e, j0, cwk0, min(u, (H + 255) / 256 - 1));
     // (loads below are unconditional at clamped addresses, masked afterwards)
-    float sgu = load_scale(a, e, j0, cwk0);
+    float2 sgu = load_scale(a, e, j0, cwk0);
     constexpr int kBtPer = kMaxRank * kSubChunk / NT;   // Bt values per thread and sub-chunk (<= 16)
     uint32_t btv[kBtPer];
     load_bt(a, e, j0, cwk0, zl, zg, groups, btv);
@@ -711,7 +712,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         uint4 snext[kSketchPre];
 #pragma unroll
         for (int u = 0; u < kSketchPre; ++u) snext[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
-        const float nsgu = load_scale(a, e, nj0, ncwk);
+        const float2 nsgu = load_scale(a, e, nj0, ncwk);
         uint32_t nbtv[kBtPer];
         load_bt(a, e, nj0, ncwk, zl, zg, groups, nbtv);
         screen_and_sum<EPT>(a, L, p, e, sj0, kSubChunk, F0, spre, sgu, btv, zg, groups, zacc, tag);
