@@ -53,7 +53,7 @@ constexpr int GT = 256;            // threads per workgroup
 constexpr int kTile = 64;          // channels per screen work item (128 sketch rows, 8 MFMA row tiles)
 constexpr int kTokGroup = 16;      // tokens per screen work item
 constexpr int kSbReg = 8;          // super-blocks of sketch rows held in registers (H <= 2048)
-constexpr int kRowBlk = 16;        // union rows per exact work item (one MFMA row tile)
+constexpr int kRowBlk = 64;        // union rows per exact work item (one MFMA row tile per wavefront)
 constexpr int kKc = 8;             // 32-element steps of one exact load batch (two batches in flight; fewer for H < 256)
 constexpr int kColTile = 64;       // output columns per down work item (16 per wavefront)
 constexpr int kRPad = 128;         // recovery rank padded to whole 32-element steps (r <= 128)
@@ -512,83 +512,134 @@ __global__ __launch_bounds__(GT) void k_g_topc(GArgs a) {
 
 // ------------------------------------------------------------------ stage 4: exact gate / up
 
-// One load batch of an exact work item: KC 32-element steps from kc on of the
-// lane's gate and up rows and of its token's x. KC divides the step count, so a
-// batch is either whole or past the end (then it repeats the last batch, which
-// is not multiplied); the loads of a batch share one address.
+// Work items (64-row block, used expert): union rows [64 b, 64 b + 64) of the
+// expert's candidate union (every channel when dense) over the whole hidden
+// width, against all of its tokens. Wavefront w takes rows 64 b + 16 w .. + 15
+// (one MFMA row tile) and up to 64 tokens (four MFMA column tiles) per pass over
+// the rows, so a row is read once per 64 tokens. The tokens' x for one batch of
+// KC 32-element steps is staged in LDS and shared by the four wavefronts
+// (double-buffered, one barrier per batch); the next batch's gate / up rows and
+// x are requested before the current batch is multiplied. A persistent loop
+// walks the work list.
 template <int KC>
-struct ExactBatch {
-  uint4 g[KC], u[KC], x[KC];
+struct ExactRows {
+  uint4 g[KC], u[KC];
 };
 template <int KC>
-__device__ __forceinline__ void exact_load(ExactBatch<KC>& b, const uint16_t* wgr, const uint16_t* wur,
-                                           const uint16_t* xr, int kc, int nks) {
-  const int k0 = 32 * min(kc, nks - KC);
+__device__ __forceinline__ void exact_rows_load(ExactRows<KC>& b, const uint16_t* wgr, const uint16_t* wur, int kb,
+                                                int nbat) {
+  const int k0 = 32 * KC * min(kb, nbat - 1);        // past the end: the last batch again (not multiplied)
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     b.g[i] = ld16(wgr + k0 + 32 * i);
     b.u[i] = ld16(wur + k0 + 32 * i);
-    b.x[i] = ld16c(xr + k0 + 32 * i);
+  }
+}
+// x of this pass's tokens for batch kb: piece f = tid + 256 v is token f / (4 KC),
+// 16-byte part f % (4 KC); tokens past the pass repeat its last token.
+template <int KC>
+__device__ __forceinline__ void exact_x_load(uint4 (&xv)[KC], const GArgs& a, const int* tok, int ntk, int kb,
+                                             int nbat) {
+  const int k0 = 32 * KC * min(kb, nbat - 1);
+#pragma unroll
+  for (int v = 0; v < KC; ++v) {
+    const int f = threadIdx.x + GT * v, m = f / (4 * KC), pc = f % (4 * KC);
+    xv[v] = ld16c(a.x + (size_t)tok[min(m, ntk - 1)] * a.H + k0 + 8 * pc);
   }
 }
 template <int KC>
-__device__ __forceinline__ void exact_mul(const ExactBatch<KC>& b, v4f& ag, v4f& au) {
+__device__ __forceinline__ void exact_x_store(const uint4 (&xv)[KC], uint16_t* xb) {
 #pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    ag = mfma_bf16(b.g[i], b.x[i], ag);
-    au = mfma_bf16(b.u[i], b.x[i], au);
+  for (int v = 0; v < KC; ++v) {
+    const int f = threadIdx.x + GT * v, m = f / (4 * KC), pc = f % (4 * KC);
+    *reinterpret_cast<uint4*>(xb + m * (32 * KC + 8) + 8 * pc) = xv[v];
+  }
+}
+template <int KC>
+__device__ __forceinline__ void exact_rows_mul(const ExactRows<KC>& b, const uint16_t* xb, int ngrp, v4f (&ag)[4],
+                                               v4f (&au)[4]) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < ngrp) {
+      const uint16_t* xr = xb + (16 * q + col) * (32 * KC + 8) + 8 * g;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const uint4 xq = *reinterpret_cast<const uint4*>(xr + 32 * i);
+        ag[q] = mfma_bf16(b.g[i], xq, ag[q]);
+        au[q] = mfma_bf16(b.u[i], xq, au[q]);
+      }
+    }
   }
 }
 
-// One wavefront per work item (row block, used expert): union rows
-// [16 b, 16 b + 16) of the expert's candidate union (every channel when dense)
-// over the whole hidden width, against its tokens, 16 per pass (one MFMA
-// column tile). The rows stream in batches of kKc steps, each batch requested
-// before the previous one is multiplied; the wavefronts of a workgroup run
-// independently (no barriers).
 template <int KC>
 __global__ __launch_bounds__(GT, 2) void k_g_exact(GArgs a) {
-  const int lane = threadIdx.x & 63;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* xs0 = reinterpret_cast<uint16_t*>(smem);                     // [64][32 KC + 8]
+  uint16_t* xs1 = xs0 + 64 * (32 * KC + 8);
+  __shared__ int tok[64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I;
   const uint32_t nwork = a.dense ? a.meta[0] * (uint32_t)a.nrb : a.meta[2];
   const int row = lane & 15, g = lane >> 4;
-  const int nks = H / 32;
-  const uint32_t nwave = gridDim.x * (GT / 64);
-  for (uint32_t wi = blockIdx.x * (GT / 64) + (threadIdx.x >> 6); wi < nwork; wi += nwave) {
+  const int nbat = H / (32 * KC);
+  for (uint32_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
     int u, b;
     if (a.dense) { u = (int)(wi / a.nrb); b = (int)(wi % a.nrb); }
     else { const int it = a.gexw[wi]; u = it >> 16; b = it & 0xFFFF; }
     const int e = a.gue[u];
     const int p0 = a.goff[e], n = a.goff[e + 1] - p0;
     const int nU = a.dense ? I : (int)a.ucnt[u];
-    const int nrow = min(kRowBlk, nU - kRowBlk * b);
-    const int q = kRowBlk * b + min(row, nrow - 1);
+    const int r0 = kRowBlk * b + 16 * wv;
+    const int nrow = min(16, nU - r0);                  // rows of this wavefront (may be <= 0)
+    const int q = min(r0 + row, nU - 1);
     const int j = a.dense ? q : a.urows[(size_t)u * a.IP + q];
     const uint16_t* wgr = a.wg + ((size_t)e * I + j) * H + 8 * g;
     const uint16_t* wur = a.wu + ((size_t)e * I + j) * H + 8 * g;
     const int32_t* pl = a.gpl + p0;
-    for (int s0 = 0; s0 < n; s0 += 16) {
-      const int s = s0 + row;                  // this lane's token slot (B operand column)
-      const int pp = pl[min(s, n - 1)];
-      const uint16_t* xr = a.x + (size_t)(pp / a.K) * H + 8 * g;
-      v4f ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-      ExactBatch<KC> A, B;
-      exact_load(A, wgr, wur, xr, 0, nks);
-      for (int kc = 0; kc < nks; kc += 2 * KC) {
-        exact_load(B, wgr, wur, xr, kc + KC, nks);
-        exact_mul(A, ag, au);
-        exact_load(A, wgr, wur, xr, kc + 2 * KC, nks);
-        if (kc + KC < nks) exact_mul(B, ag, au);
-      }
-      // lane holds D[4 g + v][lane % 16]: union rows 4 g + v, token slot s
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int ntk = min(64, n - s0), ngrp = (ntk + 15) / 16;
+      __syncthreads();                                   // the previous pass is done with tok and the x buffers
+      if (tid < 64) tok[tid] = pl[s0 + min(tid, ntk - 1)] / a.K;
+      __syncthreads();
+      v4f ag[4], au[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 4 * g + v;
-        const int jr = __shfl(j, rr, 64);
-        if (rr < nrow && s < n) {
-          const float h = silu_f32(ag[v]) * au[v];
-          if (a.dense) a.hk[(size_t)pp * I + jr] = f32_to_bf16(h);
-          else a.hx[(size_t)pp * I + jr] = h;
+      for (int qq = 0; qq < 4; ++qq) { ag[qq] = (v4f){0.f, 0.f, 0.f, 0.f}; au[qq] = ag[qq]; }
+      ExactRows<KC> A, B;
+      uint4 xv[KC];
+      exact_rows_load(A, wgr, wur, 0, nbat);
+      exact_x_load(xv, a, tok, ntk, 0, nbat);
+      exact_x_store(xv, xs0);
+      __syncthreads();
+      for (int kb = 0; kb < nbat; kb += 2) {
+        exact_rows_load(B, wgr, wur, kb + 1, nbat);
+        exact_x_load(xv, a, tok, ntk, kb + 1, nbat);
+        exact_rows_mul(A, xs0, ngrp, ag, au);
+        exact_x_store(xv, xs1);
+        __syncthreads();
+        exact_rows_load(A, wgr, wur, kb + 2, nbat);
+        exact_x_load(xv, a, tok, ntk, kb + 2, nbat);
+        if (kb + 1 < nbat) exact_rows_mul(B, xs1, ngrp, ag, au);
+        exact_x_store(xv, xs0);
+        __syncthreads();
+      }
+      // lane holds D[4 g + v][lane % 16] of token tile qq: rows r0 + 4 g + v, token slot s0 + 16 qq + lane % 16
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        if (qq < ngrp) {
+          const int s = s0 + 16 * qq + row;
+          const int pp = pl[min(s, n - 1)];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int rr = 4 * g + v;
+            const int jr = __shfl(j, rr, 64);
+            if (rr < nrow && s < n) {
+              const float h = silu_f32(ag[qq][v]) * au[qq][v];
+              if (a.dense) a.hk[(size_t)pp * I + jr] = f32_to_bf16(h);
+              else a.hx[(size_t)pp * I + jr] = h;
+            }
+          }
         }
       }
     }
@@ -1074,12 +1125,13 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   }
   // 4. exact gate / up over the candidate unions (all channels when dense)
   if (g.dense || g.k > 0) {
-    const int grid = std::min(kExactGrid, (g.maxu * g.nrb + 3) / 4);
+    const int grid = std::min(kExactGrid, g.maxu * g.nrb);
     const int kc = std::min(kKc, H / 32);
     const void* fn = kc == 8 ? reinterpret_cast<const void*>(&k_g_exact<8>)
                    : kc == 4 ? reinterpret_cast<const void*>(&k_g_exact<4>)
                              : reinterpret_cast<const void*>(&k_g_exact<2>);
-    if (int rc = launch_k("k_g_exact", fn, dim3(grid), 0, a, stream)) return rc;
+    const size_t lds = 2 * 64 * (size_t)(32 * kc + 8) * 2;
+    if (int rc = launch_k("k_g_exact", fn, dim3(grid), lds, a, stream)) return rc;
   }
   if (!g.dense) {
     // 5. top-k, masked activations, recovery coefficients, kept unions
