@@ -796,10 +796,10 @@ __device__ __forceinline__ void down_load(DownChunk& d, const GArgs& a, int e, i
 }
 
 __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
-  __shared__ __align__(16) uint16_t rows[kMaxI];
-  __shared__ __align__(16) uint16_t wT[4][kColTile * kDnP];   // per wavefront: [column][row]
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* rows = reinterpret_cast<uint16_t*>(smem);          // [IP] kept-union rows (selected layer)
+  __shared__ __align__(16) uint16_t wT[4][kColTile * kDnP];   // per wavefront: [column][row]; then its partial tile
   __shared__ __align__(16) uint16_t hA[4][16 * kDnP];         // per wavefront: [token][row]
-  __shared__ __align__(16) float red[4][16 * kColTile];       // per wavefront: [token][column]
   __shared__ int pls[16];
   __shared__ int lastt[16];
   const int u = blockIdx.y;
@@ -893,21 +893,23 @@ __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
         cur = nxt;
       }
     }
-    // partial tiles of the four wavefronts: lane holds D[4 g + v][m16] of column tile ct
+    // partial tiles of the four wavefronts (each into its own transpose buffer,
+    // which it no longer needs): lane holds D[4 g + v][m16] of column tile ct
+    float* myR = reinterpret_cast<float*>(myT);                // [token][column]
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const v4f d = ct == wv ? acc[ct] + accr : acc[ct];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wv][(4 * g + v) * kColTile + 16 * ct + m16] = d[v];
+      for (int v = 0; v < 4; ++v) myR[(4 * g + v) * kColTile + 16 * ct + m16] = d[v];
     }
     __syncthreads();
     {
       const int m = tid >> 4, cq = 4 * (tid & 15);
       if (m < nt) {
-        float4 y = *reinterpret_cast<const float4*>(&red[0][m * kColTile + cq]);
+        float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(wT[0]) + m * kColTile + cq);
 #pragma unroll
         for (int w = 1; w < 4; ++w) {
-          const float4 t4 = *reinterpret_cast<const float4*>(&red[w][m * kColTile + cq]);
+          const float4 t4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(wT[w]) + m * kColTile + cq);
           y.x += t4.x; y.y += t4.y; y.z += t4.z; y.w += t4.w;
         }
         float* dst = a.yp + (size_t)pls[m] * H + c0 + cq;
@@ -1141,8 +1143,8 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
     if (int rc = launch_k("k_g_topk", fn, dim3(g.P), 0, a, stream)) return rc;
   }
   // 6. down + recovery + combine
-  if (int rc = launch_k("k_g_down", reinterpret_cast<const void*>(&k_g_down), dim3(H / kColTile, g.maxu), 0, a,
-                        stream))
+  if (int rc = launch_k("k_g_down", reinterpret_cast<const void*>(&k_g_down), dim3(H / kColTile, g.maxu),
+                        g.dense ? 16 : 2 * (size_t)g.IP, a, stream))
     return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_g_stats, dim3(1), dim3(64), 0, stream, a, static_cast<cfm_stats*>(s.stats));
