@@ -288,7 +288,12 @@ def exact_activations(x_bits, wg_rows_bits, wu_rows_bits):
     return silu(g) * u
 
 
-def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c):
+RECOVERY_SKETCH = "sketch"
+RECOVERY_CANDIDATES_EXACT = "candidates_exact"
+
+
+def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
+                recovery=RECOVERY_SKETCH):
     """The method for one routed (token, expert) pair.
 
     1. screen: hhat for all channels from the sketch; C = top-c by |hhat|
@@ -297,14 +302,19 @@ def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt,
        ("the top-k is computed exactly from the native BF16 weights");
     3. down over kept: y = sum_{j in S} h_j · Wd_t[j] (read only the kept
        channels' weights, abstract);
-    4. recovery: z = sum_{j not in S} hhat_j · Bt[j]; y += A · z ("skipped
-       channels are recovered through a low-rank map"). Reading: every skipped
-       channel enters with its sketch activation, including candidates that
-       were screened in but not kept.
+    4. recovery: z = sum_{j not in S} a_j · Bt[j]; y += A · z ("skipped
+       channels are recovered through a low-rank map"). The coefficient a_j of
+       a skipped channel is its sketch activation hhat_j (the default reading:
+       every skipped channel, including candidates screened in but not kept).
+       recovery="candidates_exact" is the variant that gives the candidates
+       screened in but not kept their exact h_j instead (they were computed
+       for the top-k anyway); channels never screened in keep hhat_j.
 
     A [E][H][r], Bt [E][I][r] are the stored map (BF16 bits, or floats).
     Returns a dict with hhat [I], C, h_all [I] (exact, every channel), S, y [H].
     """
+    if recovery not in (RECOVERY_SKETCH, RECOVERY_CANDIDATES_EXACT):
+        raise ValueError(f"unknown recovery variant {recovery!r}")
     I = w_gate.shape[1]
     hhat = screen_scores(x_bits, tg[e], tu[e], sg[e], su[e], signs)
     C = topk_set(np.abs(hhat), c)
@@ -314,9 +324,12 @@ def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt,
     y = h_all[S] @ wd[S] if k > 0 else np.zeros(wd.shape[1])
     r = A.shape[-1]
     if r > 0:
+        coef = hhat.copy()
+        if recovery == RECOVERY_CANDIDATES_EXACT:
+            coef[C] = h_all[C]
         skip = np.ones(I, bool)
         skip[S] = False
-        z = as_f64(Bt[e])[skip].T @ hhat[skip]
+        z = as_f64(Bt[e])[skip].T @ coef[skip]
         y = y + as_f64(A[e]) @ z
     return {"hhat": hhat, "C": C, "h_all": h_all, "S": S, "y": y}
 
@@ -331,13 +344,13 @@ def combine(ys: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
-                   tokens=None):
+                   tokens=None, recovery=RECOVERY_SKETCH):
     """Selected-channel MoE layer over a decode batch.
 
     x [T][H] BF16 bits, ids [T][K], w [T][K]. Selection is per (token, expert)
     pair and does not depend on the rest of the batch ("each token's k
     highest-scoring channels", abstract). tokens: optional subset of token
-    indices to evaluate (the others are skipped).
+    indices to evaluate (the others are skipped). recovery: as in select_pair.
 
     Returns (out BF16 bits [len(tokens)][H], per-pair details
     {(t, q): select_pair dict}).
@@ -350,7 +363,7 @@ def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, 
         ys = np.zeros((K, H))
         for q in range(K):
             d = select_pair(x[t], int(ids[t, q]), w_gate, w_up, w_down_t, tg, tu, sg, su, signs,
-                            A, Bt, k, c)
+                            A, Bt, k, c, recovery=recovery)
             pairs[(t, q)] = d
             ys[q] = d["y"]
         outs.append(combine(ys, w[t]))
@@ -376,7 +389,7 @@ def dense_forward(x, ids, w, w_gate, w_up, w_down_t, tokens=None):
 # ----------------------------------------------------------------------------- byte accounting
 
 
-def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None):
+def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=RECOVERY_SKETCH):
     """Bytes the method must read for one layer call (algorithmic count).
 
     Reads are counted the way hardware bills them: a touched segment is paid
@@ -389,8 +402,13 @@ def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None):
     states (2·T·H) and router output (8·T·K) and the BF16 result (2·T·H).
 
     cand_sets/keep_sets: {(t, q): index array}; when absent the sets are taken
-    as disjoint per pair (c and k rows each).
+    as disjoint per pair (c and k rows each). The candidates' gate and up rows
+    are read only when their exact activations are used: to rank them for
+    the kept set (k > 0) or, in the candidates_exact recovery variant, as the
+    dropped candidates' recovery coefficients. With k = 0 and the default
+    recovery nothing reads them.
     """
+    exact_step = k > 0 or recovery == RECOVERY_CANDIDATES_EXACT
     T, K = ids.shape
     total = 0
     for e in sorted(set(int(v) for v in ids.reshape(-1))):
@@ -400,6 +418,8 @@ def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None):
         else:
             nc = len(set().union(*[set(map(int, cand_sets[p])) for p in pairs]))
             nk = len(set().union(*[set(map(int, keep_sets[p])) for p in pairs]))
+        if not exact_step:
+            nc = 0
         total += 2 * (I * H // 4) + 2 * 4 * I + 2 * H * r + 2 * I * r + 4 * H * nc + 2 * H * nk
     return total + 2 * T * H + 8 * T * K + 2 * T * H
 

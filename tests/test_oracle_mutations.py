@@ -86,8 +86,8 @@ def test_recovery_over_unscreened_only_is_caught(monkeypatch):
     """Dropping the screened-in-but-not-kept channels from the recovery sum must be caught."""
     orig = O.select_pair
 
-    def bad(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c):
-        d = orig(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c)
+    def bad(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, **kw):
+        d = orig(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, **kw)
         lost = [j for j in d["C"] if j not in set(d["S"])]
         if A.shape[-1] and lost:
             corr = O.as_f64(A[e]) @ sum(d["hhat"][j] * O.as_f64(Bt[e][j]) for j in lost)
@@ -101,8 +101,8 @@ def test_exact_scores_from_sketch_are_caught(monkeypatch):
     """Keeping the top-k by sketch score instead of the exact BF16 score must be caught."""
     orig = O.select_pair
 
-    def bad(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c):
-        d = orig(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c)
+    def bad(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, **kw):
+        d = orig(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, **kw)
         d["S"] = d["C"][O.topk_set(np.abs(d["hhat"][d["C"]]), k)]
         return d
     monkeypatch.setattr(O, "select_pair", bad)
@@ -123,3 +123,33 @@ def test_map_without_singular_values_is_caught(monkeypatch):
         return A / np.maximum(np.linalg.norm(A, axis=0), 1e-300), Bt
     monkeypatch.setattr(O, "lowrank", bad)
     _fails(P.test_lowrank_eckart_young_and_orthonormal)
+
+
+def test_candidates_exact_ignored_is_caught(monkeypatch):
+    """A variant flag that falls back to the sketch activations must be caught."""
+    orig = O.select_pair
+    monkeypatch.setattr(O, "select_pair", lambda *a, **kw: orig(*a))
+    _fails(P.test_candidates_exact_all_screened_full_rank_is_dense, 5)
+
+
+def test_candidates_exact_on_every_skipped_channel_is_caught(monkeypatch):
+    """Giving every skipped channel (not only the dropped candidates) its exact activation must be caught."""
+    orig = O.select_pair
+
+    def bad(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, recovery="sketch"):
+        d = orig(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c, recovery=recovery)
+        if recovery == "candidates_exact" and A.shape[-1]:
+            outside = [j for j in range(w_gate.shape[1]) if j not in set(d["C"])]
+            if outside:
+                d["y"] = d["y"] + O.as_f64(A[e]) @ sum((d["h_all"][j] - d["hhat"][j]) * O.as_f64(Bt[e][j])
+                                                       for j in outside)
+        return d
+    monkeypatch.setattr(O, "select_pair", bad)
+    _fails(P.test_candidates_exact_changes_only_dropped_candidates)
+
+
+def test_candidate_rows_billed_at_k0_is_caught(monkeypatch):
+    """Billing candidate rows that nothing reads (k = 0, default recovery) must be caught."""
+    orig = O.read_bytes
+    monkeypatch.setattr(O, "read_bytes", lambda *a, **kw: orig(*a, **dict(kw, recovery="candidates_exact")))
+    _fails(P.test_read_bytes_candidate_rows_only_when_exact_activations_are_used)

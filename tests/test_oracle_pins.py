@@ -301,6 +301,78 @@ def test_kept_part_and_recovery_are_separate_terms():
     assert S.tolist() == S_b
 
 
+# The recovery variant that feeds the dropped candidates' exact activations
+# into the map (candidates_exact). Checked against an independent SVD (numpy)
+# and an independent decode of the BF16 weights.
+
+def _decode(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _full_rank_map(wd):
+    """Float factors of every expert's W_down (H x I) at full rank from numpy's SVD."""
+    As, Bts = [], []
+    for e in range(wd.shape[0]):
+        U, s, Vt = np.linalg.svd(_decode(wd[e]).T, full_matrices=False)
+        As.append(U * s)
+        Bts.append(Vt.T)
+    return np.stack(As), np.stack(Bts)
+
+
+def _dense_pair(x, wg, wu, wd, e):
+    xv = _decode(x)
+    g = _decode(wg[e]) @ xv
+    u = _decode(wu[e]) @ xv
+    return (g * scipy.special.expit(g) * u) @ _decode(wd[e])
+
+
+@pytest.mark.parametrize("k", [0, 5, 32])
+def test_candidates_exact_all_screened_full_rank_is_dense(k):
+    """c = I and a full-rank map: every channel enters with its exact activation, either
+    through the kept rows or through the map, so y is the dense FFN for any k; the
+    default (sketch) recovery is not."""
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = _full_rank_map(wd)
+    for t in range(ids.shape[0]):
+        e = int(ids[t, 0])
+        ref = _dense_pair(x[t], wg, wu, wd, e)
+        p = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, k, 32, recovery="candidates_exact")
+        assert np.allclose(p["y"], ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max())
+        if k < 32:
+            q = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, k, 32)
+            assert np.linalg.norm(q["y"] - ref) > 1e-3 * np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("kc", [(0, 0), (7, 7), (32, 32)])
+def test_candidates_exact_same_as_sketch_when_nothing_dropped(kc):
+    """k = c: no candidate is dropped, so both recovery variants give the same bits."""
+    k, c = kc
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 6)
+    a, _ = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, k, c)
+    b, _ = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, k, c, recovery="candidates_exact")
+    assert np.array_equal(a, b)
+
+
+def test_candidates_exact_changes_only_dropped_candidates():
+    """Full-rank map: y(candidates_exact) - y(sketch) = sum over C minus S of (h_j - hhat_j) Wd_j."""
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = _full_rank_map(wd)
+    e = int(ids[1, 1])
+    a = O.select_pair(x[1], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 12)
+    b = O.select_pair(x[1], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 12, recovery="candidates_exact")
+    assert np.array_equal(a["C"], b["C"]) and np.array_equal(a["S"], b["S"])
+    dropped = sorted(set(a["C"].tolist()) - set(a["S"].tolist()))
+    assert len(dropped) == 7
+    want = sum((a["h_all"][j] - a["hhat"][j]) * _decode(wd[e][j]) for j in dropped)
+    assert np.allclose(b["y"] - a["y"], want, rtol=1e-8, atol=1e-11 * np.abs(want).max())
+    with pytest.raises(ValueError):
+        O.select_pair(x[1], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 12, recovery="exact")
+
+
 def test_combine_linear_and_slot_order_free():
     r = _rng(10)
     ys = r.standard_normal((3, 64))
@@ -375,3 +447,14 @@ def test_read_bytes_unions_shared_experts():
     per = lambda nc, nk: 2 * (I * H // 4) + 8 * I + 2 * H * r + 2 * I * r + 4 * H * nc + 2 * H * nk
     want = per(3, 1) + per(1, 1) + per(1, 1) + 2 * 2 * H + 8 * 2 * 2 + 2 * 2 * H
     assert O.read_bytes(ids, 3, I, H, 1, 2, r, cs, ks) == want
+
+
+def test_read_bytes_candidate_rows_only_when_exact_activations_are_used():
+    """k = 0: the default recovery never reads candidate rows; the candidates_exact variant reads 4Hc per pair."""
+    ids = np.arange(2, dtype=np.int32)[None]
+    I, H, r, c = 64, 128, 4, 10
+    base = 2 * (I * H // 4) + 8 * I + 2 * H * r + 2 * I * r
+    io = 2 * H + 8 * 2 + 2 * H
+    assert O.read_bytes(ids, 4, I, H, 0, c, r) == 2 * base + io
+    assert O.read_bytes(ids, 4, I, H, 0, c, r, recovery="candidates_exact") == 2 * (base + 4 * H * c) + io
+    assert O.read_bytes(ids, 4, I, H, 3, c, r) == O.read_bytes(ids, 4, I, H, 3, c, r, recovery="candidates_exact")
