@@ -49,6 +49,9 @@ def parse():
                          "batches 1/4/8/16/32, budgets 10.8/13/18/53/67 %%")
     ap.add_argument("--olmoe", action="store_true",
                     help="instead of the default line: the OLMoE-1B-7B-shaped layer, 64 tokens, Zipf(1.1) experts")
+    ap.add_argument("--recovery", action="store_true",
+                    help="instead of the default line: recovery rank sweep (r 0..128) of both recovery variants "
+                         "at batch 1 and 16, 18 %% budget, with each output's deviation from the dense layer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -241,6 +244,60 @@ def stack(torch, cfm, args):
                       "rows": rows}), flush=True)
 
 
+def recovery_sweep(torch, cfm, args):
+    """Recovery rank r and the two recovery variants (every skipped channel through the map with its
+    sketch activation, or the dropped candidates with their exact activation) on the Qwen3-30B-A3B-shaped
+    layer ring at k 138, c 276: time per token, and the relative L2 distance of each token's output from
+    the dense layer's output on the same inputs (synthetic Gaussian weights: an approximation error, not
+    a model-quality figure)."""
+    E, K, I, H = 128, 8, 768, 2048
+    k, c = 138, 276
+    NL = args.layers
+    ranks = (0, 16, 32, 64, 128)
+    base = []
+    for l in range(NL):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        base.append((wg, wu, wd, signs, cfm.sketch_build(wg, wu, signs)))
+    rows = []
+    for T in (1, 16):
+        n = NL * 4
+        x, ids, w = make_tokens(torch, args.seed + 300 + T, n, T, E, K, H)
+        dense_out = torch.empty((n, T, H), dtype=torch.bfloat16, device="cuda")
+        wsd = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+        for i in range(n):
+            wg, wu, wd, *_ = base[i % NL]
+            cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=dense_out[i], ws=wsd)
+        ms_d, _ = timed_graph(torch, lambda i: cfm.moe_dense_forward(
+            x[i], ids[i], w[i], *base[i % NL][:3], out=dense_out[i], ws=wsd), n)
+        ref = dense_out.float()
+        for r in ranks:
+            maps = [cfm.lowrank_build(b[2], r) for b in base]
+            wss = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+            out = torch.empty((n, T, H), dtype=torch.bfloat16, device="cuda")
+            for rec in ((cfm.RECOVER_SKETCH, cfm.RECOVER_CANDIDATES_EXACT) if r > 0 else (cfm.RECOVER_SKETCH,)):
+                def sel(i, rec=rec):
+                    wg, wu, wd, signs, sk = base[i % NL]
+                    A, Bt = maps[i % NL]
+                    cfm.moe_select_forward(x[i], ids[i], w[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
+                                           out=out[i], ws=wss, recovery=rec)
+                for i in range(n):
+                    sel(i)
+                torch.cuda.synchronize()
+                dev_ = ((out.float() - ref).norm(dim=-1) / ref.norm(dim=-1)).flatten()
+                ms_s, _ = timed_graph(torch, sel, n)
+                row = {"T": T, "r": r, "recovery": rec,
+                       "us_per_token": round(ms_s * 1e3 / (n * T), 3),
+                       "dense_us_per_token": round(ms_d * 1e3 / (n * T), 3),
+                       "rel_l2_vs_dense_mean": round(float(dev_.mean()), 4),
+                       "rel_l2_vs_dense_max": round(float(dev_.max()), 4)}
+                rows.append(row)
+                log(f"recovery sweep: {row}")
+            del maps, wss, out
+        del wsd, dense_out, x, ids, w
+    print(json.dumps({"workload": "recovery rank sweep on the Qwen3-30B-A3B-shaped layer (H 2048, E 128, top-8, "
+                                  "I 768), k 138, c 276", "data": "synthetic", "rows": rows}), flush=True)
+
+
 def olmoe(torch, cfm, args):
     """OLMoE-1B-7B-shaped layer (H 2048, E 64, top-8, I 1024, no per-channel scale), 64 tokens routed
     with Zipf(1.1) expert popularity, k 184, c 368, r 64: both passes and both dense kernels."""
@@ -311,8 +368,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert-parallel sharding is described in DESIGN.md but not built).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(expert-parallel sharding is not built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -332,6 +389,9 @@ def main():
     torch.manual_seed(args.seed)
     if args.stack:
         stack(torch, cfm, args)
+        return
+    if args.recovery:
+        recovery_sweep(torch, cfm, args)
         return
     if args.olmoe:
         olmoe(torch, cfm, args)

@@ -33,6 +33,8 @@ _SIGS = {
     "select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "moe_select_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
+    "moe_select_forward_ex": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
+                                   _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
     "dense_workspace": (_z, [_i, _i, _i, _i, _i]),
     "moe_dense_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _z, _p]),
     "cfm_set_forward_path": (_i, [_i]),
@@ -145,9 +147,20 @@ def new_workspace(nbytes, device):
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+RECOVER_SKETCH = "sketch"                       # every skipped channel enters the map with hhat
+RECOVER_CANDIDATES_EXACT = "candidates_exact"   # dropped candidates enter with their exact h
+_RECOVER_FLAGS = {RECOVER_SKETCH: 0, RECOVER_CANDIDATES_EXACT: 1}   # CFM_RECOVER_CANDIDATES_EXACT
+
+
 def moe_select_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, tu, sg, su, A, Bt,
-                       k, c, r, out=None, ws=None, cand_out=None, keep_out=None, stats=None):
-    """Selected-channel MoE layer. Returns out [T][H] BF16."""
+                       k, c, r, out=None, ws=None, cand_out=None, keep_out=None, stats=None,
+                       recovery=RECOVER_SKETCH):
+    """Selected-channel MoE layer. Returns out [T][H] BF16.
+
+    recovery: RECOVER_SKETCH (moe_select_forward) or RECOVER_CANDIDATES_EXACT
+    (moe_select_forward_ex with CFM_RECOVER_CANDIDATES_EXACT)."""
+    if recovery not in _RECOVER_FLAGS:
+        raise ValueError(f"unknown recovery variant {recovery!r}")
     T, H = x.shape
     K = topk_ids.shape[1]
     E, I, _ = w_gate.shape
@@ -156,12 +169,15 @@ def moe_select_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, t
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     if ws is None:
         ws = new_workspace(select_workspace(T, K, E, I, H, k, c, r), dev)
-    _check(_lib.moe_select_forward(
-        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
-        E, I, H, _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su),
-        _ptr(A) if r > 0 else None, _ptr(Bt) if r > 0 else None, k, c, r, _ptr(out),
-        _ptr(cand_out), _ptr(keep_out), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)),
-        "moe_select_forward")
+    head = (_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
+            E, I, H, _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su),
+            _ptr(A) if r > 0 else None, _ptr(Bt) if r > 0 else None, k, c, r)
+    tail = (_ptr(out), _ptr(cand_out), _ptr(keep_out), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev))
+    flags = _RECOVER_FLAGS[recovery]
+    if flags:
+        _check(_lib.moe_select_forward_ex(*head, flags, *tail), "moe_select_forward_ex")
+    else:
+        _check(_lib.moe_select_forward(*head, *tail), "moe_select_forward")
     return out
 
 

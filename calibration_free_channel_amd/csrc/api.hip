@@ -194,14 +194,15 @@ size_t select_workspace(int T, int K, int E, int I, int H, int k, int c, int r) 
   return group_plan(T, K, E, I, H, k, c, r, false, base).bytes;
 }
 
-int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
-                       int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
-                       const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
-                       const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
-                       const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, cfm_bf16* out,
-                       int32_t* cand_out, int32_t* keep_out, cfm_stats* stats, void* ws,
-                       size_t ws_bytes, void* stream) {
+int moe_select_forward_ex(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                          int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                          const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                          const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                          const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r,
+                          unsigned flags, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out,
+                          cfm_stats* stats, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
+  if (flags & ~CFM_RECOVER_CANDIDATES_EXACT) return set_error(CFM_EINVAL, "moe_select_forward_ex: unknown flag bits");
   if (int rc = check_tokens(T, K)) return rc;
   if (int rc = check_shape(E, I, H, true)) return rc;
   if (int rc = check_budget(I, H, k, c, r)) return rc;
@@ -217,11 +218,23 @@ int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* 
   if (!ws || ws_bytes < need)
     return set_error(CFM_EWORKSPACE, "moe_select_forward: workspace smaller than select_workspace()");
   SelectArgs a{x, w_gate, w_up, w_down_t, A, Bt, topk_ids, topk_w, signs, tg, tu, sg, su, out,
-               cand_out, keep_out, stats, static_cast<char*>(ws)};
+               cand_out, keep_out, stats, static_cast<char*>(ws), flags};
   if (grouped)
     return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
                                   static_cast<hipStream_t>(stream));
   return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+
+int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                       const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                       const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                       const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, cfm_bf16* out,
+                       int32_t* cand_out, int32_t* keep_out, cfm_stats* stats, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return moe_select_forward_ex(x, topk_ids, topk_w, T, K, w_gate, w_up, w_down_t, E, I, H, signs, tg, tu,
+                               sg, su, A, Bt, k, c, r, 0u, out, cand_out, keep_out, stats, ws, ws_bytes,
+                               stream);
 }
 
 size_t dense_workspace(int T, int K, int E, int I, int H) {

@@ -55,6 +55,7 @@ struct SelectArgs {
   int32_t *cand_out, *keep_out;
   void* stats;
   char* ws;
+  unsigned flags;   // CFM_RECOVER_* variant bits (0: the default method)
 };
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);

@@ -174,6 +174,7 @@ struct FusedArgs {
   float* ypart;      // [P][H]
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
   int pre;           // column chunks per workgroup when the candidates' rows are prefetched into LDS, else 0
+  int rec_exact;     // dropped candidates enter the recovery with their exact activation
 };
 
 struct Lds {
@@ -644,7 +645,7 @@ __device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) 
 
 // ------------------------------------------------------------------ kernels
 
-template <int EPT>
+template <int EPT, bool RECX>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) uint32_t wred[NT / 64];
@@ -789,7 +790,8 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 
     // ---- phase B: exact activations of this workgroup's candidates
     const int q0 = min(a.c, w * a.cpw), q1 = min(a.c, q0 + a.cpw);
-    if (a.k > 0 && q0 < q1) {
+    const bool exact_step = a.k > 0 || RECX;   // the candidates' exact activations are used
+    if (exact_step && q0 < q1) {
       uint4 xr[CH];
       const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
@@ -801,7 +803,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     if (a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck);
 
     // ---- top-k kept set and recovery coefficients
-    if (a.k > 0) {
+    if (exact_step) {
       int cnt;
       const int i0 = topk_range<NT>(a.c, &cnt);
       const uint64_t* src = a.xc + (size_t)p * a.c + i0;
@@ -839,6 +841,15 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       __syncthreads();
       if (w == 0 && a.keep_out)
         for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = L.keep[i];
+      if (RECX && r > 0) {
+        // each candidate's term to take out of the screen's recovery sum: its
+        // sketch activation if kept, (sketch - exact) if dropped, so that a
+        // dropped candidate is recovered with its exact activation
+        for (int i = tid; i < a.c; i += NT) L.hcl[i] = L.hh[L.candp[i]] - L.hcl[i];
+        __syncthreads();
+        for (int i = tid; i < a.k; i += NT) L.hcl[L.sel[i]] = L.hh[L.keep[i]];
+        __syncthreads();
+      }
     } else {
       __syncthreads();
     }
@@ -853,8 +864,12 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         float acc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-        for (int m = g; m < a.k; m += ng)
-          fma8(acc, L.hh[L.keep[m]], *reinterpret_cast<const uint4*>(L.btc + (size_t)L.sel[m] * 2 * r + 16 * cc));
+        const int nz = RECX ? a.c : a.k;       // terms taken out of the screen's sum
+        for (int m = g; m < nz; m += ng) {
+          const int pos = RECX ? m : L.sel[m];
+          const float cf = RECX ? L.hcl[m] : L.hh[L.keep[m]];
+          fma8(acc, cf, *reinterpret_cast<const uint4*>(L.btc + (size_t)pos * 2 * r + 16 * cc));
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], cpr);
         if (lane < cpr)
@@ -899,7 +914,9 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       continue;
     }
     if (r > 0) {
-      // z = zsum - sum_{j in S} hhat_j Bt[e][j]
+      // z = zsum - sum_{j in S} hhat_j Bt[e][j] (with dropped candidates recovered
+      // exactly: minus sum over the candidates of their coefficient in hcl)
+      const int nz = RECX ? a.c : a.k;
       if (r % 8 == 0) {
         const int cpr = r / 8, ng = NT / cpr;       // r <= 128: cpr <= 16, ng >= 16
         const int cc = tid % cpr, g = tid / cpr;
@@ -907,15 +924,15 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
         constexpr int ZB = 8;
-        for (int i0 = g; i0 < a.k; i0 += ng * ZB) {
+        for (int i0 = g; i0 < nz; i0 += ng * ZB) {
           uint4 bw[ZB];
           float hv[ZB];
 #pragma unroll
           for (int u = 0; u < ZB; ++u) {
             const int i = i0 + ng * u;
-            const bool ok = i < a.k;
-            const int j = ok ? L.keep[i] : 0;
-            hv[u] = ok ? L.hh[j] : 0.f;
+            const bool ok = i < nz;
+            const int j = ok ? (RECX ? L.candp[i] : L.keep[i]) : 0;
+            hv[u] = ok ? (RECX ? L.hcl[i] : L.hh[j]) : 0.f;
             bw[u] = ok ? ld16c(a.Bt + ((size_t)e * a.I + j) * r + 8 * cc) : make_uint4(0, 0, 0, 0);
           }
 #pragma unroll
@@ -932,9 +949,9 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       } else {
         for (int l = tid; l < r; l += NT) {
           float s = 0.f;
-          for (int i = 0; i < a.k; ++i) {
-            const int j = L.keep[i];
-            s += L.hh[j] * bf16_to_f32(a.Bt[((size_t)e * a.I + j) * r + l]);
+          for (int i = 0; i < nz; ++i) {
+            const int j = RECX ? L.candp[i] : L.keep[i];
+            s += (RECX ? L.hcl[i] : L.hh[j]) * bf16_to_f32(a.Bt[((size_t)e * a.I + j) * r + l]);
           }
           L.zv[l] = L.zsum[l] - s;
         }
@@ -996,7 +1013,7 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
 // ------------------------------------------------------------------ stats
 
 __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, int c, int r, int T,
-                        int K, int select, cfm_stats* st) {
+                        int K, int select, int exact_step, cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   unsigned used = 0;
   for (int pp = 0; pp < P; ++pp) {
@@ -1011,10 +1028,10 @@ __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, i
   s.experts_used = used;
   if (select) {
     s.bytes_sketch = Pu * (2ull * I * (H / 4) + 8ull * I);
-    s.bytes_candidates = k > 0 ? Pu * 4ull * H * c : 0;
+    s.bytes_candidates = exact_step ? Pu * 4ull * H * c : 0;
     s.bytes_down = Pu * 2ull * H * k;
     s.bytes_recovery = r > 0 ? Pu * (2ull * H * r + 2ull * I * r) : 0;
-    s.rows_candidates = k > 0 ? (uint32_t)(P * c) : 0;
+    s.rows_candidates = exact_step ? (uint32_t)(P * c) : 0;
     s.rows_down = (uint32_t)(P * k);
   } else {
     s.bytes_sketch = 0;
@@ -1033,8 +1050,9 @@ int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream) {
   const int H = fa.H;
   const int ept = H >= 1024 ? H / 256 : 0;
   const void* fn = nullptr;
-#define CFM_PICK(E) fn = SELECT ? reinterpret_cast<const void*>(&k_select_fused<E>) \
-                                : reinterpret_cast<const void*>(&k_dense_fused<E>)
+#define CFM_PICK(E) fn = !SELECT ? reinterpret_cast<const void*>(&k_dense_fused<E>) \
+                       : fa.rec_exact ? reinterpret_cast<const void*>(&k_select_fused<E, true>) \
+                                      : reinterpret_cast<const void*>(&k_select_fused<E, false>)
   switch (ept) {
     case 0: if (H == 512) CFM_PICK(2); else CFM_PICK(0); break;
     case 4: CFM_PICK(4); break;
@@ -1140,6 +1158,7 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.log2H = log2H;
   a.k = p.k; a.c = p.c; a.r = p.r; a.nw = p.nw; a.cw = p.cw; a.cpw = p.cpw; a.nhs = p.nhs; a.G = p.G;
   a.pre = p.pre;
+  a.rec_exact = (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
   return a;
 }
 
@@ -1149,7 +1168,7 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
-                       p.r, p.T, p.K, 1, static_cast<cfm_stats*>(s.stats));
+                       p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;
@@ -1161,7 +1180,7 @@ int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t 
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.I, p.I, 0,
-                       p.T, p.K, 0, static_cast<cfm_stats*>(s.stats));
+                       p.T, p.K, 0, 1, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;

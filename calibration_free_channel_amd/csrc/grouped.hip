@@ -135,6 +135,7 @@ struct GArgs {
   uint32_t* kctr;     // [E] top-k arrivals per expert (zero between calls)
   uint32_t* octr;     // [T][H / 64] pair outputs arrived per (token, column tile) (zero between calls)
   int T, K, P, E, I, H, log2H, k, c, r, ntile, nz, IW, nrb, IP, dense;
+  int rec_exact;      // dropped candidates enter the recovery with their exact activation
 };
 
 // ------------------------------------------------------------------ block helpers
@@ -697,8 +698,9 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
   }
   for (int w = tid; w < a.IW; w += GT) st_u(a.km + (size_t)p * a.IW + w, bm[w]);
   // z = sum over all channels of hhat_j Bt[j] (the screen's tile sums) minus the
-  // kept channels' terms. Thread (cc, gi): 8 columns 8 cc .. 8 cc + 7, rows and
-  // tiles gi, gi + groups, ... (loads in batches of four)
+  // kept channels' terms (with dropped candidates recovered exactly: minus
+  // (hhat_j - h_j) Bt[j] for each of them too). Thread (cc, gi): 8 columns
+  // 8 cc .. 8 cc + 7, rows and tiles gi, gi + groups, ... (loads in batches of four)
   if (r > 0) {
     const int npr = r / 8, groups = GT / npr;
     const int cc = tid % npr, gi = tid / npr;
@@ -724,18 +726,22 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
         }
       }
       const float* hsp = a.hs + (size_t)p * I;
-      for (int i0 = gi; i0 < k; i0 += 4 * groups) {
+      const float* hxp = a.hx + (size_t)p * I;
+      const int nzr = a.rec_exact ? c : k;          // terms taken out of the screen's sum
+      for (int i0 = gi; i0 < nzr; i0 += 4 * groups) {
         uint4 bw[4];
         float hv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int j = sel[min(i0 + u * groups, k - 1)];
+          const int i = min(i0 + u * groups, nzr - 1);
+          const int j = a.rec_exact ? cl[i] : sel[i];
           bw[u] = ld16c(a.Bt + ((size_t)e * I + j) * r + 8 * cc);
-          hv[u] = hsp[j];
+          const bool dropped = a.rec_exact && !((bm[j >> 5] >> (j & 31)) & 1u);
+          hv[u] = hsp[j] - (dropped ? hxp[j] : 0.f);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float h = i0 + u * groups < k ? -hv[u] : 0.f;
+          const float h = i0 + u * groups < nzr ? -hv[u] : 0.f;
           acc[0] += h * bf16lo(bw[u].x); acc[1] += h * bf16hi(bw[u].x);
           acc[2] += h * bf16lo(bw[u].y); acc[3] += h * bf16hi(bw[u].y);
           acc[4] += h * bf16lo(bw[u].z); acc[5] += h * bf16hi(bw[u].z);
@@ -965,7 +971,7 @@ __global__ void k_g_stats(GArgs a, cfm_stats* st) {
       uc += a.ucnt[u];
       dc += a.dcnt[u];
     }
-    if (a.k == 0) uc = 0;                       // no exact phase ran
+    if (a.k == 0 && !a.rec_exact) uc = 0;       // no exact phase ran
   } else {
     uc = dc = (uint64_t)nue * a.I;
   }
@@ -1093,6 +1099,7 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.log2H = log2H;
   a.k = g.dense ? g.I : g.k; a.c = g.dense ? g.I : g.c; a.r = g.dense ? 0 : g.r;
   a.ntile = g.ntile; a.nz = (g.I + 15) / 16; a.IW = g.IW; a.nrb = g.nrb; a.IP = g.IP; a.dense = g.dense ? 1 : 0;
+  a.rec_exact = !g.dense && (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
   const int H = g.H;
 
   // 1. rotation + grouping
@@ -1126,7 +1133,7 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
     }
   }
   // 4. exact gate / up over the candidate unions (all channels when dense)
-  if (g.dense || g.k > 0) {
+  if (g.dense || g.k > 0 || a.rec_exact) {
     const int grid = std::min(kExactGrid, g.maxu * g.nrb);
     const int kc = std::min(kKc, H / 32);
     const void* fn = kc == 8 ? reinterpret_cast<const void*>(&k_g_exact<8>)

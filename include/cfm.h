@@ -160,6 +160,32 @@ int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* 
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_select_forward_ex - moe_select_forward with variant flags (flags = 0 is
+ * moe_select_forward exactly).
+ *
+ * CFM_RECOVER_CANDIDATES_EXACT: a variant of the recovery step (article
+ * section "A reader that needs no data at all" names only a low-rank map of
+ * the down projection for the skipped channels). Candidates screened in but
+ * not kept (j in C, j not in S) enter the map with their exact activation h_j,
+ * which the top-k step has computed, instead of hhat_j; channels never
+ * screened in keep hhat_j:
+ *   y = sum_{j in S} h_j Wd_t[e][j] + A[e] (sum_{j in C \ S} h_j Bt[e][j]
+ *                                          + sum_{j not in C} hhat_j Bt[e][j])
+ * With k = 0 the candidates' exact activations are still computed (the only
+ * case where the flag adds reads). Every other argument, the supported range,
+ * the workspace and the error codes are those of moe_select_forward; a flag
+ * bit that is not defined here returns CFM_EINVAL.
+ */
+#define CFM_RECOVER_CANDIDATES_EXACT 1u
+int moe_select_forward_ex(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                          int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                          const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                          const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                          const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r,
+                          unsigned flags, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out,
+                          cfm_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_dense_forward - the same routed-expert SwiGLU layer reading every channel
  * (the comparator the method is measured against: abstract, "MoE blocks ...
  * faster than optimized vLLM").

@@ -74,6 +74,27 @@ def test_select_forward_rejects(lib, kw, code):
     assert lib.cfm_last_error().decode() != ""
 
 
+def _sel_ex(lib, flags, T=1, K=2, E=8, I=128, H=256, k=23, c=46, r=8, ptr=FAKE, ws=FAKE, wsb=1 << 40):
+    f = lib.moe_select_forward_ex
+    f.restype = ctypes.c_int
+    P = ptr
+    return f(P, P, P, T, K, P, P, P, E, I, H, P, P, P, P, P, P, P, k, c, r, ctypes.c_uint(flags), P, None,
+             None, None, ws, ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("flags,kw,code", [
+    (2, {}, EINVAL),                 # undefined flag bit
+    (0x80000000, {}, EINVAL),
+    (1, dict(k=47), EUNSUP),         # the variant keeps every other check
+    (1, dict(ptr=None), EINVAL),
+    (1, dict(wsb=16), EWS),
+    (0, dict(wsb=16), EWS),
+    (1, dict(T=0, ptr=None, ws=None), OK),
+])
+def test_select_forward_ex_flags(lib, flags, kw, code):
+    assert _sel_ex(lib, flags, **kw) == code
+
+
 def test_select_forward_empty_batch_is_a_noop(lib):
     assert _sel(lib, T=0, ptr=None, ws=None) == OK
 

@@ -30,20 +30,20 @@ def gpu_sketch(cfm, L):
     return tg, tu, sg, su
 
 
-def run_select(cfm, L, sk, A, Bt, k, c, r, stats=False):
+def run_select(cfm, L, sk, A, Bt, k, c, r, stats=False, recovery="sketch"):
     T, K = L.host.ids.shape
     cand = torch.empty((max(T * K, 1), max(c, 1)), dtype=torch.int32, device=dev())
     keep = torch.empty((max(T * K, 1), max(k, 1)), dtype=torch.int32, device=dev())
     st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device=dev()) if stats else None
     out = cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, k, c, r,
                                  cand_out=cand if c > 0 else None, keep_out=keep if k > 0 else None,
-                                 stats=st)
+                                 stats=st, recovery=recovery)
     torch.cuda.synchronize()
     res = (down_bf16(out), cand.cpu().numpy()[:, :c], keep.cpu().numpy()[:, :k])
     return res + ((cfm.decode_stats(st),) if stats else ())
 
 
-def compare_forward(L, A_bits, Bt_bits, got, cand, keep, k, c, tokens=None, what=""):
+def compare_forward(L, A_bits, Bt_bits, got, cand, keep, k, c, tokens=None, what="", recovery="sketch"):
     """Oracle run on the host inputs (its own sketch) vs the library's results."""
     h = L.host
     T, K = h.ids.shape
@@ -58,7 +58,7 @@ def compare_forward(L, A_bits, Bt_bits, got, cand, keep, k, c, tokens=None, what
         return z
     tg, tu, sg, su = full(tg), full(tu), full(sg), full(su)
     out, pairs = O.select_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su,
-                                  h.signs, A_bits, Bt_bits, k, c, tokens=tokens)
+                                  h.signs, A_bits, Bt_bits, k, c, tokens=tokens, recovery=recovery)
     exact_tokens, errs = 0, []
     for n, t in enumerate(tokens):
         same = True
@@ -312,6 +312,17 @@ def test_q18_b1_full_size(cfm, q18_layer):
     for e in used[:3]:
         excess, _ = _eckart_young_excess(L.host.w_down_t[e], Ag[e], Bg[e], wl.r)
         assert excess <= 1e-2
+
+
+def test_q18_b1_full_size_candidates_exact(cfm, q18_layer):
+    """The recovery variant (dropped candidates recovered with their exact activation) at full size."""
+    L, wl = q18_layer, q18_layer.wl
+    E, I, H = L.host.w_gate.shape
+    used = sorted(set(L.host.ids.reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r, recovery="candidates_exact")
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, what="q18_b1 candidates_exact", recovery="candidates_exact")
 
 
 @pytest.mark.parametrize("name", ["q13_b8", "q13_b16", "q18_b16"])
