@@ -434,13 +434,14 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-// Requests the Bt rows of all candidates ([c][r] BF16 into L.btc) and their
-// down rows for output chunks [ck0, ck0 + nck) ([c][nck] 16-byte pieces into
-// L.dnc). Lanes past the end repeat the last row (their bytes land in the
-// padding).
-__device__ __forceinline__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e, int ck0, int nck) {
+// Requests the down rows of all candidates for output chunks [ck0, ck0 + nck)
+// ([c][nck] 16-byte pieces into L.dnc) and, if with_bt, their Bt rows ([c][r]
+// BF16 into L.btc). Lanes past the end repeat the last row (their bytes land
+// in the padding).
+__device__ __forceinline__ void prefetch_candidate_rows(const FusedArgs& a, const Lds& L, int e, int ck0, int nck,
+                                                        bool with_bt) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int cpr = a.r / 8, nb = a.c * cpr;
+  const int cpr = a.r / 8, nb = with_bt ? a.c * cpr : 0;
   for (int q = wv; q * 64 < nb; q += NT / 64) {
     const int f = q * 64 + lane;
     const int i = min(f / cpr, a.c - 1), cc = f % cpr;
@@ -594,24 +595,38 @@ __device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p,
 // Partial recovery sums of all nw workgroups of pair p: thread (zl, zg) adds
 // those of workgroups zg, zg + groups, ... into L.red[NT + zg r + zl]. All its
 // loads are issued before the first wait.
-__device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int p, int zl, int zg,
-                                           int groups, uint32_t tag) {
-  constexpr int kMaxPer = 16;                      // nw <= 32 and groups >= 2 (r <= 128)
+constexpr int kZsumPer = 16;                       // nw <= 32 and groups >= 2 (r <= 128)
+
+// Issues the loads of fetch_zsum (so that they can be in flight with others);
+// N >= ceil(nw / groups).
+template <int N>
+__device__ __forceinline__ void zsum_issue(const FusedArgs& a, int p, int zl, int zg, int groups,
+                                           uint64_t (&raw)[N]) {
+  const uint64_t* zp = a.xz + (size_t)p * a.nw * a.r + zl;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int q = zg + groups * u;
+    raw[u] = (zg < groups && q < a.nw) ? ld_tagged(zp + (size_t)q * a.r) : 0;
+  }
+}
+template <int N>
+__device__ __forceinline__ void zsum_finish(const FusedArgs& a, const Lds& L, int p, int zl, int zg, int groups,
+                                            const uint64_t (&raw)[N], uint32_t tag) {
   if (zg >= groups) return;
   const uint64_t* zp = a.xz + (size_t)p * a.nw * a.r + zl;
-  uint64_t raw[kMaxPer];
-#pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int q = zg + groups * u;
-    raw[u] = q < a.nw ? ld_tagged(zp + (size_t)q * a.r) : 0;
-  }
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
+  for (int u = 0; u < N; ++u) {
     const int q = zg + groups * u;
     if (q < a.nw) s += await_tagged(zp + (size_t)q * a.r, raw[u], tag, a.fail);
   }
   L.red[NT + zg * a.r + zl] = s;
+}
+__device__ __forceinline__ void fetch_zsum(const FusedArgs& a, const Lds& L, int p, int zl, int zg,
+                                           int groups, uint32_t tag) {
+  uint64_t raw[kZsumPer];
+  zsum_issue(a, p, zl, zg, groups, raw);
+  zsum_finish(a, L, p, zl, zg, groups, raw, tag);
 }
 
 // One sub-chunk of phase A: the screen, then this thread's partial recovery sum.
@@ -757,14 +772,19 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         uint32_t k4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+        // recovery sums of all workgroups of the pair: requested with the
+        // activations when each thread reads at most 8 of them
+        const bool zpre = EPT <= 16 && r > 0 && a.nw * r <= 8 * NT;
+        uint64_t zraw[8];
+        if (zpre) zsum_issue(a, p, zl, zg, groups, zraw);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
           if (j < cnt) L.hh[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
-        // recovery sums of all workgroups of the pair
-        if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
+        if (zpre) zsum_finish(a, L, p, zl, zg, groups, zraw, tag);
+        else if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
         block_topk<NT, 4>(k4, i0, cnt, a.I, a.c, L.candp, L.tks);
       } else {
 #pragma unroll
@@ -800,7 +820,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     }
     // candidate rows for z and the down projection: requested once the exact
     // rows are in (so they do not share bandwidth with them), used after top-k
-    if (a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck);
+    // (z needs the kept channels' Bt rows, read after top-k; with the variant,
+    // or at the largest hidden width where registers are short, every
+    // candidate's Bt row is prefetched into LDS with the down rows instead)
+    constexpr bool kBtLate = !RECX && EPT <= 16;
+    if (a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck, !kBtLate);
 
     // ---- top-k kept set and recovery coefficients
     if (exact_step) {
@@ -854,44 +878,33 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       __syncthreads();
     }
     if (a.pre) {
-      // candidate rows are in LDS: z, the recovery term and the down projection
-      // of this workgroup's slice need no further memory reads
+      // candidate down rows are in LDS: the down projection of this workgroup's
+      // slice needs no further memory reads. z takes the kept channels' Bt rows,
+      // requested once the prefetch has landed and in flight while the down
+      // projection runs (default), or prefetched into LDS with the down rows
+      // (variant)
+      constexpr int ZB = 5;
+      const int cpr = r > 0 ? r / 8 : 1, ng = NT / cpr;
+      const int zc = tid % cpr, zgi = tid / cpr;
+      uint4 bz[ZB];
+      float hz[ZB];
+      auto kept_bt = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < ZB; ++u) {
+          const int i = i0 + ng * u;
+          const bool ok = i < a.k;
+          const int j = ok ? L.keep[i] : 0;
+          hz[u] = ok ? L.hh[j] : 0.f;
+          bz[u] = ok ? ld16c(a.Bt + ((size_t)e * a.I + j) * r + 8 * zc) : make_uint4(0, 0, 0, 0);
+        }
+      };
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (r > 0) {
-        const int cpr = r / 8, ng = NT / cpr;
-        const int cc = tid % cpr, g = tid / cpr;
-        float acc[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-        const int nz = RECX ? a.c : a.k;       // terms taken out of the screen's sum
-        for (int m = g; m < nz; m += ng) {
-          const int pos = RECX ? m : L.sel[m];
-          const float cf = RECX ? L.hcl[m] : L.hh[L.keep[m]];
-          fma8(acc, cf, *reinterpret_cast<const uint4*>(L.btc + (size_t)pos * 2 * r + 16 * cc));
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], cpr);
-        if (lane < cpr)
-#pragma unroll
-          for (int u = 0; u < 8; ++u) L.red[(tid >> 6) * r + 8 * lane + u] = acc[u];
-        __syncthreads();
-        for (int l = tid; l < r; l += NT) L.zv[l] = L.zsum[l] - (L.red[l] + L.red[r + l] + L.red[2 * r + l] + L.red[3 * r + l]);
-        __syncthreads();
-      }
-      if (ck0 < H / 8) {
-        float* rec = L.red + 4 * 128;                     // [8 nck] recovery term (nck <= 8)
-        float* part = L.red + 4 * 128 + 64;               // [4][8 nck] per-wavefront down partials
-        if (r > 0) {
-          const int cpr = r / 8;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int f = tid + NT * u;
-            float d = f < nck * r ? dot8_f(apre[u], L.zv + 8 * (f % cpr)) : 0.f;
-            d = sum_over_low_lanes(d, cpr);
-            if (f < nck * r && f % cpr == 0) rec[f / cpr] = d;
-          }
-        }
+      if (kBtLate && r > 0) kept_bt(zgi);
+      const bool cols = ck0 < H / 8;
+      float* rec = L.red + 4 * 128;                       // [8 nck] recovery term (nck <= 8)
+      float* part = L.red + 4 * 128 + 64;                 // [4][8 nck] per-wavefront down partials
+      if (cols) {
         const int cc = tid % nck, g = tid / nck;
         float acc[8];
 #pragma unroll
@@ -903,6 +916,46 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         if (lane < nck)
 #pragma unroll
           for (int u = 0; u < 8; ++u) part[(tid >> 6) * 8 * nck + 8 * lane + u] = acc[u];
+      }
+      if (r > 0) {
+        float acc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+        if constexpr (!kBtLate) {
+          const int nz = RECX ? a.c : a.k;     // terms taken out of the screen's sum
+          for (int m = zgi; m < nz; m += ng) {
+            const int pos = RECX ? m : L.sel[m];
+            const float cf = RECX ? L.hcl[m] : L.hh[L.keep[m]];
+            fma8(acc, cf, *reinterpret_cast<const uint4*>(L.btc + (size_t)pos * 2 * r + 16 * zc));
+          }
+        } else {
+          for (int i0 = zgi;;) {
+#pragma unroll
+            for (int u = 0; u < ZB; ++u) fma8(acc, hz[u], bz[u]);
+            i0 += ng * ZB;
+            if (i0 >= a.k) break;
+            kept_bt(i0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], cpr);
+        if (lane < cpr)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) L.red[(tid >> 6) * r + 8 * lane + u] = acc[u];
+        __syncthreads();
+        for (int l = tid; l < r; l += NT) L.zv[l] = L.zsum[l] - (L.red[l] + L.red[r + l] + L.red[2 * r + l] + L.red[3 * r + l]);
+        __syncthreads();
+        if (cols) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int f = tid + NT * u;
+            float d = f < nck * r ? dot8_f(apre[u], L.zv + 8 * (f % cpr)) : 0.f;
+            d = sum_over_low_lanes(d, cpr);
+            if (f < nck * r && f % cpr == 0) rec[f / cpr] = d;
+          }
+        }
+      }
+      if (cols) {
         __syncthreads();
         for (int col = tid; col < 8 * nck; col += NT) {
           const float y = part[col] + part[8 * nck + col] + part[16 * nck + col] + part[24 * nck + col] +
