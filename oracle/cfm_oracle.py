@@ -334,23 +334,29 @@ def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt,
     return {"hhat": hhat, "C": C, "h_all": h_all, "S": S, "y": y}
 
 
-def combine(ys: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """out = sum_q w_q · y_q over a token's K routed experts, as BF16 bits.
+def combine(ys: np.ndarray, w: np.ndarray, resid=None) -> np.ndarray:
+    """out = resid + sum_q w_q · y_q over a token's K routed experts, as BF16 bits.
 
     Router weights are used as given (never renormalised); the sum is in
-    float64 and rounded once to BF16.
+    float64 and rounded once to BF16. resid: optional BF16 bits [H] (the
+    residual stream the decode layer adds the block's output to).
     """
-    return f64_to_bf16(np.tensordot(np.asarray(w, np.float64), ys, axes=(0, 0)))
+    acc = np.tensordot(np.asarray(w, np.float64), ys, axes=(0, 0))
+    if resid is not None:
+        acc = acc + bf16_to_f64(resid)
+    return f64_to_bf16(acc)
 
 
 def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
-                   tokens=None, recovery=RECOVERY_SKETCH):
+                   tokens=None, recovery=RECOVERY_SKETCH, resid=None):
     """Selected-channel MoE layer over a decode batch.
 
     x [T][H] BF16 bits, ids [T][K], w [T][K]. Selection is per (token, expert)
     pair and does not depend on the rest of the batch ("each token's k
     highest-scoring channels", abstract). tokens: optional subset of token
     indices to evaluate (the others are skipped). recovery: as in select_pair.
+    resid: optional BF16 bits [T][H] added to each token's output before its
+    single rounding (see combine).
 
     Returns (out BF16 bits [len(tokens)][H], per-pair details
     {(t, q): select_pair dict}).
@@ -366,11 +372,11 @@ def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, 
                             A, Bt, k, c, recovery=recovery)
             pairs[(t, q)] = d
             ys[q] = d["y"]
-        outs.append(combine(ys, w[t]))
+        outs.append(combine(ys, w[t], None if resid is None else resid[t]))
     return (np.stack(outs) if outs else np.zeros((0, H), np.uint16)), pairs
 
 
-def dense_forward(x, ids, w, w_gate, w_up, w_down_t, tokens=None):
+def dense_forward(x, ids, w, w_gate, w_up, w_down_t, tokens=None, resid=None):
     """The same layer with every channel read: y = sum_j h_j · Wd_t[j]."""
     T, K = ids.shape
     H = w_gate.shape[2]
@@ -382,8 +388,71 @@ def dense_forward(x, ids, w, w_gate, w_up, w_down_t, tokens=None):
             e = int(ids[t, q])
             h = exact_activations(x[t], w_gate[e], w_up[e])
             ys[q] = h @ bf16_to_f64(w_down_t[e])
-        outs.append(combine(ys, w[t]))
+        outs.append(combine(ys, w[t], None if resid is None else resid[t]))
     return np.stack(outs) if outs else np.zeros((0, H), np.uint16)
+
+
+# ----------------------------------------------------------------------------- decode-layer envelope
+#
+# The steps on either side of the routed-expert block in a decode layer: the
+# block's input is the RMS-normalised hidden state, the router picks each
+# token's K experts from it, and the block's output is added to the residual
+# stream (abstract: MoE blocks and whole-model decoding; the block speedups
+# are measured with routing in place). Readings: RMSNorm with a learned
+# per-feature weight, rounded once to BF16; router logits W_r x from the BF16
+# normalised state; softmax over all experts; the K most probable experts in
+# descending probability, lower id first on ties; their probabilities as
+# weights, optionally renormalised to sum to 1; output = BF16(h + block).
+
+
+def rmsnorm(h_bits, gamma_bits, eps: float):
+    """x = BF16( h / sqrt(mean(h^2) + eps) * gamma ), per token, float64, one rounding."""
+    h = bf16_to_f64(h_bits)
+    inv = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + float(eps))
+    return f64_to_bf16(h * inv * bf16_to_f64(gamma_bits))
+
+
+def router(x_bits, w_router_bits, K: int, renorm: bool):
+    """Top-K softmax routing of BF16 states x [T][H] with router rows W_r [E][H].
+
+    Returns (ids int32 [T][K] in descending probability, lower id first on
+    ties; weights float64 [T][K]; logits float64 [T][E])."""
+    x = bf16_to_f64(x_bits)
+    logits = x @ bf16_to_f64(w_router_bits).T
+    p = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    T, E = p.shape
+    ids = np.zeros((T, K), np.int32)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-p[t, e], e))
+        ids[t] = order[:K]
+    w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renorm:
+        w = w / w.sum(axis=-1, keepdims=True)
+    return ids, w, logits
+
+
+def layer_forward(h, gamma, eps, w_router, K, renorm, w_gate, w_up, w_down_t, tg=None, tu=None, sg=None,
+                  su=None, signs=None, A=None, Bt=None, k=0, c=0, recovery=RECOVERY_SKETCH, dense=False,
+                  x=None, ids=None, w=None, tokens=None):
+    """One decode layer's routed-expert block with its envelope:
+    out = BF16(h + sum_q w_q y_(t,q)) with x = rmsnorm(h), (ids, w) = router(x).
+
+    dense=True runs the dense block (every channel) instead of the selected
+    one. x, ids, w: optional overrides (e.g. the values a device computed), so
+    that later steps can be checked on the same selections.
+    Returns (out BF16 bits, x, ids, w, per-pair details or None)."""
+    xs = rmsnorm(h, gamma, eps) if x is None else x
+    if ids is None or w is None:
+        ids_r, w_r, _ = router(xs, w_router, K, renorm)
+        ids = ids_r if ids is None else ids
+        w = w_r if w is None else w
+    if dense:
+        out = dense_forward(xs, ids, w, w_gate, w_up, w_down_t, tokens=tokens, resid=h)
+        return out, xs, ids, w, None
+    out, pairs = select_forward(xs, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
+                                tokens=tokens, recovery=recovery, resid=h)
+    return out, xs, ids, w, pairs
 
 
 # ----------------------------------------------------------------------------- byte accounting

@@ -153,3 +153,32 @@ def test_candidate_rows_billed_at_k0_is_caught(monkeypatch):
     orig = O.read_bytes
     monkeypatch.setattr(O, "read_bytes", lambda *a, **kw: orig(*a, **dict(kw, recovery="candidates_exact")))
     _fails(P.test_read_bytes_candidate_rows_only_when_exact_activations_are_used)
+
+
+def test_router_lowest_probabilities_are_caught(monkeypatch):
+    orig = O.router
+
+    def bad(x_bits, w_router_bits, K, renorm):
+        ids, w, logits = orig(x_bits, -O.as_f64(w_router_bits), K, renorm)
+        return ids, w, -logits
+    monkeypatch.setattr(O, "router", bad)
+    _fails(P.test_router_matches_torch_softmax_topk)
+
+
+def test_rmsnorm_without_weight_is_caught(monkeypatch):
+    orig = O.rmsnorm
+    monkeypatch.setattr(O, "rmsnorm", lambda h, g, eps: orig(h, O.f64_to_bf16(np.ones(np.shape(g))), eps))
+    _fails(P.test_rmsnorm_matches_torch)
+
+
+def test_residual_rounded_separately_is_caught(monkeypatch):
+    orig = O.combine
+
+    def bad(ys, w, resid=None):
+        out = orig(ys, w)
+        if resid is None:
+            return out
+        return O.f64_to_bf16(O.bf16_to_f64(out) + O.bf16_to_f64(resid))
+    monkeypatch.setattr(O, "combine", bad)
+    _fails(P.test_layer_all_kept_matches_torch_envelope, False)
+

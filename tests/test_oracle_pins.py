@@ -458,3 +458,115 @@ def test_read_bytes_candidate_rows_only_when_exact_activations_are_used():
     assert O.read_bytes(ids, 4, I, H, 0, c, r) == 2 * base + io
     assert O.read_bytes(ids, 4, I, H, 0, c, r, recovery="candidates_exact") == 2 * (base + 4 * H * c) + io
     assert O.read_bytes(ids, 4, I, H, 3, c, r) == O.read_bytes(ids, 4, I, H, 3, c, r, recovery="candidates_exact")
+
+
+# ----------------------------------------------------------------------------- decode-layer envelope
+
+def _bf16_bits_of(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_rmsnorm_matches_torch():
+    r = _rng(40)
+    h = O.f64_to_bf16(r.standard_normal((5, 256)) * np.exp(r.uniform(-4, 4, (5, 1))))
+    g = O.f64_to_bf16(1.0 + 0.3 * r.standard_normal(256))
+    ht = torch.from_numpy(O.bf16_to_f64(h))
+    ref = torch.nn.functional.rms_norm(ht, (256,), weight=torch.from_numpy(O.bf16_to_f64(g)), eps=1e-6)
+    assert np.array_equal(O.rmsnorm(h, g, 1e-6), _bf16_bits_of(ref))
+    # scale invariance by a power of two (eps negligible): the same bits
+    assert np.array_equal(O.rmsnorm(O.f64_to_bf16(O.bf16_to_f64(h) / 64), g, 0.0), O.rmsnorm(h, g, 0.0))
+
+
+def test_router_matches_torch_softmax_topk():
+    r = _rng(41)
+    x = O.f64_to_bf16(r.standard_normal((6, 64)))
+    wr = O.f64_to_bf16(0.1 * r.standard_normal((32, 64)))
+    ids, w, logits = O.router(x, wr, 5, False)
+    lt = torch.from_numpy(O.bf16_to_f64(x)) @ torch.from_numpy(O.bf16_to_f64(wr)).T
+    pt = torch.softmax(lt, dim=-1)
+    tw, ti = torch.topk(pt, 5, dim=-1)                # distinct values here: order is well defined
+    assert np.array_equal(ids, ti.numpy().astype(np.int32))
+    assert np.allclose(w, tw.numpy(), rtol=1e-12, atol=0)
+    assert np.allclose(logits, lt.numpy(), rtol=1e-12, atol=1e-14)
+    _, wn, _ = O.router(x, wr, 5, True)
+    assert np.allclose(wn, (tw / tw.sum(-1, keepdim=True)).numpy(), rtol=1e-12)
+
+
+def test_router_ties_go_to_the_lower_id():
+    x = O.f64_to_bf16(np.ones((1, 8)))
+    wr = np.zeros((6, 8))
+    wr[[1, 4]] = 0.5                                  # experts 1 and 4 tie at the top, 0, 2, 3, 5 below
+    wr[[0, 5]] = 0.25
+    ids, w, _ = O.router(x, O.f64_to_bf16(wr), 3, False)
+    assert ids.tolist() == [[1, 4, 0]]
+    assert w[0, 0] == w[0, 1] > w[0, 2]
+
+
+def _torch_layer(h, g, eps, wr, K, renorm, wg, wu, wd):
+    """The whole envelope with torch ops in float64 (dense block)."""
+    ht = torch.from_numpy(O.bf16_to_f64(h))
+    x = torch.nn.functional.rms_norm(ht, (ht.shape[1],), weight=torch.from_numpy(O.bf16_to_f64(g)), eps=eps)
+    x = torch.from_numpy(O.bf16_to_f64(_bf16_bits_of(x)))
+    p = torch.softmax(x @ torch.from_numpy(O.bf16_to_f64(wr)).T, dim=-1)
+    tw, ti = torch.topk(p, K, dim=-1)
+    if renorm:
+        tw = tw / tw.sum(-1, keepdim=True)
+    outs = []
+    for t in range(h.shape[0]):
+        acc = ht[t].clone()
+        for q in range(K):
+            e = int(ti[t, q])
+            gg = torch.from_numpy(O.bf16_to_f64(wg[e])) @ x[t]
+            uu = torch.from_numpy(O.bf16_to_f64(wu[e])) @ x[t]
+            acc += tw[t, q] * (torch.from_numpy(O.bf16_to_f64(wd[e])).T @ (torch.nn.functional.silu(gg) * uu))
+        outs.append(acc.numpy())
+    return np.stack(outs), ti.numpy()
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_layer_all_kept_matches_torch_envelope(renorm):
+    """k = c = I, r = 0: the envelope around the selected block is torch's RMSNorm, softmax top-K
+    routing, SwiGLU experts and residual add, rounded once."""
+    wg, wu, wd, d, x, ids, w = _small_layer(E=6, I=16, H=64, T=3, K=2)
+    wg, wu, wd = (O.f64_to_bf16(8.0 * O.bf16_to_f64(m)) for m in (wg, wu, wd))   # block output ~ residual
+    r = _rng(42)
+    h = O.f64_to_bf16(0.5 * r.standard_normal((3, 64)))
+    g = O.f64_to_bf16(1.0 + 0.2 * r.standard_normal(64))
+    wr = O.f64_to_bf16(0.2 * r.standard_normal((6, 64)))
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 0)
+    out, xs, oids, ow, _ = O.layer_forward(h, g, 1e-6, wr, 2, renorm, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 16, 16)
+    ref, rids = _torch_layer(h, g, 1e-6, wr, 2, renorm, wg, wu, wd)
+    assert np.array_equal(oids, rids)
+    # one rounding of the same float64 sum: equal bits, except where the two float64 sums
+    # (different summation order) straddle a BF16 rounding boundary
+    want = O.f64_to_bf16(ref)
+    near = O.f64_to_bf16(ref * (1 - 1e-12)) != O.f64_to_bf16(ref * (1 + 1e-12))
+    assert np.all((out == want) | near)
+    assert np.sum(out == want) >= 0.99 * out.size
+    dense, *_ = O.layer_forward(h, g, 1e-6, wr, 2, renorm, wg, wu, wd, dense=True)
+    assert np.array_equal(dense, out)
+
+
+def test_layer_residual_added_once_before_rounding():
+    """Zero residual stream direction: with h scaled by 2^-6 the block input is the same (RMSNorm is
+    scale-free), so out(h) - out(h/64) carries the residual difference and one rounding per output."""
+    wg, wu, wd, d, x, ids, w = _small_layer(E=6, I=16, H=64, T=2, K=2)
+    r = _rng(43)
+    h = O.f64_to_bf16(r.standard_normal((2, 64)))
+    hs = O.f64_to_bf16(O.bf16_to_f64(h) / 64)
+    g = O.f64_to_bf16(np.ones(64))
+    wr = O.f64_to_bf16(0.2 * r.standard_normal((6, 64)))
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 4)
+    a = O.layer_forward(h, g, 0.0, wr, 2, False, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 9)
+    b = O.layer_forward(hs, g, 0.0, wr, 2, False, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 9)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    # the block output y: recovered from the no-residual run of the same selections
+    y, _ = O.select_forward(a[1], a[2], a[3], wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 9)
+    yb = O.bf16_to_f64(y)
+    for out, hh in ((a[0], h), (b[0], hs)):
+        got = O.bf16_to_f64(out)
+        want = O.bf16_to_f64(hh) + yb
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 2.0 ** -8 * np.abs(yb) + 1e-30)
+
