@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     FORWARD_AUTO, FORWARD_GROUPED, FORWARD_PER_PAIR, RECOVER_CANDIDATES_EXACT, RECOVER_SKETCH, CfmError,
     EXPORTED, STATS_BYTES, decode_stats,
     dense_workspace, forward_path, last_error, lowrank_build, lowrank_workspace, moe_dense_forward,
+    moe_layer_dense_forward, moe_layer_forward,
     moe_select_forward, new_workspace, select_workspace, set_forward_path, sketch_build, timing_enable,
     timing_report, version,
 )

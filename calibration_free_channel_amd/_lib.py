@@ -35,6 +35,10 @@ _SIGS = {
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
     "moe_select_forward_ex": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                    _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
+    "moe_layer_forward": (_i, [_p, _p, ctypes.c_float, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
+                               _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
+    "moe_layer_dense_forward": (_i, [_p, _p, ctypes.c_float, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p,
+                                     _p, _p, _z, _p]),
     "dense_workspace": (_z, [_i, _i, _i, _i, _i]),
     "moe_dense_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _z, _p]),
     "cfm_set_forward_path": (_i, [_i]),
@@ -194,6 +198,45 @@ def moe_dense_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, out=None, ws=
     _check(_lib.moe_dense_forward(
         _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
         E, I, H, _ptr(out), _ptr(ws), ws.numel(), _stream(dev)), "moe_dense_forward")
+    return out
+
+
+def moe_layer_forward(h, norm_w, eps, w_router, K, w_gate, w_up, w_down_t, signs, tg, tu, sg, su, A, Bt,
+                      k, c, r, renorm=False, out=None, ws=None, ids_out=None, w_out=None, x_out=None,
+                      recovery=RECOVER_SKETCH):
+    """The routed-expert block of a decode layer with its envelope (RMSNorm, router, residual add) in one
+    launch. Returns out [T][H] BF16 (h + block output); out may be h."""
+    if recovery not in _RECOVER_FLAGS:
+        raise ValueError(f"unknown recovery variant {recovery!r}")
+    T, H = h.shape
+    E, I, _ = w_gate.shape
+    dev = h.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = new_workspace(select_workspace(T, K, E, I, H, k, c, r), dev)
+    _check(_lib.moe_layer_forward(
+        _ptr(h), _ptr(norm_w), float(eps), _ptr(w_router), 1 if renorm else 0, T, K, _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down_t), E, I, H, _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su),
+        _ptr(A) if r > 0 else None, _ptr(Bt) if r > 0 else None, k, c, r, _RECOVER_FLAGS[recovery], _ptr(out),
+        _ptr(ids_out), _ptr(w_out), _ptr(x_out), _ptr(ws), ws.numel(), _stream(dev)), "moe_layer_forward")
+    return out
+
+
+def moe_layer_dense_forward(h, norm_w, eps, w_router, K, w_gate, w_up, w_down_t, renorm=False, out=None, ws=None,
+                            ids_out=None, w_out=None, x_out=None):
+    """The same envelope around the dense block. Returns out [T][H] BF16."""
+    T, H = h.shape
+    E, I, _ = w_gate.shape
+    dev = h.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = new_workspace(dense_workspace(T, K, E, I, H), dev)
+    _check(_lib.moe_layer_dense_forward(
+        _ptr(h), _ptr(norm_w), float(eps), _ptr(w_router), 1 if renorm else 0, T, K, _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down_t), E, I, H, _ptr(out), _ptr(ids_out), _ptr(w_out), _ptr(x_out), _ptr(ws), ws.numel(),
+        _stream(dev)), "moe_layer_dense_forward")
     return out
 
 

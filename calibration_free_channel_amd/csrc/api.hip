@@ -237,6 +237,62 @@ int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* 
                                stream);
 }
 
+namespace {
+int check_envelope(int K, int E, float eps, const void* h, const void* norm_w, const void* w_router,
+                   const void* out) {
+  if (E > 1024) return set_error(CFM_EUNSUPPORTED, "decode-layer envelope: E must be at most 1024");
+  if (K > E) return set_error(CFM_EUNSUPPORTED, "decode-layer envelope: K must not exceed E");
+  if (!(eps >= 0.f) || eps > 1.f) return set_error(CFM_EINVAL, "decode-layer envelope: eps must lie in [0, 1]");
+  if (!h || !norm_w || !w_router || !out) return set_error(CFM_EINVAL, "decode-layer envelope: null pointer");
+  return CFM_OK;
+}
+}  // namespace
+
+int moe_layer_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
+                      int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                      const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                      const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                      const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, unsigned flags,
+                      cfm_bf16* out, int32_t* ids_out, float* w_out, cfm_bf16* x_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  clear_error();
+  if (flags & ~CFM_RECOVER_CANDIDATES_EXACT) return set_error(CFM_EINVAL, "moe_layer_forward: unknown flag bits");
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (int rc = check_budget(I, H, k, c, r)) return rc;
+  if (T == 0) return CFM_OK;
+  if (int rc = check_envelope(K, E, eps, h, norm_w, w_router, out)) return rc;
+  if (!w_gate || !w_up || !w_down_t || !signs || !tg || !tu || !sg || !su)
+    return set_error(CFM_EINVAL, "moe_layer_forward: null pointer");
+  if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_layer_forward: null A or Bt with r > 0");
+  const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r, true);
+  if (!ws || ws_bytes < plan.bytes)
+    return set_error(CFM_EWORKSPACE, "moe_layer_forward: workspace smaller than select_workspace()");
+  SelectArgs a{nullptr, w_gate, w_up, w_down_t, A, Bt, nullptr, nullptr, signs, tg, tu, sg, su, out,
+               nullptr, nullptr, nullptr, static_cast<char*>(ws), flags,
+               h, norm_w, w_router, eps, renorm ? 1 : 0, ids_out, w_out, x_out};
+  return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
+                            int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                            const cfm_bf16* w_down_t, int E, int I, int H, cfm_bf16* out, int32_t* ids_out,
+                            float* w_out, cfm_bf16* x_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, false)) return rc;
+  if (T == 0) return CFM_OK;
+  if (int rc = check_envelope(K, E, eps, h, norm_w, w_router, out)) return rc;
+  if (!w_gate || !w_up || !w_down_t) return set_error(CFM_EINVAL, "moe_layer_dense_forward: null pointer");
+  const ForwardPlan plan = dense_plan(T, K, E, I, H, true);
+  if (!ws || ws_bytes < plan.bytes)
+    return set_error(CFM_EWORKSPACE, "moe_layer_dense_forward: workspace smaller than dense_workspace()");
+  SelectArgs a{nullptr, w_gate, w_up, w_down_t, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+               nullptr, nullptr, nullptr, out, nullptr, nullptr, nullptr, static_cast<char*>(ws), 0u,
+               h, norm_w, w_router, eps, renorm ? 1 : 0, ids_out, w_out, x_out};
+  return launch_dense_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+
 size_t dense_workspace(int T, int K, int E, int I, int H) {
   if (T < 0 || K <= 0 || K > kMaxK || E <= 0 || I <= 0 || I > kMaxI || H < 64 || H > kMaxH ||
       H % 64)

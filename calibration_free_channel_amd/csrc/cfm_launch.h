@@ -36,13 +36,15 @@ struct ForwardPlan {
   int nhs;        // 64-column output slices per token
   size_t lds;     // dynamic LDS bytes per workgroup
   int pre;        // candidate rows prefetched into LDS (selected pass)
+  int env;        // decode-layer envelope (norm, router, residual) fused into the launch
   size_t off_seq, off_err, off_ctr;      // u32 [256], u32, u32 [T][nhs]
   size_t off_xh, off_xz, off_xc;         // tagged u64 [P][I], [P][nw][r], [P][c]
   size_t off_ypart;                      // f32 [P][H]
+  size_t off_xl;                         // tagged u64 [T][E] router logits (envelope)
   size_t bytes;
 };
-ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r);
-ForwardPlan dense_plan(int T, int K, int E, int I, int H);
+ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool env = false);
+ForwardPlan dense_plan(int T, int K, int E, int I, int H, bool env = false);
 
 struct SelectArgs {
   const uint16_t *x, *w_gate, *w_up, *w_down_t, *A, *Bt;
@@ -56,6 +58,14 @@ struct SelectArgs {
   void* stats;
   char* ws;
   unsigned flags;   // CFM_RECOVER_* variant bits (0: the default method)
+  // decode-layer envelope (moe_layer_forward): x above is unused; the block's
+  // input is RMSNorm(resid) and the routing comes from the router rows wr
+  const uint16_t *resid, *gamma, *wr;
+  float eps;
+  int renorm;
+  int32_t* ids_out;
+  float* w_out;
+  uint16_t* x_out;
 };
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);

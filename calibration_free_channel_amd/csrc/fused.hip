@@ -175,6 +175,15 @@ struct FusedArgs {
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
   int pre;           // column chunks per workgroup when the candidates' rows are prefetched into LDS, else 0
   int rec_exact;     // dropped candidates enter the recovery with their exact activation
+  // decode-layer envelope (env != 0): x = RMSNorm(resid) computed in the
+  // launch, routing from the router rows wr, resid added to the output
+  int env, renorm;
+  float eps;
+  const uint16_t *resid, *gamma, *wr;
+  uint64_t* xl;      // [T][E] router logits (tagged)
+  int32_t* ids_out;  // [T][K] (optional)
+  float* w_out;      // [T][K] (optional)
+  uint16_t* x_out;   // [T][H] (optional)
 };
 
 struct Lds {
@@ -196,9 +205,16 @@ struct Lds {
   uint32_t* tks;     // top-k scratch
   uint8_t* btc;      // [c][r] Bt rows of the candidates (BF16), when prefetched
   uint8_t* dnc;      // [c][64] down rows of the candidates for this workgroup's slice, when prefetched
+  // envelope only
+  uint16_t* xb;      // [H] the token's normalised state (BF16)
+  float* rl;         // [E] the token's router logits
+  int32_t* rida;     // [K] its experts in ascending id order
+  int32_t* rid;      // [K] its experts in slot order (descending probability)
+  float* rw;         // [K] their weights
 };
 
-__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cpw, int pre, size_t* off) {
+__host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, int cpw, int pre, size_t* off,
+                                             int env = 0, int E = 0, int K = 0) {
   size_t o = 0;
   int n = 0;
   auto take = [&](size_t b) { off[n++] = o; o = (o + b + 15) & ~size_t(15); };
@@ -224,12 +240,17 @@ __host__ __device__ inline size_t lds_layout(int H, int I, int c, int k, int r, 
   const size_t nbt = pre ? (size_t)c * (r / 8) : 0, ndn = pre ? (size_t)c * pre : 0;   // pre: column chunks
   take(16 * ((nbt + 63) / 64 * 64));
   take(16 * ((ndn + 63) / 64 * 64));
+  take(env ? 2 * (size_t)H : 0);
+  take(env ? 4 * (size_t)E : 0);
+  take(env ? 4 * (size_t)K : 0);
+  take(env ? 4 * (size_t)K : 0);
+  take(env ? 4 * (size_t)K : 0);
   return o;
 }
 
 __device__ __forceinline__ Lds carve(unsigned char* smem, const FusedArgs& a) {
-  size_t off[20];
-  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, a.pre, off);
+  size_t off[24];
+  lds_layout(a.H, a.I, a.c, a.k, a.r, a.cpw, a.pre, off, a.env, a.E, a.K);
   Lds L;
   L.xs = reinterpret_cast<int32_t*>(smem + off[0]);
   L.limb = smem + off[1];
@@ -249,6 +270,11 @@ __device__ __forceinline__ Lds carve(unsigned char* smem, const FusedArgs& a) {
   L.tks = reinterpret_cast<uint32_t*>(smem + off[15]);
   L.btc = smem + off[16];
   L.dnc = smem + off[17];
+  L.xb = reinterpret_cast<uint16_t*>(smem + off[18]);
+  L.rl = reinterpret_cast<float*>(smem + off[19]);
+  L.rida = reinterpret_cast<int32_t*>(smem + off[20]);
+  L.rid = reinterpret_cast<int32_t*>(smem + off[21]);
+  L.rw = reinterpret_cast<float*>(smem + off[22]);
   return L;
 }
 
@@ -566,7 +592,10 @@ __device__ __forceinline__ void cols_block(const FusedArgs& a, const Lds& L, int
 
 // After this workgroup's y columns of pair p are stored: the last of the
 // token's K pairs to arrive writes out[t][8 ck0 .. 8 (ck0 + nck)) in BF16.
-__device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, int ck0, int nck, int* s_flag, uint32_t tag) {
+// lw: the token's router weights in LDS (envelope), else null (topk_w). With
+// the envelope the residual is added before the single rounding.
+__device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, int ck0, int nck, int* s_flag, uint32_t tag,
+                                             const float* lw = nullptr) {
   const int tid = threadIdx.x;
   unsigned* cc = a.ctr + (size_t)t * kMaxNw + w;
   if (last_of(cc, (unsigned)a.K, s_flag)) {
@@ -574,7 +603,8 @@ __device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, i
     for (int col = 8 * ck0 + tid; col < 8 * (ck0 + nck); col += NT) {
       float o = 0.f;
       for (int q = 0; q < a.K; ++q)
-        o += a.topk_w[(size_t)t * a.K + q] * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + col);
+        o += (lw ? lw[q] : a.topk_w[(size_t)t * a.K + q]) * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + col);
+      if (lw) o += bf16_to_f32(a.resid[(size_t)t * a.H + col]);
       a.out[(size_t)t * a.H + col] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
     }
   }
@@ -583,11 +613,12 @@ __device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, i
 
 // Phase C of a workgroup: its columns in blocks of at most NT chunks, then the combine.
 __device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p, int t, int e, int w,
-                        const int32_t* rows, const float* hv, int n, bool use_rec, int* s_flag, uint32_t tag) {
+                        const int32_t* rows, const float* hv, int n, bool use_rec, int* s_flag, uint32_t tag,
+                        const float* lw = nullptr) {
   const int nck = col_chunks(a), ck0 = w * nck;
   if (ck0 >= a.H / 8) return;
   for (int cb = 0; cb < nck; cb += NT) cols_block(a, L, p, e, ck0 + cb, min(NT, nck - cb), rows, hv, n, use_rec);
-  combine_cols(a, t, w, ck0, nck, s_flag, tag);
+  combine_cols(a, t, w, ck0, nck, s_flag, tag, lw);
 }
 
 // ------------------------------------------------------------------ exchange reads
@@ -647,6 +678,162 @@ __device__ __forceinline__ void screen_and_sum(const FusedArgs& a, const Lds& L,
   __syncthreads();
 }
 
+// 16-byte piece i of a row of x (in LDS with the envelope, global memory otherwise).
+__device__ __forceinline__ uint4 x16(const uint16_t* row, int i) {
+  return ld16c(reinterpret_cast<const uint4*>(row) + i);
+}
+
+// ------------------------------------------------------------------ decode-layer envelope
+
+// Order-preserving map of a finite float to an unsigned key.
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The envelope's first steps for token t, run by every workgroup that serves
+// one of its pairs (slot q, workgroup w of the pair):
+//   x = RMSNorm(h[t]) into L.xb: BF16 of (h s) g in float32, one rounding,
+//       s = 1 / sqrt(mean(h^2) + eps);
+//   the router logits W_r[e] . x of experts u, u + UT, ... (u = q nw + w,
+//       UT = K nw: the token's workgroups share its E logits), published as
+//       tagged words, then all E read back;
+//   softmax over the E logits; the K most probable experts in descending
+//       probability, lower id first on ties, into L.rid, their probabilities
+//       (renormalised to sum 1 if asked) into L.rw.
+// Every workgroup of the token forms the same L.xb, L.rid and L.rw (the same
+// arithmetic on the same values). Returns the expert of slot q.
+__device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t, int q, int w, uint32_t tag) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, E = a.E, K = a.K;
+  const int nch = H / 8;                                  // 16-byte chunks of a row (H >= 64)
+  const int UT = K * a.nw, u = q * a.nw + w;
+  const int nlog = u < E ? (E - u + UT - 1) / UT : 0;     // logits this workgroup computes
+  float* red = L.red;                                     // scratch (free until the screen)
+  const uint4* xb4 = reinterpret_cast<const uint4*>(L.xb);
+  // requests first: the first router row of each wavefront (chunks lane, lane + 64, ...),
+  // then the hidden state (chunks tid, tid + NT, ...)
+  constexpr int RP = 4;                                   // prefetched chunks per lane of the first row
+  uint4 rp[RP];
+  {
+    const bool has = wv < nlog;
+    const uint4* row = reinterpret_cast<const uint4*>(a.wr + (size_t)(has ? u + UT * wv : 0) * H);
+#pragma unroll
+    for (int m = 0; m < RP; ++m) {
+      const int ci = lane + 64 * m;
+      rp[m] = (has && ci < nch) ? ld16c(row + ci) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const uint4* hrow = reinterpret_cast<const uint4*>(a.resid + (size_t)t * H);
+  const uint4* grow = reinterpret_cast<const uint4*>(a.gamma);
+  // mean square of the row
+  float ss = 0.f;
+  for (int ci = tid; ci < nch; ci += NT) {
+    const uint4 h4 = ld16c(hrow + ci);
+    const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16lo(hw[i]), hi = bf16hi(hw[i]);
+      ss += lo * lo + hi * hi;
+    }
+  }
+  ss = wave_sum_f(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  const float sc = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + a.eps);
+  for (int ci = tid; ci < nch; ci += NT) {
+    const uint4 h4 = ld16c(hrow + ci), g4 = ld16c(grow + ci);
+    const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+    const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_bf16(bf16lo(hw[i]) * sc * bf16lo(gw[i])) |
+             ((uint32_t)f32_to_bf16(bf16hi(hw[i]) * sc * bf16hi(gw[i])) << 16);
+    reinterpret_cast<uint4*>(L.xb)[ci] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __syncthreads();
+  // this workgroup's logits: wavefront v takes experts u + UT (v + 4 i)
+  for (int i = wv; i < nlog; i += NT / 64) {
+    const uint4* row = reinterpret_cast<const uint4*>(a.wr + (size_t)(u + UT * i) * H);
+    float d = 0.f;
+#pragma unroll
+    for (int m = 0; m < RP; ++m) {
+      const int ci = lane + 64 * m;
+      if (ci < nch) d = dot8_bf16(i == wv ? rp[m] : ld16c(row + ci), xb4[ci], d);
+    }
+    for (int ci = lane + 64 * RP; ci < nch; ci += 64) d = dot8_bf16(ld16c(row + ci), xb4[ci], d);
+    d = wave_sum_f(d);
+    if (lane == 0) put_tagged(a.xl + (size_t)t * E + u + UT * i, d, tag);
+  }
+  // all E logits of the token (thread: indices [i0, i0 + cnt), E <= 4 NT)
+  int cnt;
+  const int i0 = topk_range<NT>(E, &cnt);
+  uint32_t keys[4];
+  float lv[4];
+  {
+    const uint64_t* src = a.xl + (size_t)t * E + i0;
+    uint64_t raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lv[j] = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
+      if (j < cnt) L.rl[i0 + j] = lv[j];
+      keys[j] = j < cnt ? ordered_key(lv[j]) : 0u;
+    }
+  }
+  // softmax: the largest logit, then the sum of exp(l - max)
+  uint32_t km = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) km = max(km, keys[j]);
+  km = wave_max_u32(km);
+  if (lane == 0) reinterpret_cast<uint32_t*>(red)[4 + wv] = km;
+  __syncthreads();
+  const uint32_t* rk = reinterpret_cast<const uint32_t*>(red) + 4;
+  const float lmax = key_value(max(max(rk[0], rk[1]), max(rk[2], rk[3])));
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) se += j < cnt ? expf(lv[j] - lmax) : 0.f;
+  se = wave_sum_f(se);
+  if (lane == 0) red[8 + wv] = se;
+  // the K largest logits (ascending ids into L.rida; ends with a barrier)
+  block_topk<NT, 4>(keys, i0, cnt, E, K, L.rida, L.tks);
+  const float sum = red[8] + red[9] + red[10] + red[11];
+  // slot order: descending logit, lower id first on ties
+  if (tid < K) {
+    const int id = L.rida[tid];
+    const float l = L.rl[id];
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int o = L.rida[j];
+      const float lo = L.rl[o];
+      rank += (lo > l) || (lo == l && o < id);
+    }
+    L.rid[rank] = id;
+    L.rw[rank] = expf(l - lmax) / sum;
+  }
+  __syncthreads();
+  if (a.renorm) {
+    float ws = 0.f;
+    for (int j = 0; j < K; ++j) ws += L.rw[j];
+    __syncthreads();
+    if (tid < K) L.rw[tid] = L.rw[tid] / ws;
+    __syncthreads();
+  }
+  // the token's routing and normalised state, for the caller (first workgroup of its first pair)
+  if (q == 0 && w == 0) {
+    if (a.ids_out && tid < K) a.ids_out[(size_t)t * K + tid] = L.rid[tid];
+    if (a.w_out && tid < K) a.w_out[(size_t)t * K + tid] = L.rw[tid];
+    if (a.x_out)
+      for (int ci = tid; ci < nch; ci += NT) reinterpret_cast<uint4*>(a.x_out + (size_t)t * H)[ci] = xb4[ci];
+  }
+  return __builtin_amdgcn_readfirstlane(L.rid[q]);
+}
+
 // ------------------------------------------------------------------ launch tag
 
 // Every thread reads the tag itself (no barrier); it is first needed when this
@@ -660,7 +847,7 @@ __device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) 
 
 // ------------------------------------------------------------------ kernels
 
-template <int EPT, bool RECX>
+template <int EPT, bool RECX, bool ENV>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) uint32_t wred[NT / 64];
@@ -684,13 +871,18 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     //      them: x (this thread's elements and the whole row) and signs first,
     //      then the sketch rows, scales and Bt rows of the first sub-chunk, and
     //      the A slice
+    // (with the envelope, x is formed here from the hidden state and the
+    // routing is computed: the pair's expert comes from it)
+    int e = 0;
+    if constexpr (ENV) e = env_route(a, L, t, p % a.K, w, tag);
+    const uint16_t* xrow = ENV ? L.xb : a.x + (size_t)t * H;
     uint4 xq[EPT >= 8 ? EPT / 8 : 1];
     uint32_t sq[EPT >= 4 ? EPT / 4 : 1];
     if constexpr (EPT >= 4) {
-      const uint16_t* xt = a.x + (size_t)t * H + EPT * tid;
+      const uint16_t* xt = xrow + EPT * tid;
       if constexpr (EPT >= 8) {
 #pragma unroll
-        for (int g = 0; g < EPT / 8; ++g) xq[g] = ld16c(xt + 8 * g);
+        for (int g = 0; g < EPT / 8; ++g) xq[g] = x16(xt, g);
       } else {
         const uint2 u = *reinterpret_cast<const uint2*>(xt);
         xq[0] = make_uint4(u.x, u.y, 0, 0);
@@ -698,7 +890,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
       for (int g = 0; g < EPT / 4; ++g) sq[g] = *reinterpret_cast<const uint32_t*>(a.signs + EPT * tid + 4 * g);
     }
-    const int e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
+    if constexpr (!ENV) e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
     const int cwk0 = min(j1 - j0, kSubChunk);
     // (every prefetch below is issued on every path, so no later wait has to
     //  assume that some of them were skipped; unused ones read valid addresses)
@@ -714,7 +906,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     int F0;
     const RotBuf rb{H, a.log2H, L.xs, L.limb};
     if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
-    else F0 = rotate_small(rb, a.x + (size_t)t * H, a.signs, wred);
+    else F0 = rotate_small(rb, xrow, a.signs, wred);
     float zacc = 0.f;                               // partial recovery sum for (zl, zg)
     if (j1 - j0 <= kSubChunk) {
       if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
@@ -813,9 +1005,8 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     const bool exact_step = a.k > 0 || RECX;   // the candidates' exact activations are used
     if (exact_step && q0 < q1) {
       uint4 xr[CH];
-      const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
-      for (int m = 0; m < CH; ++m) xr[m] = ld16c(xg + min(lane + 64 * m, H / 8 - 1));   // past H / 8: times zero rows
+      for (int m = 0; m < CH; ++m) xr[m] = x16(xrow, min(lane + 64 * m, H / 8 - 1));   // past H / 8: times zero rows
       exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag, [] {});
     }
     // candidate rows for z and the down projection: requested once the exact
@@ -962,7 +1153,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
                           (r > 0 ? rec[col] : 0.f);
           st_f(a.ypart + (size_t)p * H + 8 * ck0 + col, y);
         }
-        combine_cols(a, t, w, ck0, nck, &s_flag, tag);
+        combine_cols(a, t, w, ck0, nck, &s_flag, tag, ENV ? L.rw : nullptr);
       }
       continue;
     }
@@ -1013,12 +1204,12 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     }
 
     // ---- phase C: down projection over kept rows for this workgroup's output slices
-    phase_c(a, L, p, t, e, w, L.keep, L.hk, a.k, r > 0, &s_flag, tag);
+    phase_c(a, L, p, t, e, w, L.keep, L.hk, a.k, r > 0, &s_flag, tag, ENV ? L.rw : nullptr);
   }
   finish_launch(a, tag);
 }
 
-template <int EPT>
+template <int EPT, bool ENV>
 __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_flag;
@@ -1030,15 +1221,17 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
   for (int slot = blockIdx.x; slot < a.P * nw; slot += a.G) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
-    const int e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
+    int e;
+    if constexpr (ENV) e = env_route(a, L, t, p % a.K, w, tag);
+    else e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
+    const uint16_t* xrow = ENV ? L.xb : a.x + (size_t)t * H;
     const int q0 = min(a.I, w * a.cpw), q1 = min(a.I, q0 + a.cpw);
     if (q0 < q1) {
       uint4 xr[CH];
-      const uint4* xg = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
       for (int m = 0; m < CH; ++m) {
         const int ci = lane + 64 * m;
-        xr[m] = ci < H / 8 ? ld16c(xg + ci) : make_uint4(0, 0, 0, 0);
+        xr[m] = ci < H / 8 ? x16(xrow, ci) : make_uint4(0, 0, 0, 0);
       }
       exact_rows<CH>(a, L, e, nullptr, q0, q1, xr, a.xh + (size_t)p * a.I, tag, [] {});
     }
@@ -1058,7 +1251,7 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
       }
     }
     __syncthreads();
-    phase_c(a, L, p, t, e, w, nullptr, L.hh, a.I, false, &s_flag, tag);
+    phase_c(a, L, p, t, e, w, nullptr, L.hh, a.I, false, &s_flag, tag, ENV ? L.rw : nullptr);
   }
   finish_launch(a, tag);
 }
@@ -1103,9 +1296,10 @@ int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream) {
   const int H = fa.H;
   const int ept = H >= 1024 ? H / 256 : 0;
   const void* fn = nullptr;
-#define CFM_PICK(E) fn = !SELECT ? reinterpret_cast<const void*>(&k_dense_fused<E>) \
-                       : fa.rec_exact ? reinterpret_cast<const void*>(&k_select_fused<E, true>) \
-                                      : reinterpret_cast<const void*>(&k_select_fused<E, false>)
+#define CFM_PICK3(E, V) fn = !SELECT ? reinterpret_cast<const void*>(&k_dense_fused<E, V>) \
+                           : fa.rec_exact ? reinterpret_cast<const void*>(&k_select_fused<E, true, V>) \
+                                          : reinterpret_cast<const void*>(&k_select_fused<E, false, V>)
+#define CFM_PICK(E) do { if (fa.env) CFM_PICK3(E, true); else CFM_PICK3(E, false); } while (0)
   switch (ept) {
     case 0: if (H == 512) CFM_PICK(2); else CFM_PICK(0); break;
     case 4: CFM_PICK(4); break;
@@ -1115,6 +1309,7 @@ int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream) {
     default: return set_error(CFM_EUNSUPPORTED, "hidden width not supported");
   }
 #undef CFM_PICK
+#undef CFM_PICK3
   if (lds > 163840) return set_error(CFM_EUNSUPPORTED, "shape needs more LDS than a workgroup has");
   if (lds > 65536)
     CFM_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -1144,21 +1339,33 @@ static void common_regions(ForwardPlan& p, Carve& cv) {
   p.off_seq = cv.take(4 * (size_t)kSeqSlots);
   p.off_err = cv.take(4);
   p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * kMaxNw);
+  p.off_xl = cv.take(8 * (size_t)std::max(p.T, 1) * p.E);   // router logits (envelope calls)
 }
 
-ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) {
+// With the envelope a workgroup waits for router logits computed by the other
+// workgroups of its token: when the grid is smaller than the slot count, it is
+// a whole number of tokens' slots (K nw), so that no token straddles two rounds
+// of the persistent loop.
+static void env_geometry(ForwardPlan& p) {
+  if (!p.env || p.P * p.nw <= p.G) return;
+  const int ut = p.K * p.nw;
+  p.G = std::max(ut, (p.G / ut) * ut);
+}
+
+ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool env) {
   ForwardPlan p{};
-  p.T = T; p.K = K; p.P = T * K; p.E = E; p.I = I; p.H = H; p.k = k; p.c = c; p.r = r;
+  p.T = T; p.K = K; p.P = T * K; p.E = E; p.I = I; p.H = H; p.k = k; p.c = c; p.r = r; p.env = env ? 1 : 0;
   fused_geometry(p, 256);
+  env_geometry(p);
   p.cw = (I + p.nw - 1) / p.nw;
   p.cpw = std::max(1, (c + p.nw - 1) / p.nw);
-  size_t off[20];
+  size_t off[24];
   // prefetch of the candidates' rows when every workgroup has at most one output
   // slice and the buffers fit
   const int nck = std::max(1, (H / 8) / p.nw);
   const bool pre_ok = nck <= 8 && k > 0 && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0));
-  p.pre = pre_ok && lds_layout(H, I, c, k, r, p.cpw, nck, off) <= 160 * 1024 ? nck : 0;
-  p.lds = lds_layout(H, I, c, k, r, p.cpw, p.pre, off);
+  p.pre = pre_ok && lds_layout(H, I, c, k, r, p.cpw, nck, off, p.env, E, K) <= 160 * 1024 ? nck : 0;
+  p.lds = lds_layout(H, I, c, k, r, p.cpw, p.pre, off, p.env, E, K);
   Carve cv;
   common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
@@ -1170,14 +1377,15 @@ ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r) 
   return p;
 }
 
-ForwardPlan dense_plan(int T, int K, int E, int I, int H) {
+ForwardPlan dense_plan(int T, int K, int E, int I, int H, bool env) {
   ForwardPlan p{};
-  p.T = T; p.K = K; p.P = T * K; p.E = E; p.I = I; p.H = H; p.k = 0; p.c = 0; p.r = 0;
+  p.T = T; p.K = K; p.P = T * K; p.E = E; p.I = I; p.H = H; p.k = 0; p.c = 0; p.r = 0; p.env = env ? 1 : 0;
   fused_geometry(p, 256);
+  env_geometry(p);
   p.cw = 1;
   p.cpw = std::max(1, (I + p.nw - 1) / p.nw);
-  size_t off[20];
-  p.lds = lds_layout(H, I, 0, 0, 0, p.cpw, 0, off);
+  size_t off[24];
+  p.lds = lds_layout(H, I, 0, 0, 0, p.cpw, 0, off, p.env, E, K);
   Carve cv;
   common_regions(p, cv);
   const size_t Pz = (size_t)p.P;
@@ -1193,7 +1401,11 @@ ForwardPlan dense_plan(int T, int K, int E, int I, int H) {
 
 static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   FusedArgs a{};
-  a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
+  // (with the envelope x is formed in LDS; a.x still serves as a valid address
+  // for requests whose result is unused: Bt at rank 0, the A slice when it is
+  // not prefetched, so it points at the hidden states then)
+  a.x = s.x ? s.x : s.resid;
+  a.ids = s.ids; a.topk_w = s.topk_w;
   a.wg = s.w_gate; a.wu = s.w_up; a.wd = s.w_down_t;
   a.signs = s.signs; a.tg = s.tg; a.tu = s.tu; a.sg = s.sg; a.su = s.su;
   a.A = s.A; a.Bt = s.Bt;
@@ -1212,11 +1424,18 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.k = p.k; a.c = p.c; a.r = p.r; a.nw = p.nw; a.cw = p.cw; a.cpw = p.cpw; a.nhs = p.nhs; a.G = p.G;
   a.pre = p.pre;
   a.rec_exact = (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
+  a.env = p.env;
+  a.renorm = s.renorm;
+  a.eps = s.eps;
+  a.resid = s.resid; a.gamma = s.gamma; a.wr = s.wr;
+  a.xl = reinterpret_cast<uint64_t*>(s.ws + p.off_xl);
+  a.ids_out = s.ids_out; a.w_out = s.w_out; a.x_out = s.x_out;
   return a;
 }
 
 int launch_select_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t stream) {
   const FusedArgs a = fused_args(s, p);
+  if (!a.x) return set_error(CFM_EINVAL, "select forward: no hidden states");
   int rc = launch_fused<true>(a, p.lds, stream);
   if (rc) return rc;
   if (s.stats) {
@@ -1229,6 +1448,7 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t
 
 int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t stream) {
   const FusedArgs a = fused_args(s, p);
+  if (!a.x) return set_error(CFM_EINVAL, "dense forward: no hidden states");
   int rc = launch_fused<false>(a, p.lds, stream);
   if (rc) return rc;
   if (s.stats) {

@@ -200,6 +200,47 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
                       size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_forward - the routed-expert block of one decode layer with its
+ * envelope, in one launch: the RMSNorm before it, the router, and the
+ * residual add after it (the pages measure MoE-block and whole-model decoding
+ * with routing in place: abstract). For each token t:
+ *   x[t]   = BF16( (h[t] s) norm_w ),  s = 1 / sqrt(mean_i h[t][i]^2 + eps)
+ *            (float32, one rounding);
+ *   l_e    = W_r[e] . x[t] (float32 accumulation), p = softmax(l) over E;
+ *   ids[t] = the K experts of largest p in descending order (lower id first
+ *            on ties), w[t] = their p, divided by their sum if renorm != 0;
+ *   out[t] = BF16( h[t] + sum_q w[t][q] y_(t,q) ), y as in moe_select_forward
+ *            (or moe_select_forward_ex with flags) on x, ids, w.
+ *
+ *   h        : [T][H] BF16 hidden states (the residual stream); out may be h.
+ *   norm_w   : [H] BF16 RMSNorm weight. eps: 0 <= eps <= 1.
+ *   w_router : [E][H] BF16 router rows.
+ *   ids_out, w_out : optional out [T][K] int32 / float32, the routing used.
+ *   x_out    : optional out [T][H] BF16, the normalised states.
+ *   Every other argument as in moe_select_forward_ex; the workspace is
+ *   select_workspace(T, K, E, I, H, k, c, r) bytes, same rules.
+ * Supported: as moe_select_forward, and E <= 1024, K <= E. Runs the per-pair
+ * pass at every batch size.
+ */
+int moe_layer_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
+                      int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                      const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                      const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                      const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, unsigned flags,
+                      cfm_bf16* out, int32_t* ids_out, float* w_out, cfm_bf16* x_out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_dense_forward - the same envelope around the dense block
+ * (moe_dense_forward), the comparator. Workspace: dense_workspace(T, K, E, I, H).
+ * Supported: as moe_dense_forward, and E <= 1024, K <= E.
+ */
+int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
+                            int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                            const cfm_bf16* w_down_t, int E, int I, int H, cfm_bf16* out, int32_t* ids_out,
+                            float* w_out, cfm_bf16* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * cfm_set_forward_path - which kernels serve moe_select_forward and
  * moe_dense_forward (process-wide; returns the previous setting, or CFM_EINVAL).
  *   0 automatic (default): the expert-grouped pass where the shape allows it

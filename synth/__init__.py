@@ -27,6 +27,7 @@ import numpy as np
 _T_GATE, _T_UP, _T_DOWN = 1, 2, 3
 _T_SCALE_GATE, _T_SCALE_UP, _T_SCALE_DOWN = 4, 5, 6
 _T_X, _T_LOGITS, _T_SIGNS, _T_ZIPF_PERM, _T_ZIPF_DRAW = 7, 8, 9, 10, 11
+_T_ROUTER, _T_NORM, _T_RESID = 12, 13, 14
 
 
 def _rng(seed: int, layer: int, tensor: int, sub: int = 0) -> np.random.Generator:
@@ -155,6 +156,23 @@ def hidden_states(T: int, H: int, seed: int, layer: int = 0, rmsnorm: bool = Fal
     if rmsnorm and T > 0:
         z = z / np.sqrt(np.mean(z * z, axis=1, keepdims=True) + 1e-6)
     return f32_to_bf16_bits(z.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- decode-layer envelope inputs
+
+def router_weights(E: int, H: int, seed: int, layer: int = 0, sigma: float = 0.02) -> np.ndarray:
+    """Router rows W_r [E][H] BF16 bits, N(0, sigma)."""
+    return f32_to_bf16_bits((_rng(seed, layer, _T_ROUTER).standard_normal((E, H)) * sigma).astype(np.float32))
+
+
+def norm_weight(H: int, seed: int, layer: int = 0) -> np.ndarray:
+    """RMSNorm weight [H] BF16 bits, 1 + 0.1 N(0, 1)."""
+    return f32_to_bf16_bits((1.0 + 0.1 * _rng(seed, layer, _T_NORM).standard_normal(H)).astype(np.float32))
+
+
+def residual_states(T: int, H: int, seed: int, layer: int = 0, scale: float = 1.0) -> np.ndarray:
+    """The residual stream entering a decode layer's MoE block, [T][H] BF16 bits, N(0, scale^2)."""
+    return f32_to_bf16_bits((scale * _rng(seed, layer, _T_RESID).standard_normal((T, H))).astype(np.float32))
 
 
 def routing(T: int, E: int, K: int, seed: int, layer: int = 0, zipf: float | None = None):

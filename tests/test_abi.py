@@ -171,3 +171,36 @@ def test_workspace_covers_both_passes(lib):
     assert many > 16 * 8 * 768 * (8 + 4 + 4 + 2)      # per-pair exchange words plus grouped activations
     assert many > one
     assert lib.dense_workspace(16, 8, 128, 768, 2048) > 16 * 8 * 768 * 8
+
+
+def _layer(lib, E=8, K=2, eps=1e-6, ptr=FAKE, T=1, wsb=1 << 40, flags=0):
+    f = lib.moe_layer_forward
+    f.restype = ctypes.c_int
+    P = ptr
+    return f(P, P, ctypes.c_float(eps), P, 0, T, K, P, P, P, E, 128, 256, P, P, P, P, P, P, P, 23, 46, 8,
+             ctypes.c_uint(flags), P, None, None, None, FAKE, ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=2048), EUNSUP),          # the envelope's router covers at most 1024 experts
+    (dict(E=4, K=5), EUNSUP),        # K > E
+    (dict(eps=-1.0), EINVAL),
+    (dict(eps=float("nan")), EINVAL),
+    (dict(ptr=None), EINVAL),
+    (dict(flags=4), EINVAL),
+    (dict(wsb=16), EWS),
+    (dict(T=0, ptr=None), OK),
+])
+def test_layer_forward_rejects(lib, kw, code):
+    assert _layer(lib, **kw) == code
+
+
+def test_layer_dense_forward_rejects(lib):
+    f = lib.moe_layer_dense_forward
+    f.restype = ctypes.c_int
+    P = FAKE
+    args = lambda eps, wsb: (P, P, ctypes.c_float(eps), P, 0, 1, 2, P, P, P, 8, 128, 256, P, None, None, None, P,
+                             ctypes.c_size_t(wsb), None)
+    assert f(*args(-1.0, 1 << 40)) == EINVAL
+    assert f(*args(1e-6, 16)) == EWS
+

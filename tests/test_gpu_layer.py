@@ -1,0 +1,191 @@
+"""GPU parity of the decode-layer envelope (moe_layer_forward,
+moe_layer_dense_forward): RMSNorm, router and residual add fused around the
+routed-expert block in one launch.
+
+Staged comparison, step by step on the device's own intermediate values:
+  * the normalised states x_out against the oracle's RMSNorm (equal bits, or
+    one BF16 ulp apart where float32 and float64 round differently);
+  * the routing (ids_out, w_out) against the oracle's router run on x_out
+    (equal, up to near-ties of the logits; weights to float32 rounding);
+  * the block on (x_out, ids_out, w_out) through the plain entry point (forced
+    onto the per-pair pass, which the envelope uses at every batch size),
+    against the oracle with the usual set and output bars;
+  * the layer output against that block output plus the residual, one rounding
+    each (and the residual must matter).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cfm_oracle as O
+from gpu_util import DevLayer, custom_workload, dev, down_bf16, log, oracle_map, up, up_bf16, upload
+from parity import OUT_TOL, rel_l2
+from test_gpu_parity import compare_forward, gpu_sketch, run_select
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def cfm():
+    import calibration_free_channel_amd as m
+    return m
+
+
+def _envelope_inputs(wl, sigma_router):
+    T, E, H = wl.T, wl.shape.E, wl.shape.H
+    h = synth.residual_states(T, H, wl.seed + 100)
+    g = synth.norm_weight(H, wl.seed + 100)
+    wr = synth.router_weights(E, H, wl.seed + 100, sigma=sigma_router)
+    return h, g, wr
+
+
+def _run_layer(cfm, L, sk, h, g, wr, A, Bt, renorm, recovery="sketch", dense=False):
+    wl = L.wl
+    T, K, H = wl.T, wl.shape.K, wl.shape.H
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev())
+    w = torch.empty((T, K), dtype=torch.float32, device=dev())
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev())
+    if dense:
+        out = cfm.moe_layer_dense_forward(up_bf16(h), up_bf16(g), EPS, up_bf16(wr), K, L.wg, L.wu, L.wd,
+                                          renorm=renorm, ids_out=ids, w_out=w, x_out=x)
+    else:
+        out = cfm.moe_layer_forward(up_bf16(h), up_bf16(g), EPS, up_bf16(wr), K, L.wg, L.wu, L.wd, L.signs, *sk, A,
+                                    Bt, wl.k, wl.c, wl.r, renorm=renorm, ids_out=ids, w_out=w, x_out=x,
+                                    recovery=recovery)
+    torch.cuda.synchronize()
+    return down_bf16(out), down_bf16(x), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_x(xg, h, g):
+    xo = O.rmsnorm(h, g, EPS)
+    diff = np.abs(xg.astype(np.int32) - xo.astype(np.int32))
+    n = int(np.sum(diff != 0))
+    log(f"  x: {n} of {xg.size} BF16 values one ulp from the oracle")
+    assert diff.max() <= 1 and n <= max(2, 0.01 * xg.size)
+
+
+def _check_routing(xg, wr, K, renorm, ids, w):
+    oids, ow, logits = O.router(xg, wr, K, renorm)
+    for t in range(ids.shape[0]):
+        if np.array_equal(ids[t], oids[t]):
+            assert np.allclose(w[t], ow[t], rtol=1e-5, atol=1e-7), f"token {t}: weights"
+            continue
+        # only near-ties of the logits may reorder or swap experts
+        lt = logits[t]
+        bad = [e for e in set(ids[t]) ^ set(oids[t]) if abs(lt[e] - lt[oids[t, K - 1]]) > 1e-4 * np.abs(lt).max()]
+        assert not bad, f"token {t}: routing differs beyond near-ties: {ids[t]} vs {oids[t]}"
+        for q in range(K):
+            if ids[t, q] != oids[t, q]:
+                assert abs(lt[ids[t, q]] - lt[oids[t, q]]) <= 1e-4 * np.abs(lt).max()
+
+
+def _staged_layer(L, xg, ids, w):
+    """The same layer with the device's x and routing as the block's inputs."""
+    host = dataclasses.replace(L.host, x=xg, ids=ids.astype(np.int32), w=w.astype(np.float32))
+    return DevLayer(L.wl, host, L.wg, L.wu, L.wd, L.signs, up_bf16(xg), up(ids.astype(np.int32)),
+                    up(w.astype(np.float32)))
+
+
+def _check_residual(out, h, block):
+    o, hh, b = O.bf16_to_f64(out), O.bf16_to_f64(h), O.bf16_to_f64(block)
+    err = np.abs(o - (hh + b))
+    assert np.all(err <= 2.0 ** -8 * (np.abs(o) + np.abs(b)) + 1e-30), f"residual add: max err {err.max():.3e}"
+    assert rel_l2(out, block) > 0.05, "the residual should change the output"
+
+
+CASES = [
+    custom_workload("lay_tiny", 8, 2, 128, 256, 1, 23, 46, 8, 0, chan_scale=False),
+    custom_workload("lay_ragged", 6, 3, 101, 128, 5, 17, 33, 8, 5),
+    custom_workload("lay_h512_b16", 16, 4, 64, 512, 16, 12, 24, 8, 6),
+    custom_workload("lay_h2048", 32, 8, 96, 2048, 2, 17, 34, 16, 7),
+    custom_workload("lay_rounds", 8, 2, 32, 64, 150, 6, 12, 8, 8),    # 300 pairs: several rounds of workgroups
+]
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_layer_forward_staged(cfm, wl, renorm):
+    log(f"layer {wl.name} renorm={renorm}")
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    K = wl.shape.K
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    out, xg, ids, w = _run_layer(cfm, L, sk, h, g, wr, up_bf16(A), up_bf16(Bt), renorm)
+    _check_x(xg, h, g)
+    _check_routing(xg, wr, K, renorm, ids, w)
+    S = _staged_layer(L, xg, ids, w)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        block, cand, keep = run_select(cfm, S, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(S, A, Bt, block, cand, keep, wl.k, wl.c, what=f"{wl.name} block")
+    _check_residual(out, h, block)
+
+
+def test_layer_forward_candidates_exact(cfm):
+    wl = CASES[1]
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    out, xg, ids, w = _run_layer(cfm, L, sk, h, g, wr, up_bf16(A), up_bf16(Bt), False, recovery="candidates_exact")
+    S = _staged_layer(L, xg, ids, w)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        block, cand, keep = run_select(cfm, S, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r,
+                                       recovery="candidates_exact")
+    compare_forward(S, A, Bt, block, cand, keep, wl.k, wl.c, what="layer candidates_exact", recovery="candidates_exact")
+    _check_residual(out, h, block)
+
+
+@pytest.mark.parametrize("wl", [CASES[1], CASES[3], CASES[4]], ids=lambda w: w.name)
+def test_layer_dense_forward_staged(cfm, wl):
+    L = upload(wl)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    K = wl.shape.K
+    out, xg, ids, w = _run_layer(cfm, L, None, h, g, wr, None, None, True, dense=True)
+    _check_x(xg, h, g)
+    _check_routing(xg, wr, K, True, ids, w)
+    S = _staged_layer(L, xg, ids, w)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        block = down_bf16(cfm.moe_dense_forward(S.x, S.ids, S.w, L.wg, L.wu, L.wd))
+    want = O.dense_forward(xg, ids, w, L.host.w_gate, L.host.w_up, L.host.w_down_t)
+    errs = [rel_l2(block[t], want[t]) for t in range(wl.T)]
+    log(f"  dense block max rel L2 {max(errs):.3e}")
+    assert max(errs) <= OUT_TOL
+    _check_residual(out, h, block)
+
+
+def test_layer_all_kept_equals_layer_dense(cfm):
+    """k = c = I, r = 0: the selected layer reads every channel and equals the dense layer bit for bit."""
+    wl = custom_workload("lay_allkept", 8, 2, 128, 256, 4, 128, 128, 0, 14)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    a = _run_layer(cfm, L, sk, h, g, wr, None, None, False)
+    b = _run_layer(cfm, L, None, h, g, wr, None, None, False, dense=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_layer_in_place_and_deterministic(cfm):
+    """out may be h itself; two runs give the same bits."""
+    wl = CASES[2]
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    ref = _run_layer(cfm, L, sk, h, g, wr, up_bf16(A), up_bf16(Bt), False)
+    again = _run_layer(cfm, L, sk, h, g, wr, up_bf16(A), up_bf16(Bt), False)
+    for u, v in zip(ref, again):
+        assert np.array_equal(u, v)
+    hd = up_bf16(h)
+    cfm.moe_layer_forward(hd, up_bf16(g), EPS, up_bf16(wr), wl.shape.K, L.wg, L.wu, L.wd, L.signs, *sk,
+                          up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r, out=hd)
+    torch.cuda.synchronize()
+    assert np.array_equal(down_bf16(hd), ref[0])
