@@ -49,6 +49,10 @@ def parse():
                          "batches 1/4/8/16/32, budgets 10.8/13/18/53/67 %%")
     ap.add_argument("--olmoe", action="store_true",
                     help="instead of the default line: the OLMoE-1B-7B-shaped layer, 64 tokens, Zipf(1.1) experts")
+    ap.add_argument("--layer-stack", action="store_true",
+                    help="instead of the default line: the 48-layer stack run as a chained decode step with the "
+                         "envelope (RMSNorm, router, residual add) fused into each layer's launch, batches 1-32, "
+                         "18 %% budget, against the fused dense layer and an unfused torch envelope")
     ap.add_argument("--recovery", action="store_true",
                     help="instead of the default line: recovery rank sweep (r 0..128) of both recovery variants "
                          "at batch 1 and 16, 18 %% budget, with each output's deviation from the dense layer")
@@ -244,6 +248,74 @@ def stack(torch, cfm, args):
                       "rows": rows}), flush=True)
 
 
+def layer_stack(torch, cfm, args):
+    """One decode step through 48 independently drawn Qwen3-30B-A3B-shaped MoE blocks with their envelope:
+    h_(l+1) = h_l + block_l(RMSNorm_l(h_l)) with the router's top-8 routing, each layer one launch reading
+    the previous layer's output (a real chain, captured as one HIP graph). Compared with the same chain on
+    the dense block, and with an unfused envelope (torch RMSNorm, router matmul, softmax, top-k and add
+    around the plain selected entry point)."""
+    E, K, I, H, r = 128, 8, 768, 2048, 64
+    k, c = 138, 276
+    NL = 48
+    eps = 1e-6
+    layers = []
+    lr_ws = torch.empty(cfm.lowrank_workspace(E, I, H, r), dtype=torch.uint8, device="cuda")
+    t0 = time.perf_counter()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed * 131 + 7)
+    for l in range(NL):
+        wg, wu, wd, signs = make_layer(torch, args.seed + 3000, l, E, I, H)
+        sk = cfm.sketch_build(wg, wu, signs)
+        A, Bt = cfm.lowrank_build(wd, r, ws=lr_ws)
+        wr = torch.randn((E, H), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+        gam = (1.0 + 0.1 * torch.randn((H,), generator=g, device="cuda")).to(torch.bfloat16)
+        layers.append((wg, wu, wd, signs, sk, A, Bt, wr, gam))
+        if l % 8 == 7:
+            log(f"  {l + 1} layers built ({time.perf_counter() - t0:.0f} s)")
+    del lr_ws
+    torch.cuda.synchronize()
+    rows = []
+    for T in (1, 4, 8, 16, 32):
+        hs = torch.empty((NL + 1, T, H), dtype=torch.bfloat16, device="cuda")
+        hs[0] = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+        wss = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+        wsd = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+
+        def fused_sel(i):
+            wg, wu, wd, signs, sk, A, Bt, wr, gam = layers[i]
+            cfm.moe_layer_forward(hs[i], gam, eps, wr, K, wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=hs[i + 1], ws=wss)
+
+        def fused_dense(i):
+            wg, wu, wd, signs, sk, A, Bt, wr, gam = layers[i]
+            cfm.moe_layer_dense_forward(hs[i], gam, eps, wr, K, wg, wu, wd, out=hs[i + 1], ws=wsd)
+
+        def unfused_sel(i):
+            wg, wu, wd, signs, sk, A, Bt, wr, gam = layers[i]
+            x = torch.nn.functional.rms_norm(hs[i].float(), (H,), weight=gam.float(), eps=eps).to(torch.bfloat16)
+            p = torch.softmax((x @ wr.t()).float(), dim=-1)
+            w, ids = torch.topk(p, K, dim=-1)
+            y = cfm.moe_select_forward(x, ids.to(torch.int32), w.contiguous(), wg, wu, wd, signs, *sk, A, Bt, k, c,
+                                       r, ws=wss)
+            hs[i + 1].copy_(hs[i] + y)
+
+        res = {}
+        for name, fn in (("selected_fused", fused_sel), ("dense_fused", fused_dense), ("selected_unfused", unfused_sel)):
+            with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+                for i in range(NL):
+                    fn(i)
+                ms, _ = timed_graph(torch, fn, NL)
+            res[name] = round(ms * 1e3 / (NL * T), 3)
+        row = {"T": T, "us_per_token_per_layer": res,
+               "speedup_fused_vs_dense": round(res["dense_fused"] / res["selected_fused"], 3),
+               "fused_vs_unfused_envelope": round(res["selected_unfused"] / res["selected_fused"], 3)}
+        rows.append(row)
+        log(f"layer stack T={T}: {row}")
+        del hs, wss, wsd
+    print(json.dumps({"workload": "48-layer chained decode step, Qwen3-30B-A3B-shaped MoE blocks (H 2048, E 128, "
+                                  "top-8, I 768) with RMSNorm, router and residual add; k 138 c 276 r 64",
+                      "data": "synthetic", "rows": rows}), flush=True)
+
+
 def recovery_sweep(torch, cfm, args):
     """Recovery rank r and the two recovery variants (every skipped channel through the map with its
     sketch activation, or the dropped candidates with their exact activation) on the Qwen3-30B-A3B-shaped
@@ -392,6 +464,9 @@ def main():
         return
     if args.recovery:
         recovery_sweep(torch, cfm, args)
+        return
+    if args.layer_stack:
+        layer_stack(torch, cfm, args)
         return
     if args.olmoe:
         olmoe(torch, cfm, args)

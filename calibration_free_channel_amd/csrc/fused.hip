@@ -178,9 +178,10 @@ struct FusedArgs {
   // decode-layer envelope (env != 0): x = RMSNorm(resid) computed in the
   // launch, routing from the router rows wr, resid added to the output
   int env, renorm;
+  int env_pair;      // the router logits are computed by each pair's own workgroups (else shared by the token's)
   float eps;
   const uint16_t *resid, *gamma, *wr;
-  uint64_t* xl;      // [T][E] router logits (tagged)
+  uint64_t* xl;      // [T or P][E] router logits (tagged), per token or per pair
   int32_t* ids_out;  // [T][K] (optional)
   float* w_out;      // [T][K] (optional)
   uint16_t* x_out;   // [T][H] (optional)
@@ -698,9 +699,11 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // one of its pairs (slot q, workgroup w of the pair):
 //   x = RMSNorm(h[t]) into L.xb: BF16 of (h s) g in float32, one rounding,
 //       s = 1 / sqrt(mean(h^2) + eps);
-//   the router logits W_r[e] . x of experts u, u + UT, ... (u = q nw + w,
-//       UT = K nw: the token's workgroups share its E logits), published as
-//       tagged words, then all E read back;
+//   the router logits W_r[e] . x of experts u, u + UT, ..., published as
+//       tagged words, then all E read back. The workgroups that share them:
+//       the pair's own (u = w, UT = nw; they sit on one XCD, so no pair waits
+//       for a later-starting XCD) when that leaves at most one logit to each
+//       wavefront, else all of the token's (u = q nw + w, UT = K nw);
 //   softmax over the E logits; the K most probable experts in descending
 //       probability, lower id first on ties, into L.rid, their probabilities
 //       (renormalised to sum 1 if asked) into L.rw.
@@ -710,7 +713,8 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, E = a.E, K = a.K;
   const int nch = H / 8;                                  // 16-byte chunks of a row (H >= 64)
-  const int UT = K * a.nw, u = q * a.nw + w;
+  const int UT = a.env_pair ? a.nw : K * a.nw, u = a.env_pair ? w : q * a.nw + w;
+  uint64_t* xl = a.xl + (size_t)(a.env_pair ? t * K + q : t) * E;   // this group's logits
   const int nlog = u < E ? (E - u + UT - 1) / UT : 0;     // logits this workgroup computes
   float* red = L.red;                                     // scratch (free until the screen)
   const uint4* xb4 = reinterpret_cast<const uint4*>(L.xb);
@@ -767,7 +771,7 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
     }
     for (int ci = lane + 64 * RP; ci < nch; ci += 64) d = dot8_bf16(ld16c(row + ci), xb4[ci], d);
     d = wave_sum_f(d);
-    if (lane == 0) put_tagged(a.xl + (size_t)t * E + u + UT * i, d, tag);
+    if (lane == 0) put_tagged(xl + u + UT * i, d, tag);
   }
   // all E logits of the token (thread: indices [i0, i0 + cnt), E <= 4 NT)
   int cnt;
@@ -775,7 +779,7 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
   uint32_t keys[4];
   float lv[4];
   {
-    const uint64_t* src = a.xl + (size_t)t * E + i0;
+    const uint64_t* src = xl + i0;
     uint64_t raw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
@@ -1339,7 +1343,7 @@ static void common_regions(ForwardPlan& p, Carve& cv) {
   p.off_seq = cv.take(4 * (size_t)kSeqSlots);
   p.off_err = cv.take(4);
   p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * kMaxNw);
-  p.off_xl = cv.take(8 * (size_t)std::max(p.T, 1) * p.E);   // router logits (envelope calls)
+  p.off_xl = cv.take(8 * (size_t)std::max(p.P, 1) * p.E);   // router logits (envelope calls)
 }
 
 // With the envelope a workgroup waits for router logits computed by the other
@@ -1425,6 +1429,7 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.pre = p.pre;
   a.rec_exact = (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
   a.env = p.env;
+  a.env_pair = p.E <= 4 * p.nw ? 1 : 0;      // one logit per wavefront at most
   a.renorm = s.renorm;
   a.eps = s.eps;
   a.resid = s.resid; a.gamma = s.gamma; a.wr = s.wr;
