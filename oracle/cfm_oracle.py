@@ -475,9 +475,12 @@ def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=R
     are read only when their exact activations are used: to rank them for
     the kept set (k > 0) or, in the candidates_exact recovery variant, as the
     dropped candidates' recovery coefficients. With k = 0 and the default
-    recovery nothing reads them.
+    recovery nothing reads them. With the variant and c = I every channel is
+    a candidate, so no sketch activation enters the result and the sketch is
+    not read.
     """
     exact_step = k > 0 or recovery == RECOVERY_CANDIDATES_EXACT
+    sketch_read = not (recovery == RECOVERY_CANDIDATES_EXACT and c >= I)
     T, K = ids.shape
     total = 0
     for e in sorted(set(int(v) for v in ids.reshape(-1))):
@@ -489,7 +492,8 @@ def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=R
             nk = len(set().union(*[set(map(int, keep_sets[p])) for p in pairs]))
         if not exact_step:
             nc = 0
-        total += 2 * (I * H // 4) + 2 * 4 * I + 2 * H * r + 2 * I * r + 4 * H * nc + 2 * H * nk
+        sketch = 2 * (I * H // 4) + 2 * 4 * I if sketch_read else 0
+        total += sketch + 2 * H * r + 2 * I * r + 4 * H * nc + 2 * H * nk
     return total + 2 * T * H + 8 * T * K + 2 * T * H
 
 

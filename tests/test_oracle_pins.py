@@ -460,6 +460,19 @@ def test_read_bytes_candidate_rows_only_when_exact_activations_are_used():
     assert O.read_bytes(ids, 4, I, H, 3, c, r) == O.read_bytes(ids, 4, I, H, 3, c, r, recovery="candidates_exact")
 
 
+def test_read_bytes_no_sketch_when_every_channel_is_a_candidate():
+    """The variant with c = I uses no sketch activation: the sketch is not billed (the default still is)."""
+    ids = np.arange(2, dtype=np.int32)[None]
+    I, H, r, k = 64, 128, 4, 10
+    sk = 2 * (I * H // 4) + 8 * I
+    rest = 2 * H * r + 2 * I * r + 4 * H * I + 2 * H * k
+    io = 2 * H + 8 * 2 + 2 * H
+    assert O.read_bytes(ids, 4, I, H, k, I, r, recovery="candidates_exact") == 2 * rest + io
+    assert O.read_bytes(ids, 4, I, H, k, I, r) == 2 * (sk + rest) + io
+    assert O.read_bytes(ids, 4, I, H, k, I - 1, r, recovery="candidates_exact") == \
+        2 * (sk + rest - 4 * H) + io
+
+
 # ----------------------------------------------------------------------------- decode-layer envelope
 
 def _bf16_bits_of(t):
