@@ -895,54 +895,60 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       for (int g = 0; g < EPT / 4; ++g) sq[g] = *reinterpret_cast<const uint32_t*>(a.signs + EPT * tid + 4 * g);
     }
     if constexpr (!ENV) e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
-    const int cwk0 = min(j1 - j0, kSubChunk);
-    // (every prefetch below is issued on every path, so no later wait has to
-    //  assume that some of them were skipped; unused ones read valid addresses)
-    uint4 spre[kSketchPre];
-#pragma unroll
-    for (int u = 0; u < kSketchPre; ++u) spre[u] = sketch_item(a, e, j0, cwk0, min(u, (H + 255) / 256 - 1));
-    // (loads below are unconditional at clamped addresses, masked afterwards)
-    float2 sgu = load_scale(a, e, j0, cwk0);
-    constexpr int kBtPer = kMaxRank * kSubChunk / NT;   // Bt values per thread and sub-chunk (<= 16)
-    uint32_t btv[kBtPer];
-    load_bt(a, e, j0, cwk0, zl, zg, groups, btv);
-    // ---- phase A: screen this workgroup's channels, sub-chunk by sub-chunk
-    int F0;
-    const RotBuf rb{H, a.log2H, L.xs, L.limb};
-    if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
-    else F0 = rotate_small(rb, xrow, a.signs, wred);
-    float zacc = 0.f;                               // partial recovery sum for (zl, zg)
-    if (j1 - j0 <= kSubChunk) {
-      if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
-    } else {
-      // several sub-chunks: the next one's rows are requested before this one is
-      // screened (unconditionally inside the loop; the last one is peeled)
-      const int nsb = (H + 255) / 256;
-      int sj0 = j0;
-      for (; sj0 + kSubChunk < j1; sj0 += kSubChunk) {
-        const int nj0 = sj0 + kSubChunk, ncwk = min(j1 - nj0, kSubChunk);
-        uint4 snext[kSketchPre];
-#pragma unroll
-        for (int u = 0; u < kSketchPre; ++u) snext[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
-        const float2 nsgu = load_scale(a, e, nj0, ncwk);
-        uint32_t nbtv[kBtPer];
-        load_bt(a, e, nj0, ncwk, zl, zg, groups, nbtv);
-        screen_and_sum<EPT>(a, L, p, e, sj0, kSubChunk, F0, spre, sgu, btv, zg, groups, zacc, tag);
-#pragma unroll
-        for (int u = 0; u < kSketchPre; ++u) spre[u] = snext[u];
-        sgu = nsgu;
-#pragma unroll
-        for (int u = 0; u < kBtPer; ++u) btv[u] = nbtv[u];
+    // with the recovery variant and every channel a candidate no sketch
+    // activation enters the result: the screen is skipped (ĥ = 0, zero recovery
+    // sums, every channel a candidate) and the sketch is not read
+    const bool nosk = RECX && a.c >= a.I;
+    if (!nosk) {
+      const int cwk0 = min(j1 - j0, kSubChunk);
+      // (every prefetch below is issued on every path, so no later wait has to
+      //  assume that some of them were skipped; unused ones read valid addresses)
+      uint4 spre[kSketchPre];
+  #pragma unroll
+      for (int u = 0; u < kSketchPre; ++u) spre[u] = sketch_item(a, e, j0, cwk0, min(u, (H + 255) / 256 - 1));
+      // (loads below are unconditional at clamped addresses, masked afterwards)
+      float2 sgu = load_scale(a, e, j0, cwk0);
+      constexpr int kBtPer = kMaxRank * kSubChunk / NT;   // Bt values per thread and sub-chunk (<= 16)
+      uint32_t btv[kBtPer];
+      load_bt(a, e, j0, cwk0, zl, zg, groups, btv);
+      // ---- phase A: screen this workgroup's channels, sub-chunk by sub-chunk
+      int F0;
+      const RotBuf rb{H, a.log2H, L.xs, L.limb};
+      if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
+      else F0 = rotate_small(rb, xrow, a.signs, wred);
+      float zacc = 0.f;                               // partial recovery sum for (zl, zg)
+      if (j1 - j0 <= kSubChunk) {
+        if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
+      } else {
+        // several sub-chunks: the next one's rows are requested before this one is
+        // screened (unconditionally inside the loop; the last one is peeled)
+        const int nsb = (H + 255) / 256;
+        int sj0 = j0;
+        for (; sj0 + kSubChunk < j1; sj0 += kSubChunk) {
+          const int nj0 = sj0 + kSubChunk, ncwk = min(j1 - nj0, kSubChunk);
+          uint4 snext[kSketchPre];
+  #pragma unroll
+          for (int u = 0; u < kSketchPre; ++u) snext[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
+          const float2 nsgu = load_scale(a, e, nj0, ncwk);
+          uint32_t nbtv[kBtPer];
+          load_bt(a, e, nj0, ncwk, zl, zg, groups, nbtv);
+          screen_and_sum<EPT>(a, L, p, e, sj0, kSubChunk, F0, spre, sgu, btv, zg, groups, zacc, tag);
+  #pragma unroll
+          for (int u = 0; u < kSketchPre; ++u) spre[u] = snext[u];
+          sgu = nsgu;
+  #pragma unroll
+          for (int u = 0; u < kBtPer; ++u) btv[u] = nbtv[u];
+        }
+        screen_and_sum<EPT>(a, L, p, e, sj0, j1 - sj0, F0, spre, sgu, btv, zg, groups, zacc, tag);
       }
-      screen_and_sum<EPT>(a, L, p, e, sj0, j1 - sj0, F0, spre, sgu, btv, zg, groups, zacc, tag);
-    }
-    if (r > 0) {
-      if (zg < groups) L.red[zg * r + zl] = zacc;
-      __syncthreads();
-      for (int l = tid; l < r; l += NT) {
-        float s = 0.f;
-        for (int g = 0; g < groups; ++g) s += L.red[g * r + l];
-        put_tagged(a.xz + ((size_t)p * nw + w) * r + l, s, tag);
+      if (r > 0) {
+        if (zg < groups) L.red[zg * r + zl] = zacc;
+        __syncthreads();
+        for (int l = tid; l < r; l += NT) {
+          float s = 0.f;
+          for (int g = 0; g < groups; ++g) s += L.red[g * r + l];
+          put_tagged(a.xz + ((size_t)p * nw + w) * r + l, s, tag);
+        }
       }
     }
 
@@ -957,7 +963,14 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     }
 
     // ---- top-c candidates (identical in every workgroup of the pair)
-    {
+    if (nosk) {
+      for (int i = tid; i < a.I; i += NT) {
+        L.hh[i] = 0.f;
+        L.candp[i] = i;
+      }
+      for (int i = tid; i < groups * r; i += NT) L.red[NT + i] = 0.f;
+      __syncthreads();
+    } else {
       int cnt;
       const int i0 = topk_range<NT>(a.I, &cnt);
       const uint64_t* src = a.xh + (size_t)p * a.I + i0;
@@ -1263,7 +1276,7 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
 // ------------------------------------------------------------------ stats
 
 __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, int c, int r, int T,
-                        int K, int select, int exact_step, cfm_stats* st) {
+                        int K, int select, int exact_step, int sketch_read, cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   unsigned used = 0;
   for (int pp = 0; pp < P; ++pp) {
@@ -1277,7 +1290,7 @@ __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, i
   s.bytes_dense_equiv = (uint64_t)used * 6ull * I * H + s.bytes_io;
   s.experts_used = used;
   if (select) {
-    s.bytes_sketch = Pu * (2ull * I * (H / 4) + 8ull * I);
+    s.bytes_sketch = sketch_read ? Pu * (2ull * I * (H / 4) + 8ull * I) : 0;
     s.bytes_candidates = exact_step ? Pu * 4ull * H * c : 0;
     s.bytes_down = Pu * 2ull * H * k;
     s.bytes_recovery = r > 0 ? Pu * (2ull * H * r + 2ull * I * r) : 0;
@@ -1445,7 +1458,8 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
-                       p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0, static_cast<cfm_stats*>(s.stats));
+                       p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0,
+                       (a.rec_exact && p.c >= p.I) ? 0 : 1, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;
@@ -1458,7 +1472,7 @@ int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t 
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.I, p.I, 0,
-                       p.T, p.K, 0, 1, static_cast<cfm_stats*>(s.stats));
+                       p.T, p.K, 0, 1, 0, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;

@@ -130,3 +130,29 @@ def test_default_flags_match_plain_entry_point(cfm):
     assert rc == 0
     torch.cuda.synchronize()
     assert np.array_equal(down_bf16(out), a)
+
+
+def test_candidates_exact_every_channel_a_candidate_reads_no_sketch(cfm):
+    """c = I with the variant: the per-pair pass skips the screen; its bytes leave out the sketch, and its
+    output matches the grouped pass (which screens anyway) and the oracle."""
+    wl = custom_workload("rx_nosk", 4, 2, 64, 128, 6, 20, 64, 8, 34)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, 8, range(4), 4, 64, 128)
+    A, Bt = up_bf16(A), up_bf16(Bt)
+    with cfm.forward_path(PATHS["per_pair"]):
+        got, cand, keep, st = run_select(cfm, L, sk, A, Bt, 20, 64, 8, stats=True, recovery=EXACT)
+    assert st["bytes_sketch"] == 0
+    # (the per-pair pass bills every pair on its own; compared on a token whose experts are distinct)
+    L1 = upload(custom_workload("rx_nosk1", 4, 2, 64, 128, 1, 20, 64, 8, 35))
+    with cfm.forward_path(PATHS["per_pair"]):
+        *_, st1 = run_select(cfm, L1, gpu_sketch(cfm, L1), A, Bt, 20, 64, 8, stats=True, recovery=EXACT)
+    tot = sum(st1[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
+    assert tot == O.read_bytes(L1.host.ids, 4, 64, 128, 20, 64, 8, recovery=EXACT)
+    with cfm.forward_path(PATHS["grouped"]):
+        gg, gc, gk = run_select(cfm, L, sk, A, Bt, 20, 64, 8, recovery=EXACT)
+    assert np.array_equal(cand, gc)
+    for t in range(wl.T):
+        assert rel_l2(got[t], gg[t]) <= 1e-2
+    Ah, Bh = oracle_map(L.host.w_down_t, 8, range(4), 4, 64, 128)
+    compare_forward(L, Ah, Bh, got, cand, keep, 20, 64, what="rx_nosk", recovery=EXACT)
