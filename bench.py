@@ -365,9 +365,35 @@ def recovery_sweep(torch, cfm, args):
                 rows.append(row)
                 log(f"recovery sweep: {row}")
             del maps, wss, out
+        # every channel a candidate (53 % budget, k 407, c = I): the variant needs no sketch
+        kb, cb, rb = 407, I, 64
+        maps = [cfm.lowrank_build(b[2], rb) for b in base]
+        wss = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, kb, cb, rb), "cuda")
+        out = torch.empty((n, T, H), dtype=torch.bfloat16, device="cuda")
+        for rec in (cfm.RECOVER_SKETCH, cfm.RECOVER_CANDIDATES_EXACT):
+            def selb(i, rec=rec):
+                wg, wu, wd, signs, sk = base[i % NL]
+                A, Bt = maps[i % NL]
+                cfm.moe_select_forward(x[i], ids[i], w[i], wg, wu, wd, signs, *sk, A, Bt, kb, cb, rb,
+                                       out=out[i], ws=wss, recovery=rec)
+            with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+                for i in range(n):
+                    selb(i)
+                torch.cuda.synchronize()
+                dev_ = ((out.float() - ref).norm(dim=-1) / ref.norm(dim=-1)).flatten()
+                ms_s, _ = timed_graph(torch, selb, n)
+            row = {"T": T, "r": rb, "k": kb, "c": cb, "recovery": rec,
+                   "us_per_token": round(ms_s * 1e3 / (n * T), 3),
+                   "dense_us_per_token": round(ms_d * 1e3 / (n * T), 3),
+                   "rel_l2_vs_dense_mean": round(float(dev_.mean()), 4),
+                   "rel_l2_vs_dense_max": round(float(dev_.max()), 4)}
+            rows.append(row)
+            log(f"recovery sweep: {row}")
+        del maps, wss, out
         del wsd, dense_out, x, ids, w
     print(json.dumps({"workload": "recovery rank sweep on the Qwen3-30B-A3B-shaped layer (H 2048, E 128, top-8, "
-                                  "I 768), k 138, c 276", "data": "synthetic", "rows": rows}), flush=True)
+                                  "I 768), k 138, c 276; and k 407, c = I", "data": "synthetic", "rows": rows}),
+          flush=True)
 
 
 def olmoe(torch, cfm, args):
