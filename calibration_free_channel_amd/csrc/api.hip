@@ -44,14 +44,14 @@ void timing_begin(const char* name, hipStream_t s) {
   if (!g_timing) return;
   g_open = name;
   g_open_ev = take_event();
-  if (g_open_ev) hipEventRecord(g_open_ev, s);
+  if (g_open_ev) (void)hipEventRecord(g_open_ev, s);
 }
 
 void timing_end(hipStream_t s) {
   if (!g_timing || !g_open_ev) return;
   hipEvent_t b = take_event();
   if (!b) return;
-  hipEventRecord(b, s);
+  (void)hipEventRecord(b, s);
   g_pending.push_back({g_open, g_open_ev, b});
   g_open_ev = nullptr;
 }
@@ -265,12 +265,18 @@ int moe_layer_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, cons
   if (!w_gate || !w_up || !w_down_t || !signs || !tg || !tu || !sg || !su)
     return set_error(CFM_EINVAL, "moe_layer_forward: null pointer");
   if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_layer_forward: null A or Bt with r > 0");
+  bool grouped = false;
+  if (int rc = pick_grouped(T, K, E, I, H, r, false, &grouped)) return rc;
   const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r, true);
-  if (!ws || ws_bytes < plan.bytes)
+  const size_t need = grouped ? group_plan(T, K, E, I, H, k, c, r, false, plan.bytes).bytes : plan.bytes;
+  if (!ws || ws_bytes < need)
     return set_error(CFM_EWORKSPACE, "moe_layer_forward: workspace smaller than select_workspace()");
   SelectArgs a{nullptr, w_gate, w_up, w_down_t, A, Bt, nullptr, nullptr, signs, tg, tu, sg, su, out,
                nullptr, nullptr, nullptr, static_cast<char*>(ws), flags,
                h, norm_w, w_router, eps, renorm ? 1 : 0, ids_out, w_out, x_out};
+  if (grouped)
+    return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
+                                  static_cast<hipStream_t>(stream));
   return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
 }
 
@@ -284,12 +290,18 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
   if (T == 0) return CFM_OK;
   if (int rc = check_envelope(K, E, eps, h, norm_w, w_router, out)) return rc;
   if (!w_gate || !w_up || !w_down_t) return set_error(CFM_EINVAL, "moe_layer_dense_forward: null pointer");
+  bool grouped = false;
+  if (int rc = pick_grouped(T, K, E, I, H, 0, true, &grouped)) return rc;
   const ForwardPlan plan = dense_plan(T, K, E, I, H, true);
-  if (!ws || ws_bytes < plan.bytes)
+  const size_t need = grouped ? group_plan(T, K, E, I, H, I, I, 0, true, plan.bytes).bytes : plan.bytes;
+  if (!ws || ws_bytes < need)
     return set_error(CFM_EWORKSPACE, "moe_layer_dense_forward: workspace smaller than dense_workspace()");
   SelectArgs a{nullptr, w_gate, w_up, w_down_t, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                nullptr, nullptr, nullptr, out, nullptr, nullptr, nullptr, static_cast<char*>(ws), 0u,
                h, norm_w, w_router, eps, renorm ? 1 : 0, ids_out, w_out, x_out};
+  if (grouped)
+    return launch_grouped_forward(a, group_plan(T, K, E, I, H, I, I, 0, true, plan.bytes),
+                                  static_cast<hipStream_t>(stream));
   return launch_dense_forward(a, plan, static_cast<hipStream_t>(stream));
 }
 

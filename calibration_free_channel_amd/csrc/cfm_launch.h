@@ -80,6 +80,8 @@ struct GroupPlan {
   int IP;                 // row pitch of the union row lists (I rounded up to 8)
   int maxu, maxwork;      // bounds on used experts and screen work items (grid sizes)
   size_t off_uctr, off_kctr, off_octr;   // arrival counters (zero between calls)
+  size_t off_rctr;                       // router arrivals per token (zero between calls)
+  size_t off_xw, off_lg, off_idw, off_ww; // envelope: normalised states, logits, routing
   size_t off_meta, off_goff, off_gpl, off_gue, off_gux, off_gwork, off_gexw, off_xf0, off_xd, off_hs, off_zp,
       off_cm, off_cl, off_hx, off_km, off_hk, off_zf, off_yp, off_ucnt, off_dcnt, off_urows, off_drows;
   size_t bytes;           // end of the layout (including base)

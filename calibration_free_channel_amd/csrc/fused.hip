@@ -34,6 +34,7 @@
 
 #include "cfm_internal.h"
 #include "cfm_launch.h"
+#include "envelope.h"
 #include "rotate.h"
 #include "topk.h"
 
@@ -686,15 +687,6 @@ __device__ __forceinline__ uint4 x16(const uint16_t* row, int i) {
 
 // ------------------------------------------------------------------ decode-layer envelope
 
-// Order-preserving map of a finite float to an unsigned key.
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-  const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 // The envelope's first steps for token t, run by every workgroup that serves
 // one of its pairs (slot q, workgroup w of the pair):
 //   x = RMSNorm(h[t]) into L.xb: BF16 of (h s) g in float32, one rounding,
@@ -714,13 +706,10 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
   const int H = a.H, E = a.E, K = a.K;
   const int nch = H / 8;                                  // 16-byte chunks of a row (H >= 64)
   const int UT = a.env_pair ? a.nw : K * a.nw, u = a.env_pair ? w : q * a.nw + w;
-  uint64_t* xl = a.xl + (size_t)(a.env_pair ? t * K + q : t) * E;   // this group's logits
   const int nlog = u < E ? (E - u + UT - 1) / UT : 0;     // logits this workgroup computes
-  float* red = L.red;                                     // scratch (free until the screen)
-  const uint4* xb4 = reinterpret_cast<const uint4*>(L.xb);
-  // requests first: the first router row of each wavefront (chunks lane, lane + 64, ...),
-  // then the hidden state (chunks tid, tid + NT, ...)
-  constexpr int RP = 4;                                   // prefetched chunks per lane of the first row
+  uint64_t* xl = a.xl + (size_t)(a.env_pair ? t * K + q : t) * E;   // this group's logits
+  // requests first: the first router row of each wavefront (chunks lane, lane + 64, ...)
+  constexpr int RP = 4;
   uint4 rp[RP];
   {
     const bool has = wv < nlog;
@@ -731,52 +720,15 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
       rp[m] = (has && ci < nch) ? ld16c(row + ci) : make_uint4(0, 0, 0, 0);
     }
   }
-  const uint4* hrow = reinterpret_cast<const uint4*>(a.resid + (size_t)t * H);
-  const uint4* grow = reinterpret_cast<const uint4*>(a.gamma);
-  // mean square of the row
-  float ss = 0.f;
-  for (int ci = tid; ci < nch; ci += NT) {
-    const uint4 h4 = ld16c(hrow + ci);
-    const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = bf16lo(hw[i]), hi = bf16hi(hw[i]);
-      ss += lo * lo + hi * hi;
-    }
-  }
-  ss = wave_sum_f(ss);
-  if (lane == 0) red[wv] = ss;
-  __syncthreads();
-  const float sc = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + a.eps);
-  for (int ci = tid; ci < nch; ci += NT) {
-    const uint4 h4 = ld16c(hrow + ci), g4 = ld16c(grow + ci);
-    const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
-    const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(bf16lo(hw[i]) * sc * bf16lo(gw[i])) |
-             ((uint32_t)f32_to_bf16(bf16hi(hw[i]) * sc * bf16hi(gw[i])) << 16);
-    reinterpret_cast<uint4*>(L.xb)[ci] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-  __syncthreads();
+  env_normalise(a.resid + (size_t)t * H, a.gamma, H, a.eps, L.xb, L.red);
   // this workgroup's logits: wavefront v takes experts u + UT (v + 4 i)
   for (int i = wv; i < nlog; i += NT / 64) {
-    const uint4* row = reinterpret_cast<const uint4*>(a.wr + (size_t)(u + UT * i) * H);
-    float d = 0.f;
-#pragma unroll
-    for (int m = 0; m < RP; ++m) {
-      const int ci = lane + 64 * m;
-      if (ci < nch) d = dot8_bf16(i == wv ? rp[m] : ld16c(row + ci), xb4[ci], d);
-    }
-    for (int ci = lane + 64 * RP; ci < nch; ci += 64) d = dot8_bf16(ld16c(row + ci), xb4[ci], d);
-    d = wave_sum_f(d);
+    const float d = env_logit<RP>(a.wr + (size_t)(u + UT * i) * H, L.xb, H, rp, i == wv);
     if (lane == 0) put_tagged(xl + u + UT * i, d, tag);
   }
-  // all E logits of the token (thread: indices [i0, i0 + cnt), E <= 4 NT)
+  // all E logits of the group (thread: indices [i0, i0 + cnt), E <= 4 NT)
   int cnt;
   const int i0 = topk_range<NT>(E, &cnt);
-  uint32_t keys[4];
   float lv[4];
   {
     const uint64_t* src = xl + i0;
@@ -787,53 +739,16 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
     for (int j = 0; j < 4; ++j) {
       lv[j] = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
       if (j < cnt) L.rl[i0 + j] = lv[j];
-      keys[j] = j < cnt ? ordered_key(lv[j]) : 0u;
     }
   }
-  // softmax: the largest logit, then the sum of exp(l - max)
-  uint32_t km = 0u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) km = max(km, keys[j]);
-  km = wave_max_u32(km);
-  if (lane == 0) reinterpret_cast<uint32_t*>(red)[4 + wv] = km;
-  __syncthreads();
-  const uint32_t* rk = reinterpret_cast<const uint32_t*>(red) + 4;
-  const float lmax = key_value(max(max(rk[0], rk[1]), max(rk[2], rk[3])));
-  float se = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) se += j < cnt ? expf(lv[j] - lmax) : 0.f;
-  se = wave_sum_f(se);
-  if (lane == 0) red[8 + wv] = se;
-  // the K largest logits (ascending ids into L.rida; ends with a barrier)
-  block_topk<NT, 4>(keys, i0, cnt, E, K, L.rida, L.tks);
-  const float sum = red[8] + red[9] + red[10] + red[11];
-  // slot order: descending logit, lower id first on ties
-  if (tid < K) {
-    const int id = L.rida[tid];
-    const float l = L.rl[id];
-    int rank = 0;
-    for (int j = 0; j < K; ++j) {
-      const int o = L.rida[j];
-      const float lo = L.rl[o];
-      rank += (lo > l) || (lo == l && o < id);
-    }
-    L.rid[rank] = id;
-    L.rw[rank] = expf(l - lmax) / sum;
-  }
-  __syncthreads();
-  if (a.renorm) {
-    float ws = 0.f;
-    for (int j = 0; j < K; ++j) ws += L.rw[j];
-    __syncthreads();
-    if (tid < K) L.rw[tid] = L.rw[tid] / ws;
-    __syncthreads();
-  }
+  env_pick(lv, i0, cnt, L.rl, E, K, a.renorm, L.rida, L.rid, L.rw, L.red, L.tks);
   // the token's routing and normalised state, for the caller (first workgroup of its first pair)
   if (q == 0 && w == 0) {
     if (a.ids_out && tid < K) a.ids_out[(size_t)t * K + tid] = L.rid[tid];
     if (a.w_out && tid < K) a.w_out[(size_t)t * K + tid] = L.rw[tid];
     if (a.x_out)
-      for (int ci = tid; ci < nch; ci += NT) reinterpret_cast<uint4*>(a.x_out + (size_t)t * H)[ci] = xb4[ci];
+      for (int ci = tid; ci < nch; ci += NT)
+        reinterpret_cast<uint4*>(a.x_out + (size_t)t * H)[ci] = reinterpret_cast<const uint4*>(L.xb)[ci];
   }
   return __builtin_amdgcn_readfirstlane(L.rid[q]);
 }

@@ -43,6 +43,7 @@
 
 #include "cfm_internal.h"
 #include "cfm_launch.h"
+#include "envelope.h"
 #include "rotate.h"
 #include "topk.h"
 
@@ -136,6 +137,7 @@ struct GArgs {
   uint32_t* octr;     // [T][H / 64] pair outputs arrived per (token, column tile) (zero between calls)
   int T, K, P, E, I, H, log2H, k, c, r, ntile, nz, IW, nrb, IP, dense;
   int rec_exact;      // dropped candidates enter the recovery with their exact activation
+  const uint16_t* resid;   // decode-layer envelope: the residual stream added to the output, else null
 };
 
 // ------------------------------------------------------------------ block helpers
@@ -953,10 +955,78 @@ __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
           for (int q = 0; q < 8; ++q)
             if (q0 + q < K) sum += wq[q] * yv[q];
         }
+        if (a.resid) sum += bf16_to_f32(a.resid[(size_t)t * H + c0 + tid]);
         a.out[(size_t)t * H + c0 + tid] = f32_to_bf16(sum);
       }
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ stage 0 (envelope): router
+
+// The decode-layer envelope ahead of the grouped pass. Workgroup (t, b)
+// normalises token t (every workgroup of the token forms the same bits; the
+// first writes them out), computes the router logits of experts
+// [64 b, 64 b + 64) (16 per wavefront, one row each at a time) and stores
+// them; the last of the token's workgroups to finish reads its E logits and
+// forms the routing (softmax, top-K slot order, weights). The same helpers as
+// the per-pair kernel's envelope, so both passes route identically.
+struct RouteArgs {
+  const uint16_t *h, *gamma, *wr;
+  float eps;
+  int renorm, T, K, E, H, nb;
+  uint16_t* xw;        // [T][H] normalised states (BF16)
+  float* lg;           // [T][E] logits
+  int32_t* ids;        // [T][K] routing, slot order
+  float* w;            // [T][K] weights
+  uint32_t* rctr;      // [T] arrivals (zero between calls)
+  int32_t* ids_out;
+  float* w_out;
+  uint16_t* x_out;
+};
+constexpr int kRouteRows = 64;
+
+__global__ __launch_bounds__(GT) void k_g_route(RouteArgs a) {
+  __shared__ __align__(16) uint16_t xb[kMaxH];
+  __shared__ __align__(16) float rl[kEnvMaxE];
+  __shared__ __align__(16) float red[8];
+  __shared__ __align__(16) uint32_t tks[kTopkScratchWords];
+  __shared__ int32_t rida[kMaxK], rid[kMaxK];
+  __shared__ float rw[kMaxK];
+  __shared__ int s_flag;
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, E = a.E, K = a.K, nch = H / 8;
+  env_normalise(a.h + (size_t)t * H, a.gamma, H, a.eps, xb, red);
+  if (b == 0)
+    for (int ci = tid; ci < nch; ci += GT) {
+      const uint4 v = reinterpret_cast<const uint4*>(xb)[ci];
+      reinterpret_cast<uint4*>(a.xw + (size_t)t * H)[ci] = v;
+      if (a.x_out) reinterpret_cast<uint4*>(a.x_out + (size_t)t * H)[ci] = v;
+    }
+  const uint4 none[1] = {make_uint4(0, 0, 0, 0)};
+  for (int j = wv; j < kRouteRows; j += GT / 64) {
+    const int e = b * kRouteRows + j;
+    if (e < E) {
+      const float d = env_logit<1>(a.wr + (size_t)e * H, xb, H, none, false);
+      if (lane == 0) st_f(a.lg + (size_t)t * E + e, d);
+    }
+  }
+  if (!arrive_last(a.rctr + t, (uint32_t)a.nb, &s_flag)) return;
+  int cnt;
+  const int i0 = topk_range<GT>(E, &cnt);
+  float lv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lv[j] = j < cnt ? ld_f(a.lg + (size_t)t * E + i0 + j) : 0.f;
+    if (j < cnt) rl[i0 + j] = lv[j];
+  }
+  env_pick(lv, i0, cnt, rl, E, K, a.renorm, rida, rid, rw, red, tks);
+  if (tid < K) {
+    a.ids[(size_t)t * K + tid] = rid[tid];
+    a.w[(size_t)t * K + tid] = rw[tid];
+    if (a.ids_out) a.ids_out[(size_t)t * K + tid] = rid[tid];
+    if (a.w_out) a.w_out[(size_t)t * K + tid] = rw[tid];
   }
 }
 
@@ -1034,6 +1104,7 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   g.off_uctr = cv.take(4 * (size_t)E);
   g.off_kctr = cv.take(4 * (size_t)E);
   g.off_octr = cv.take(4 * (size_t)T * (H / kColTile));
+  g.off_rctr = cv.take(4 * (size_t)std::max(T, 1));
   g.off_meta = cv.take(16);
   g.off_goff = cv.take(4 * ((size_t)E + 1));
   g.off_gpl = cv.take(4 * P);
@@ -1056,6 +1127,10 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   g.off_dcnt = cv.take(4 * U);
   g.off_urows = cv.take(2 * U * g.IP);
   g.off_drows = cv.take(2 * U * g.IP);
+  g.off_xw = cv.take(2 * (size_t)T * H);
+  g.off_lg = cv.take(4 * (size_t)T * E);
+  g.off_idw = cv.take(4 * (size_t)T * K);
+  g.off_ww = cv.take(4 * (size_t)T * K);
   g.bytes = cv.off;
   return g;
 }
@@ -1063,6 +1138,25 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
 int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
   GArgs a{};
   a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
+  if (s.resid) {
+    // decode-layer envelope: the router first; the pass then reads the
+    // normalised states and the routing it wrote, and adds the residual
+    RouteArgs ra{};
+    ra.h = s.resid; ra.gamma = s.gamma; ra.wr = s.wr; ra.eps = s.eps; ra.renorm = s.renorm;
+    ra.T = g.T; ra.K = g.K; ra.E = g.E; ra.H = g.H; ra.nb = (g.E + kRouteRows - 1) / kRouteRows;
+    ra.xw = reinterpret_cast<uint16_t*>(s.ws + g.off_xw);
+    ra.lg = reinterpret_cast<float*>(s.ws + g.off_lg);
+    ra.ids = reinterpret_cast<int32_t*>(s.ws + g.off_idw);
+    ra.w = reinterpret_cast<float*>(s.ws + g.off_ww);
+    ra.rctr = reinterpret_cast<uint32_t*>(s.ws + g.off_rctr);
+    ra.ids_out = s.ids_out; ra.w_out = s.w_out; ra.x_out = s.x_out;
+    timing_begin("k_g_route", stream);
+    hipLaunchKernelGGL(k_g_route, dim3(g.T, ra.nb), dim3(GT), 0, stream, ra);
+    timing_end(stream);
+    CFM_LAUNCH_CHECK("k_g_route");
+    a.x = ra.xw; a.ids = ra.ids; a.topk_w = ra.w;
+    a.resid = s.resid;
+  }
   a.wg = s.w_gate; a.wu = s.w_up; a.wd = s.w_down_t;
   a.signs = s.signs; a.tg = s.tg; a.tu = s.tu; a.sg = s.sg; a.su = s.su;
   a.A = s.A; a.Bt = s.Bt;

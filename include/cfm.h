@@ -219,8 +219,10 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
  *   x_out    : optional out [T][H] BF16, the normalised states.
  *   Every other argument as in moe_select_forward_ex; the workspace is
  *   select_workspace(T, K, E, I, H, k, c, r) bytes, same rules.
- * Supported: as moe_select_forward, and E <= 1024, K <= E. Runs the per-pair
- * pass at every batch size.
+ * Supported: as moe_select_forward, and E <= 1024, K <= E. The pass is chosen
+ * as for moe_select_forward (cfm_set_forward_path): the per-pair kernel forms
+ * the envelope inside its one launch; the expert-grouped pass runs a router
+ * step first. Both form the same normalised states and routing.
  */
 int moe_layer_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
                       int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
