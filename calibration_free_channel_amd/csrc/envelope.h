@@ -107,19 +107,26 @@ __device__ __forceinline__ float env_logit(const uint16_t* wrow, const uint16_t*
   return env_wave_sum(d);
 }
 
-// The routing from the token's E logits (E <= kEnvMaxE): thread t holds lv[j]
-// for indices [i0, i0 + cnt) as given by topk_range, and rl (LDS) holds all E.
-// Writes the K experts in slot order to rid and their weights to rw (LDS).
-// Whole workgroup; rida: K ints of LDS; red: 8 floats of LDS (distinct from
-// what the caller still reads); tks: top-k scratch. Ends with a barrier.
-__device__ __forceinline__ void env_pick(const float (&lv)[4], int i0, int cnt, const float* rl, int E, int K,
-                                         int renorm, int32_t* rida, int32_t* rid, float* rw, float* red,
-                                         uint32_t* tks) {
+// The routing from the token's E logits, all in rl (LDS; E <= kEnvMaxE,
+// K <= 64): the softmax denominator (the largest logit, then the sum of
+// exp(l - max) over per-thread ranges and the four wavefronts in a fixed
+// order), the K largest logits by block_topk (ascending ids into rida), then
+// each one's slot by its rank (descending logit, lower id first on ties).
+// Writes the experts to rid and their weights to rw (LDS), renormalised to sum
+// 1 if asked. Whole workgroup: joins it before (rl complete) and after.
+// red: 8 floats of LDS scratch; rida: K ints; tks: top-k scratch.
+__device__ __forceinline__ void env_pick(const float* rl, int E, int K, int renorm, int32_t* rida, int32_t* rid,
+                                         float* rw, float* red, uint32_t* tks) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __syncthreads();
+  int cnt;
+  const int i0 = topk_range<kEnvNT>(E, &cnt);
+  float lv[4];
   uint32_t keys[4];
   uint32_t km = 0u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    lv[j] = j < cnt ? rl[i0 + j] : 0.f;
     keys[j] = j < cnt ? ordered_key(lv[j]) : 0u;
     km = max(km, keys[j]);
   }
@@ -136,7 +143,6 @@ __device__ __forceinline__ void env_pick(const float (&lv)[4], int i0, int cnt, 
   // the K largest logits, ascending ids (ends with a barrier)
   block_topk<kEnvNT, 4>(keys, i0, cnt, E, K, rida, tks);
   const float sum = red[4] + red[5] + red[6] + red[7];
-  // slot order: descending logit, lower id first on ties
   if (tid < K) {
     const int id = rida[tid];
     const float l = rl[id];

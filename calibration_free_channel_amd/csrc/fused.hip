@@ -688,26 +688,27 @@ __device__ __forceinline__ uint4 x16(const uint16_t* row, int i) {
 // ------------------------------------------------------------------ decode-layer envelope
 
 // The envelope's first steps for token t, run by every workgroup that serves
-// one of its pairs (slot q, workgroup w of the pair):
-//   x = RMSNorm(h[t]) into L.xb: BF16 of (h s) g in float32, one rounding,
-//       s = 1 / sqrt(mean(h^2) + eps);
-//   the router logits W_r[e] . x of experts u, u + UT, ..., published as
-//       tagged words, then all E read back. The workgroups that share them:
-//       the pair's own (u = w, UT = nw; they sit on one XCD, so no pair waits
-//       for a later-starting XCD) when that leaves at most one logit to each
-//       wavefront, else all of the token's (u = q nw + w, UT = K nw);
-//   softmax over the E logits; the K most probable experts in descending
-//       probability, lower id first on ties, into L.rid, their probabilities
-//       (renormalised to sum 1 if asked) into L.rw.
-// Every workgroup of the token forms the same L.xb, L.rid and L.rw (the same
-// arithmetic on the same values). Returns the expert of slot q.
-__device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t, int q, int w, uint32_t tag) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// one of its pairs (slot q, workgroup w of the pair), in two parts so that
+// work that needs no routing can run while the logits are exchanged:
+// env_begin forms x = RMSNorm(h[t]) into L.xb and publishes this workgroup's
+// router logits W_r[e] . x (experts u, u + UT, ...) as tagged words;
+// env_finish reads all E back and forms the routing (L.rid, L.rw) and returns
+// the expert of slot q. The workgroups that share the logits: the pair's own
+// (u = w, UT = nw; they sit on one XCD, so no pair waits for a later-starting
+// XCD) when that leaves at most one logit to each wavefront, else all of the
+// token's (u = q nw + w, UT = K nw). Every workgroup of the token forms the
+// same L.xb, L.rid and L.rw (the same arithmetic on the same values, shared
+// with the grouped pass's router step).
+__device__ __forceinline__ uint64_t* env_logits(const FusedArgs& a, int t, int q) {
+  return a.xl + (size_t)(a.env_pair ? t * a.K + q : t) * a.E;
+}
+__device__ __forceinline__ void env_begin(const FusedArgs& a, const Lds& L, int t, int q, int w, uint32_t tag) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, E = a.E, K = a.K;
   const int nch = H / 8;                                  // 16-byte chunks of a row (H >= 64)
   const int UT = a.env_pair ? a.nw : K * a.nw, u = a.env_pair ? w : q * a.nw + w;
   const int nlog = u < E ? (E - u + UT - 1) / UT : 0;     // logits this workgroup computes
-  uint64_t* xl = a.xl + (size_t)(a.env_pair ? t * K + q : t) * E;   // this group's logits
+  uint64_t* xl = env_logits(a, t, q);
   // requests first: the first router row of each wavefront (chunks lane, lane + 64, ...)
   constexpr int RP = 4;
   uint4 rp[RP];
@@ -726,22 +727,25 @@ __device__ __forceinline__ int env_route(const FusedArgs& a, const Lds& L, int t
     const float d = env_logit<RP>(a.wr + (size_t)(u + UT * i) * H, L.xb, H, rp, i == wv);
     if (lane == 0) put_tagged(xl + u + UT * i, d, tag);
   }
-  // all E logits of the group (thread: indices [i0, i0 + cnt), E <= 4 NT)
-  int cnt;
-  const int i0 = topk_range<NT>(E, &cnt);
-  float lv[4];
+}
+__device__ __forceinline__ int env_finish(const FusedArgs& a, const Lds& L, int t, int q, int w, uint32_t tag) {
+  const int tid = threadIdx.x;
+  const int H = a.H, E = a.E, K = a.K, nch = H / 8;
+  const uint64_t* xl = env_logits(a, t, q);
   {
-    const uint64_t* src = xl + i0;
-    uint64_t raw[4];
+    uint64_t raw[kEnvMaxE / NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+    for (int j = 0; j < kEnvMaxE / NT; ++j) {
+      const int i = tid + NT * j;
+      raw[j] = i < E ? ld_tagged(xl + i) : 0;
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lv[j] = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail) : 0.f;
-      if (j < cnt) L.rl[i0 + j] = lv[j];
+    for (int j = 0; j < kEnvMaxE / NT; ++j) {
+      const int i = tid + NT * j;
+      if (i < E) L.rl[i] = await_tagged(xl + i, raw[j], tag, a.fail);
     }
   }
-  env_pick(lv, i0, cnt, L.rl, E, K, a.renorm, L.rida, L.rid, L.rw, L.red, L.tks);
+  env_pick(L.rl, E, K, a.renorm, L.rida, L.rid, L.rw, L.red, L.tks);
   // the token's routing and normalised state, for the caller (first workgroup of its first pair)
   if (q == 0 && w == 0) {
     if (a.ids_out && tid < K) a.ids_out[(size_t)t * K + tid] = L.rid[tid];
@@ -793,7 +797,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     // (with the envelope, x is formed here from the hidden state and the
     // routing is computed: the pair's expert comes from it)
     int e = 0;
-    if constexpr (ENV) e = env_route(a, L, t, p % a.K, w, tag);
+    if constexpr (ENV) env_begin(a, L, t, p % a.K, w, tag);
     const uint16_t* xrow = ENV ? L.xb : a.x + (size_t)t * H;
     uint4 xq[EPT >= 8 ? EPT / 8 : 1];
     uint32_t sq[EPT >= 4 ? EPT / 4 : 1];
@@ -814,12 +818,22 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     // activation enters the result: the screen is skipped (ĥ = 0, zero recovery
     // sums, every channel a candidate) and the sketch is not read
     const bool nosk = RECX && a.c >= a.I;
+    const RotBuf rb{H, a.log2H, L.xs, L.limb};
+    int F0 = 0;
+    if constexpr (ENV) {
+      // x is ready: rotate it while the router logits are exchanged, then route
+      if (!nosk) {
+        if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
+        else F0 = rotate_small(rb, xrow, a.signs, wred);
+      }
+      e = env_finish(a, L, t, p % a.K, w, tag);
+    }
     if (!nosk) {
       const int cwk0 = min(j1 - j0, kSubChunk);
       // (every prefetch below is issued on every path, so no later wait has to
       //  assume that some of them were skipped; unused ones read valid addresses)
       uint4 spre[kSketchPre];
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < kSketchPre; ++u) spre[u] = sketch_item(a, e, j0, cwk0, min(u, (H + 255) / 256 - 1));
       // (loads below are unconditional at clamped addresses, masked afterwards)
       float2 sgu = load_scale(a, e, j0, cwk0);
@@ -827,10 +841,10 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       uint32_t btv[kBtPer];
       load_bt(a, e, j0, cwk0, zl, zg, groups, btv);
       // ---- phase A: screen this workgroup's channels, sub-chunk by sub-chunk
-      int F0;
-      const RotBuf rb{H, a.log2H, L.xs, L.limb};
-      if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
-      else F0 = rotate_small(rb, xrow, a.signs, wred);
+      if constexpr (!ENV) {
+        if constexpr (EPT >= 4) F0 = rotate_fast<EPT>(rb, xq, sq, wf0);
+        else F0 = rotate_small(rb, xrow, a.signs, wred);
+      }
       float zacc = 0.f;                               // partial recovery sum for (zl, zg)
       if (j1 - j0 <= kSubChunk) {
         if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
@@ -842,16 +856,16 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         for (; sj0 + kSubChunk < j1; sj0 += kSubChunk) {
           const int nj0 = sj0 + kSubChunk, ncwk = min(j1 - nj0, kSubChunk);
           uint4 snext[kSketchPre];
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < kSketchPre; ++u) snext[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
           const float2 nsgu = load_scale(a, e, nj0, ncwk);
           uint32_t nbtv[kBtPer];
           load_bt(a, e, nj0, ncwk, zl, zg, groups, nbtv);
           screen_and_sum<EPT>(a, L, p, e, sj0, kSubChunk, F0, spre, sgu, btv, zg, groups, zacc, tag);
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < kSketchPre; ++u) spre[u] = snext[u];
           sgu = nsgu;
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < kBtPer; ++u) btv[u] = nbtv[u];
         }
         screen_and_sum<EPT>(a, L, p, e, sj0, j1 - sj0, F0, spre, sgu, btv, zg, groups, zacc, tag);
@@ -1154,8 +1168,12 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
     const int p = slot % a.P, w = slot / a.P;
     const int t = p / a.K;
     int e;
-    if constexpr (ENV) e = env_route(a, L, t, p % a.K, w, tag);
-    else e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
+    if constexpr (ENV) {
+      env_begin(a, L, t, p % a.K, w, tag);
+      e = env_finish(a, L, t, p % a.K, w, tag);
+    } else {
+      e = (int)ld_scalar(a.ids + __builtin_amdgcn_readfirstlane(p));
+    }
     const uint16_t* xrow = ENV ? L.xb : a.x + (size_t)t * H;
     const int q0 = min(a.I, w * a.cpw), q1 = min(a.I, q0 + a.cpw);
     if (q0 < q1) {

@@ -1013,15 +1013,8 @@ __global__ __launch_bounds__(GT) void k_g_route(RouteArgs a) {
     }
   }
   if (!arrive_last(a.rctr + t, (uint32_t)a.nb, &s_flag)) return;
-  int cnt;
-  const int i0 = topk_range<GT>(E, &cnt);
-  float lv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lv[j] = j < cnt ? ld_f(a.lg + (size_t)t * E + i0 + j) : 0.f;
-    if (j < cnt) rl[i0 + j] = lv[j];
-  }
-  env_pick(lv, i0, cnt, rl, E, K, a.renorm, rida, rid, rw, red, tks);
+  for (int i = tid; i < E; i += GT) rl[i] = ld_f(a.lg + (size_t)t * E + i);
+  env_pick(rl, E, K, a.renorm, rida, rid, rw, red, tks);
   if (tid < K) {
     a.ids[(size_t)t * K + tid] = rid[tid];
     a.w[(size_t)t * K + tid] = rw[tid];
