@@ -469,6 +469,161 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
   }
 }
 
+// The same screen for H <= 2048 with each token pair's digit planes staged
+// in LDS once per workgroup (the four wavefronts share them; reading them from
+// L2 in every wavefront made the screen L2-bound): the next pair's planes are
+// requested while the current pair is multiplied, one barrier per pair.
+constexpr int kStgPS = 2048 + 16;                                  // plane pitch in LDS (bytes)
+constexpr int kStgPieces = 2 * kPlanes * 2048 / 16 / GT;           // 16-byte pieces per thread and pair
+
+__device__ __forceinline__ void stage_load(const GArgs& a, int pa, int pb, int Hp, uint4 (&v)[kStgPieces]) {
+  const int tid = threadIdx.x, ppl = Hp / 16;
+  const int ta = pa / a.K, tb = pb / a.K;
+#pragma unroll
+  for (int u = 0; u < kStgPieces; ++u) {
+    const int i = tid + GT * u, pl = i / ppl, off = i % ppl;
+    const uint8_t* src = a.xd + (size_t)(pl < kPlanes ? ta : tb) * kPlanes * Hp + (size_t)(pl % kPlanes) * Hp + 16 * off;
+    v[u] = pl < 2 * kPlanes ? ld16c(src) : make_uint4(0, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void stage_store(uint8_t* buf, int Hp, const uint4 (&v)[kStgPieces]) {
+  const int tid = threadIdx.x, ppl = Hp / 16;
+#pragma unroll
+  for (int u = 0; u < kStgPieces; ++u) {
+    const int i = tid + GT * u, pl = i / ppl, off = i % ppl;
+    if (pl < 2 * kPlanes) *reinterpret_cast<uint4*>(buf + pl * kStgPS + 16 * off) = v[u];
+  }
+}
+// B operand halves of super-block sb, half m, from the staged planes (the layout of digit_load2).
+__device__ __forceinline__ void digit_lds2(const uint8_t* buf, int sb, int m, uint4& lo, uint4& hi) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, gB = lane >> 4;
+  const int pl = min(col, 2 * kPlanes - 1);
+  const uint8_t* row = buf + pl * kStgPS + sb * 256 + 64 * (gB >> 1) + 32 * m + 16 * (gB & 1);
+  lo = *reinterpret_cast<const uint4*>(row);
+  hi = *reinterpret_cast<const uint4*>(row + 128);
+}
+
+__global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
+  __shared__ __align__(16) float dsw[4][32 * 16];
+  __shared__ __align__(16) float hw[4][2 * 16];
+  __shared__ __align__(16) uint16_t btw[4][16 * kRPad];
+  __shared__ __align__(16) uint8_t stg[2][2 * kPlanes * kStgPS];
+  if ((uint32_t)blockIdx.y >= a.meta[1]) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, r = a.r;
+  const int Hp = max(H, 256);
+  const int nsb = (H + 255) / 256;                         // <= kSbReg
+  const int item = a.gwork[blockIdx.y];
+  const int e = a.gue[item >> 16];
+  const int g0 = (item & 0xFFFF) * kTokGroup;
+  const int p0 = a.goff[e], n = min(a.goff[e + 1] - p0 - g0, kTokGroup);
+  const int jw = blockIdx.x * kTile + 16 * wv;
+  const int cwv = min(16, I - jw);
+  const bool active = cwv > 0;                             // (inactive wavefronts still stage and join)
+  const int zslot = jw / 16;
+  const int row = lane & 15, qe = (lane >> 4) & 1, tk = lane >> 5;
+  float* myD = dsw[wv];
+  float* myH = hw[wv];
+  uint16_t* myB = btw[wv];
+  uint4 wa[2][kSbReg];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int s = 0; s < kSbReg; ++s)
+      wa[q][s] = active ? sketch_item2(a, e, jw, cwv, q, min(s, nsb - 1)) : make_uint4(0, 0, 0, 0);
+  const float sc = active ? (qe ? a.su : a.sg)[(size_t)e * I + jw + min(row, cwv - 1)] : 0.f;
+  if (active && r > 0) {
+    const uint4* src4 = reinterpret_cast<const uint4*>(a.Bt + ((size_t)e * I + jw) * r);
+    const int npc = cwv * r / 8;
+    uint4 bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = ld16c(src4 + min(lane + 64 * i, npc - 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < 2 * r) reinterpret_cast<uint4*>(myB)[idx] = idx < npc ? bv[i] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  uint4 nx[kStgPieces];
+  stage_load(a, a.gpl[p0 + g0], a.gpl[p0 + g0 + min(1, n - 1)], Hp, nx);
+  stage_store(stg[0], Hp, nx);
+  __syncthreads();
+  int buf = 0;
+  for (int q2 = 0; q2 < n; q2 += 2) {
+    const int pa = a.gpl[p0 + g0 + q2], pb = a.gpl[p0 + g0 + min(q2 + 1, n - 1)];
+    const bool more = q2 + 2 < n;
+    if (more) stage_load(a, a.gpl[p0 + g0 + q2 + 2], a.gpl[p0 + g0 + min(q2 + 3, n - 1)], Hp, nx);
+    if (active) {
+      const uint8_t* sb8 = stg[buf];
+      v4f acc[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kSbReg; ++s) {
+        if (s < nsb) {
+          uint4 lo0, hi0, lo1, hi1;
+          digit_lds2(sb8, s, 0, lo0, hi0);
+          digit_lds2(sb8, s, 1, lo1, hi1);
+          const uint32_t km = 64 * s + 16 * (lane >> 4) < H / 4 ? ~0u : 0u;   // codes past the row end (H < 256)
+          const v8i d0 = digit_operand2(lo0, hi0);
+          const v8i d1 = digit_operand2(lo1, hi1);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                trit_operand(wa[q][s].x & km, wa[q][s].y & km), d0, acc[q], 4, 0, 0, 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                trit_operand(wa[q][s].z & km, wa[q][s].w & km), d1, acc[q], 4, 0, 0, 0, 0, 0);
+          }
+        }
+      }
+      {
+        const int col = lane & 15;
+        if (col <= 2 * kPlanes) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * 16 + col] = acc[q][v];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int F0 = a.xf0[(tk ? pb : pa) / a.K];
+      const float* d = myD + (16 * qe + row) * 16 + kPlanes * tk;
+      const long long S = (long long)(int)d[0] + ((long long)(int)d[1] << 4) + ((long long)(int)d[2] << 8) +
+                          ((long long)(int)d[3] << 12) + ((long long)(int)d[4] << 16) + ((long long)(int)d[5] << 20) -
+                          ((long long)(int)myD[(16 * qe + row) * 16 + 2 * kPlanes] << 23);
+      const float val = (float)((double)sc * ldexp((double)S, kDShift - F0));
+      const float other = __int_as_float(lane_xor<16>(__float_as_int(val)));
+      const bool ok = row < cwv && q2 + tk < n;
+      if (qe == 0) {
+        const float hv = silu_f32(val) * other;
+        myH[tk * 16 + row] = ok ? hv : 0.f;
+        if (ok) a.hs[(size_t)(tk ? pb : pa) * I + jw + row] = hv;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int idx = lane; idx < 2 * r; idx += 64) {
+        const int t2 = idx / r, l = idx % r;
+        if (q2 + t2 < n) {
+          float z = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) z += myH[t2 * 16 + jj] * bf16_to_f32(myB[jj * r + l]);
+          a.zp[((size_t)(t2 ? pb : pa) * a.nz + zslot) * r + l] = z;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (more) stage_store(stg[buf ^ 1], Hp, nx);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
 // ------------------------------------------------------------------ stage 3: top-c
 
 template <int KPT>
@@ -1207,7 +1362,7 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
     // 2. screen
     {
       const bool reg = (H + 255) / 256 <= kSbReg;
-      const void* fn = reg ? reinterpret_cast<const void*>(&k_g_screen<true>)
+      const void* fn = reg ? reinterpret_cast<const void*>(&k_g_screen_lds)
                            : reinterpret_cast<const void*>(&k_g_screen<false>);
       if (int rc = launch_k("k_g_screen", fn, dim3(g.ntile, g.maxwork), 0, a, stream)) return rc;
     }
