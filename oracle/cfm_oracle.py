@@ -265,6 +265,37 @@ def topk_set(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def threshold_set(scores: np.ndarray, tau: float) -> np.ndarray:
+    """The indices whose score reaches tau, {j : s_j >= tau}, ascending.
+
+    The keep rule that top-k replaces: a selector keeps the channels whose
+    score passes a threshold fixed offline, so how many it keeps, and reads,
+    depends on the input (abstract; article section "Calibrated thresholds do
+    not pin down how much you read"). NaN counts as 0, as in topk_set.
+    """
+    s = np.nan_to_num(np.asarray(scores, dtype=np.float64), nan=0.0)
+    return np.flatnonzero(s >= tau)
+
+
+def calibrate_threshold(score_sets, k: int) -> float:
+    """The threshold that keeps k channels per pair on average over calibration pairs.
+
+    The offline step a threshold selector needs (abstract: thresholds
+    calibrated for a read budget). Plain reading: one threshold per layer,
+    matched to the budget's mean, i.e. the (k n)-th largest of the pooled
+    scores of the n calibration pairs, so that exactly k n of them reach it
+    when they are distinct (more on ties). k = 0 gives +inf (nothing passes).
+    """
+    pooled = np.concatenate([np.nan_to_num(np.asarray(s, np.float64), nan=0.0) for s in score_sets]) \
+        if len(score_sets) else np.zeros(0)
+    m = k * len(score_sets)
+    if m <= 0:
+        return float("inf")
+    if m > pooled.size:
+        raise ValueError("budget above the number of calibration scores")
+    return float(np.sort(pooled)[::-1][m - 1])
+
+
 def screen_scores(x_bits, tg_rows, tu_rows, sg_rows, su_rows, signs):
     """Sketch activations of every channel of one expert for one token.
 
@@ -293,7 +324,7 @@ RECOVERY_CANDIDATES_EXACT = "candidates_exact"
 
 
 def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
-                recovery=RECOVERY_SKETCH):
+                recovery=RECOVERY_SKETCH, tau=None):
     """The method for one routed (token, expert) pair.
 
     1. screen: hhat for all channels from the sketch; C = top-c by |hhat|
@@ -310,6 +341,10 @@ def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt,
        screened in but not kept their exact h_j instead (they were computed
        for the top-k anyway); channels never screened in keep hhat_j.
 
+    tau: when given, step 2 uses the threshold keep rule on the same score in
+    place of top-k, S = {j in C : |h_j| >= tau} (threshold_set), and k is not
+    used; |S| then varies with the input.
+
     A [E][H][r], Bt [E][I][r] are the stored map (BF16 bits, or floats).
     Returns a dict with hhat [I], C, h_all [I] (exact, every channel), S, y [H].
     """
@@ -319,9 +354,12 @@ def select_pair(x_bits, e, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt,
     hhat = screen_scores(x_bits, tg[e], tu[e], sg[e], su[e], signs)
     C = topk_set(np.abs(hhat), c)
     h_all = exact_activations(x_bits, w_gate[e], w_up[e])   # the scores the kernel needs only on C
-    S = C[topk_set(np.abs(h_all[C]), k)] if k > 0 else np.zeros(0, np.int64)
+    if tau is None:
+        S = C[topk_set(np.abs(h_all[C]), k)] if k > 0 else np.zeros(0, np.int64)
+    else:
+        S = C[threshold_set(np.abs(h_all[C]), tau)]
     wd = bf16_to_f64(w_down_t[e])
-    y = h_all[S] @ wd[S] if k > 0 else np.zeros(wd.shape[1])
+    y = h_all[S] @ wd[S] if len(S) > 0 else np.zeros(wd.shape[1])
     r = A.shape[-1]
     if r > 0:
         coef = hhat.copy()
@@ -348,13 +386,14 @@ def combine(ys: np.ndarray, w: np.ndarray, resid=None) -> np.ndarray:
 
 
 def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, Bt, k, c,
-                   tokens=None, recovery=RECOVERY_SKETCH, resid=None):
+                   tokens=None, recovery=RECOVERY_SKETCH, resid=None, tau=None):
     """Selected-channel MoE layer over a decode batch.
 
     x [T][H] BF16 bits, ids [T][K], w [T][K]. Selection is per (token, expert)
     pair and does not depend on the rest of the batch ("each token's k
     highest-scoring channels", abstract). tokens: optional subset of token
-    indices to evaluate (the others are skipped). recovery: as in select_pair.
+    indices to evaluate (the others are skipped). recovery, tau: as in
+    select_pair.
     resid: optional BF16 bits [T][H] added to each token's output before its
     single rounding (see combine).
 
@@ -369,7 +408,7 @@ def select_forward(x, ids, w, w_gate, w_up, w_down_t, tg, tu, sg, su, signs, A, 
         ys = np.zeros((K, H))
         for q in range(K):
             d = select_pair(x[t], int(ids[t, q]), w_gate, w_up, w_down_t, tg, tu, sg, su, signs,
-                            A, Bt, k, c, recovery=recovery)
+                            A, Bt, k, c, recovery=recovery, tau=tau)
             pairs[(t, q)] = d
             ys[q] = d["y"]
         outs.append(combine(ys, w[t], None if resid is None else resid[t]))
@@ -458,7 +497,8 @@ def layer_forward(h, gamma, eps, w_router, K, renorm, w_gate, w_up, w_down_t, tg
 # ----------------------------------------------------------------------------- byte accounting
 
 
-def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=RECOVERY_SKETCH):
+def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=RECOVERY_SKETCH,
+               threshold=False):
     """Bytes the method must read for one layer call (algorithmic count).
 
     Reads are counted the way hardware bills them: a touched segment is paid
@@ -477,19 +517,22 @@ def read_bytes(ids, E, I, H, k, c, r, cand_sets=None, keep_sets=None, recovery=R
     dropped candidates' recovery coefficients. With k = 0 and the default
     recovery nothing reads them. With the variant and c = I every channel is
     a candidate, so no sketch activation enters the result and the sketch is
-    not read.
+    not read. threshold: the kept sets come from the threshold keep rule, so
+    the candidates' exact activations are always used and keep_sets must be
+    given (k is not used).
     """
-    exact_step = k > 0 or recovery == RECOVERY_CANDIDATES_EXACT
+    if threshold and keep_sets is None:
+        raise ValueError("the threshold keep rule needs the kept sets")
+    exact_step = k > 0 or threshold or recovery == RECOVERY_CANDIDATES_EXACT
     sketch_read = not (recovery == RECOVERY_CANDIDATES_EXACT and c >= I)
     T, K = ids.shape
     total = 0
     for e in sorted(set(int(v) for v in ids.reshape(-1))):
         pairs = [(t, q) for t in range(T) for q in range(K) if ids[t, q] == e]
-        if cand_sets is None:
-            nc, nk = c * len(pairs), k * len(pairs)
-        else:
-            nc = len(set().union(*[set(map(int, cand_sets[p])) for p in pairs]))
-            nk = len(set().union(*[set(map(int, keep_sets[p])) for p in pairs]))
+        nc = c * len(pairs) if cand_sets is None else \
+            len(set().union(*[set(map(int, cand_sets[p])) for p in pairs]))
+        nk = k * len(pairs) if keep_sets is None else \
+            len(set().union(*[set(map(int, keep_sets[p])) for p in pairs]))
         if not exact_step:
             nc = 0
         sketch = 2 * (I * H // 4) + 2 * 4 * I if sketch_read else 0

@@ -182,3 +182,31 @@ def test_residual_rounded_separately_is_caught(monkeypatch):
     monkeypatch.setattr(O, "combine", bad)
     _fails(P.test_layer_all_kept_matches_torch_envelope, False)
 
+
+# ----------------------------------------------------------------------------- threshold keep rule
+
+def test_threshold_strict_comparison_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "threshold_set",
+                        lambda scores, tau: np.flatnonzero(np.nan_to_num(np.asarray(scores, np.float64)) > tau))
+    _fails(P.test_threshold_set_brute_force_with_ties)
+
+
+def test_threshold_calibration_off_by_one_is_caught(monkeypatch):
+    def bad(score_sets, k):   # the (k n + 1)-th largest instead of the (k n)-th
+        pooled = np.sort(np.concatenate([np.asarray(s, np.float64) for s in score_sets]))[::-1]
+        m = k * len(score_sets)
+        return float("inf") if m <= 0 else float(pooled[min(m, pooled.size - 1)])
+    monkeypatch.setattr(O, "calibrate_threshold", bad)
+    _fails(P.test_calibrate_threshold_worked_example)
+
+
+def test_threshold_ignored_by_select_pair_is_caught(monkeypatch):
+    orig = O.select_pair
+    monkeypatch.setattr(O, "select_pair", lambda *a, tau=None, **kw: orig(*a, **kw))
+    _fails(P.test_select_pair_threshold_equals_topk_of_the_same_size)
+
+
+def test_threshold_rule_billed_like_topk_is_caught(monkeypatch):
+    orig = O.read_bytes
+    monkeypatch.setattr(O, "read_bytes", lambda *a, threshold=False, **kw: orig(*a, **kw))
+    _fails(P.test_read_bytes_threshold_counts_the_kept_sets)

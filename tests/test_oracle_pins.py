@@ -429,6 +429,82 @@ def test_lowrank_exact_on_low_rank_matrix():
     assert np.allclose(A @ Bt.T, W, atol=1e-10)
 
 
+# ----------------------------------------------------------------------------- threshold keep rule
+
+def test_threshold_set_brute_force_with_ties():
+    """{j : s_j >= tau}, checked by a plain loop; tau is often one of the scores (ties at the boundary)."""
+    r = _rng(17)
+    for trial in range(60):
+        n = int(r.integers(0, 50))
+        s = r.integers(0, 6, n).astype(np.float64)
+        tau = float(r.choice(s)) if n and trial % 2 else float(r.uniform(-1, 6))
+        brute = [j for j in range(n) if s[j] >= tau]
+        assert O.threshold_set(s, tau).tolist() == brute
+
+
+def test_threshold_nan_counts_as_zero():
+    s = np.array([np.nan, 0.5, 0.0, np.nan])
+    assert O.threshold_set(s, 0.0).tolist() == [0, 1, 2, 3]
+    assert O.threshold_set(s, 0.1).tolist() == [1]
+    assert O.threshold_set(s, float("inf")).tolist() == []
+
+
+def test_threshold_at_the_kth_score_is_topk_when_scores_are_distinct():
+    r = _rng(18)
+    for _ in range(30):
+        s = r.standard_normal(int(r.integers(1, 80))) ** 2
+        k = int(r.integers(1, s.size + 1))
+        tau = np.sort(s)[::-1][k - 1]
+        assert O.threshold_set(s, tau).tolist() == O.topk_set(s, k).tolist()
+
+
+def test_calibrate_threshold_worked_example():
+    """Pooled scores 4, 3, 2.5, 2, 1, 0.5 of two pairs: k = 2 per pair keeps 4 of them, so tau = 2."""
+    sets = [np.array([3.0, 1.0, 2.0]), np.array([0.5, 4.0, 2.5])]
+    assert O.calibrate_threshold(sets, 2) == 2.0
+    assert O.calibrate_threshold(sets, 1) == 3.0
+    assert O.calibrate_threshold(sets, 3) == 0.5
+    assert O.calibrate_threshold(sets, 0) == float("inf")
+    with pytest.raises(ValueError):
+        O.calibrate_threshold(sets, 4)
+
+
+def test_calibrated_threshold_keeps_k_per_pair_on_average():
+    r = _rng(19)
+    sets = [r.standard_normal(40) ** 2 for _ in range(25)]
+    for k in (1, 7, 40):
+        tau = O.calibrate_threshold(sets, k)
+        kept = [int(np.sum(st >= tau)) for st in sets]
+        assert sum(kept) == k * len(sets)
+        if k < 40:
+            assert len(set(kept)) > 1          # the per-pair count varies with the input
+
+
+def test_select_pair_threshold_equals_topk_of_the_same_size():
+    """tau = the 5th largest exact |h| among the candidates keeps the same 5 channels as k = 5,
+    with the same bits; tau = 0 keeps every candidate (k = c); tau = inf none (k = 0)."""
+    wg, wu, wd, d, x, ids, w = _small_layer(I=32, H=64)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 6)
+    for t in range(ids.shape[0]):
+        e = int(ids[t, 0])
+        ref = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 5, 12)
+        hc = np.abs(ref["h_all"][ref["C"]])
+        tau = float(np.sort(hc)[::-1][4])
+        th = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, 12, tau=tau)
+        assert th["S"].tolist() == ref["S"].tolist() and np.array_equal(th["y"], ref["y"])
+        # S brute force: the candidates whose exact |h| reaches tau
+        assert th["S"].tolist() == sorted(j for j in ref["C"] if abs(ref["h_all"][j]) >= tau)
+        for rec in ("sketch", "candidates_exact"):
+            allk = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 12, 12, recovery=rec)
+            th0 = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 3, 12, recovery=rec, tau=0.0)
+            assert th0["S"].tolist() == allk["S"].tolist() and np.array_equal(th0["y"], allk["y"])
+            none = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, 12, recovery=rec)
+            thi = O.select_pair(x[t], e, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 3, 12, recovery=rec,
+                                tau=float("inf"))
+            assert len(thi["S"]) == 0 and np.array_equal(thi["y"], none["y"])
+
+
 # ----------------------------------------------------------------------------- byte accounting
 
 def test_read_bytes_closed_form_q18():
@@ -471,6 +547,21 @@ def test_read_bytes_no_sketch_when_every_channel_is_a_candidate():
     assert O.read_bytes(ids, 4, I, H, k, I, r) == 2 * (sk + rest) + io
     assert O.read_bytes(ids, 4, I, H, k, I - 1, r, recovery="candidates_exact") == \
         2 * (sk + rest - 4 * H) + io
+
+
+def test_read_bytes_threshold_counts_the_kept_sets():
+    """Threshold rule: candidate rows are always read (their exact |h| decides S) and the down
+    rows are the kept sets' sizes, whatever k says."""
+    ids = np.array([[0, 1]], np.int32)
+    I, H, r, c = 64, 128, 4, 10
+    base = 2 * (I * H // 4) + 8 * I + 2 * H * r + 2 * I * r
+    io = 2 * H + 8 * 2 + 2 * H
+    ks = {(0, 0): np.array([1, 4, 9]), (0, 1): np.array([], np.int64)}
+    want = (base + 4 * H * c + 2 * H * 3) + (base + 4 * H * c) + io
+    assert O.read_bytes(ids, 2, I, H, 0, c, r, keep_sets=ks, threshold=True) == want
+    assert O.read_bytes(ids, 2, I, H, 7, c, r, keep_sets=ks, threshold=True) == want
+    with pytest.raises(ValueError):
+        O.read_bytes(ids, 2, I, H, 0, c, r, threshold=True)
 
 
 # ----------------------------------------------------------------------------- decode-layer envelope
