@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--recovery", action="store_true",
                     help="instead of the default line: recovery rank sweep (r 0..128) of both recovery variants "
                          "at batch 1 and 16, 18 %% budget, with each output's deviation from the dense layer")
+    ap.add_argument("--threshold", action="store_true",
+                    help="instead of the default line: the threshold keep rule against top-k at batch 1, "
+                         "tau calibrated offline for 18 %% and 13 %% budgets: kept channels, bytes read and "
+                         "time per token on evaluation tokens, same-distribution and RMS-shifted")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -396,6 +400,104 @@ def recovery_sweep(torch, cfm, args):
           flush=True)
 
 
+def calibrate_tau(torch, cfm, layer, x, ids, w, k, c, r, ws):
+    """Offline calibration of the threshold for one layer with the library's own threshold calls: the
+    largest tau (over float bit patterns, by bisection) with which the calibration pairs keep at least
+    k channels each on average, i.e. the (k P)-th largest exact |h| among their candidates."""
+    import struct
+    wg, wu, wd, signs, sk, A, Bt = layer
+    T, K = ids.shape
+    cnt = torch.empty((T * K,), dtype=torch.int32, device="cuda")
+    need = k * T * K
+
+    def kept(bits):
+        tau = struct.unpack("<f", struct.pack("<I", bits))[0]
+        cfm.moe_select_forward_threshold(x, ids, w, wg, wu, wd, signs, *sk, A, Bt, tau, c, r, ws=ws, keep_count=cnt)
+        return int(cnt.sum().item())
+
+    lo, hi = 0, 0x7F800000                # kept(lo) >= need > kept(hi) (tau +inf keeps nothing)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if kept(mid) >= need:
+            lo = mid
+        else:
+            hi = mid
+    return struct.unpack("<f", struct.pack("<I", lo))[0]
+
+
+def threshold_study(torch, cfm, args):
+    """The threshold keep rule against top-k on the Qwen3-30B-A3B-shaped layer ring (c 276, r 64), batch 1.
+    Per layer, tau is calibrated offline on 64 calibration tokens so that their pairs keep k channels
+    each on average (k 138: 18 %; k 100: 13 %), then applied to evaluation tokens drawn the same way
+    and to tokens whose RMS is 0.8x and 1.25x (a stand-in for inputs that differ from the calibration
+    data): kept channels per pair, routed-expert bytes each token reads as a fraction of the dense
+    layer's, and time per token, beside top-k at the same k."""
+    import numpy as np
+    E, K, I, H = 128, 8, 768, 2048
+    c, r = 276, 64
+    NL = args.layers
+    log(f"threshold study: building {NL} layers ...")
+    layers = []
+    for l in range(NL):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        A, Bt = cfm.lowrank_build(wd, r)
+        layers.append((wg, wu, wd, signs, cfm.sketch_build(wg, wu, signs), A, Bt))
+    Tc = 64
+    xc, idc, wc = make_tokens(torch, args.seed + 900, NL, Tc, E, K, H)
+    wsc = cfm.new_workspace(cfm.select_workspace(Tc, K, E, I, H, c, c, r), "cuda")
+    n = NL * 8
+    xe, ide, we = make_tokens(torch, args.seed + 901, n, 1, E, K, H)
+    sets = {"same distribution": xe}
+    for f in (0.8, 1.25):
+        sets[f"RMS x{f}"] = (xe.float() * f).to(torch.bfloat16).contiguous()
+    ws1 = cfm.new_workspace(cfm.select_workspace(1, K, E, I, H, c, c, r), "cuda")
+    wsd = cfm.new_workspace(cfm.dense_workspace(1, K, E, I, H), "cuda")
+    out = torch.empty((n, 1, H), dtype=torch.bfloat16, device="cuda")
+    cnt = torch.empty((n, K), dtype=torch.int32, device="cuda")
+    per_pair_fixed = I * H // 2 + 8 * I + 2 * H * r + 2 * I * r + 4 * H * c   # sketch, scales, map, candidates
+    io = 2 * H + 8 * K + 2 * H
+    dense_bytes = K * 6 * I * H + io
+    ms_d, _ = timed_graph(torch, lambda i: cfm.moe_dense_forward(xe[i], ide[i], we[i], *layers[i % NL][:3],
+                                                                 out=out[i], ws=wsd), n)
+    rows = []
+    for k in (138, 100):
+        taus = [calibrate_tau(torch, cfm, layers[l], xc[l], idc[l], wc[l], k, c, r, wsc) for l in range(NL)]
+        log(f"k {k}: calibrated tau per layer {[f'{t:.4g}' for t in taus]}")
+
+        def topk(i, k=k):
+            wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
+            cfm.moe_select_forward(xe[i], ide[i], we[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out[i], ws=ws1)
+        ms_k, _ = timed_graph(torch, topk, n)
+        topk_frac = (K * (per_pair_fixed + 2 * H * k) + io) / dense_bytes
+        for name, xs in sets.items():
+            def thr(i, xs=xs, taus=taus):
+                wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
+                cfm.moe_select_forward_threshold(xs[i], ide[i], we[i], wg, wu, wd, signs, *sk, A, Bt,
+                                                 taus[i % NL], c, r, out=out[i], ws=ws1, keep_count=cnt[i])
+            for i in range(n):
+                thr(i)
+            torch.cuda.synchronize()
+            kc = cnt.cpu().numpy().astype(np.float64)
+            frac = (kc.sum(1) * 2 * H + K * per_pair_fixed + io) / dense_bytes
+            ms_t, _ = timed_graph(torch, thr, n)
+            row = {"k": k, "budget_pct": round(100 * k / I, 1), "eval": name,
+                   "kept_per_pair": {"mean": round(float(kc.mean()), 1), "min": int(kc.min()),
+                                     "p10": float(np.percentile(kc, 10)), "p90": float(np.percentile(kc, 90)),
+                                     "max": int(kc.max())},
+                   "kept_mean_pct_of_I": round(100 * float(kc.mean()) / I, 2),
+                   "read_frac_of_dense": {"mean": round(float(frac.mean()), 4), "min": round(float(frac.min()), 4),
+                                          "max": round(float(frac.max()), 4)},
+                   "topk_read_frac_of_dense": round(topk_frac, 4),
+                   "us_per_token_threshold": round(ms_t * 1e3 / n, 3),
+                   "us_per_token_topk": round(ms_k * 1e3 / n, 3),
+                   "dense_us_per_token": round(ms_d * 1e3 / n, 3)}
+            rows.append(row)
+            log(f"threshold: {row}")
+    print(json.dumps({"workload": "threshold keep rule vs top-k, Qwen3-30B-A3B-shaped layer (H 2048, E 128, top-8, "
+                                  "I 768), c 276, r 64, batch 1; tau calibrated per layer on 64 synthetic tokens",
+                      "data": "synthetic", "layers": NL, "eval_tokens": n, "rows": rows}), flush=True)
+
+
 def olmoe(torch, cfm, args):
     """OLMoE-1B-7B-shaped layer (H 2048, E 64, top-8, I 1024, no per-channel scale), 64 tokens routed
     with Zipf(1.1) expert popularity, k 184, c 368, r 64: both passes and both dense kernels."""
@@ -496,6 +598,9 @@ def main():
         return
     if args.olmoe:
         olmoe(torch, cfm, args)
+        return
+    if args.threshold:
+        threshold_study(torch, cfm, args)
         return
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     EXPORTED, STATS_BYTES, decode_stats,
     dense_workspace, forward_path, last_error, lowrank_build, lowrank_workspace, moe_dense_forward,
     moe_layer_dense_forward, moe_layer_forward,
-    moe_select_forward, new_workspace, select_workspace, set_forward_path, sketch_build, timing_enable,
+    moe_select_forward, moe_select_forward_threshold, new_workspace, select_workspace, set_forward_path,
+    sketch_build, timing_enable,
     timing_report, version,
 )

@@ -35,6 +35,9 @@ _SIGS = {
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
     "moe_select_forward_ex": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                    _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
+    "moe_select_forward_threshold": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
+                                          _p, _p, ctypes.c_float, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p,
+                                          _p, _z, _p]),
     "moe_layer_forward": (_i, [_p, _p, ctypes.c_float, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
     "moe_layer_dense_forward": (_i, [_p, _p, ctypes.c_float, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p,
@@ -182,6 +185,32 @@ def moe_select_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, t
         _check(_lib.moe_select_forward_ex(*head, flags, *tail), "moe_select_forward_ex")
     else:
         _check(_lib.moe_select_forward(*head, *tail), "moe_select_forward")
+    return out
+
+
+def moe_select_forward_threshold(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, tu, sg, su, A, Bt,
+                                 tau, c, r, out=None, ws=None, cand_out=None, keep_out=None, keep_count=None,
+                                 stats=None, recovery=RECOVER_SKETCH):
+    """Selected-channel MoE layer with the threshold keep rule S = {j in C : |h_j| >= tau}.
+
+    keep_out: optional [T*K][c] int32 (S ascending, then -1); keep_count:
+    optional [T*K] int32. Returns out [T][H] BF16."""
+    if recovery not in _RECOVER_FLAGS:
+        raise ValueError(f"unknown recovery variant {recovery!r}")
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = new_workspace(select_workspace(T, K, E, I, H, c, c, r), dev)
+    _check(_lib.moe_select_forward_threshold(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
+        E, I, H, _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su),
+        _ptr(A) if r > 0 else None, _ptr(Bt) if r > 0 else None, float(tau), c, r, _RECOVER_FLAGS[recovery],
+        _ptr(out), _ptr(cand_out), _ptr(keep_out), _ptr(keep_count), _ptr(stats), _ptr(ws), ws.numel(),
+        _stream(dev)), "moe_select_forward_threshold")
     return out
 
 

@@ -107,6 +107,44 @@ int check_tokens(int T, int K) {
 
 using namespace cfm;
 
+namespace {
+// The selected forward pass behind moe_select_forward_ex and
+// moe_select_forward_threshold (thr: S by the threshold tau on |h| in place of
+// the top k; k is then c, the most that can pass).
+int select_entry(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int K,
+                 const cfm_bf16* w_gate, const cfm_bf16* w_up, const cfm_bf16* w_down_t, int E, int I, int H,
+                 const int8_t* signs, const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                 const cfm_bf16* A, const cfm_bf16* Bt, int k, int c, int r, unsigned flags, bool thr, float tau,
+                 cfm_bf16* out, int32_t* cand_out, int32_t* keep_out, int32_t* keep_count, cfm_stats* stats,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (flags & ~CFM_RECOVER_CANDIDATES_EXACT) return set_error(CFM_EINVAL, "moe_select_forward_ex: unknown flag bits");
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (int rc = check_budget(I, H, k, c, r)) return rc;
+  if (T == 0) return CFM_OK;
+  if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down_t || !signs || !tg || !tu ||
+      !sg || !su || !out)
+    return set_error(CFM_EINVAL, "moe_select_forward: null pointer");
+  if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_select_forward: null A or Bt with r > 0");
+  bool grouped = false;
+  if (int rc = pick_grouped(T, K, E, I, H, r, false, &grouped)) return rc;
+  const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r);
+  const size_t need = grouped ? group_plan(T, K, E, I, H, k, c, r, false, plan.bytes).bytes : plan.bytes;
+  if (!ws || ws_bytes < need)
+    return set_error(CFM_EWORKSPACE, "moe_select_forward: workspace smaller than select_workspace()");
+  SelectArgs a{x, w_gate, w_up, w_down_t, A, Bt, topk_ids, topk_w, signs, tg, tu, sg, su, out,
+               cand_out, keep_out, stats, static_cast<char*>(ws), flags};
+  a.thr = thr ? 1 : 0;
+  const float tpos = tau == 0.f ? 0.f : tau;             // -0 as +0: every score reaches it
+  std::memcpy(&a.tkey, &tpos, sizeof a.tkey);             // |h| >= tau iff bits(|h|) >= bits(tau)
+  a.keep_count = thr ? keep_count : nullptr;
+  if (grouped)
+    return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
+                                  static_cast<hipStream_t>(stream));
+  return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
 extern "C" {
 
 const char* cfm_last_error(void) { return g_last_error.c_str(); }
@@ -202,27 +240,23 @@ int moe_select_forward_ex(const cfm_bf16* x, const int32_t* topk_ids, const floa
                           unsigned flags, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out,
                           cfm_stats* stats, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  if (flags & ~CFM_RECOVER_CANDIDATES_EXACT) return set_error(CFM_EINVAL, "moe_select_forward_ex: unknown flag bits");
-  if (int rc = check_tokens(T, K)) return rc;
-  if (int rc = check_shape(E, I, H, true)) return rc;
-  if (int rc = check_budget(I, H, k, c, r)) return rc;
-  if (T == 0) return CFM_OK;
-  if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down_t || !signs || !tg || !tu ||
-      !sg || !su || !out)
-    return set_error(CFM_EINVAL, "moe_select_forward: null pointer");
-  if (r > 0 && (!A || !Bt)) return set_error(CFM_EINVAL, "moe_select_forward: null A or Bt with r > 0");
-  bool grouped = false;
-  if (int rc = pick_grouped(T, K, E, I, H, r, false, &grouped)) return rc;
-  const ForwardPlan plan = select_plan(T, K, E, I, H, k, c, r);
-  const size_t need = grouped ? group_plan(T, K, E, I, H, k, c, r, false, plan.bytes).bytes : plan.bytes;
-  if (!ws || ws_bytes < need)
-    return set_error(CFM_EWORKSPACE, "moe_select_forward: workspace smaller than select_workspace()");
-  SelectArgs a{x, w_gate, w_up, w_down_t, A, Bt, topk_ids, topk_w, signs, tg, tu, sg, su, out,
-               cand_out, keep_out, stats, static_cast<char*>(ws), flags};
-  if (grouped)
-    return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
-                                  static_cast<hipStream_t>(stream));
-  return launch_select_forward(a, plan, static_cast<hipStream_t>(stream));
+  return select_entry(x, topk_ids, topk_w, T, K, w_gate, w_up, w_down_t, E, I, H, signs, tg, tu, sg, su, A, Bt,
+                      k, c, r, flags, false, 0.f, out, cand_out, keep_out, nullptr, stats, ws, ws_bytes, stream);
+}
+
+int moe_select_forward_threshold(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                                 int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                                 const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                                 const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                                 const cfm_bf16* A, const cfm_bf16* Bt, float tau, int c, int r,
+                                 unsigned flags, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out,
+                                 int32_t* keep_count, cfm_stats* stats, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  clear_error();
+  if (!(tau >= 0.f)) return set_error(CFM_EINVAL, "moe_select_forward_threshold: tau must be >= 0 (not NaN)");
+  return select_entry(x, topk_ids, topk_w, T, K, w_gate, w_up, w_down_t, E, I, H, signs, tg, tu, sg, su, A, Bt,
+                      c, c, r, flags, true, tau, out, cand_out, keep_out, keep_count, stats, ws, ws_bytes,
+                      stream);
 }
 
 int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,

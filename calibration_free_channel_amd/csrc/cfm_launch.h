@@ -41,6 +41,7 @@ struct ForwardPlan {
   size_t off_xh, off_xz, off_xc;         // tagged u64 [P][I], [P][nw][r], [P][c]
   size_t off_ypart;                      // f32 [P][H]
   size_t off_xl;                         // tagged u64 [T][E] router logits (envelope)
+  size_t off_kc;                         // i32 [P] kept counts (threshold keep rule)
   size_t bytes;
 };
 ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool env = false);
@@ -66,6 +67,11 @@ struct SelectArgs {
   int32_t* ids_out;
   float* w_out;
   uint16_t* x_out;
+  // threshold keep rule (thr != 0): S = the candidates whose score key
+  // (the bits of |h|) reaches tkey, in place of the top k; the plan's k is c
+  int thr;
+  uint32_t tkey;
+  int32_t* keep_count;
 };
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);

@@ -176,6 +176,12 @@ struct FusedArgs {
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
   int pre;           // column chunks per workgroup when the candidates' rows are prefetched into LDS, else 0
   int rec_exact;     // dropped candidates enter the recovery with their exact activation
+  // threshold keep rule (thr != 0): S = the candidates whose score key reaches
+  // tkey, in place of the top k; k is then c (the most that can pass)
+  int thr;
+  uint32_t tkey;
+  int32_t* kcnt;       // [P] |S| of each pair (workspace; threshold rule)
+  int32_t* keep_count; // [P] |S| (optional output; threshold rule)
   // decode-layer envelope (env != 0): x = RMSNorm(resid) computed in the
   // launch, routing from the router rows wr, resid added to the output
   int env, renorm;
@@ -963,7 +969,8 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     constexpr bool kBtLate = !RECX && EPT <= 16;
     if (a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck, !kBtLate);
 
-    // ---- top-k kept set and recovery coefficients
+    // ---- top-k (or threshold) kept set and recovery coefficients
+    int kk = a.k;                              // |S| (the threshold rule's count varies by pair)
     if (exact_step) {
       int cnt;
       const int i0 = topk_range<NT>(a.c, &cnt);
@@ -980,7 +987,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           if (j < cnt) L.hcl[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
-        block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
+        if (!a.thr) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
       } else {
         uint64_t raw[32];
         uint32_t kr[32];
@@ -992,26 +999,38 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           if (j < cnt) L.hcl[i0 + j] = hv;
           kr[j] = score_key(hv);
         }
-        block_topk<NT, 32>(kr, i0, cnt, a.c, a.k, L.sel, L.tks);
+        if (!a.thr) block_topk<NT, 32>(kr, i0, cnt, a.c, a.k, L.sel, L.tks);
       }
+      // threshold rule: this thread's range of the candidates' activations is
+      // in LDS (written by this thread above)
+      if (a.thr)
+        kk = block_threshold<NT>([&](int i) { return score_key(L.hcl[i]); }, i0, cnt, a.tkey, L.sel, L.tks);
       if (a.k >= a.c) __syncthreads();
-      for (int i = tid; i < a.k; i += NT) {
+      for (int i = tid; i < kk; i += NT) {
         L.keep[i] = L.candp[L.sel[i]];
         L.hk[i] = L.hcl[L.sel[i]];
       }
       __syncthreads();
       if (w == 0 && a.keep_out)
-        for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = L.keep[i];
+        for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = i < kk ? L.keep[i] : -1;
+      if (w == 0 && a.thr && tid == 0) {
+        a.kcnt[p] = kk;
+        if (a.keep_count) a.keep_count[p] = kk;
+      }
       if (RECX && r > 0) {
         // each candidate's term to take out of the screen's recovery sum: its
         // sketch activation if kept, (sketch - exact) if dropped, so that a
         // dropped candidate is recovered with its exact activation
         for (int i = tid; i < a.c; i += NT) L.hcl[i] = L.hh[L.candp[i]] - L.hcl[i];
         __syncthreads();
-        for (int i = tid; i < a.k; i += NT) L.hcl[L.sel[i]] = L.hh[L.keep[i]];
+        for (int i = tid; i < kk; i += NT) L.hcl[L.sel[i]] = L.hh[L.keep[i]];
         __syncthreads();
       }
     } else {
+      if (w == 0 && a.thr && tid == 0) {          // c = 0: nothing to keep
+        a.kcnt[p] = 0;
+        if (a.keep_count) a.keep_count[p] = 0;
+      }
       __syncthreads();
     }
     if (a.pre) {
@@ -1029,7 +1048,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
         for (int u = 0; u < ZB; ++u) {
           const int i = i0 + ng * u;
-          const bool ok = i < a.k;
+          const bool ok = i < kk;
           const int j = ok ? L.keep[i] : 0;
           hz[u] = ok ? L.hh[j] : 0.f;
           bz[u] = ok ? ld16c(a.Bt + ((size_t)e * a.I + j) * r + 8 * zc) : make_uint4(0, 0, 0, 0);
@@ -1046,7 +1065,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         float acc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-        for (int m = g; m < a.k; m += NT / nck)
+        for (int m = g; m < kk; m += NT / nck)
           fma8(acc, L.hk[m], *reinterpret_cast<const uint4*>(L.dnc + ((size_t)L.sel[m] * nck + cc) * 16));
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], nck);
@@ -1059,7 +1078,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = 0.f;
         if constexpr (!kBtLate) {
-          const int nz = RECX ? a.c : a.k;     // terms taken out of the screen's sum
+          const int nz = RECX ? a.c : kk;      // terms taken out of the screen's sum
           for (int m = zgi; m < nz; m += ng) {
             const int pos = RECX ? m : L.sel[m];
             const float cf = RECX ? L.hcl[m] : L.hh[L.keep[m]];
@@ -1070,7 +1089,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < ZB; ++u) fma8(acc, hz[u], bz[u]);
             i0 += ng * ZB;
-            if (i0 >= a.k) break;
+            if (i0 >= kk) break;
             kept_bt(i0);
           }
         }
@@ -1106,7 +1125,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     if (r > 0) {
       // z = zsum - sum_{j in S} hhat_j Bt[e][j] (with dropped candidates recovered
       // exactly: minus sum over the candidates of their coefficient in hcl)
-      const int nz = RECX ? a.c : a.k;
+      const int nz = RECX ? a.c : kk;
       if (r % 8 == 0) {
         const int cpr = r / 8, ng = NT / cpr;       // r <= 128: cpr <= 16, ng >= 16
         const int cc = tid % cpr, g = tid / cpr;
@@ -1150,7 +1169,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     }
 
     // ---- phase C: down projection over kept rows for this workgroup's output slices
-    phase_c(a, L, p, t, e, w, L.keep, L.hk, a.k, r > 0, &s_flag, tag, ENV ? L.rw : nullptr);
+    phase_c(a, L, p, t, e, w, L.keep, L.hk, kk, r > 0, &s_flag, tag, ENV ? L.rw : nullptr);
   }
   finish_launch(a, tag);
 }
@@ -1209,7 +1228,8 @@ __global__ __launch_bounds__(NT) void k_dense_fused(FusedArgs a) {
 // ------------------------------------------------------------------ stats
 
 __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, int c, int r, int T,
-                        int K, int select, int exact_step, int sketch_read, cfm_stats* st) {
+                        int K, int select, int exact_step, int sketch_read, const int32_t* kcnt,
+                        cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   unsigned used = 0;
   for (int pp = 0; pp < P; ++pp) {
@@ -1225,10 +1245,15 @@ __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, i
   if (select) {
     s.bytes_sketch = sketch_read ? Pu * (2ull * I * (H / 4) + 8ull * I) : 0;
     s.bytes_candidates = exact_step ? Pu * 4ull * H * c : 0;
-    s.bytes_down = Pu * 2ull * H * k;
+    uint64_t kept = Pu * (uint64_t)k;
+    if (kcnt) {                                  // threshold rule: the rows each pair kept
+      kept = 0;
+      for (int pp = 0; pp < P; ++pp) kept += (uint64_t)kcnt[pp];
+    }
+    s.bytes_down = 2ull * H * kept;
     s.bytes_recovery = r > 0 ? Pu * (2ull * H * r + 2ull * I * r) : 0;
     s.rows_candidates = exact_step ? (uint32_t)(P * c) : 0;
-    s.rows_down = (uint32_t)(P * k);
+    s.rows_down = (uint32_t)kept;
   } else {
     s.bytes_sketch = 0;
     s.bytes_candidates = Pu * 4ull * H * I;
@@ -1290,6 +1315,7 @@ static void common_regions(ForwardPlan& p, Carve& cv) {
   p.off_err = cv.take(4);
   p.off_ctr = cv.take(4 * (size_t)std::max(p.T, 1) * kMaxNw);
   p.off_xl = cv.take(8 * (size_t)std::max(p.P, 1) * p.E);   // router logits (envelope calls)
+  p.off_kc = cv.take(4 * (size_t)std::max(p.P, 1));           // kept counts (threshold rule)
 }
 
 // With the envelope a workgroup waits for router logits computed by the other
@@ -1374,6 +1400,10 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.k = p.k; a.c = p.c; a.r = p.r; a.nw = p.nw; a.cw = p.cw; a.cpw = p.cpw; a.nhs = p.nhs; a.G = p.G;
   a.pre = p.pre;
   a.rec_exact = (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
+  a.thr = s.thr;
+  a.tkey = s.tkey;
+  a.kcnt = reinterpret_cast<int32_t*>(s.ws + p.off_kc);
+  a.keep_count = s.keep_count;
   a.env = p.env;
   a.env_pair = p.E <= 4 * p.nw ? 1 : 0;      // one logit per wavefront at most
   a.renorm = s.renorm;
@@ -1392,7 +1422,8 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
                        p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0,
-                       (a.rec_exact && p.c >= p.I) ? 0 : 1, static_cast<cfm_stats*>(s.stats));
+                       (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr,
+                       static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;
@@ -1405,7 +1436,7 @@ int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p, hipStream_t 
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.I, p.I, 0,
-                       p.T, p.K, 0, 1, 0, static_cast<cfm_stats*>(s.stats));
+                       p.T, p.K, 0, 1, 0, nullptr, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;

@@ -138,6 +138,11 @@ struct GArgs {
   int T, K, P, E, I, H, log2H, k, c, r, ntile, nz, IW, nrb, IP, dense;
   int rec_exact;      // dropped candidates enter the recovery with their exact activation
   const uint16_t* resid;   // decode-layer envelope: the residual stream added to the output, else null
+  // threshold keep rule (thr != 0): S = the candidates whose score key reaches
+  // tkey, in place of the top k (k is then c, the most that can pass)
+  int thr;
+  uint32_t tkey;
+  int32_t* keep_count;     // [P] |S| (optional output; threshold rule)
 };
 
 // ------------------------------------------------------------------ block helpers
@@ -820,6 +825,7 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
   const int I = a.I, c = a.c, k = a.k, r = a.r;
   const int e = min(max(a.ids[p], 0), a.E - 1);
   const int32_t* cl = a.cl + (size_t)p * c;
+  int kk = k;                                     // |S| (the threshold rule's count varies by pair)
   if (k > 0) {
     int cnt;
     const int i0 = topk_range<GT>(c, &cnt);
@@ -831,12 +837,20 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
     for (int j = 0; j < KPT; ++j) kr[j] = score_key(a.hx[(size_t)p * I + jc[j]]);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) kr[j] = j < cnt ? kr[j] : 0u;
-    block_topk<GT, KPT>(kr, i0, cnt, c, k, sel, tks);
+    if (a.thr)
+      kk = block_threshold<GT>([&](int i) { return score_key(a.hx[(size_t)p * I + cl[i]]); }, i0, cnt, a.tkey,
+                               sel, tks);
+    else block_topk<GT, KPT>(kr, i0, cnt, c, k, sel, tks);
   }
+  if (a.thr && a.keep_count && tid == 0) a.keep_count[p] = kk;
   for (int i = tid; i < I; i += GT) hrow[i] = 0;
   for (int w = tid; w < a.IW; w += GT) bm[w] = 0;
   __syncthreads();
   for (int i = tid; i < k; i += GT) {
+    if (i >= kk) {
+      if (a.keep_out) a.keep_out[(size_t)p * k + i] = -1;
+      continue;
+    }
     const int j = cl[sel[i]];
     sel[i] = j;                                   // kept channel (each thread rewrites its own entries)
     hrow[j] = f32_to_bf16(a.hx[(size_t)p * I + j]);
@@ -884,7 +898,7 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
       }
       const float* hsp = a.hs + (size_t)p * I;
       const float* hxp = a.hx + (size_t)p * I;
-      const int nzr = a.rec_exact ? c : k;          // terms taken out of the screen's sum
+      const int nzr = a.rec_exact ? c : kk;         // terms taken out of the screen's sum
       for (int i0 = gi; i0 < nzr; i0 += 4 * groups) {
         uint4 bw[4];
         float hv[4];
@@ -1342,6 +1356,9 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.k = g.dense ? g.I : g.k; a.c = g.dense ? g.I : g.c; a.r = g.dense ? 0 : g.r;
   a.ntile = g.ntile; a.nz = (g.I + 15) / 16; a.IW = g.IW; a.nrb = g.nrb; a.IP = g.IP; a.dense = g.dense ? 1 : 0;
   a.rec_exact = !g.dense && (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
+  a.thr = !g.dense && s.thr ? 1 : 0;
+  a.tkey = s.tkey;
+  a.keep_count = s.keep_count;
   const int H = g.H;
 
   // 1. rotation + grouping

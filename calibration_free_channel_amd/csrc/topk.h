@@ -193,4 +193,32 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
   __syncthreads();
 }
 
+// The threshold keep rule in place of top-k (abstract: selectors typically
+// keep the channels whose score passes a threshold calibrated offline): the
+// indices whose key reaches tkey (key >= tkey) are written in ascending order
+// to out_idx (LDS); returns how many, in every thread (uniform). key_at(i)
+// gives the key of index i; this thread's indices are [i0, i0 + cnt) as given
+// by topk_range (read twice: a count, then the writes, so no key is held in
+// registers). Scratch as in block_topk (one scan per wavefront, one barrier for
+// the per-wave totals). Called by the whole workgroup; ends with a barrier.
+template <int NT, typename KeyAt>
+__device__ __forceinline__ int block_threshold(KeyAt key_at, int i0, int cnt, uint32_t tkey, int32_t* out_idx,
+                                               uint32_t* scratch) {
+  static_assert(NT == 256, "four wavefronts");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t* red = scratch + 4 * 256 + 8;
+  uint32_t n = 0;
+  for (int j = 0; j < cnt; ++j) n += key_at(i0 + j) >= tkey ? 1u : 0u;
+  const uint32_t incl = wave_incl_scan(n);
+  if (lane == 63) red[wv] = incl;
+  __syncthreads();
+  const uint4 wt = *reinterpret_cast<const uint4*>(red);
+  uint32_t pos = (wv > 0 ? wt.x : 0u) + (wv > 1 ? wt.y : 0u) + (wv > 2 ? wt.z : 0u) + incl - n;
+  const int total = __builtin_amdgcn_readfirstlane((int)(wt.x + wt.y + wt.z + wt.w));
+  for (int j = 0; j < cnt; ++j)
+    if (key_at(i0 + j) >= tkey) out_idx[pos++] = i0 + j;
+  __syncthreads();
+  return total;
+}
+
 }  // namespace cfm

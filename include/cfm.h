@@ -186,6 +186,34 @@ int moe_select_forward_ex(const cfm_bf16* x, const int32_t* topk_ids, const floa
                           cfm_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_select_forward_threshold - the reader with a threshold keep rule in
+ * place of top-k, on the same score (abstract: selectors typically keep the
+ * channels whose score passes a threshold calibrated offline, and the number
+ * that pass varies with the input; article section "Calibrated thresholds do
+ * not pin down how much you read"). For each routed pair:
+ *   C = as in moe_select_forward (the top c of |hhat|);
+ *   S = { j in C : |h_j| >= tau }, ascending, 0 <= |S| <= c (varies by pair);
+ *   y, out as in moe_select_forward (or _ex with flags) with that S.
+ *   tau        : >= 0 (+inf keeps nothing, 0 every candidate); NaN or a
+ *                negative value returns CFM_EINVAL. The calibration that picks
+ *                it is the caller's.
+ *   keep_out   : optional out [T*K][c] int32: S in ascending order, then -1.
+ *   keep_count : optional out [T*K] int32: |S| of each pair.
+ *   stats      : rows_down / bytes_down count the kept rows actually read.
+ *   ws         : at least select_workspace(T, K, E, I, H, c, c, r) bytes.
+ * Every other argument, the supported range, the pass choice and the error
+ * codes are those of moe_select_forward_ex.
+ */
+int moe_select_forward_threshold(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                                 int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
+                                 const cfm_bf16* w_down_t, int E, int I, int H, const int8_t* signs,
+                                 const uint8_t* tg, const uint8_t* tu, const float* sg, const float* su,
+                                 const cfm_bf16* A, const cfm_bf16* Bt, float tau, int c, int r,
+                                 unsigned flags, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out,
+                                 int32_t* keep_count, cfm_stats* stats, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * moe_dense_forward - the same routed-expert SwiGLU layer reading every channel
  * (the comparator the method is measured against: abstract, "MoE blocks ...
  * faster than optimized vLLM").

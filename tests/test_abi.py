@@ -95,6 +95,32 @@ def test_select_forward_ex_flags(lib, flags, kw, code):
     assert _sel_ex(lib, flags, **kw) == code
 
 
+def _sel_thr(lib, tau, flags=0, T=1, K=2, E=8, I=128, H=256, c=46, r=8, ptr=FAKE, ws=FAKE, wsb=1 << 40):
+    f = lib.moe_select_forward_threshold
+    f.restype = ctypes.c_int
+    P = ptr
+    return f(P, P, P, T, K, P, P, P, E, I, H, P, P, P, P, P, P, P, ctypes.c_float(tau), c, r,
+             ctypes.c_uint(flags), P, None, None, None, None, ws, ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("tau,flags,kw,code", [
+    (float("nan"), 0, {}, EINVAL),
+    (-1.0, 0, {}, EINVAL),
+    (float("-inf"), 0, {}, EINVAL),
+    (1.0, 2, {}, EINVAL),                # undefined flag bit
+    (1.0, 0, dict(c=129), EUNSUP),       # c > I
+    (1.0, 0, dict(r=129), EUNSUP),
+    (1.0, 0, dict(ptr=None), EINVAL),
+    (1.0, 1, dict(ptr=None), EINVAL),
+    (1.0, 0, dict(wsb=16), EWS),
+    (1.0, 0, dict(T=0, ptr=None, ws=None), OK),
+    (float("inf"), 1, dict(T=0, ptr=None, ws=None), OK),
+    (-0.0, 0, dict(T=0, ptr=None, ws=None), OK),
+])
+def test_select_forward_threshold_rejects(lib, tau, flags, kw, code):
+    assert _sel_thr(lib, tau, flags, **kw) == code
+
+
 def test_select_forward_empty_batch_is_a_noop(lib):
     assert _sel(lib, T=0, ptr=None, ws=None) == OK
 
