@@ -137,6 +137,10 @@ struct GArgs {
   uint32_t* octr;     // [T][H / 64] pair outputs arrived per (token, column tile) (zero between calls)
   int T, K, P, E, I, H, log2H, k, c, r, ntile, nz, IW, nrb, IP, dense;
   int rec_exact;      // dropped candidates enter the recovery with their exact activation
+  // the recovery variant with every channel a candidate: no sketch activation
+  // enters the result, so the screen does not run (hs and zp are not written
+  // and count as zero) and the sketch is not read
+  int nosk;
   const uint16_t* resid;   // decode-layer envelope: the residual stream added to the output, else null
   // threshold keep rule (thr != 0): S = the candidates whose score key reaches
   // tkey, in place of the top k (k is then c, the most that can pass)
@@ -648,7 +652,7 @@ __global__ __launch_bounds__(GT) void k_g_topc(GArgs a) {
   uint32_t kr[KPT];
   const float* src = a.hs + (size_t)p * I + i0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) kr[j] = j < cnt ? score_key(src[j]) : 0u;
+  for (int j = 0; j < KPT; ++j) kr[j] = j < cnt && !a.nosk ? score_key(src[j]) : 0u;
   block_topk<GT, KPT>(kr, i0, cnt, I, c, cand, tks);
   for (int w = tid; w < a.IW; w += GT) bm[w] = 0;
   __syncthreads();
@@ -880,7 +884,7 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
     for (int v = 0; v < 8; ++v) acc[v] = 0.f;
     if (gi < groups) {
       const float* zs = a.zp + (size_t)p * a.nz * r + 8 * cc;
-      for (int t0 = gi; t0 < a.nz; t0 += 4 * groups) {
+      for (int t0 = gi; t0 < (a.nosk ? 0 : a.nz); t0 += 4 * groups) {
         float4 z4[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
           const int j = a.rec_exact ? cl[i] : sel[i];
           bw[u] = ld16c(a.Bt + ((size_t)e * I + j) * r + 8 * cc);
           const bool dropped = a.rec_exact && !((bm[j >> 5] >> (j & 31)) & 1u);
-          hv[u] = hsp[j] - (dropped ? hxp[j] : 0.f);
+          hv[u] = (a.nosk ? 0.f : hsp[j]) - (dropped ? hxp[j] : 0.f);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1212,7 +1216,7 @@ __global__ void k_g_stats(GArgs a, cfm_stats* st) {
   s.bytes_io = 2ull * a.T * H + 8ull * a.T * a.K + 2ull * a.T * H;
   s.bytes_dense_equiv = (uint64_t)nue * 6ull * I * H + s.bytes_io;
   s.experts_used = nue;
-  s.bytes_sketch = a.dense ? 0 : (uint64_t)nue * (2ull * I * (H / 4) + 8ull * I);
+  s.bytes_sketch = (a.dense || a.nosk) ? 0 : (uint64_t)nue * (2ull * I * (H / 4) + 8ull * I);
   s.bytes_candidates = 4ull * H * uc;
   s.bytes_down = 2ull * H * dc;
   s.bytes_recovery = (a.dense || r == 0) ? 0 : (uint64_t)nue * (2ull * H * r + 2ull * I * r);
@@ -1356,6 +1360,7 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.k = g.dense ? g.I : g.k; a.c = g.dense ? g.I : g.c; a.r = g.dense ? 0 : g.r;
   a.ntile = g.ntile; a.nz = (g.I + 15) / 16; a.IW = g.IW; a.nrb = g.nrb; a.IP = g.IP; a.dense = g.dense ? 1 : 0;
   a.rec_exact = !g.dense && (s.flags & CFM_RECOVER_CANDIDATES_EXACT) ? 1 : 0;
+  a.nosk = a.rec_exact && g.c >= g.I ? 1 : 0;
   a.thr = !g.dense && s.thr ? 1 : 0;
   a.tkey = s.tkey;
   a.keep_count = s.keep_count;
@@ -1376,8 +1381,8 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
     if (int rc = launch_k("k_g_prep", fn, dim3(g.T + 1), prep_lds(H, g.E), a, stream)) return rc;
   }
   if (!g.dense) {
-    // 2. screen
-    {
+    // 2. screen (not needed when no sketch activation enters the result)
+    if (!a.nosk) {
       const bool reg = (H + 255) / 256 <= kSbReg;
       const void* fn = reg ? reinterpret_cast<const void*>(&k_g_screen_lds)
                            : reinterpret_cast<const void*>(&k_g_screen<false>);

@@ -133,8 +133,8 @@ def test_default_flags_match_plain_entry_point(cfm):
 
 
 def test_candidates_exact_every_channel_a_candidate_reads_no_sketch(cfm):
-    """c = I with the variant: the per-pair pass skips the screen; its bytes leave out the sketch, and its
-    output matches the grouped pass (which screens anyway) and the oracle."""
+    """c = I with the variant: both passes skip the screen; their bytes leave out the sketch, and their
+    outputs match each other and the oracle."""
     wl = custom_workload("rx_nosk", 4, 2, 64, 128, 6, 20, 64, 8, 34)
     L = upload(wl)
     sk = gpu_sketch(cfm, L)
@@ -150,8 +150,15 @@ def test_candidates_exact_every_channel_a_candidate_reads_no_sketch(cfm):
     tot = sum(st1[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
     assert tot == O.read_bytes(L1.host.ids, 4, 64, 128, 20, 64, 8, recovery=EXACT)
     with cfm.forward_path(PATHS["grouped"]):
-        gg, gc, gk = run_select(cfm, L, sk, A, Bt, 20, 64, 8, recovery=EXACT)
+        gg, gc, gk, gst = run_select(cfm, L, sk, A, Bt, 20, 64, 8, stats=True, recovery=EXACT)
     assert np.array_equal(cand, gc)
+    # the grouped pass bills the union of each expert's pairs' sets
+    T, K = L.host.ids.shape
+    cs = {(t, q): gc[t * K + q] for t in range(T) for q in range(K)}
+    ks = {(t, q): gk[t * K + q] for t in range(T) for q in range(K)}
+    assert gst["bytes_sketch"] == 0
+    gtot = sum(gst[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
+    assert gtot == O.read_bytes(L.host.ids, 4, 64, 128, 20, 64, 8, cs, ks, recovery=EXACT)
     for t in range(wl.T):
         assert rel_l2(got[t], gg[t]) <= 1e-2
     Ah, Bh = oracle_map(L.host.w_down_t, 8, range(4), 4, 64, 128)
