@@ -130,6 +130,23 @@ def kernel_times(torch, cfm, fn, n_steps):
     return {k: v[1] / v[0] for k, v in rep.items()}
 
 
+def stream_read_gbps(torch, nbytes=2 << 30, reps=10):
+    """Context for the roofline: what a plain streaming read achieves on this GPU (torch's sum over a
+    2 GiB float32 buffer, bytes read / time)."""
+    t = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    t.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        t.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del t
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def measured_traffic():
     """HBM bytes per launch of k_select_fused from the committed rocprofv3 --pmc
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
@@ -719,7 +736,8 @@ def main():
         "hbm_frac": round(r1["gbps"] / PEAK_HBM_GBPS, 4),
         "bytes_per_step": r1["bytes"],
         "dense": {"us_per_token": round(r1["dense_us_per_token"], 3),
-                  "GBps": round(r1["dense_gbps"], 1), "bytes_per_step": r1["dense_bytes"]},
+                  "GBps": round(r1["dense_gbps"], 1), "hbm_frac": round(r1["dense_gbps"] / PEAK_HBM_GBPS, 4),
+                  "bytes_per_step": r1["dense_bytes"]},
         "speedup_vs_dense": round(r1["speedup"], 3),
         "roofline": roof,
         "kernels_us": {n: round(v, 3) for n, v in r1["kernels_us"].items()},
@@ -734,6 +752,10 @@ def main():
                                  "lowrank_build": round(t_lr / L * 1e3, 2)},
         "cpu_baseline": None,
     }
+    del layers
+    torch.cuda.empty_cache()
+    line["context"] = {"stream_read_GBps": round(stream_read_gbps(torch), 1),
+                       "stream_read": "torch.sum over a 2 GiB float32 buffer"}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline()
