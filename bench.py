@@ -60,6 +60,9 @@ def parse():
                     help="instead of the default line: the threshold keep rule against top-k at batch 1, "
                          "tau calibrated offline for 18 %% and 13 %% budgets: kept channels, bytes read and "
                          "time per token on evaluation tokens, same-distribution and RMS-shifted")
+    ap.add_argument("--cold", action="store_true",
+                    help="instead of the default line: batch 1, each call timed on its own after a 1 GiB "
+                         "cache flush, median / p10 / p90 of the selected and the dense layer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -130,21 +133,27 @@ def kernel_times(torch, cfm, fn, n_steps):
     return {k: v[1] / v[0] for k, v in rep.items()}
 
 
-def stream_read_gbps(torch, nbytes=2 << 30, reps=10):
-    """Context for the roofline: what a plain streaming read achieves on this GPU (torch's sum over a
-    2 GiB float32 buffer, bytes read / time)."""
+def stream_gbps(torch, nbytes=2 << 30, reps=10):
+    """Context for the roofline: what plain streaming kernels achieve on this GPU, as (read GB/s of
+    torch's sum over a 2 GiB float32 buffer, read + write GB/s of torch's copy of 1 GiB)."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
     t = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    t.sum()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        t.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    rd = nbytes / timed(lambda: t.sum()) / 1e9
     del t
-    return nbytes / (ms * 1e-3) / 1e9
+    a = torch.ones(nbytes // 2, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    cp = nbytes / timed(lambda: b.copy_(a)) / 1e9
+    del a, b
+    return rd, cp
 
 
 def measured_traffic():
@@ -417,6 +426,62 @@ def recovery_sweep(torch, cfm, args):
           flush=True)
 
 
+def cold_timing(torch, cfm, args):
+    """Batch 1 on the Qwen3-30B-A3B-shaped layer at 18 % (k 138, c 276, r 64): every call timed on its
+    own with HIP events, after an untimed write of 1 GiB that evicts the L2 and the 256 MB last-level
+    cache, so each call reads its weights from HBM. Median, p10 and p90 over the reps, for the selected
+    and the dense layer (alternating), and the algorithmic GB/s at the median."""
+    import numpy as np
+    E, K, I, H = 128, 8, 768, 2048
+    k, c, r = 138, 276, 64
+    NL = args.layers
+    layers = []
+    for l in range(NL):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        A, Bt = cfm.lowrank_build(wd, r)
+        layers.append((wg, wu, wd, signs, cfm.sketch_build(wg, wu, signs), A, Bt))
+    reps = args.steps
+    x, ids, w = make_tokens(torch, args.seed + 77, reps + args.warmup, 1, E, K, H)
+    ws_s = cfm.new_workspace(cfm.select_workspace(1, K, E, I, H, k, c, r), "cuda")
+    ws_d = cfm.new_workspace(cfm.dense_workspace(1, K, E, I, H), "cuda")
+    out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+    times = {"selected": [], "dense": []}
+    bytes_ = {}
+    for i in range(reps + args.warmup):
+        wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
+        for name in ("selected", "dense"):
+            flush.fill_(i & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if name == "selected":
+                cfm.moe_select_forward(x[i], ids[i], w[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out, ws=ws_s,
+                                       stats=st if i == 0 else None)
+            else:
+                cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=out, ws=ws_d)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                times[name].append(e0.elapsed_time(e1) * 1e3)
+            if i == 0 and name == "selected":
+                d = cfm.decode_stats(st)
+                bytes_["selected"] = sum(d[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down",
+                                                        "bytes_recovery", "bytes_io"))
+                bytes_["dense"] = d["bytes_dense_equiv"]
+    res = {}
+    for name, v in times.items():
+        a = np.array(v)
+        med = float(np.median(a))
+        res[name] = {"median_us": round(med, 3), "p10_us": round(float(np.percentile(a, 10)), 3),
+                     "p90_us": round(float(np.percentile(a, 90)), 3),
+                     "GBps_at_median": round(bytes_[name] / (med * 1e-6) / 1e9, 1), "bytes": bytes_[name]}
+    res["speedup_at_median"] = round(res["dense"]["median_us"] / res["selected"]["median_us"], 3)
+    print(json.dumps({"workload": "Qwen3-30B-A3B-shaped MoE layer, batch 1, 18 % (k 138, c 276, r 64); "
+                                  "each call after a 1 GiB flush, HIP events around the call",
+                      "data": "synthetic", "reps": reps, "layers": NL, "result": res}), flush=True)
+
+
 def calibrate_tau(torch, cfm, layer, x, ids, w, k, c, r, ws):
     """Offline calibration of the threshold for one layer with the library's own threshold calls: the
     largest tau (over float bit patterns, by bisection) with which the calibration pairs keep at least
@@ -619,6 +684,9 @@ def main():
     if args.threshold:
         threshold_study(torch, cfm, args)
         return
+    if args.cold:
+        cold_timing(torch, cfm, args)
+        return
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64
     L = args.layers
@@ -754,8 +822,10 @@ def main():
     }
     del layers
     torch.cuda.empty_cache()
-    line["context"] = {"stream_read_GBps": round(stream_read_gbps(torch), 1),
-                       "stream_read": "torch.sum over a 2 GiB float32 buffer"}
+    rd, cp = stream_gbps(torch)
+    line["context"] = {"stream_read_GBps": round(rd, 1), "stream_copy_GBps": round(cp, 1),
+                       "stream": "torch.sum over a 2 GiB float32 buffer (bytes read); torch copy of 1 GiB "
+                                 "(bytes read + written)"}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline()
