@@ -429,8 +429,9 @@ def recovery_sweep(torch, cfm, args):
 def cold_timing(torch, cfm, args):
     """Batch 1 on the Qwen3-30B-A3B-shaped layer at 18 % (k 138, c 276, r 64): every call timed on its
     own with HIP events, after an untimed write of 1 GiB that evicts the L2 and the 256 MB last-level
-    cache, so each call reads its weights from HBM. Median, p10 and p90 over the reps, for the selected
-    and the dense layer (alternating), and the algorithmic GB/s at the median."""
+    cache, so each call reads its weights from HBM, and a GPU sleep that lets the host enqueue the
+    call before the first event is taken. Median, p10 and p90 over the reps, for the selected and the
+    dense layer (alternating), and the algorithmic GB/s at the median."""
     import numpy as np
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64
@@ -453,6 +454,9 @@ def cold_timing(torch, cfm, args):
         wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
         for name in ("selected", "dense"):
             flush.fill_(i & 255)
+            # the GPU sleeps while the host enqueues the events and the call, so the events
+            # bracket device work only (not the binding's argument marshalling)
+            torch.cuda._sleep(2_000_000)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             if name == "selected":
