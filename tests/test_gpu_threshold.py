@@ -159,6 +159,36 @@ def test_threshold_parity_small(cfm, wl, path, recovery):
                       recovery=recovery)
 
 
+@pytest.mark.parametrize("path", ["per_pair", "grouped"])
+def test_threshold_every_channel_a_candidate(cfm, path):
+    """c = I with the recovery variant (no sketch activation enters, so both passes skip the screen):
+    S = every channel whose exact |h| reaches tau, the rest through the map with their exact h."""
+    wl = custom_workload("tall", 4, 2, 64, 128, 6, 20, 64, 8, 36)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    tau = calibrated_tau(L, A, Bt, wl.k, wl.c, range(wl.T), between=True)
+    with cfm.forward_path(dict(_paths(cfm))[path]):
+        got, cand, keep, cnt, st = run_threshold(cfm, L, sk, up_bf16(A), up_bf16(Bt), tau, wl.c, wl.r,
+                                                 stats=True, recovery="candidates_exact")
+    assert st["bytes_sketch"] == 0
+    compare_threshold(L, A, Bt, got, cand, keep, cnt, tau, wl.c, what=f"tall {path}", recovery="candidates_exact")
+
+
+def test_threshold_crowded_expert_grouped(cfm):
+    """70 tokens on each of two experts through the grouped pass (several 16-token tiles per expert)."""
+    wl = custom_workload("tcrowded", 2, 2, 96, 128, 70, 10, 20, 8, 21)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    tau = calibrated_tau(L, A, Bt, wl.k, wl.c, range(wl.T), between=True)
+    with cfm.forward_path(cfm.FORWARD_GROUPED):
+        got, cand, keep, cnt = run_threshold(cfm, L, sk, up_bf16(A), up_bf16(Bt), tau, wl.c, wl.r)
+    compare_threshold(L, A, Bt, got, cand, keep, cnt, tau, wl.c, what="tcrowded grouped")
+
+
 @pytest.mark.parametrize("r", [0, 8])
 @pytest.mark.parametrize("path", ["per_pair", "grouped"])
 def test_threshold_edges_match_topk(cfm, path, r):
