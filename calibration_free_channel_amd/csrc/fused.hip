@@ -987,7 +987,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           if (j < cnt) L.hcl[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
-        if (!a.thr) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
+        if (!(!ENV && a.thr)) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
       } else {
         uint64_t raw[32];
         uint32_t kr[32];
@@ -999,11 +999,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           if (j < cnt) L.hcl[i0 + j] = hv;
           kr[j] = score_key(hv);
         }
-        if (!a.thr) block_topk<NT, 32>(kr, i0, cnt, a.c, a.k, L.sel, L.tks);
+        if (!(!ENV && a.thr)) block_topk<NT, 32>(kr, i0, cnt, a.c, a.k, L.sel, L.tks);
       }
       // threshold rule: this thread's range of the candidates' activations is
       // in LDS (written by this thread above)
-      if (a.thr)
+      if (!ENV && a.thr)   // (the envelope entry points keep the top k)
         kk = block_threshold<NT>([&](int i) { return score_key(L.hcl[i]); }, i0, cnt, a.tkey, L.sel, L.tks);
       if (a.k >= a.c) __syncthreads();
       for (int i = tid; i < kk; i += NT) {
@@ -1013,7 +1013,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       __syncthreads();
       if (w == 0 && a.keep_out)
         for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = i < kk ? L.keep[i] : -1;
-      if (w == 0 && a.thr && tid == 0) {
+      if (w == 0 && !ENV && a.thr && tid == 0) {
         a.kcnt[p] = kk;
         if (a.keep_count) a.keep_count[p] = kk;
       }
@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         __syncthreads();
       }
     } else {
-      if (w == 0 && a.thr && tid == 0) {          // c = 0: nothing to keep
+      if (w == 0 && !ENV && a.thr && tid == 0) {          // c = 0: nothing to keep
         a.kcnt[p] = 0;
         if (a.keep_count) a.keep_count[p] = 0;
       }
