@@ -232,6 +232,33 @@ def test_threshold_without_candidates(cfm, path):
 
 
 @pytest.mark.parametrize("path", ["per_pair", "grouped"])
+def test_threshold_determinism_and_batch_invariance(cfm, path):
+    """Two calls agree bit for bit (outputs, sets, counts); on the per-pair pass a token alone gets the
+    bits it gets inside the batch, and on the grouped pass its kept set is the same alone and in the batch
+    (the grouped pass's exact activations are MFMA sums over the expert's tokens, so its output bits may
+    differ with the batch)."""
+    wl = custom_workload("tinv", 8, 2, 128, 256, 8, 23, 46, 8, 15)
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, 8, range(E), E, I, H)
+    tau = calibrated_tau(L, A, Bt, wl.k, wl.c, range(wl.T), between=True)
+    A, Bt = up_bf16(A), up_bf16(Bt)
+    with cfm.forward_path(dict(_paths(cfm))[path]):
+        a = run_threshold(cfm, L, sk, A, Bt, tau, wl.c, wl.r)
+        b = run_threshold(cfm, L, sk, A, Bt, tau, wl.c, wl.r)
+        one = run_threshold(cfm, _token(L, 3), sk, A, Bt, tau, wl.c, wl.r)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    K = wl.shape.K
+    assert np.array_equal(one[3], a[3][3 * K:4 * K])
+    assert np.array_equal(one[2], a[2][3 * K:4 * K])
+    assert np.array_equal(one[1], a[1][3 * K:4 * K])
+    if path == "per_pair":
+        assert np.array_equal(one[0][0], a[0][3])
+
+
+@pytest.mark.parametrize("path", ["per_pair", "grouped"])
 def test_threshold_stats_count_kept_rows(cfm, path):
     """One token with distinct experts: the bytes the call reports equal the oracle's count for the
     kept sets the call returned (the per-pair pass bills per pair, the grouped pass per expert union;
