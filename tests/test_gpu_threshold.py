@@ -337,3 +337,21 @@ def _token(L, t):
                             w=L.host.w[t:t + 1].copy())
     return dataclasses.replace(L, host=h, x=L.x[t:t + 1].contiguous(), ids=L.ids[t:t + 1].contiguous(),
                                w=L.w[t:t + 1].contiguous())
+
+
+def test_threshold_q18_b16_both_passes(cfm):
+    """16 Qwen3-30B-A3B-shaped tokens (18 %: c 276) through both passes, each forced, tau calibrated on the
+    sampled tokens' pairs; compared with the oracle on those tokens."""
+    wl = synth.WORKLOADS["q18_b16"]
+    log("generating the 16-token Qwen3-30B-A3B-shaped layer")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    tokens = [0, wl.T // 2, wl.T - 1]
+    used = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    tau = calibrated_tau(L, A, Bt, wl.k, wl.c, tokens, between=True)
+    for name, path in _paths(cfm):
+        with cfm.forward_path(path):
+            got, cand, keep, cnt = run_threshold(cfm, L, sk, up_bf16(A), up_bf16(Bt), tau, wl.c, wl.r)
+        compare_threshold(L, A, Bt, got, cand, keep, cnt, tau, wl.c, tokens=tokens, what=f"q18_b16 {name}")
