@@ -139,6 +139,8 @@ SMALL = [
     custom_workload("shared16", 8, 2, 128, 256, 16, 23, 46, 8, 20),
     custom_workload("ragged", 6, 3, 101, 128, 9, 17, 33, 8, 5),
     custom_workload("h64", 3, 2, 40, 64, 9, 4, 9, 8, 6),
+    custom_workload("hmax", 2, 2, 24, 8192, 3, 3, 6, 8, 7),
+    custom_workload("imax", 1, 1, 8192, 64, 2, 1474, 2948, 8, 9, rmsnorm=False),
 ]
 
 
