@@ -549,6 +549,32 @@ def test_read_bytes_no_sketch_when_every_channel_is_a_candidate():
         2 * (sk + rest - 4 * H) + io
 
 
+def test_threshold_read_volume_varies_while_topk_is_fixed():
+    """The keep-rule finding on the oracle itself: a threshold calibrated on some tokens for k per pair
+    keeps a different number on each pair of other tokens, so the bytes a token reads vary, and on
+    inputs at 0.8x scale it keeps fewer on average; top-k reads the same bytes for every token."""
+    wg, wu, wd, d, x, ids, w = _small_layer(E=4, I=64, H=128, T=12, K=2, seed=21)
+    E, I, H = wg.shape
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 4)
+    k, c = 12, 24
+    _, cal = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, c, tokens=range(6))
+    tau = O.calibrate_threshold([np.abs(p["h_all"][p["C"]]) for p in cal.values()], k)
+    _, ev = O.select_forward(x, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, c, tokens=range(6, 12), tau=tau)
+    kept = [len(p["S"]) for p in ev.values()]
+    assert len(set(kept)) > 1
+    per_token = []
+    for t in range(6, 12):
+        one = ids[t:t + 1]
+        ks = {(0, q): ev[(t, q)]["S"] for q in range(2)}
+        per_token.append(O.read_bytes(one, E, I, H, 0, c, 4, keep_sets=ks, threshold=True))
+    topk = [O.read_bytes(ids[t:t + 1], E, I, H, k, c, 4) for t in range(6, 12)]
+    assert len(set(per_token)) > 1 and len(set(topk)) == 1
+    xs = O.f64_to_bf16(0.8 * O.bf16_to_f64(x))
+    _, low = O.select_forward(xs, ids, w, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 0, c, tokens=range(6, 12), tau=tau)
+    assert np.mean([len(p["S"]) for p in low.values()]) < np.mean(kept)
+
+
 def test_read_bytes_threshold_counts_the_kept_sets():
     """Threshold rule: candidate rows are always read (their exact |h| decides S) and the down
     rows are the kept sets' sizes, whatever k says."""
