@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="instead of the default line: batch 1, each call timed on its own after a 1 GiB "
                          "cache flush, median / p10 / p90 of the selected and the dense layer")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="instead of the default line: per-phase timeline of the batch-1 selected and dense "
+                         "kernels from in-kernel clock stamps (needs the trace build, CFM_PHASE_TRACE=1)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -210,6 +213,78 @@ def cpu_baseline(wl_name="q18_b1", target_s=10.0):
                       f"(screen, exact top-k, down, recovery, combine) over the tokens' "
                       f"{len(used)} routed experts; sketch and low-rank map prepared untimed",
             "dense_us_per_token": round(us_dense, 1)}
+
+
+SELECT_PHASES = {
+    0: "start", 1: "first loads issued (x, signs, router id, sketch rows, scales, Bt)", 2: "x rotated",
+    3: "screen done", 4: "recovery partial sums published", 5: "sketch activations + partial sums in",
+    6: "top-c done", 7: "exact rows done (h published)", 8: "down-row prefetch issued",
+    9: "exact activations in", 10: "top-k done", 11: "down-row prefetch landed",
+    12: "kept Bt rows in, z formed", 13: "pair output slice stored", 14: "combine done"}
+DENSE_PHASES = {0: "start", 20: "exact rows done", 21: "activations in", 22: "down + combine done"}
+
+
+def phase_trace(torch, cfm, args):
+    """Per-phase timeline of the batch-1 kernels from in-kernel clock stamps (100 MHz device clock),
+    taken from the last launch of a ring of back-to-back launches; medians over repetitions."""
+    import numpy as np
+    E, K, I, H = 128, 8, 768, 2048
+    k, c, r = 138, 276, 64
+    L = args.layers
+    layers = []
+    lr_ws = torch.empty(cfm.lowrank_workspace(E, I, H, r), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        sk = cfm.sketch_build(wg, wu, signs)
+        A, Bt = cfm.lowrank_build(wd, r, ws=lr_ws)
+        layers.append((wg, wu, wd, signs, sk, A, Bt))
+    del lr_ws
+    ring, reps = 16, 60
+    x, ids, w = make_tokens(torch, args.seed + 1, ring, 1, E, K, H)
+    ws_s = cfm.new_workspace(cfm.select_workspace(1, K, E, I, H, k, c, r), "cuda")
+    ws_d = cfm.new_workspace(cfm.dense_workspace(1, K, E, I, H), "cuda")
+    out = torch.empty((ring, 1, H), dtype=torch.bfloat16, device="cuda")
+    buf = torch.zeros(256 * 32, dtype=torch.int64, device="cuda")
+    cfm.phase_trace(buf)
+
+    def sel(i):
+        wg, wu, wd, signs, sk, A, Bt = layers[i % L]
+        cfm.moe_select_forward(x[i], ids[i], w[i], wg, wu, wd, signs, *sk, A, Bt, k, c, r, out=out[i], ws=ws_s)
+
+    def dense(i):
+        wg, wu, wd, *_ = layers[i % L]
+        cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=out[i], ws=ws_d)
+
+    res = {}
+    for name, fn, phases in (("selected", sel, SELECT_PHASES), ("dense", dense, DENSE_PHASES)):
+        for i in range(ring):
+            fn(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(ring):
+                fn(i)
+        rows = []
+        for _ in range(reps):
+            buf.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            rows.append(buf.view(256, 32).cpu().numpy().copy())
+        st = np.stack(rows)                                    # [reps][G][32]
+        t0 = st[:, :, 0].min(axis=1, keepdims=True)
+        rel = (st - t0[:, :, None]) * 0.01                     # us (100 MHz clock)
+        table = {}
+        for n, what in phases.items():
+            v = rel[:, :, n]
+            table[f"{n:02d} {what}"] = {"median_wg_us": round(float(np.median(np.median(v, axis=1))), 2),
+                                        "max_wg_us": round(float(np.median(v.max(axis=1))), 2)}
+        xcd = st[:, :, 31]
+        starts = [round(float(np.median([(st[q, xcd[q] == d, 0].min() - t0[q, 0]) * 0.01 for q in range(reps)])), 2)
+                  for d in range(8)]
+        res[name] = {"phases": table, "xcd_start_us": starts}
+        log(f"{name}: " + "; ".join(f"{kk}: {vv['median_wg_us']}/{vv['max_wg_us']}" for kk, vv in table.items()))
+        log(f"{name}: XCD start offsets (us) {starts}")
+    cfm.phase_trace(None)
+    print(json.dumps({"phase_trace": res, "workload": "q18_b1", "ring": ring, "reps": reps}), flush=True)
 
 
 def stack(torch, cfm, args):
@@ -690,6 +765,9 @@ def main():
         return
     if args.cold:
         cold_timing(torch, cfm, args)
+        return
+    if args.phase_trace:
+        phase_trace(torch, cfm, args)
         return
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64

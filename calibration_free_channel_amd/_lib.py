@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcfm.so")
+# CFM_PHASE_TRACE=1 selects the instrumented build (phase timestamps compiled in)
+LIB_PATH = os.path.join(_HERE, "libcfm_trace.so" if os.environ.get("CFM_PHASE_TRACE") == "1" else "libcfm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python calibration_free_channel_amd/build.py`")
@@ -28,6 +29,9 @@ _SIGS = {
     "cfm_last_error": (ctypes.c_char_p, []),
     "cfm_version": (ctypes.c_char_p, []),
     "sketch_build": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p]),
+    "rotation_signs": (_i, [ctypes.c_uint64, _i, _p, _p]),
+    "sketch_bytes": (_z, [_i, _i, _i]),
+    "sketch_build_seeded": (_i, [_p, _p, _i, _i, _i, ctypes.c_uint64, _p, _p, _p, _p, _p, _p]),
     "lowrank_workspace": (_z, [_i, _i, _i, _i]),
     "lowrank_build": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _z, _p]),
     "select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
@@ -47,6 +51,9 @@ _SIGS = {
     "cfm_set_forward_path": (_i, [_i]),
     "cfm_timing_enable": (_i, [_i]),
     "cfm_timing_report": (_i, [ctypes.c_char_p, _z]),
+    "cfm_phase_trace": (_i, [_p]),
+    "cfm_workspace_status": (_i, [_p, _z, _p]),
+    "cfm_set_wait_limit": (_i, [ctypes.c_uint]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -116,6 +123,42 @@ def sketch_build(w_gate, w_up, signs, out=None):
     _check(_lib.sketch_build(_ptr(w_gate), _ptr(w_up), E, I, H, _ptr(signs), _ptr(tg), _ptr(tu),
                              _ptr(sg), _ptr(su), _stream(dev)), "sketch_build")
     return tg, tu, sg, su
+
+
+def rotation_signs(seed: int, H: int, device="cuda", out=None):
+    """The layer's rotation signs (int8 [H], +-1) from a 64-bit seed (SplitMix64, bit 63)."""
+    if out is None:
+        out = torch.empty(H, dtype=torch.int8, device=device)
+    if out.dtype != torch.int8 or out.numel() != H:
+        raise ValueError("signs: int8 tensor of H entries")
+    _check(_lib.rotation_signs(ctypes.c_uint64(seed & (2**64 - 1)), H, _ptr(out), _stream(out.device)),
+           "rotation_signs")
+    return out
+
+
+def sketch_bytes(E: int, I: int, H: int) -> int:
+    """Device bytes of one layer's sketch (codes, scales and signs)."""
+    return int(_lib.sketch_bytes(E, I, H))
+
+
+def sketch_build_seeded(w_gate, w_up, seed: int, out=None):
+    """Signs from `seed`, then the sketch. Returns (signs, tg, tu, sg, su)."""
+    _bf16(w_gate, "w_gate"), _bf16(w_up, "w_up")
+    E, I, H = w_gate.shape
+    if w_up.shape != w_gate.shape:
+        raise ValueError("shape mismatch")
+    dev = w_gate.device
+    if out is None:
+        out = (torch.empty(H, dtype=torch.int8, device=dev),
+               torch.empty((E, I, H // 4), dtype=torch.uint8, device=dev),
+               torch.empty((E, I, H // 4), dtype=torch.uint8, device=dev),
+               torch.empty((E, I), dtype=torch.float32, device=dev),
+               torch.empty((E, I), dtype=torch.float32, device=dev))
+    signs, tg, tu, sg, su = out
+    _check(_lib.sketch_build_seeded(_ptr(w_gate), _ptr(w_up), E, I, H, ctypes.c_uint64(seed & (2**64 - 1)),
+                                    _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su), _stream(dev)),
+           "sketch_build_seeded")
+    return signs, tg, tu, sg, su
 
 
 def lowrank_workspace(E, I, H, r) -> int:
@@ -311,6 +354,26 @@ def timing_report() -> dict:
         name, cnt, ms = line.split()
         out[name] = (int(cnt), float(ms))
     return out
+
+
+def workspace_status(ws) -> int:
+    """Synchronise the current stream, read and clear the workspace's failure word: 0 if no bounded
+    wait of a forward call on it expired since the last check, else CFM_ETIMEOUT (-5)."""
+    return int(_lib.cfm_workspace_status(_ptr(ws), ws.numel(), _stream(ws.device)))
+
+
+def set_wait_limit(polls: int) -> int:
+    """Polls of one exchanged value before a single-launch forward call gives up (default 2^20;
+    0: every wait gives up at once, for testing the failure path). Returns the previous value."""
+    return int(_lib.cfm_set_wait_limit(int(polls)))
+
+
+def phase_trace(buf):
+    """Phase timestamps of every later per-pair launch into buf (int64 device tensor of at least
+    256 * 32 entries; None stops). Needs the trace build (CFM_PHASE_TRACE=1)."""
+    if buf is not None and (buf.dtype != torch.int64 or buf.numel() < 256 * 32):
+        raise ValueError("phase-trace buffer: int64 tensor of at least 256 * 32 entries")
+    _check(_lib.cfm_phase_trace(_ptr(buf)), "cfm_phase_trace")
 
 
 def decode_stats(buf) -> dict:

@@ -2,10 +2,13 @@
 // Validation is plain host code that runs before any HIP call, so argument
 // errors are reported the same way on machines without a GPU.
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "cfm_internal.h"
@@ -39,6 +42,30 @@ hipEvent_t take_event() {
 }  // namespace
 
 bool timing_on() { return g_timing; }
+
+// ---------------------------------------------------------------- workspace layouts
+namespace {
+std::mutex g_ws_mu;
+std::unordered_map<uintptr_t, uint64_t> g_ws_sig;    // workspace address -> layout of its last call
+std::atomic<unsigned> g_wait_limit{1u << 20};
+}  // namespace
+
+int prepare_workspace(void* ws, size_t bytes, uint64_t sig, hipStream_t stream) {
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_sig.find(reinterpret_cast<uintptr_t>(ws));
+    if (it == g_ws_sig.end()) {
+      g_ws_sig.emplace(reinterpret_cast<uintptr_t>(ws), sig);
+    } else if (it->second != sig) {
+      it->second = sig;
+      clear = true;
+    }
+  }
+  return clear ? launch_zero_fill(ws, bytes, stream) : CFM_OK;
+}
+
+unsigned wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 
 void timing_begin(const char* name, hipStream_t s) {
   if (!g_timing) return;
@@ -76,8 +103,8 @@ int check_budget(int I, int H, int k, int c, int r) {
   return CFM_OK;
 }
 
-// Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped.
-int g_path = 0;
+// Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped (process-wide).
+std::atomic<int> g_path{0};
 // Automatic choice: the grouped pass from these batch sizes on (measured on the
 // Qwen3-30B-A3B-shaped layer: below them the single-launch per-pair kernels
 // are faster; at 64 tokens the grouped selected layer takes 6.0 us/token
@@ -88,9 +115,10 @@ constexpr int kGroupedMinTokensDense = 32;
 // Whether a forward call uses the grouped pass (or an error status).
 int pick_grouped(int T, int K, int E, int I, int H, int r, bool dense, bool* grouped) {
   const bool ok = grouped_supported(T, K, E, I, H, r, dense);
-  if (g_path == 2 && !ok) return set_error(CFM_EUNSUPPORTED, "expert-grouped pass: shape not supported");
+  const int path = g_path.load(std::memory_order_relaxed);
+  if (path == 2 && !ok) return set_error(CFM_EUNSUPPORTED, "expert-grouped pass: shape not supported");
   const int min_tokens = dense ? kGroupedMinTokensDense : kGroupedMinTokensSelect;
-  *grouped = g_path == 2 || (g_path == 0 && ok && T >= min_tokens);
+  *grouped = path == 2 || (path == 0 && ok && T >= min_tokens);
   return CFM_OK;
 }
 
@@ -153,14 +181,36 @@ const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
 
 int cfm_set_forward_path(int path) {
   if (path < 0 || path > 2) return set_error(CFM_EINVAL, "path must be 0, 1 or 2");
-  const int prev = g_path;
-  g_path = path;
-  return prev;
+  return g_path.exchange(path);
 }
 
 int cfm_timing_enable(int on) {
   g_timing = on != 0;
   return CFM_OK;
+}
+
+int cfm_set_wait_limit(unsigned polls) { return (int)g_wait_limit.exchange(polls); }
+
+int cfm_workspace_status(void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!ws) return set_error(CFM_EINVAL, "cfm_workspace_status: null workspace");
+  if (ws_bytes < kFailWordOffset + 4) return set_error(CFM_EWORKSPACE, "cfm_workspace_status: workspace too small");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  char* fail = static_cast<char*>(ws) + kFailWordOffset;
+  CFM_HIP_TRY(hipMemcpyAsync(&word, fail, 4, hipMemcpyDeviceToHost, s));
+  CFM_HIP_TRY(hipStreamSynchronize(s));
+  if (word == 0) return CFM_OK;
+  static const uint32_t zero = 0;
+  CFM_HIP_TRY(hipMemcpyAsync(fail, &zero, 4, hipMemcpyHostToDevice, s));
+  CFM_HIP_TRY(hipStreamSynchronize(s));
+  return set_error(CFM_ETIMEOUT, "a bounded wait expired in a forward call on this workspace (launch tag " +
+                                     std::to_string(word) + "): that call's outputs are NaN");
+}
+
+int cfm_phase_trace(void* buf) {
+  clear_error();
+  return set_phase_trace(buf);
 }
 
 int cfm_timing_report(char* buf, size_t len) {
@@ -200,6 +250,30 @@ int sketch_build(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int
   if ((long)E * I * 2 > 0x7FFFFFFFL) return set_error(CFM_EUNSUPPORTED, "too many rows");
   return launch_sketch_build(w_gate, w_up, E, I, H, signs, tg, tu, sg, su,
                              static_cast<hipStream_t>(stream));
+}
+
+int rotation_signs(uint64_t seed, int H, int8_t* signs, void* stream) {
+  clear_error();
+  if (H <= 0 || H > (1 << 24)) return set_error(CFM_EINVAL, "rotation_signs: H must lie in [1, 2^24]");
+  if (!signs) return set_error(CFM_EINVAL, "rotation_signs: null pointer");
+  return launch_rotation_signs(seed, H, signs, static_cast<hipStream_t>(stream));
+}
+
+size_t sketch_bytes(int E, int I, int H) {
+  if (E <= 0 || I <= 0 || H < 64 || H > kMaxH || !is_pow2(H) || I > kMaxI) return 0;
+  const size_t rows = (size_t)E * I;
+  return 2 * rows * (size_t)(H / 4) + 2 * rows * sizeof(float) + (size_t)H;
+}
+
+int sketch_build_seeded(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H, uint64_t seed,
+                        int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su, void* stream) {
+  clear_error();
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (!w_gate || !w_up || !signs || !tg || !tu || !sg || !su)
+    return set_error(CFM_EINVAL, "sketch_build_seeded: null pointer");
+  if ((long)E * I * 2 > 0x7FFFFFFFL) return set_error(CFM_EUNSUPPORTED, "too many rows");
+  if (int rc = launch_rotation_signs(seed, H, signs, static_cast<hipStream_t>(stream))) return rc;
+  return launch_sketch_build(w_gate, w_up, E, I, H, signs, tg, tu, sg, su, static_cast<hipStream_t>(stream));
 }
 
 size_t lowrank_workspace(int E, int I, int H, int r) {

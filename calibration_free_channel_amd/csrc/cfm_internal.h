@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/cfm.h"
@@ -15,6 +16,25 @@ namespace cfm {
 // Records a message for cfm_last_error() and returns `code`.
 int set_error(int code, const std::string& msg);
 void clear_error();
+
+// Clears the first `bytes` of a forward workspace on `stream` (a fill kernel)
+// when its previous call laid it out differently (signature `sig`); the first
+// call on a workspace takes it as zero-filled by the caller.
+int prepare_workspace(void* ws, size_t bytes, uint64_t sig, hipStream_t stream);
+// FNV-1a hash of a plan's layout-determining values.
+inline uint64_t layout_signature(std::initializer_list<long> v) {
+  uint64_t h = 1469598103934665603ull;
+  for (long x : v) {
+    for (int b = 0; b < 8; ++b) {
+      h ^= (uint64_t)((unsigned long)x >> (8 * b)) & 0xFF;
+      h *= 1099511628211ull;
+    }
+  }
+  return h;
+}
+// Polls of one exchanged value before a single-launch forward pass gives up
+// (cfm_set_wait_limit; 0: every wait gives up at once).
+unsigned wait_limit();
 
 // Optional per-kernel event timing (cfm_timing_enable); no-ops while disabled.
 bool timing_on();

@@ -8,6 +8,14 @@
 
 namespace cfm {
 
+// Byte offset of the failed-launch word in every forward workspace (after the
+// 256 launch sequence slots; the same in every layout).
+constexpr size_t kFailWordOffset = 1024;
+// Zero-fills bytes [0, n) of device memory on `stream` (a fill kernel: no
+// memset node, so it may be captured in a graph).
+int launch_zero_fill(void* p, size_t n, hipStream_t stream);
+
+int launch_rotation_signs(uint64_t seed, int H, int8_t* signs, hipStream_t stream);
 int launch_sketch_build(const uint16_t* w_gate, const uint16_t* w_up, int E, int I, int H,
                         const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,
                         hipStream_t stream);
@@ -44,8 +52,10 @@ struct ForwardPlan {
   size_t off_kc;                         // i32 [P] kept counts (threshold keep rule)
   size_t bytes;
 };
-ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool env = false);
-ForwardPlan dense_plan(int T, int K, int E, int I, int H, bool env = false);
+// G_max: the most workgroups one launch may use (256 for the size queries;
+// the launch refits the plan to what the device holds at once)
+ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool env = false, int G_max = 256);
+ForwardPlan dense_plan(int T, int K, int E, int I, int H, bool env = false, int G_max = 256);
 
 struct SelectArgs {
   const uint16_t *x, *w_gate, *w_up, *w_down_t, *A, *Bt;
@@ -74,6 +84,8 @@ struct SelectArgs {
   int32_t* keep_count;
 };
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
+// Phase-timestamp buffer for the single-launch kernels (trace build only).
+int set_phase_trace(void* buf);
 int launch_dense_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 
 // ---------------------------------------------------------------- expert-grouped forward pass

@@ -1,0 +1,16 @@
+// Instances of the single-launch forward kernels for EPT = 0 (hidden width
+// below 1024 except 512).
+#include "fused_kernels.h"
+
+namespace cfm {
+
+const void* fused_kernel_e0(bool select, bool recx, bool env) {
+  if (!select) return env ? reinterpret_cast<const void*>(&k_dense_fused<0, true>)
+                          : reinterpret_cast<const void*>(&k_dense_fused<0, false>);
+  if (recx) return env ? reinterpret_cast<const void*>(&k_select_fused<0, true, true>)
+                       : reinterpret_cast<const void*>(&k_select_fused<0, true, false>);
+  return env ? reinterpret_cast<const void*>(&k_select_fused<0, false, true>)
+             : reinterpret_cast<const void*>(&k_select_fused<0, false, false>);
+}
+
+}  // namespace cfm

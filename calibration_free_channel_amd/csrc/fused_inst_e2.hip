@@ -1,0 +1,16 @@
+// Instances of the single-launch forward kernels for EPT = 2 (hidden width
+// 512).
+#include "fused_kernels.h"
+
+namespace cfm {
+
+const void* fused_kernel_e2(bool select, bool recx, bool env) {
+  if (!select) return env ? reinterpret_cast<const void*>(&k_dense_fused<2, true>)
+                          : reinterpret_cast<const void*>(&k_dense_fused<2, false>);
+  if (recx) return env ? reinterpret_cast<const void*>(&k_select_fused<2, true, true>)
+                       : reinterpret_cast<const void*>(&k_select_fused<2, true, false>);
+  return env ? reinterpret_cast<const void*>(&k_select_fused<2, false, true>)
+             : reinterpret_cast<const void*>(&k_select_fused<2, false, false>);
+}
+
+}  // namespace cfm

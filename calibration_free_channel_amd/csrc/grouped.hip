@@ -5,7 +5,8 @@
 // all"): each routed (token, expert) pair still screens with the sketch, takes
 // its own top-c candidates, its own exact top-k and its own recovery term. What
 // changes is who reads the weights. Once a batch routes several tokens to one
-// expert (batch 8 and up: the article's batch-size table), the pairs are
+// expert (batch 8 and up, where the article, section "Numbers and limits",
+// reports its largest gains, peaking at batch 8 or 16), the pairs are
 // grouped by expert and every weight row an expert needs is read once for all
 // of its tokens:
 //   - the sketch rows of an expert, screened for up to 16 of its tokens per
@@ -1302,6 +1303,11 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
 }
 
 int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
+  if (int rc = prepare_workspace(s.ws, g.bytes,
+                                 layout_signature({3, g.T, g.K, g.E, g.I, g.H, g.k, g.c, g.r, g.dense ? 1 : 0,
+                                                   s.resid ? 1 : 0, (long)g.bytes}),
+                                 stream))
+    return rc;
   GArgs a{};
   a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
   if (s.resid) {

@@ -97,7 +97,29 @@ __global__ __launch_bounds__(kSketchThreads) void k_sketch_rows(
   }
 }
 
+// The layer's rotation signs from a seed: d_i = +1 if bit 63 of the i-th output
+// of SplitMix64 started at `seed` is 0, else -1. SplitMix64 (Steele, Lea and
+// Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014): the
+// state advances by the golden-ratio constant and each output is the state
+// after two xor-shift-multiply rounds and a final xor-shift, so output i
+// depends only on seed + (i + 1) * gamma (counter-based).
+__global__ void k_rotation_signs(uint64_t seed, int H, int8_t* __restrict__ signs) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H) return;
+  uint64_t z = seed + (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  signs[i] = (z >> 63) ? (int8_t)-1 : (int8_t)1;
+}
+
 }  // namespace
+
+int launch_rotation_signs(uint64_t seed, int H, int8_t* signs, hipStream_t stream) {
+  hipLaunchKernelGGL(k_rotation_signs, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, stream, seed, H, signs);
+  CFM_LAUNCH_CHECK("k_rotation_signs");
+  return CFM_OK;
+}
 
 int launch_sketch_build(const uint16_t* w_gate, const uint16_t* w_up, int E, int I, int H,
                         const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,

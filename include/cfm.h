@@ -46,7 +46,8 @@ enum {
   CFM_EINVAL = -1,        /* null pointer where one is required, negative or zero sizes */
   CFM_EUNSUPPORTED = -2,  /* shape or budget outside the supported range (see each call) */
   CFM_EWORKSPACE = -3,    /* workspace missing or smaller than the size query returns */
-  CFM_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+  CFM_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  CFM_ETIMEOUT = -5       /* a bounded wait inside a forward call expired (cfm_workspace_status) */
 };
 
 /* Message of the last failing call on this thread ("" if none). */
@@ -84,6 +85,38 @@ const char* cfm_version(void);
 int sketch_build(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H,
                  const int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su,
                  void* stream);
+
+/*
+ * rotation_signs - the layer's random rotation signs from a seed (article
+ * section "A reader that needs no data at all": the sketch is a rotated
+ * ternary one; the rotation is a random-sign Walsh-Hadamard transform, and the
+ * same signs rotate the hidden states at run time).
+ *   signs[i] = +1 if bit 63 of z_i is 0, else -1, for i < H, where z_i is
+ *   output i (counting from 0) of SplitMix64 seeded with `seed`:
+ *     s = seed + (i + 1) * 0x9E3779B97F4A7C15 (mod 2^64)
+ *     z = (s ^ (s >> 30)) * 0xBF58476D1CE4E5B9
+ *     z = (z ^ (z >> 27)) * 0x94D049BB133111EB
+ *     z_i = z ^ (z >> 31)
+ *   signs : out [H] int8 (device). 1 <= H <= 2^24. Enqueued on `stream`.
+ */
+int rotation_signs(uint64_t seed, int H, int8_t* signs, void* stream);
+
+/*
+ * sketch_bytes - device bytes of one layer's sketch: the packed codes tg and
+ * tu (E*I*H/4 bytes each), the scales sg and su (E*I float32 each) and the
+ * signs (H int8). 0 for a shape sketch_build does not support.
+ */
+size_t sketch_bytes(int E, int I, int H);
+
+/*
+ * sketch_build_seeded - rotation_signs(seed, H, signs) followed by
+ * sketch_build with those signs, in stream order: the sketch of a layer from
+ * its weights and a seed alone. signs is an output here ([H] int8); every
+ * other argument, the layouts, the supported range and the errors are those
+ * of sketch_build.
+ */
+int sketch_build_seeded(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int I, int H, uint64_t seed,
+                        int8_t* signs, uint8_t* tg, uint8_t* tu, float* sg, float* su, void* stream);
 
 /*
  * lowrank_build - rank-r map of every expert's down projection.
@@ -135,7 +168,15 @@ int lowrank_build(const cfm_bf16* w_down_t, int E, int I, int H, int r, cfm_bf16
  *   stats    : optional out, device cfm_stats (bytes the call reads).
  *   ws       : device workspace of at least select_workspace(...) bytes. It
  *              must be zero-filled once after allocation; every call leaves it
- *              ready for the next. Calls sharing a workspace must not overlap.
+ *              ready for the next call of the same shape. When a call's layout
+ *              differs from the previous call on the same workspace (another
+ *              T, K, E, I, H, k, c or r, another pass, the dense layer), the
+ *              library clears the workspace first with a fill kernel on
+ *              `stream` (the library remembers, per workspace address, the
+ *              layout of its last call). Calls sharing a workspace must not
+ *              overlap. A wait between the workgroups of the single-launch
+ *              pass that expires (see cfm_workspace_status) makes that call's
+ *              outputs NaN instead of hanging.
  * Supported: H a power of two, 64 <= H <= 8192; 1 <= I <= 8192;
  *            0 <= k <= c <= I; 0 <= r <= min(H, I), r <= 128; K <= 64.
  *            T = 0 is a no-op.
@@ -272,14 +313,17 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
 
 /*
  * cfm_set_forward_path - which kernels serve moe_select_forward and
- * moe_dense_forward (process-wide; returns the previous setting, or CFM_EINVAL).
+ * moe_dense_forward (process-wide, shared by every thread of the process; an
+ * atomic setting, but a call on one thread changes the pass of concurrent
+ * calls on others; returns the previous setting, or CFM_EINVAL).
  *   0 automatic (default): the expert-grouped pass where the shape allows it
  *     and the batch is large (selected layer: 48 tokens or more; dense layer:
  *     32 or more), the per-pair pass otherwise;
  *   1 the per-pair pass (one persistent launch; lowest latency at batch 1);
  *   2 the expert-grouped pass (pairs grouped by expert; each weight row an
- *     expert needs is read once for all of its tokens: the article's batch
- *     8 / 16 regime, aimodeling.com article, batch-size table). Calls whose
+ *     expert needs is read once for all of its tokens: the larger batches at
+ *     which the article, section "Numbers and limits", reports the largest
+ *     gains, peaking at batch 8 or 16). Calls whose
  *     shape it does not cover return CFM_EUNSUPPORTED: it needs T K <= 65535,
  *     E <= 4096, and for the selected layer r a multiple of 8.
  * Both passes compute the same selections (identical sketch activations, so
@@ -299,6 +343,42 @@ int cfm_set_forward_path(int path);
  */
 int cfm_timing_enable(int on);
 int cfm_timing_report(char* buf, size_t len);
+
+/*
+ * cfm_workspace_status - the failure channel of the forward calls. The
+ * single-launch pass (the per-pair kernel behind moe_select_forward, its
+ * variants, moe_dense_forward and the moe_layer_* calls at small batch) runs
+ * all of its workgroups at once, sized from the device's compute units and the
+ * kernel's occupancy, and they exchange values through the workspace with
+ * bounded waits. If a wait expires (for instance because other work occupied
+ * compute units, so the workgroups were not all resident), the call's outputs
+ * are NaN and a failure word in the workspace records it. This call
+ * synchronises `stream`, reads and clears that word, and returns CFM_OK if no
+ * wait expired since the last check (or since the workspace was zeroed), else
+ * CFM_ETIMEOUT. ws_bytes: the workspace size (at least 1028 bytes).
+ */
+int cfm_workspace_status(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * cfm_set_wait_limit - polls of one exchanged value before a single-launch
+ * forward pass gives up (process-wide; default 2^20, about one second). 0
+ * makes every wait give up at once, so that the failure path can be exercised
+ * without a fault: every workgroup still runs to its end. Returns the
+ * previous value. Instrumentation and testing only.
+ */
+int cfm_set_wait_limit(unsigned polls);
+
+/*
+ * cfm_phase_trace - instrumentation of the single-launch kernels (not part of
+ * the method). In the trace build of the library (compiled with
+ * CFM_PHASE_TRACE), every later per-pair launch stores, from thread 0 of each
+ * workgroup b, the 100 MHz device clock at fixed points of its phases into
+ * buf[b * 32 + n] (uint64, device memory of at least 256 * 32 * 8 bytes) and
+ * the XCD it runs on into buf[b * 32 + 31]; buf = NULL stops it. Each launch
+ * overwrites the previous one's stamps. Host-side state only; not
+ * thread-safe. The default build returns CFM_EUNSUPPORTED.
+ */
+int cfm_phase_trace(void* buf);
 
 #ifdef __cplusplus
 }

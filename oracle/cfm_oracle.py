@@ -98,6 +98,33 @@ def hadamard(H: int) -> np.ndarray:
     return m
 
 
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int) -> list:
+    """The first n outputs of SplitMix64 started at `seed` (Steele, Lea and Flood,
+    "Fast splittable pseudorandom number generators", OOPSLA 2014): the state
+    advances by the 64-bit golden-ratio increment, and each output is the new
+    state passed through two xor-shift-multiply rounds and a final xor-shift
+    (all arithmetic mod 2^64)."""
+    out, state = [], seed & _M64
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & _M64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def rotation_signs(seed: int, H: int) -> np.ndarray:
+    """The layer's random signs d of the rotation, from a seed (article section
+    "A reader that needs no data at all": the sketch is rotated; the pages do
+    not say how the rotation is drawn). Reading: d_i = -1 if bit 63 of
+    SplitMix64's i-th output is set, else +1. int8 [H]."""
+    return np.array([-1 if (z >> 63) & 1 else 1 for z in splitmix64(seed, H)], dtype=np.int8)
+
+
 def rotate(v: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """T(v) = Hadamard · (d ⊙ v) along the last axis, float64.
 

@@ -700,3 +700,26 @@ def test_layer_residual_added_once_before_rounding():
         want = O.bf16_to_f64(hh) + yb
         assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 2.0 ** -8 * np.abs(yb) + 1e-30)
 
+
+
+# ----------------------------------------------------------------------------- rotation signs from a seed
+
+def test_splitmix64_matches_published_outputs(golden_dir):
+    """SplitMix64 against its reference outputs (tests/golden/splitmix64_vectors.json)."""
+    import json
+    g = json.load(open(os.path.join(golden_dir, "splitmix64_vectors.json")))
+    for v in g["vectors"]:
+        want = [int(h, 16) for h in v["outputs_hex"]] if "outputs_hex" in v else [int(d) for d in v["outputs_dec"]]
+        assert O.splitmix64(v["seed"], len(want)) == want
+
+
+def test_rotation_signs_take_bit_63():
+    """d_i = -1 exactly when the i-th output's top bit is set; +-1 only; about half each."""
+    zs = O.splitmix64(1234567, 4096)
+    d = O.rotation_signs(1234567, 4096)
+    assert d.dtype == np.int8 and set(np.unique(d)) <= {-1, 1}
+    assert np.array_equal(d, np.array([-1 if z >= 1 << 63 else 1 for z in zs], np.int8))
+    assert abs(int((d < 0).sum()) - 2048) < 4 * 32       # within 4 sigma of a fair coin
+    # the i-th sign depends only on (seed, i): a longer vector extends a shorter one
+    assert np.array_equal(O.rotation_signs(99, 64), O.rotation_signs(99, 256)[:64])
+    assert not np.array_equal(O.rotation_signs(99, 256), O.rotation_signs(100, 256))
