@@ -37,6 +37,8 @@ _SIGS = {
     "select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "moe_select_forward": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                 _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _z, _p]),
+    "moe_select_forward_noalloc": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
+                                        _p, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_select_forward_ex": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
                                    _p, _p, _i, _i, _i, ctypes.c_uint, _p, _p, _p, _p, _p, _z, _p]),
     "moe_select_forward_threshold": (_i, [_p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p,
@@ -228,6 +230,24 @@ def moe_select_forward(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, t
         _check(_lib.moe_select_forward_ex(*head, flags, *tail), "moe_select_forward_ex")
     else:
         _check(_lib.moe_select_forward(*head, *tail), "moe_select_forward")
+    return out
+
+
+def moe_select_forward_noalloc(x, topk_ids, topk_w, w_gate, w_up, w_down_t, signs, tg, tu, sg, su, A, Bt,
+                               k, c, r, out=None, cand_out=None, keep_out=None, stats=None):
+    """moe_select_forward on the library's own per-GPU scratch (no workspace argument; the call
+    allocates no device memory when `out` is given). Returns out [T][H] BF16."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(_lib.moe_select_forward_noalloc(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_w), T, K, _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), E, I, H,
+        _ptr(signs), _ptr(tg), _ptr(tu), _ptr(sg), _ptr(su), _ptr(A) if r > 0 else None,
+        _ptr(Bt) if r > 0 else None, k, c, r, _ptr(out), _ptr(cand_out), _ptr(keep_out), _ptr(stats),
+        _stream(dev)), "moe_select_forward_noalloc")
     return out
 
 

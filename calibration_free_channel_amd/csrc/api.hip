@@ -131,6 +131,39 @@ int check_tokens(int T, int K) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- scratch of the no-allocation entry point
+// Device memory of moe_select_forward_noalloc: one copy per GPU, held until
+// the process ends. In host code `scratch` is only a symbol: its device
+// address on the current GPU comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;       // device -> its copy of `scratch`
+
+// The current device's scratch address; on a device's first call, looked up
+// and zero-filled (a fill kernel on `stream`, ahead of the caller's work).
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  CFM_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return CFM_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return set_error(CFM_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  if (int rc = launch_zero_fill(ptr, kScratchBytes, stream)) return rc;
+  g_scratch_ptr.emplace(dev, ptr);
+  *out = ptr;
+  return CFM_OK;
+}
+}  // namespace
 }  // namespace cfm
 
 using namespace cfm;
@@ -331,6 +364,28 @@ int moe_select_forward_threshold(const cfm_bf16* x, const int32_t* topk_ids, con
   return select_entry(x, topk_ids, topk_w, T, K, w_gate, w_up, w_down_t, E, I, H, signs, tg, tu, sg, su, A, Bt,
                       c, c, r, flags, true, tau, out, cand_out, keep_out, keep_count, stats, ws, ws_bytes,
                       stream);
+}
+
+int moe_select_forward_noalloc(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int K,
+                               const cfm_bf16* w_gate, const cfm_bf16* w_up, const cfm_bf16* w_down_t, int E,
+                               int I, int H, const int8_t* signs, const uint8_t* tg, const uint8_t* tu,
+                               const float* sg, const float* su, const cfm_bf16* A, const cfm_bf16* Bt, int k,
+                               int c, int r, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out, cfm_stats* stats,
+                               void* stream) {
+  clear_error();
+  if (int rc = check_tokens(T, K)) return rc;
+  if (int rc = check_shape(E, I, H, true)) return rc;
+  if (int rc = check_budget(I, H, k, c, r)) return rc;
+  if (T == 0) return CFM_OK;
+  const size_t need = select_workspace(T, K, E, I, H, k, c, r);
+  if (need > kScratchBytes)
+    return set_error(CFM_EWORKSPACE, "moe_select_forward_noalloc: the call needs " + std::to_string(need) +
+                                         " bytes of scratch, more than its 32 MiB (use moe_select_forward with a "
+                                         "workspace)");
+  void* ws = nullptr;
+  if (int rc = scratch_address(static_cast<hipStream_t>(stream), &ws)) return rc;
+  return select_entry(x, topk_ids, topk_w, T, K, w_gate, w_up, w_down_t, E, I, H, signs, tg, tu, sg, su, A, Bt,
+                      k, c, r, 0u, false, 0.f, out, cand_out, keep_out, nullptr, stats, ws, kScratchBytes, stream);
 }
 
 int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,

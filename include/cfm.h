@@ -201,6 +201,31 @@ int moe_select_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* 
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_select_forward_noalloc - moe_select_forward for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). It takes no workspace:
+ * its scratch is a 32 MiB array in the library's own device memory, one copy
+ * per GPU, created with the library and held until the process ends; the call
+ * allocates nothing (no hipMalloc, no allocating library routine). The first
+ * call on a GPU looks the array up and zero-fills it on `stream`.
+ *   Every argument, output, layout and supported range is that of
+ *   moe_select_forward (flags 0, top-k keep rule). A call whose
+ *   select_workspace(T, K, E, I, H, k, c, r) exceeds 32 MiB returns
+ *   CFM_EWORKSPACE (the Qwen3-30B-A3B-shaped layer fits up to 64 tokens).
+ *   All calls on one GPU share its scratch, which keeps the last call's
+ *   contents (a call at another shape clears it first, as with any
+ *   workspace): calls that overlap on one GPU (concurrent streams or threads)
+ *   race and must not be issued. The scratch has no handle for
+ *   cfm_workspace_status; an expired exchange wait shows only as NaN outputs.
+ */
+int moe_select_forward_noalloc(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int K,
+                               const cfm_bf16* w_gate, const cfm_bf16* w_up, const cfm_bf16* w_down_t, int E,
+                               int I, int H, const int8_t* signs, const uint8_t* tg, const uint8_t* tu,
+                               const float* sg, const float* su, const cfm_bf16* A, const cfm_bf16* Bt, int k,
+                               int c, int r, cfm_bf16* out, int32_t* cand_out, int32_t* keep_out, cfm_stats* stats,
+                               void* stream);
+
+/*
  * moe_select_forward_ex - moe_select_forward with variant flags (flags = 0 is
  * moe_select_forward exactly).
  *
