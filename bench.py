@@ -220,7 +220,12 @@ SELECT_PHASES = {
     3: "screen done", 4: "recovery partial sums published", 5: "sketch activations + partial sums in",
     6: "top-c done", 7: "exact rows done (h published)", 8: "down-row prefetch issued",
     9: "exact activations in", 10: "top-k done", 11: "down-row prefetch landed",
-    12: "kept Bt rows in, z formed", 13: "pair output slice stored", 14: "combine done"}
+    12: "kept Bt rows in, z formed", 13: "pair output slice stored", 14: "combine done",
+    15: "wave 0 sketch activations in", 16: "wave 1 sketch activations in", 17: "wave 2 sketch activations in",
+    18: "wave 3 sketch activations in", 19: "wave 0 exact activations in", 20: "wave 1 exact activations in",
+    21: "wave 2 exact activations in", 22: "wave 3 exact activations in", 23: "top-c range known",
+    24: "top-c pass 1", 25: "top-c last pass", 26: "top-c ranks known", 27: "top-k range known",
+    28: "top-k pass 1", 29: "top-k last pass", 30: "top-k ranks known"}
 DENSE_PHASES = {0: "start", 20: "exact rows done", 21: "activations in", 22: "down + combine done"}
 
 
@@ -270,19 +275,29 @@ def phase_trace(torch, cfm, args):
             torch.cuda.synchronize()
             rows.append(buf.view(256, 32).cpu().numpy().copy())
         st = np.stack(rows)                                    # [reps][G][32]
+        passes = {}
+        if name == "selected":                                 # (clock << 4 | passes) in the last-pass slots
+            for slot, what in ((25, "top-c"), (29, "top-k")):
+                v = st[:, :, slot]
+                passes[what] = np.bincount(np.where(v > 0, v & 15, 1).ravel()).tolist()
+                st[:, :, slot] = v >> 4
         t0 = st[:, :, 0].min(axis=1, keepdims=True)
-        rel = (st - t0[:, :, None]) * 0.01                     # us (100 MHz clock)
+        rel = np.where(st > 0, (st - t0[:, :, None]) * 0.01, np.nan)   # us (100 MHz clock); 0 = not stamped
         table = {}
         for n, what in phases.items():
             v = rel[:, :, n]
-            table[f"{n:02d} {what}"] = {"median_wg_us": round(float(np.median(np.median(v, axis=1))), 2),
-                                        "max_wg_us": round(float(np.median(v.max(axis=1))), 2)}
+            if np.isnan(v).all():
+                continue
+            table[f"{n:02d} {what}"] = {"median_wg_us": round(float(np.nanmedian(np.nanmedian(v, axis=1))), 2),
+                                        "max_wg_us": round(float(np.nanmedian(np.nanmax(v, axis=1))), 2)}
         xcd = st[:, :, 31]
         starts = [round(float(np.median([(st[q, xcd[q] == d, 0].min() - t0[q, 0]) * 0.01 for q in range(reps)])), 2)
                   for d in range(8)]
-        res[name] = {"phases": table, "xcd_start_us": starts}
+        res[name] = {"phases": table, "xcd_start_us": starts, "select_pass_histogram": passes}
+        if os.environ.get("CFM_TRACE_DUMP"):
+            np.save(os.environ["CFM_TRACE_DUMP"] + f"_{name}.npy", st)
         log(f"{name}: " + "; ".join(f"{kk}: {vv['median_wg_us']}/{vv['max_wg_us']}" for kk, vv in table.items()))
-        log(f"{name}: XCD start offsets (us) {starts}")
+        log(f"{name}: XCD start offsets (us) {starts}; passes per select (count of workgroups by passes) {passes}")
     cfm.phase_trace(None)
     print(json.dumps({"phase_trace": res, "workload": "q18_b1", "ring": ring, "reps": reps}), flush=True)
 

@@ -48,6 +48,7 @@ struct ForwardPlan {
   size_t off_seq, off_err, off_ctr;      // u32 [256], u32, u32 [T][nhs]
   size_t off_xh, off_xz, off_xc;         // tagged u64 [P][I], [P][nw][r], [P][c]
   size_t off_ypart;                      // f32 [P][H]
+  size_t off_ypt;                        // tagged u64 [P][H] pair outputs (lean instance's combine)
   size_t off_xl;                         // tagged u64 [T][E] router logits (envelope)
   size_t off_kc;                         // i32 [P] kept counts (threshold keep rule)
   size_t bytes;

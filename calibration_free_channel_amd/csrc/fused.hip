@@ -107,11 +107,11 @@ int resident_workgroups(const void* fn, size_t lds, int* out) {
 // Whether the lean instance serves a selected launch: the plain method at
 // hidden width 2048 with the candidates' rows prefetched over 8 output chunks
 // per workgroup, rank 64, one screen sub-chunk per workgroup, at most 4 keys
-// per thread in each selection and 1 to 160 kept channels (the configuration
-// it is compiled for).
+// per thread in each selection, 1 to 160 kept channels and at most 8 experts
+// per token (the configuration it is compiled for).
 bool lean_fits(const ForwardPlan& p, const SelectArgs& s) {
   return p.H == 2048 && !(s.flags & CFM_RECOVER_CANDIDATES_EXACT) && !p.env && !s.thr && p.pre == 8 && p.r == 64 &&
-         p.k > 0 && p.k <= 160 && p.cw <= kSubChunk && p.I <= 4 * NT && p.c <= 4 * NT;
+         p.k > 0 && p.k <= 160 && p.cw <= kSubChunk && p.I <= 4 * NT && p.c <= 4 * NT && p.K <= 8 && p.off_ypt != 0;
 }
 
 template <bool SELECT>
@@ -182,6 +182,7 @@ ForwardPlan select_plan(int T, int K, int E, int I, int H, int k, int c, int r, 
   p.off_xz = cv.take(Pz * p.nw * std::max(r, 1) * 8);
   p.off_xc = cv.take(Pz * std::max(c, 1) * 8);
   p.off_ypart = cv.take(Pz * H * 4);
+  p.off_ypt = p.P <= 8 ? cv.take(Pz * H * 8) : 0;         // (only the lean instance's batch-1 grid uses it)
   p.bytes = cv.off;
   return p;
 }
@@ -241,6 +242,7 @@ static FusedArgs fused_args(const SelectArgs& s, const ForwardPlan& p) {
   a.xz = reinterpret_cast<uint64_t*>(s.ws + p.off_xz);
   a.xc = reinterpret_cast<uint64_t*>(s.ws + p.off_xc);
   a.ypart = reinterpret_cast<float*>(s.ws + p.off_ypart);
+  a.ypt = reinterpret_cast<uint64_t*>(s.ws + (p.off_ypt ? p.off_ypt : p.off_ypart));
   a.T = p.T; a.K = p.K; a.P = p.P; a.E = p.E; a.I = p.I; a.H = p.H;
   int log2H = 0;
   while ((1 << log2H) < p.H) ++log2H;

@@ -123,6 +123,34 @@ __device__ __forceinline__ float await_tagged(const uint64_t* p, uint64_t v, uin
   return __uint_as_float((uint32_t)v);
 }
 
+// The values at ptr[0..N) once each carries `tag` (v: their first loads, in
+// flight). Every round reloads all N words together and the wavefront leaves
+// when every lane has all of its values, so a round costs one round trip
+// whatever N is. Entries a lane does not need must point at a word that does
+// get this launch's tag. On expiry (as await_tagged) the launch is marked
+// failed and the values become 0.
+template <int N>
+__device__ __forceinline__ void await_all(const uint64_t* const (&ptr)[N], uint64_t (&v)[N], uint32_t tag,
+                                          uint32_t* fail, unsigned limit) {
+  for (unsigned it = 0;; ++it) {
+    bool ok = limit != 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ok = ok && (uint32_t)(v[j] >> 32) == tag;
+    if (__all(ok)) return;
+    if (it >= limit || g_wait_expired) {
+      st_u(fail, tag);
+      g_wait_expired = 1;
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[j] = 0;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = ld_tagged(ptr[j]);
+  }
+}
+__device__ __forceinline__ float tagged_value(uint64_t v) { return __uint_as_float((uint32_t)v); }
+
 // Completes this wave's outstanding memory operations, then joins the workgroup.
 __device__ __forceinline__ void drain_and_join() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -193,6 +221,7 @@ struct FusedArgs {
   uint64_t* xz;      // [P][nw][r] partial recovery sums
   uint64_t* xc;      // [P][c]  exact activations of the candidates
   float* ypart;      // [P][H]
+  uint64_t* ypt;     // [P][H] tagged pair outputs (lean instance)
   int T, K, P, E, I, H, log2H, k, c, r, nw, cw, cpw, nhs, G;
   int pre;           // column chunks per workgroup when the candidates' rows are prefetched into LDS, else 0
   int rec_exact;     // dropped candidates enter the recovery with their exact activation
@@ -231,6 +260,34 @@ __device__ __forceinline__ void phase_stamp(const FusedArgs& a, int n) {
   (void)a; (void)n;
 #endif
 }
+// The same from lane 0 of every wavefront, into slot n + wavefront.
+__device__ __forceinline__ void wave_stamp(const FusedArgs& a, int n) {
+#ifdef CFM_PHASE_TRACE
+  if (a.trace && (threadIdx.x & 63) == 0)
+    a.trace[(size_t)blockIdx.x * kTraceSlots + n + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)a; (void)n;
+#endif
+}
+// A block_topk step observer: the clock after step 0 (range known) into slot
+// base, after the first pass into base + 1, after each later pass into
+// base + 2 as (clock << 4 | passes so far), after the ranks into base + 3.
+struct TopkStamp {
+  const FusedArgs* a;
+  int base;
+  __device__ void operator()(int st) const {
+#ifdef CFM_PHASE_TRACE
+    if (a->trace && threadIdx.x == 0) {
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      const int slot = st == 0 ? 0 : st == 1 ? 1 : st == 8 ? 3 : st == 9 ? -1 : 2;
+      if (slot >= 0)
+        a->trace[(size_t)blockIdx.x * kTraceSlots + base + slot] = slot == 2 ? (now << 4) | (uint64_t)st : now;
+    }
+#else
+    (void)st;
+#endif
+  }
+};
 
 struct Lds {
   int32_t* xs;       // [max(H, 256)] rotation exchange
@@ -983,23 +1040,43 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const int per = (a.I + NT - 1) / NT;
       if (LEAN || per <= 4) {
         uint32_t k4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
-        // recovery sums of all workgroups of the pair: requested with the
-        // activations when each thread reads at most 8 of them
+        // this thread's sketch activations and, when each thread reads at most
+        // 8 of them, its share of the pair's partial recovery sums, awaited
+        // together (unused entries watch the pair's first activation)
         const bool zpre = EPT <= 16 && r > 0 && a.nw * r <= 8 * NT;
-        uint64_t zraw[8];
-        if (zpre) zsum_issue(a, p, zl, zg, groups, zraw);
+        const uint64_t* pb = a.xh + (size_t)p * a.I;
+        const uint64_t* zp = a.xz + (size_t)p * a.nw * r + zl;
+        const uint64_t* ptr[12];
+        uint64_t v[12];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ptr[j] = pb + (j < cnt ? i0 + j : 0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = zg + groups * u;
+          ptr[4 + u] = (zpre && zg < groups && q < nw) ? zp + (size_t)q * r : pb;
+        }
+#pragma unroll
+        for (int j = 0; j < 12; ++j) v[j] = ld_tagged(ptr[j]);
+        await_all<12>(ptr, v, tag, a.fail, a.spin);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail, a.spin) : 0.f;
+          const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
           if (j < cnt) L.hh[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
-        if (zpre) zsum_finish(a, L, p, zl, zg, groups, zraw, tag);
-        else if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
+        if (zpre) {
+          if (zg < groups) {
+            float zs = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) zs += zg + groups * u < nw ? tagged_value(v[4 + u]) : 0.f;
+            L.red[NT + zg * r + zl] = zs;
+          }
+        } else if (r > 0) {
+          fetch_zsum(a, L, p, zl, zg, groups, tag);
+        }
         phase_stamp(a, 5);
-        block_topk<NT, 4>(k4, i0, cnt, a.I, a.c, L.candp, L.tks);
+        wave_stamp(a, 15);
+        block_topk<NT, 4>(k4, i0, cnt, a.I, a.c, L.candp, L.tks, TopkStamp{&a, 23});
       } else {
 #pragma unroll
         for (int j = 0; j < 32; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
@@ -1051,18 +1128,27 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const uint64_t* src = a.xc + (size_t)p * a.c + i0;
       const int per = (a.c + NT - 1) / NT;
       if (LEAN || per <= 4) {
-        uint64_t raw[4];
         uint32_t k4[4];
+        const uint64_t* pc = a.xc + (size_t)p * a.c;
+        const uint64_t* ptr[4];
+        uint64_t v[4] = {0, 0, 0, 0};
+        if (a.c > 0) {     // (unused entries watch the pair's first candidate, which exists)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+          for (int j = 0; j < 4; ++j) {
+            ptr[j] = pc + (j < cnt ? i0 + j : 0);
+            v[j] = ld_tagged(ptr[j]);
+          }
+          await_all<4>(ptr, v, tag, a.fail, a.spin);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail, a.spin) : 0.f;
+          const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
           if (j < cnt) L.hcl[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
         phase_stamp(a, 9);
-        if (!thr) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks);
+        wave_stamp(a, 19);
+        if (!thr) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks, TopkStamp{&a, 27});
       } else {
         uint64_t raw[32];
         uint32_t kr[32];
@@ -1167,10 +1253,43 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         if ((f & 7) == 0) rec[f >> 3] = d;
       }
       __syncthreads();
-      for (int col = tid; col < 64; col += NT)
-        st_f(a.ypart + (size_t)p * H + 8 * ck0 + col, part[col] + part[64 + col] + part[128 + col] + part[192 + col] + rec[col]);
+      // this pair's 64 output columns as tagged words; workgroup w of the
+      // token's pair w mod K combines column block w: it waits for the K
+      // pairs' words of its columns and sums them in slot order (the order of
+      // the other instances' combine), then writes the BF16 output
+      if (tid < 64)
+        put_tagged(a.ypt + (size_t)p * H + 8 * ck0 + tid,
+                   part[tid] + part[64 + tid] + part[128 + tid] + part[192 + tid] + rec[tid], tag);
       phase_stamp(a, 13);
-      combine_cols(a, t, w, ck0, nck, &s_flag, tag, nullptr);
+      if (p % a.K == w % a.K) {
+        constexpr int KQ = 2;                            // pair slots per thread (this instance: K <= 8)
+        const int col = tid & 63, q0 = tid >> 6;
+        const uint64_t* yt = a.ypt + (size_t)t * a.K * H + 8 * ck0 + col;
+        const uint64_t* ptr[KQ];
+        uint64_t v[KQ];
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) {
+          const int q = q0 + (NT / 64) * u;
+          ptr[u] = yt + (size_t)(q < a.K ? q : 0) * H;
+        }
+        const int nq = (a.K - q0 + (NT / 64) - 1) / (NT / 64);   // slots of this thread
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) if (u < nq) v[u] = ld_tagged(ptr[u]); else v[u] = ((uint64_t)tag << 32);
+        await_all<KQ>(ptr, v, tag, a.fail, a.spin);
+        float* ys = L.red + 1024;                        // [K][64]
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) {
+          const int q = q0 + (NT / 64) * u;
+          if (q < a.K) ys[q * 64 + col] = tagged_value(v[u]);
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const bool bad = ld_u(a.fail) == tag;
+          float o = 0.f;
+          for (int q = 0; q < a.K; ++q) o += a.topk_w[(size_t)t * a.K + q] * ys[q * 64 + tid];
+          a.out[(size_t)t * H + 8 * ck0 + tid] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
+        }
+      }
       phase_stamp(a, 14);
       continue;
     } else if (a.pre) {

@@ -26,6 +26,13 @@ namespace cfm {
 
 constexpr int kTopkScratchWords = 4 * 256 + 32;    // three histograms, a dummy row, per-wave words
 
+// Default observer of block_topk's steps (instrumentation builds pass one that
+// records a clock stamp): called by every thread after each barrier with the
+// step: 0 range known, 1.. histogram passes, 8 ranks known, 9 done.
+struct NoStepHook {
+  __device__ void operator()(int) const {}
+};
+
 // Inclusive prefix sum over the 64 lanes of a wavefront: row shifts by 1..3
 // build sums of four, shifts by 4 and 8 (bank-masked) extend them over a row of
 // 16, and the row broadcasts of lanes 15 and 31 carry across rows.
@@ -103,9 +110,9 @@ __device__ __forceinline__ int topk_range(int n, int* cnt) {
 // thread's keys for indices [i0, i0 + cnt) as given by topk_range (requires
 // ceil(n / NT) <= KPT and n < 65536). scratch: kTopkScratchWords words of LDS,
 // 16-byte aligned. Called by the whole workgroup; ends with a barrier.
-template <int NT, int KPT>
+template <int NT, int KPT, typename StepHook = NoStepHook>
 __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
-                           uint32_t* scratch) {
+                           uint32_t* scratch, StepHook step = StepHook()) {
   static_assert(NT == 256, "four wavefronts");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (k <= 0) return;
@@ -138,6 +145,7 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
     kmin = min(min(a.x, a.z), min(b.x, b.z));
     kmax = max(max(a.y, a.w), max(b.y, b.w));
   }
+  step(0);
   int s = kmax == kmin ? 0 : max(0, 24 - __builtin_clz(kmax - kmin));
   if ((kmax >> s) - (kmin >> s) > 255u) ++s;
   uint32_t base = kmin >> s;       // digit = (key >> s) - base
@@ -157,6 +165,7 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
     }
     hist[256 * ((pass + 1) % 3) + tid] = 0;      // the next pass's histogram
     __syncthreads();
+    step(1 + pass);
     V = base + boundary_digit(h, need, &m);
     S = s;
     if (m == need || S == 0) break;
@@ -176,6 +185,7 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
   const uint32_t incl = wave_incl_scan(packed);
   if (lane == 63) red[8 + wv] = incl;
   __syncthreads();
+  step(8);
   const uint4 wt = *reinterpret_cast<const uint4*>(red + 8);
   const uint32_t basew = (wv > 0 ? wt.x : 0u) + (wv > 1 ? wt.y : 0u) + (wv > 2 ? wt.z : 0u);
   const uint32_t ex = basew + incl - packed;
@@ -191,6 +201,7 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
     e += eq;
   }
   __syncthreads();
+  step(9);
 }
 
 // The threshold keep rule in place of top-k (abstract: selectors typically
