@@ -1129,6 +1129,17 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const int per = (a.c + NT - 1) / NT;
       if (LEAN || per <= 4) {
         uint32_t k4[4];
+        // (lean instance) this thread's candidates' channels and sketch
+        // activations, read before the exchange so that the kept set's
+        // writer below needs no further LDS round
+        int32_t chn[4];
+        float hzc[4], hvv[4];
+        if constexpr (LEAN) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) chn[j] = L.candp[min(i0 + j, a.c - 1)];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hzc[j] = L.hh[chn[j]];
+        }
         const uint64_t* pc = a.xc + (size_t)p * a.c;
         const uint64_t* ptr[4];
         uint64_t v[4] = {0, 0, 0, 0};
@@ -1144,11 +1155,25 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         for (int j = 0; j < 4; ++j) {
           const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
           if (j < cnt) L.hcl[i0 + j] = hv;
+          hvv[j] = hv;
           k4[j] = score_key(hv);
         }
         phase_stamp(a, 9);
         wave_stamp(a, 19);
-        if (!thr) block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks, TopkStamp{&a, 27});
+        if constexpr (LEAN) {
+          // the kept set written as (channel, exact activation, sketch
+          // activation bits in L.sel) at each rank
+          auto emit = [&](bool take, uint32_t pos, int j) {
+            if (take) {
+              L.keep[pos] = chn[j];
+              L.hk[pos] = hvv[j];
+              L.sel[pos] = __float_as_int(hzc[j]);
+            }
+          };
+          block_topk_emit<NT, 4>(k4, i0, cnt, a.c, a.k, emit, L.tks, TopkStamp{&a, 27});
+        } else if (!thr) {
+          block_topk<NT, 4>(k4, i0, cnt, a.c, a.k, L.sel, L.tks, TopkStamp{&a, 27});
+        }
       } else {
         uint64_t raw[32];
         uint32_t kr[32];
@@ -1166,12 +1191,14 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       // in LDS (written by this thread above)
       if (thr)   // (the envelope entry points keep the top k)
         kk = block_threshold<NT>([&](int i) { return score_key(L.hcl[i]); }, i0, cnt, a.tkey, L.sel, L.tks);
-      if (a.k >= a.c) __syncthreads();
-      for (int i = tid; i < kk; i += NT) {
-        L.keep[i] = L.candp[L.sel[i]];
-        L.hk[i] = L.hcl[L.sel[i]];
+      if (!LEAN && a.k >= a.c) __syncthreads();
+      if constexpr (!LEAN) {
+        for (int i = tid; i < kk; i += NT) {
+          L.keep[i] = L.candp[L.sel[i]];
+          L.hk[i] = L.hcl[L.sel[i]];
+        }
+        __syncthreads();
       }
-      __syncthreads();
       phase_stamp(a, 10);
       if (w == 0 && a.keep_out)
         for (int i = tid; i < a.k; i += NT) a.keep_out[(size_t)p * a.k + i] = i < kk ? L.keep[i] : -1;
@@ -1207,11 +1234,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 #pragma unroll
       for (int u = 0; u < LKPT; ++u) {
         const int m = min(g + 32 * u, kk - 1);
+        const bool ok = g + 32 * u < kk;
         jj[u] = L.keep[m];
-        hd[u] = g + 32 * u < kk ? L.hk[m] : 0.f;
+        hd[u] = ok ? L.hk[m] : 0.f;
+        hz[u] = ok ? __int_as_float(L.sel[m]) : 0.f;
       }
-#pragma unroll
-      for (int u = 0; u < LKPT; ++u) hz[u] = g + 32 * u < kk ? L.hh[jj[u]] : 0.f;
       const uint16_t* db = a.wd + (size_t)e * a.I * H + 8 * (ck0 + cc);
       const uint16_t* bb = a.Bt + (size_t)e * a.I * r + 8 * cc;
       uint4 dw[LKPT], bw[LKPT];

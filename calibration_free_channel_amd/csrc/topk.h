@@ -105,6 +105,17 @@ __device__ __forceinline__ int topk_range(int n, int* cnt) {
   return i0;
 }
 
+// Writer of the selected indices: index i0 + j goes to out[pos] (taken) or to
+// a per-thread sink (not taken), without a branch.
+struct IndexEmit {
+  int32_t* out;
+  uint32_t* sink;
+  int i0;
+  __device__ __forceinline__ void operator()(bool take, uint32_t pos, int j) const {
+    *(take ? reinterpret_cast<uint32_t*>(out) + pos : sink + threadIdx.x) = (uint32_t)(i0 + j);
+  }
+};
+
 // Selects the k largest of n keys by (key desc, index asc) and writes their
 // indices in ascending order to out_idx[0..k) (LDS). kr[0..cnt) are this
 // thread's keys for indices [i0, i0 + cnt) as given by topk_range (requires
@@ -112,17 +123,24 @@ __device__ __forceinline__ int topk_range(int n, int* cnt) {
 // 16-byte aligned. Called by the whole workgroup; ends with a barrier.
 template <int NT, int KPT, typename StepHook = NoStepHook>
 __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
-                           uint32_t* scratch, StepHook step = StepHook()) {
+                           uint32_t* scratch, StepHook step = StepHook());
+
+// The same with the writer of the result given: emit(take, pos, j) is called
+// for each of this thread's keys j < KPT (take: key j is selected, at rank pos
+// of the ascending result; j >= cnt is never taken), then the workgroup joins.
+template <int NT, int KPT, typename Emit, typename StepHook = NoStepHook>
+__device__ __forceinline__ void block_topk_emit(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, Emit emit,
+                                                uint32_t* scratch, StepHook step = StepHook()) {
   static_assert(NT == 256, "four wavefronts");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = tid; i < n; i += NT) out_idx[i] = i;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) emit(j < cnt, (uint32_t)(i0 + j), j);
     __syncthreads();
     return;
   }
   uint32_t* hist = scratch;
-  uint32_t* dummy = scratch + 3 * 256;     // sink for the stores of keys not taken
   uint32_t* red = scratch + 4 * 256;       // [0, 8): per-wave min / max; [8, 12): per-wave totals
   // keys beyond this thread's range become a sentinel above every real key
   // (real keys are nonnegative floats, below 2^31), which no pass counts
@@ -196,12 +214,18 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, in
     const bool gt = j < cnt && v > V, eq = v == V;
     const bool take = gt || (eq && e < need);
     const uint32_t pos = gt ? d + min(e, need) : d + e;
-    *(take ? reinterpret_cast<uint32_t*>(out_idx) + pos : dummy + tid) = (uint32_t)(i0 + j);
+    emit(take, pos, j);
     d += gt;
     e += eq;
   }
   __syncthreads();
   step(9);
+}
+
+template <int NT, int KPT, typename StepHook>
+__device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
+                                           uint32_t* scratch, StepHook step) {
+  block_topk_emit<NT, KPT>(kr, i0, cnt, n, k, IndexEmit{out_idx, scratch + 3 * 256, i0}, scratch, step);
 }
 
 // The threshold keep rule in place of top-k (abstract: selectors typically
