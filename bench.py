@@ -176,18 +176,30 @@ def measured_traffic():
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
-def cpu_baseline(wl_name="q18_b1", target_s=10.0):
-    """The CPU oracle on a bounded sample of the same workload (per-token forward)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl_name="q18_b1", target_s=8.0):
+    """The CPU oracle (plain C++, float64) on a bounded sample of the same workload: the selected forward
+    (screen, exact top-k, down, recovery, combine) of whole tokens, routed pairs spread over the threads,
+    timed on 1 thread and on all of the host's threads (at most 16)."""
     import numpy as np
-    import threadpoolctl
 
     import synth
     from oracle import cfm_oracle as O
 
     wl = synth.WORKLOADS[wl_name]
     s = wl.shape
-    ids, w = synth.routing(2, s.E, s.K, wl.seed + 101, 0)
-    x = synth.hidden_states(2, s.H, wl.seed + 101, 0, rmsnorm=True)
+    n_tok = 2
+    ids, w = synth.routing(n_tok, s.E, s.K, wl.seed + 101, 0)
+    x = synth.hidden_states(n_tok, s.H, wl.seed + 101, 0, rmsnorm=True)
     used = sorted(set(int(e) for e in ids.reshape(-1)))
     local = {e: n for n, e in enumerate(used)}
     ids_l = np.vectorize(local.get)(ids).astype(np.int32)
@@ -195,24 +207,27 @@ def cpu_baseline(wl_name="q18_b1", target_s=10.0):
     signs = synth.rotation_signs(s.H, wl.seed, 0)
     tg, tu, sg, su = O.sketch_build(wg, wu, signs)          # offline steps: not timed
     A, Bt = O.lowrank_build(wd, wl.r)
-    info = threadpoolctl.threadpool_info()
-    cores = max([d.get("num_threads", 1) for d in info] + [1])
-    n_tok, t0 = 0, time.perf_counter()
-    while True:
-        O.select_forward(x, ids_l, w, wg, wu, wd, tg, tu, sg, su, signs, A, Bt, wl.k, wl.c)
-        n_tok += x.shape[0]
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-    us_sel = el / n_tok * 1e6
-    t0 = time.perf_counter()
-    O.dense_forward(x, ids_l, w, wg, wu, wd)
-    us_dense = (time.perf_counter() - t0) / x.shape[0] * 1e6
-    return {"value": round(us_sel, 1), "unit": "us/token", "cores": int(cores), "kind": "oracle",
-            "sample": f"{wl_name}: 2 tokens x {n_tok // 2} repeats of the float64 numpy oracle forward "
-                      f"(screen, exact top-k, down, recovery, combine) over the tokens' "
-                      f"{len(used)} routed experts; sketch and low-rank map prepared untimed",
-            "dense_us_per_token": round(us_dense, 1)}
+    all_threads = max(1, min(16, os.cpu_count() or 1))
+    res = {}
+    for th in sorted({1, all_threads}):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            O.select_forward(x, ids_l, w, wg, wu, wd, tg, tu, sg, su, signs, A, Bt, wl.k, wl.c, threads=th,
+                             details=False)
+            done += n_tok
+            el = time.perf_counter() - t0
+            if el >= target_s / 2:
+                break
+        t0 = time.perf_counter()
+        O.dense_forward(x, ids_l, w, wg, wu, wd, threads=th)
+        res[th] = (el / done * 1e6, (time.perf_counter() - t0) / n_tok * 1e6, done)
+    us_all, dense_all, done_all = res[all_threads]
+    return {"value": round(us_all, 1), "unit": "us/token", "cores": all_threads, "kind": "oracle",
+            "sample": f"{wl_name}: {n_tok} tokens (their {len(used)} routed experts) through the plain-C++ float64 "
+                      f"oracle's selected forward, repeated to {done_all} tokens on {all_threads} threads and "
+                      f"{res[1][2]} on 1 thread; sketch and low-rank map prepared untimed",
+            "us_per_token_1_thread": round(res[1][0], 1), "cpu_model": cpu_model(),
+            "dense_us_per_token": round(dense_all, 1), "dense_us_per_token_1_thread": round(res[1][1], 1)}
 
 
 SELECT_PHASES = {

@@ -65,8 +65,8 @@ for _name, (_res, _args) in _SIGS.items():
 EXPORTED = tuple(_SIGS)
 
 STATS_FIELDS = ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io",
-                "bytes_dense_equiv", "experts_used", "rows_candidates", "rows_down")
-STATS_BYTES = 6 * 8 + 4 * 4
+                "bytes_dense_equiv", "experts_used", "rows_candidates", "rows_down", "bytes_requested")
+STATS_BYTES = 6 * 8 + 4 * 4 + 8
 
 
 class CfmError(RuntimeError):
@@ -402,5 +402,6 @@ def decode_stats(buf) -> dict:
     raw = buf.detach().cpu().numpy().tobytes()
     u64 = np.frombuffer(raw[:48], dtype="<u8")
     u32 = np.frombuffer(raw[48:64], dtype="<u4")
-    vals = list(map(int, u64)) + list(map(int, u32[:3]))
+    req = np.frombuffer(raw[64:72], dtype="<u8")
+    vals = list(map(int, u64)) + list(map(int, u32[:3])) + [int(req[0])]
     return dict(zip(STATS_FIELDS, vals))

@@ -21,9 +21,14 @@ namespace {
 
 // ------------------------------------------------------------------ stats
 
+// Byte counts of a per-pair launch. Every field bills each pair's rows (when
+// pairs share an expert this is an upper bound of the per-expert unions the
+// method needs); bytes_requested bills every pair's requests as issued, with
+// down_req down rows per pair (the c candidates' where they are prefetched,
+// -1: the kept rows as in bytes_down).
 __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, int c, int r, int T,
                         int K, int select, int exact_step, int sketch_read, const int32_t* kcnt,
-                        cfm_stats* st) {
+                        int down_req, cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   unsigned used = 0;
   for (int pp = 0; pp < P; ++pp) {
@@ -57,6 +62,13 @@ __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, i
     s.rows_down = (uint32_t)(P * I);
   }
   s.pad = 0;
+  if (select) {
+    const uint64_t per_pair = (sketch_read ? 2ull * I * (H / 4) + 8ull * I : 0) +
+                              (exact_step ? 4ull * H * c : 0) + (r > 0 ? 2ull * H * r + 2ull * I * r : 0);
+    s.bytes_requested = Pu * per_pair + (down_req >= 0 ? Pu * 2ull * H * down_req : s.bytes_down) + s.bytes_io;
+  } else {
+    s.bytes_requested = Pu * 6ull * I * H + s.bytes_io;
+  }
   *st = s;
 }
 
@@ -294,12 +306,15 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
     return rc;
   const FusedArgs a = fused_args(s, p);
   if (!a.x) return set_error(CFM_EINVAL, "select forward: no hidden states");
-  int rc = launch_fused<true>(a, p.lds, stream, lean_fits(p, s));
+  const bool lean = lean_fits(p, s);
+  int rc = launch_fused<true>(a, p.lds, stream, lean);
   if (rc) return rc;
   if (s.stats) {
+    // the general instances prefetch every candidate's down row (for their columns) when p.pre
+    const int down_req = (p.pre && !lean) ? p.c : -1;
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
                        p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0,
-                       (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr,
+                       (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr, down_req,
                        static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
@@ -318,7 +333,7 @@ int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_t
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.I, p.I, 0,
-                       p.T, p.K, 0, 1, 0, nullptr, static_cast<cfm_stats*>(s.stats));
+                       p.T, p.K, 0, 1, 0, nullptr, -1, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;

@@ -1224,6 +1224,7 @@ __global__ void k_g_stats(GArgs a, cfm_stats* st) {
   s.rows_candidates = (uint32_t)uc;
   s.rows_down = (uint32_t)dc;
   s.pad = 0;
+  s.bytes_requested = s.bytes_sketch + s.bytes_candidates + s.bytes_down + s.bytes_recovery + s.bytes_io;
   *st = s;
 }
 

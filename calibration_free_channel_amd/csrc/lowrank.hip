@@ -11,8 +11,10 @@
 //   Rayleigh-Ritz: M = Q^T G Q, Jacobi eigen-decomposition M = W L W^T in LDS,
 //   V_r = Q W[:, top r]                        (k_subspace)
 //   Bt = V_r, A = W_down V_r                   (k_lowrank_a)
-// The block is r plus 32 columns of oversampling (at most 96, or r if larger),
-// which the iteration count is sized for.
+// The block is r plus 32 columns of oversampling (at most 96, or r if larger,
+// and never more than min(I, H), the rank bound of G);
+// the iteration runs until the energy its leading r columns capture has
+// converged (relative change at most 1e-13 per iteration).
 #include <algorithm>
 
 #include "cfm_internal.h"
@@ -161,8 +163,10 @@ __device__ void gram_ab(const double* A, const double* B, double* lds, int I, in
 }
 
 // In place: Y [I][p] -> Y R^-1 with R^T R = Y^T Y (Cholesky QR); R lives in LDS.
-// A pivot that falls below 1e-13 * trace / p is raised to that value (the
-// second pass of CholQR2 restores orthogonality).
+// A column whose pivot falls to 1e-13 * trace / p or below depends on the
+// columns before it (to rounding): it is dropped (set to zero, its row of R
+// zero) rather than divided by a tiny pivot, which would amplify rounding
+// until it overflows. Dropped columns stay zero in later passes.
 __device__ void cholqr(double* Y, int I, int p, double* lds, double* sh) {
   gram_ab(Y, Y, lds, I, p);
   double* S = lds;
@@ -175,15 +179,14 @@ __device__ void cholqr(double* Y, int I, int p, double* lds, double* sh) {
   __syncthreads();
   for (int k = 0; k < p; ++k) {
     if (tid == 0) {
-      double d = S[k * p + k];
-      if (!(d > sh[0])) d = sh[0];
-      d = sqrt(d);
+      const double d2 = S[k * p + k];
+      const double d = d2 > sh[0] ? sqrt(d2) : 0.0;
       S[k * p + k] = d;
       sh[1] = d;
     }
     __syncthreads();
     const double d = sh[1];
-    for (int b = k + 1 + tid; b < p; b += LT) S[k * p + b] /= d;
+    for (int b = k + 1 + tid; b < p; b += LT) S[k * p + b] = d > 0.0 ? S[k * p + b] / d : 0.0;
     __syncthreads();
     const int m = p - k - 1;
     for (int o = tid; o < m * m; o += LT) {
@@ -197,7 +200,8 @@ __device__ void cholqr(double* Y, int I, int p, double* lds, double* sh) {
     for (int b = 0; b < p; ++b) {
       double s = y[b];
       for (int a = 0; a < b; ++a) s -= y[a] * S[a * p + b];
-      y[b] = s / S[b * p + b];
+      const double d = S[b * p + b];
+      y[b] = d > 0.0 ? s / d : 0.0;
     }
   }
   __syncthreads();
@@ -231,13 +235,25 @@ __global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qal
   __syncthreads();
   cholqr(Q, I, p, lds, sh);
   cholqr(Q, I, p, lds, sh);
+  // iterate until the energy the leading r columns capture, tr(Q_r^T G Q_r)
+  // (the Eckart-Young objective), changes by at most 1e-13 of itself between
+  // iterations (at least 4, at most `iters` iterations)
+  double prev = -1.0;
   for (int it = 0; it < iters; ++it) {
     gemm_gq(G, Q, Y, I, p, lds);
     __syncthreads();
+    double part = 0.0;
+    for (int o = tid; o < I * r; o += LT) {
+      const int i = o / r, b = o % r;
+      part += Q[(size_t)i * p + b] * Y[(size_t)i * p + b];
+    }
+    const double energy = block_sum_lr(part, red);
     cholqr(Y, I, p, lds, sh);
     cholqr(Y, I, p, lds, sh);
     for (int o = tid; o < I * p; o += LT) Q[o] = Y[o];
     __syncthreads();
+    if (it >= 3 && fabs(energy - prev) <= 1e-13 * energy) break;
+    prev = energy;
   }
   // Rayleigh-Ritz: M = Q^T (G Q), padded to even size pp with a zero row/column
   gemm_gq(G, Q, Y, I, p, lds);
@@ -408,10 +424,12 @@ __global__ __launch_bounds__(LT) void k_lowrank_a(const uint16_t* __restrict__ w
 
 LowrankPlan lowrank_plan(int E, int I, int H, int r) {
   LowrankPlan pl{};
+  // the block never exceeds the rank bound of G = W_down^T W_down, min(I, H):
+  // columns beyond it would only carry rounding
   int p = std::max(r, std::min(r + 32, 96));
-  p = std::min(p, I);
+  p = std::min(p, std::min(I, H));
   pl.p = std::max(p, 1);     // p <= 128
-  pl.iters = 24;
+  pl.iters = 200;             // at most; the iteration stops once the captured energy has converged
   const int pp = (pl.p + 1) & ~1;
   Carve cv;
   pl.off_gram = cv.take((size_t)E * I * I * 8);

@@ -127,9 +127,12 @@ int sketch_build_seeded(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int
  * Computes the rank-r truncated SVD W_down ~ A * Bt^T per expert, with
  * A = W_down V_r = U_r diag(s_r) and Bt = V_r (orthonormal columns), both
  * rounded to BF16. Computed on the device in float64: Gram matrix
- * W_down^T W_down, block subspace iteration with oversampling and a
- * Rayleigh-Ritz step. Each column of V_r is signed so that its
- * largest-magnitude entry is positive.
+ * W_down^T W_down, block subspace iteration with oversampling (until the
+ * energy the leading r columns capture changes by at most 1e-13 of itself per
+ * iteration, at most 200 iterations) and a Rayleigh-Ritz step. Each column of
+ * V_r is signed so that its largest-magnitude entry is positive. Where an
+ * expert's W_down has rank below r, the columns past its rank are zero in
+ * both A and Bt (they would carry no energy).
  *
  *   w_down_t : [E][I][H] BF16 (channel-major W_down).
  *   A        : out [E][H][r] BF16.   Bt : out [E][I][r] BF16.
@@ -165,7 +168,9 @@ int lowrank_build(const cfm_bf16* w_down_t, int E, int I, int H, int r, cfm_bf16
  *   out      : out [T][H] BF16.
  *   cand_out : optional out [T*K][c] int32, C of each pair in ascending order.
  *   keep_out : optional out [T*K][k] int32, S of each pair in ascending order.
- *   stats    : optional out, device cfm_stats (bytes the call reads).
+ *   stats    : optional out, device cfm_stats (bytes the call reads: the
+ *              per-expert algorithmic count of the method per field, and
+ *              bytes_requested as the kernels issue them).
  *   ws       : device workspace of at least select_workspace(...) bytes. It
  *              must be zero-filled once after allocation; every call leaves it
  *              ready for the next call of the same shape. When a call's layout
@@ -189,6 +194,12 @@ typedef struct {
   uint64_t bytes_io;           /* x, router output, out */
   uint64_t bytes_dense_equiv;  /* what the dense layer reads for the same routing */
   uint32_t experts_used, rows_candidates, rows_down, pad;
+  /* bytes the kernels request from memory (cache hits included), as issued:
+     the per-pair pass requests each pair's rows on its own, also when pairs
+     share an expert, and where it prefetches the down rows of all c
+     candidates (every per-pair instance except the lean one) it requests
+     those; the grouped pass requests the per-expert unions above */
+  uint64_t bytes_requested;
 } cfm_stats;
 
 size_t select_workspace(int T, int K, int E, int I, int H, int k, int c, int r);

@@ -117,3 +117,30 @@ def test_failure_channel_forced_from_host(cfm):
                                                  wl.k, wl.c, wl.r, ws=ws))
         assert np.array_equal(again, good)
         assert cfm.workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("which", ["lean", "general"])
+def test_bytes_requested(cfm, which):
+    """bytes_requested equals the kept-row count where only kept rows are read (the lean batch-1
+    instance: 8 pairs, H 2048, I 768, r 64) and adds the candidates' down rows where they are
+    prefetched (the general instance, here at H 256)."""
+    log(f"bytes_requested {which}")
+    if which == "lean":
+        wl = custom_workload("req_lean", 8, 8, 768, 2048, 1, 138, 276, 64, 51)
+    else:
+        wl = custom_workload("req_gen", 8, 2, 128, 256, 1, 23, 46, 8, 52, chan_scale=False)
+    L, A, Bt = _layer_and_map(wl)
+    sk = cfm.sketch_build(L.wg, L.wu, L.signs)
+    st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device=dev())
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, wl.k, wl.c, wl.r, stats=st)
+    torch.cuda.synchronize()
+    d = cfm.decode_stats(st)
+    algo = sum(d[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down", "bytes_recovery", "bytes_io"))
+    P = L.host.ids.size
+    H = L.host.w_gate.shape[2]
+    if which == "lean":
+        assert d["bytes_requested"] == algo
+    else:
+        assert d["bytes_requested"] == algo - d["bytes_down"] + P * 2 * H * wl.c
+    assert cfm.workspace_status(cfm.new_workspace(2048, dev())) == 0

@@ -396,35 +396,63 @@ def test_batch_independence():
     assert all(np.array_equal(pf[(2, q)]["S"], p1[(0, q)]["S"]) for q in range(ids.shape[1]))
 
 
+def test_large_batch_with_converted_inputs_matches_token_by_token():
+    """A 70-token batch whose routing weights arrive as float32 (converted on the way in) over several
+    threads gives each token what a one-token call gives it (the converted copy must outlive the call)."""
+    wg, wu, wd, d, x, ids, w = _small_layer(T=70)
+    w32 = np.asarray(w, np.float32)
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    A, Bt = O.lowrank_build(wd, 4)
+    full, _ = O.select_forward(x, ids, w32, wg, wu, wd, tg, tu, sg, su, d, A, Bt, 6, 12, threads=4)
+    dense = O.dense_forward(x, ids, w32, wg, wu, wd, threads=4)
+    for t in (0, 33, 69):
+        one, _ = O.select_forward(x[t:t + 1], ids[t:t + 1], w32[t:t + 1], wg, wu, wd, tg, tu, sg, su, d, A, Bt,
+                                  6, 12, threads=1)
+        assert np.array_equal(full[t], one[0])
+        assert np.array_equal(dense[t], O.dense_forward(x[t:t + 1], ids[t:t + 1], w32[t:t + 1], wg, wu, wd,
+                                                        threads=1)[0])
+    assert np.isfinite(O.bf16_to_f64(full)).all() and np.abs(O.bf16_to_f64(dense)).max() > 0
+
+
 # ----------------------------------------------------------------------------- low-rank map
 
-def test_lowrank_eckart_young_and_orthonormal():
+@pytest.mark.parametrize("HI", [(96, 40), (40, 96), (48, 48)], ids=["tall", "wide", "square"])
+def test_lowrank_eckart_young_and_orthonormal(HI):
+    H, I = HI
     r = _rng(11)
-    W = r.standard_normal((96, 40)) * np.exp(r.standard_normal(40))[None, :]   # H x I
-    for rank in (0, 1, 7, 40):
+    W = r.standard_normal((H, I)) * np.exp(r.standard_normal(I))[None, :]   # H x I
+    for rank in sorted({0, 1, 7, min(H, I)}):
         A, Bt = O.lowrank(W.T, rank)
         resid = np.sum((W - A @ Bt.T) ** 2)
         ev = np.sort(np.linalg.eigvalsh(W.T @ W))[::-1]       # squared singular values, another routine
         assert np.isclose(resid, max(ev[rank:].sum(), 0.0), rtol=1e-9, atol=1e-9)
-        assert np.allclose(Bt.T @ Bt, np.eye(rank), atol=1e-12)
+        assert np.allclose(Bt.T @ Bt, np.eye(rank), atol=1e-11)
 
 
-def test_lowrank_known_factorisation():
+@pytest.mark.parametrize("HI", [(64, 20), (20, 64)], ids=["tall", "wide"])
+def test_lowrank_known_factorisation(HI):
+    H, I = HI
+    n = min(H, I)
     r = _rng(12)
-    U, _ = np.linalg.qr(r.standard_normal((64, 20)))
-    V, _ = np.linalg.qr(r.standard_normal((20, 20)))
-    s = np.linspace(10, 1, 20)
+    U, _ = np.linalg.qr(r.standard_normal((H, n)))
+    V, _ = np.linalg.qr(r.standard_normal((I, n)))
+    s = np.linspace(10, 1, n)
     W = U @ np.diag(s) @ V.T                                  # H x I with known SVD
     A, Bt = O.lowrank(W.T, 5)
     assert np.allclose(A @ Bt.T, U[:, :5] @ np.diag(s[:5]) @ V[:, :5].T, atol=1e-10)
+    # each column of Bt is +-V_l, signed so that its largest-magnitude entry is positive
     for l in range(5):
+        assert np.allclose(np.abs(Bt[:, l]), np.abs(V[:, l]), atol=1e-10)
         j = int(np.argmax(np.abs(Bt[:, l])))
         assert Bt[j, l] > 0
+        assert np.allclose(A[:, l], s[l] * U[:, l] * np.sign(Bt[:, l] @ V[:, l]), atol=1e-10)
 
 
-def test_lowrank_exact_on_low_rank_matrix():
+@pytest.mark.parametrize("HI", [(50, 30), (30, 50)], ids=["tall", "wide"])
+def test_lowrank_exact_on_low_rank_matrix(HI):
+    H, I = HI
     r = _rng(13)
-    W = r.standard_normal((50, 3)) @ r.standard_normal((3, 30))
+    W = r.standard_normal((H, 3)) @ r.standard_normal((3, I))
     A, Bt = O.lowrank(W.T, 3)
     assert np.allclose(A @ Bt.T, W, atol=1e-10)
 
@@ -723,3 +751,42 @@ def test_rotation_signs_take_bit_63():
     # the i-th sign depends only on (seed, i): a longer vector extends a shorter one
     assert np.array_equal(O.rotation_signs(99, 64), O.rotation_signs(99, 256)[:64])
     assert not np.array_equal(O.rotation_signs(99, 256), O.rotation_signs(100, 256))
+
+
+# ----------------------------------------------------------------------------- staged outputs
+
+def test_staged_forward_reproduces_select_forward_on_its_own_sets():
+    """Given the oracle's own candidate and kept sets, the staged entry gives the same bits; given a kept
+    set with one channel swapped, it gives the output of exactly that set (the swap moves the output)."""
+    wl = synth.WORKLOADS["tiny"]
+    h = synth.make_inputs(wl)
+    tg, tu, sg, su = O.sketch_build(h.w_gate, h.w_up, h.signs)
+    A, Bt = O.lowrank_build(h.w_down_t, wl.r)
+    out, pairs = O.select_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su, h.signs, A, Bt,
+                                  wl.k, wl.c)
+    cand = {p: d["C"] for p, d in pairs.items()}
+    keep = {p: d["S"] for p, d in pairs.items()}
+    for rec in ("sketch", "candidates_exact"):
+        o2, p2 = O.select_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su, h.signs, A, Bt,
+                                  wl.k, wl.c, recovery=rec)
+        st = O.staged_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su, h.signs, A, Bt,
+                              {p: d["C"] for p, d in p2.items()}, {p: d["S"] for p, d in p2.items()}, [0],
+                              recovery=rec)
+        assert np.array_equal(st, o2)
+    # swap the weakest kept channel of pair (0, 0) for the strongest dropped candidate
+    d = pairs[(0, 0)]
+    dropped = np.setdiff1d(d["C"], d["S"])
+    weakest = d["S"][np.argmin(np.abs(d["h_all"][d["S"]]))]
+    strongest = dropped[np.argmax(np.abs(d["h_all"][dropped]))]
+    keep2 = dict(keep)
+    keep2[(0, 0)] = np.sort(np.append(np.setdiff1d(d["S"], [weakest]), strongest))
+    st2 = O.staged_forward(h.x, h.ids, h.w, h.w_gate, h.w_up, h.w_down_t, tg, tu, sg, su, h.signs, A, Bt, cand,
+                           keep2, [0])
+    assert not np.array_equal(st2, out)
+    # by hand: y changes by (h_s - hhat_s) Wd_s - (h_w - hhat_w) Wd_w + A Bt^T corrections of the swap
+    wd = O.bf16_to_f64(h.w_down_t[h.ids[0, 0]])
+    Ae, Be = O.bf16_to_f64(A[h.ids[0, 0]]), O.bf16_to_f64(Bt[h.ids[0, 0]])
+    y = d["y"] + d["h_all"][strongest] * wd[strongest] - d["h_all"][weakest] * wd[weakest] \
+        + Ae @ (d["hhat"][weakest] * Be[weakest] - d["hhat"][strongest] * Be[strongest])
+    ys = np.stack([y] + [pairs[(0, q)]["y"] for q in range(1, h.ids.shape[1])])
+    assert np.array_equal(O.combine(ys, h.w[0]), st2[0])
