@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--phase-trace", action="store_true",
                     help="instead of the default line: per-phase timeline of the batch-1 selected and dense "
                          "kernels from in-kernel clock stamps (needs the trace build, CFM_PHASE_TRACE=1)")
+    ap.add_argument("--cold-reps", type=int, default=40, help="cold calls timed for the default line")
+    ap.add_argument("--summarize-pmc", default="", metavar="F,W,CF,CW,MIB",
+                    help="only print the per-launch traffic record from rocprofv3 --pmc result folders (bench "
+                         "FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE) and the copy size")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
@@ -74,7 +78,9 @@ def parse():
 # ----------------------------------------------------------------------------- inputs on the device
 
 def make_layer(torch, seed, layer, E, I, H, sigma=0.02, chan_scale=True):
-    """Synthetic BF16 expert weights drawn on the device (same recipe as synth/)."""
+    """Synthetic BF16 expert weights drawn on the device (same recipe as synth/), and the layer's
+    rotation signs from its 64-bit seed through the library's own generator."""
+    import calibration_free_channel_amd as cfm
     g = torch.Generator(device="cuda")
     g.manual_seed(seed * 100003 + layer)
     mats = []
@@ -85,8 +91,7 @@ def make_layer(torch, seed, layer, E, I, H, sigma=0.02, chan_scale=True):
             w.mul_(s)
         mats.append(w.to(torch.bfloat16))
         del w
-    bits = torch.randint(0, 2, (H,), generator=g, device="cuda", dtype=torch.int8)
-    signs = (1 - 2 * bits).to(torch.int8)
+    signs = cfm.rotation_signs(seed * 100003 + layer, H)
     return mats[0], mats[1], mats[2], signs
 
 
@@ -133,7 +138,7 @@ def kernel_times(torch, cfm, fn, n_steps):
         fn(i)
     cfm.timing_enable(False)
     rep = cfm.timing_report()
-    return {k: v[1] / v[0] for k, v in rep.items()}
+    return {k: v[1] / v[0] for k, v in rep.items()}, {k: v[0] / n_steps for k, v in rep.items()}
 
 
 def stream_gbps(torch, nbytes=2 << 30, reps=10):
@@ -163,17 +168,79 @@ def measured_traffic():
     """HBM bytes per launch of k_select_fused from the committed rocprofv3 --pmc
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
     None when the kernel sources have changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "k_select_fused_q18_b1_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["source_files"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec["source_sha256"]:
+    if rec["source_files"] != kernel_sources() or rec["source_sha256"] != sources_sha256(rec["source_files"]):
         return None
     return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def kernel_sources():
+    """The files the single-launch kernels are built from (every header of the library and the
+    fused translation units), relative to the repository root."""
+    import glob
+    csrc = os.path.join(ROOT, "calibration_free_channel_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "fused*.hip")))
+    return [os.path.relpath(f, ROOT) for f in files]
+
+
+def sources_sha256(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_pmc(spec):
+    """Per-launch HBM bytes of the batch-1 kernels from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE of the bench, then of a plain copy of known size), scaled by what the counters read for
+    the copy; prints the record that bench.py reads back as `traffic`. spec: comma-separated
+    fetch_dir,write_dir,copy_fetch_dir,copy_write_dir,copy_mib."""
+    import glob
+    import sqlite3
+    import statistics
+    fdir, wdir, cfdir, cwdir, mib = spec.split(",")
+    mib = int(mib)
+
+    def per_kernel(d, counter):
+        """{kernel name: median over dispatches of the counter (KiB)} from rocprofv3's result database."""
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+            con = sqlite3.connect(f)
+            for name, disp, v in con.execute(
+                    "select kernel_name, dispatch_id, sum(value) from counters_collection "
+                    "where counter_name = ? group by dispatch_id", (counter,)):
+                vals.setdefault(name, []).append(float(v))
+            con.close()
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    def find(d, name):
+        hits = {k: v for k, v in d.items() if name + "<" in k}
+        if not hits:
+            raise SystemExit(f"no {name} dispatches in the counter output")
+        return max(hits.items(), key=lambda kv: kv[1])
+
+    copy_kib = mib * 1024.0
+    cf = max(per_kernel(cfdir, "FETCH_SIZE").values())
+    cw = max(per_kernel(cwdir, "WRITE_SIZE").values())
+    fscale, wscale = copy_kib / cf, copy_kib / cw
+    fetch, write = per_kernel(fdir, "FETCH_SIZE"), per_kernel(wdir, "WRITE_SIZE")
+    rec = {"kernel": "k_select_fused", "workload": "q18_b1"}
+    for key, name in (("", "k_select_fused"), ("dense_", "k_dense_fused")):
+        kn, fk = find(fetch, name)
+        _, wk = find(write, name)
+        rec[key + "kernel_name"] = kn
+        rec[key + "fetch_kib_raw"] = round(fk, 2)
+        rec[key + "write_kib_raw"] = round(wk, 2)
+        rec[key + "fetch_bytes"] = int(round(fk * fscale * 1024))
+        rec[key + "write_bytes"] = int(round(wk * wscale * 1024))
+    rec.update({"fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+                "copy_probe_mib": mib, "source_files": kernel_sources()})
+    rec["source_sha256"] = sources_sha256(rec["source_files"])
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_model():
@@ -233,8 +300,9 @@ def cpu_baseline(wl_name="q18_b1", target_s=8.0):
 SELECT_PHASES = {
     0: "start", 1: "first loads issued (x, signs, router id, sketch rows, scales, Bt)", 2: "x rotated",
     3: "screen done", 4: "recovery partial sums published", 5: "sketch activations + partial sums in",
-    6: "top-c done", 7: "exact rows done (h published)", 8: "down-row prefetch issued",
-    9: "exact activations in", 10: "top-k done", 11: "down-row prefetch landed",
+    6: "top-c done", 7: "exact rows done (h published)", 8: "candidate-row prefetch issued (general instance)",
+    9: "exact activations in", 10: "top-k done",
+    11: "kept down and Bt row loads issued (batch-1 instance) / candidate rows landed (general)",
     12: "kept Bt rows in, z formed", 13: "pair output slice stored", 14: "combine done",
     15: "wave 0 sketch activations in", 16: "wave 1 sketch activations in", 17: "wave 2 sketch activations in",
     18: "wave 3 sketch activations in", 19: "wave 0 exact activations in", 20: "wave 1 exact activations in",
@@ -531,23 +599,17 @@ def recovery_sweep(torch, cfm, args):
           flush=True)
 
 
-def cold_timing(torch, cfm, args):
-    """Batch 1 on the Qwen3-30B-A3B-shaped layer at 18 % (k 138, c 276, r 64): every call timed on its
-    own with HIP events, after an untimed write of 1 GiB that evicts the L2 and the 256 MB last-level
-    cache, so each call reads its weights from HBM, and a GPU sleep that lets the host enqueue the
-    call before the first event is taken. Median, p10 and p90 over the reps, for the selected and the
-    dense layer (alternating), and the algorithmic GB/s at the median."""
+def cold_measure(torch, cfm, layers, reps, warmup, seed, k=138, c=276, r=64):
+    """Batch 1 on Qwen3-30B-A3B-shaped layers: every call timed on its own with HIP events, after an
+    untimed write of 1 GiB that evicts the L2 and the 256 MB last-level cache, so each call reads its
+    weights from HBM, and a GPU sleep that lets the host enqueue the call before the first event is
+    taken. Median, p10 and p90 over the reps for the selected and the dense layer (alternating), and
+    the algorithmic GB/s at the median."""
     import numpy as np
-    E, K, I, H = 128, 8, 768, 2048
-    k, c, r = 138, 276, 64
-    NL = args.layers
-    layers = []
-    for l in range(NL):
-        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
-        A, Bt = cfm.lowrank_build(wd, r)
-        layers.append((wg, wu, wd, signs, cfm.sketch_build(wg, wu, signs), A, Bt))
-    reps = args.steps
-    x, ids, w = make_tokens(torch, args.seed + 77, reps + args.warmup, 1, E, K, H)
+    E, I, H = layers[0][0].shape
+    K = 8
+    NL = len(layers)
+    x, ids, w = make_tokens(torch, seed + 77, reps + warmup, 1, E, K, H)
     ws_s = cfm.new_workspace(cfm.select_workspace(1, K, E, I, H, k, c, r), "cuda")
     ws_d = cfm.new_workspace(cfm.dense_workspace(1, K, E, I, H), "cuda")
     out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
@@ -555,7 +617,7 @@ def cold_timing(torch, cfm, args):
     st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
     times = {"selected": [], "dense": []}
     bytes_ = {}
-    for i in range(reps + args.warmup):
+    for i in range(reps + warmup):
         wg, wu, wd, signs, sk, A, Bt = layers[i % NL]
         for name in ("selected", "dense"):
             flush.fill_(i & 255)
@@ -571,13 +633,14 @@ def cold_timing(torch, cfm, args):
                 cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=out, ws=ws_d)
             e1.record()
             torch.cuda.synchronize()
-            if i >= args.warmup:
+            if i >= warmup:
                 times[name].append(e0.elapsed_time(e1) * 1e3)
             if i == 0 and name == "selected":
                 d = cfm.decode_stats(st)
                 bytes_["selected"] = sum(d[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down",
                                                         "bytes_recovery", "bytes_io"))
                 bytes_["dense"] = d["bytes_dense_equiv"]
+    del flush, ws_s, ws_d
     res = {}
     for name, v in times.items():
         a = np.array(v)
@@ -586,9 +649,23 @@ def cold_timing(torch, cfm, args):
                      "p90_us": round(float(np.percentile(a, 90)), 3),
                      "GBps_at_median": round(bytes_[name] / (med * 1e-6) / 1e9, 1), "bytes": bytes_[name]}
     res["speedup_at_median"] = round(res["dense"]["median_us"] / res["selected"]["median_us"], 3)
+    res["reps"] = reps
+    return res
+
+
+def cold_timing(torch, cfm, args):
+    """The cold-call measurement on its own, over args.steps reps."""
+    E, K, I, H = 128, 8, 768, 2048
+    r = 64
+    layers = []
+    for l in range(args.layers):
+        wg, wu, wd, signs = make_layer(torch, args.seed, l, E, I, H)
+        A, Bt = cfm.lowrank_build(wd, r)
+        layers.append((wg, wu, wd, signs, cfm.sketch_build(wg, wu, signs), A, Bt))
+    res = cold_measure(torch, cfm, layers, args.steps, args.warmup, args.seed)
     print(json.dumps({"workload": "Qwen3-30B-A3B-shaped MoE layer, batch 1, 18 % (k 138, c 276, r 64); "
                                   "each call after a 1 GiB flush, HIP events around the call",
-                      "data": "synthetic", "reps": reps, "layers": NL, "result": res}), flush=True)
+                      "data": "synthetic", "reps": args.steps, "layers": args.layers, "result": res}), flush=True)
 
 
 def calibrate_tau(torch, cfm, layer, x, ids, w, k, c, r, ws):
@@ -735,7 +812,7 @@ def olmoe(torch, cfm, args):
                 dense(i)
             ms_s, _ = timed_graph(torch, lambda i: sel(args.warmup + i), steps)
             ms_d, _ = timed_graph(torch, lambda i: dense(args.warmup + steps + i), steps)
-            kt = kernel_times(torch, cfm, lambda i: sel(args.warmup + i), steps)
+            kt, _ = kernel_times(torch, cfm, lambda i: sel(args.warmup + i), steps)
         res[name] = {"us_per_token": round(ms_s * 1e3 / (steps * T), 3),
                      "dense_us_per_token": round(ms_d * 1e3 / (steps * T), 3),
                      "kernels_us": {kn: round(v * 1e3, 2) for kn, v in kt.items()}}
@@ -762,6 +839,10 @@ def main():
         print("bench.py measures one GPU only: there is no multi-GPU path "
               "(expert-parallel sharding is not built).", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
 
     import torch
 
@@ -847,8 +928,8 @@ def main():
         off = args.warmup
         ms_sel, wall_sel = timed_graph(torch, lambda i: sel(off + i), steps)
         ms_den, wall_den = timed_graph(torch, lambda i: dense(off + steps + i), steps)
-        kt_sel = kernel_times(torch, cfm, lambda i: sel(off + i), steps)
-        kt_den = kernel_times(torch, cfm, lambda i: dense(off + steps + i), steps)
+        kt_sel, launches_sel = kernel_times(torch, cfm, lambda i: sel(off + i), steps)
+        kt_den, launches_den = kernel_times(torch, cfm, lambda i: dense(off + steps + i), steps)
         pp = None
         if T >= 8:
             # both passes forced on the same steps (the automatic choice is timed above)
@@ -862,40 +943,66 @@ def main():
                     ms_pd, _ = timed_graph(torch, lambda i: dense(off + steps + i), steps)
                 pp[name] = {"us_per_token": round(ms_p / steps * 1e3 / T, 3),
                             "dense_us_per_token": round(ms_pd / steps * 1e3 / T, 3)}
-        st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+        # Bytes of the step's first call (every step draws from the same distribution). The
+        # algorithmic bytes bill each used expert's rows once (the union over the pairs routed to it),
+        # as the grouped pass reports them; the automatic pass's own stats also give the bytes its
+        # kernels request (per pair on the per-pair pass).
         wg, wu, wd, signs, sk, A, Bt = layers[0]
+        st = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
         cfm.moe_select_forward(x[0], ids[0], w[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
                                out=out[0], ws=ws_s, stats=st)
         torch.cuda.synchronize()
         stats = cfm.decode_stats(st)
-        bytes_sel = sum(stats[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down",
-                                           "bytes_recovery", "bytes_io"))
-        bytes_den = stats["bytes_dense_equiv"]
+        if T > 1:
+            stu = torch.zeros(cfm.STATS_BYTES, dtype=torch.uint8, device="cuda")
+            with cfm.forward_path(cfm.FORWARD_GROUPED):
+                cfm.moe_select_forward(x[0], ids[0], w[0], wg, wu, wd, signs, *sk, A, Bt, k, c, r,
+                                       out=out[0], ws=ws_s, stats=stu)
+            torch.cuda.synchronize()
+            ustats = cfm.decode_stats(stu)
+        else:
+            ustats = stats
+        bytes_sel = sum(ustats[f] for f in ("bytes_sketch", "bytes_candidates", "bytes_down",
+                                            "bytes_recovery", "bytes_io"))
+        bytes_den = ustats["bytes_dense_equiv"]
         us_step = ms_sel / steps * 1e3
         us_step_d = ms_den / steps * 1e3
         results[T] = dict(steps=steps, us_per_step=us_step, us_per_token=us_step / T,
                           gbps=bytes_sel / (us_step * 1e-6) / 1e9, bytes=bytes_sel,
+                          bytes_requested=stats["bytes_requested"], experts_used=ustats["experts_used"],
                           dense_us_per_token=us_step_d / T,
                           dense_gbps=bytes_den / (us_step_d * 1e-6) / 1e9, dense_bytes=bytes_den,
                           speedup=us_step_d / us_step, kernels_us={n: v * 1e3 for n, v in kt_sel.items()},
+                          launches_per_step=launches_sel, dense_launches_per_step=launches_den,
                           dense_kernels_us={n: v * 1e3 for n, v in kt_den.items()},
                           wall_ms=wall_sel, stats=stats, per_pair=pp)
         log(f"B={T}: selected {us_step:.2f} us/step ({us_step / T:.2f} us/token, "
             f"{results[T]['gbps']:.0f} GB/s on {bytes_sel / 1e6:.1f} MB), dense {us_step_d:.2f} us/step "
             f"({results[T]['dense_gbps']:.0f} GB/s), speedup {results[T]['speedup']:.2f}x; kernels "
-            f"{ {n: round(v * 1e3, 2) for n, v in kt_sel.items()} }; dense kernels "
+            f"{ {n: round(v * 1e3, 2) for n, v in kt_sel.items()} } launches/step {launches_sel}; dense kernels "
             f"{ {n: round(v * 1e3, 2) for n, v in kt_den.items()} }; passes {pp}")
         del ws_s, ws_d, out, x, ids, w
 
     r1 = results[1] if 1 in results else results[batches[0]]     # (profiling runs may skip batch 1)
-    # the whole hot path is one kernel: its algorithmic bytes per launch are the call's bytes
-    k_us = r1["kernels_us"].get("k_select_fused")
+    # At batch 1 the whole hot path is one launch of k_select_fused per step, back to back in the
+    # graph: its average duration is the timed region (HIP events on the launch stream) over the
+    # launches in it, and its algorithmic bytes per launch are the call's bytes.
     roof = None
-    if k_us:
+    one_launch = set(r1["launches_per_step"]) == {"k_select_fused"} and \
+        abs(r1["launches_per_step"]["k_select_fused"] - 1.0) < 1e-9
+    if one_launch:
+        k_us = r1["us_per_step"]
         ach = r1["bytes"] / (k_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": "k_select_fused", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic(), "bytes_per_launch": r1["bytes"], "avg_launch_us": round(k_us, 3)}
+                "traffic": measured_traffic(), "bytes_per_launch": r1["bytes"],
+                "bytes_requested_per_launch": r1["bytes_requested"], "avg_launch_us": round(k_us, 3),
+                "avg_launch_us_source": "timed region / launches (HIP events on the launch stream)"}
+    cold = None
+    if 1 in results and args.cold_reps > 0:
+        log("cold calls (1 GiB flush before each) ...")
+        cold = cold_measure(torch, cfm, layers, args.cold_reps, 5, args.seed)
+        log(f"cold: {cold}")
     line = {
         "metric": METRIC,
         "value": round(r1["us_per_token"], 3),
@@ -915,17 +1022,24 @@ def main():
         "hbm_GBps": round(r1["gbps"], 1),
         "hbm_frac": round(r1["gbps"] / PEAK_HBM_GBPS, 4),
         "bytes_per_step": r1["bytes"],
+        "bytes_requested_per_step": r1["bytes_requested"],
         "dense": {"us_per_token": round(r1["dense_us_per_token"], 3),
                   "GBps": round(r1["dense_gbps"], 1), "hbm_frac": round(r1["dense_gbps"] / PEAK_HBM_GBPS, 4),
                   "bytes_per_step": r1["dense_bytes"]},
         "speedup_vs_dense": round(r1["speedup"], 3),
         "roofline": roof,
+        "cold": cold,
         "kernels_us": {n: round(v, 3) for n, v in r1["kernels_us"].items()},
         "dense_kernels_us": {n: round(v, 3) for n, v in r1["dense_kernels_us"].items()},
-        "batches": {str(T): {"us_per_token": round(v["us_per_token"], 3), "GBps": round(v["gbps"], 1),
+        "batches": {str(T): {"us_per_token": round(v["us_per_token"], 3),
+                             "GBps_on_expert_union_bytes": round(v["gbps"], 1),
+                             "bytes_per_step": v["bytes"], "bytes_requested_per_step": v["bytes_requested"],
+                             "experts_used": v["experts_used"],
                              "dense_us_per_token": round(v["dense_us_per_token"], 3),
-                             "speedup_vs_dense": round(v["speedup"], 3), "bytes_per_step": v["bytes"],
+                             "dense_bytes_per_step": v["dense_bytes"],
+                             "speedup_vs_dense": round(v["speedup"], 3),
                              "kernels_us": {n: round(x, 3) for n, x in v["kernels_us"].items()},
+                             "launches_per_step": {n: round(x, 3) for n, x in v["launches_per_step"].items()},
                              "passes": v["per_pair"]}
                     for T, v in results.items()},
         "offline_ms_per_layer": {"sketch_build": round(t_sketch / L * 1e3, 2),

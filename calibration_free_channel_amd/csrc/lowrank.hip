@@ -8,13 +8,14 @@
 //   G = W_down^T W_down                      (k_gram, tiled fp64 GEMM)
 //   Q <- orth(G Q), repeated                  (k_subspace: block subspace
 //                                              iteration, CholQR2)
-//   Rayleigh-Ritz: M = Q^T G Q, Jacobi eigen-decomposition M = W L W^T in LDS,
-//   V_r = Q W[:, top r]                        (k_subspace)
+//   every 4 iterations Rayleigh-Ritz: M = Q^T G Q, Jacobi eigen-decomposition
+//   M = W L W^T in LDS, Q <- Q W ordered by Ritz value (k_subspace)
+//   V_r = the leading r columns of Q
 //   Bt = V_r, A = W_down V_r                   (k_lowrank_a)
 // The block is r plus 32 columns of oversampling (at most 96, or r if larger,
 // and never more than min(I, H), the rank bound of G);
-// the iteration runs until the energy its leading r columns capture has
-// converged (relative change at most 1e-13 per iteration).
+// the iteration runs until the energy the r leading Ritz vectors capture has
+// converged (relative change at most 1e-11 between Rayleigh-Ritz steps).
 #include <algorithm>
 
 #include "cfm_internal.h"
@@ -217,45 +218,16 @@ __device__ double block_sum_lr(double v, double* red) {
   return s;
 }
 
-__global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qall, double* Yall,
-                                                 double* Wall, int I, int p, int pp, int r,
-                                                 int iters) {
-  extern __shared__ double lds[];      // GEMM staging / Cholesky factor / Jacobi matrix
-  __shared__ double sh[2];
-  __shared__ double red[LT / 64];
-  __shared__ int order[kMaxRank + 2];
-  __shared__ double cs[4 * (kMaxRank / 2 + 1)];   // per-pair (c, s, a, b) of one Jacobi round
-  const int e = blockIdx.x, tid = threadIdx.x;
-  const double* G = Gall + (size_t)e * I * I;
-  double* Q = Qall + (size_t)e * I * p;
-  double* Y = Yall + (size_t)e * I * p;
-  double* W = Wall + (size_t)e * pp * pp;   // Ritz vectors of M
-
-  for (int o = tid; o < I * p; o += LT) Q[o] = hash_uniform(((uint64_t)e << 40) ^ (uint64_t)o);
-  __syncthreads();
-  cholqr(Q, I, p, lds, sh);
-  cholqr(Q, I, p, lds, sh);
-  // iterate until the energy the leading r columns capture, tr(Q_r^T G Q_r)
-  // (the Eckart-Young objective), changes by at most 1e-13 of itself between
-  // iterations (at least 4, at most `iters` iterations)
-  double prev = -1.0;
-  for (int it = 0; it < iters; ++it) {
-    gemm_gq(G, Q, Y, I, p, lds);
-    __syncthreads();
-    double part = 0.0;
-    for (int o = tid; o < I * r; o += LT) {
-      const int i = o / r, b = o % r;
-      part += Q[(size_t)i * p + b] * Y[(size_t)i * p + b];
-    }
-    const double energy = block_sum_lr(part, red);
-    cholqr(Y, I, p, lds, sh);
-    cholqr(Y, I, p, lds, sh);
-    for (int o = tid; o < I * p; o += LT) Q[o] = Y[o];
-    __syncthreads();
-    if (it >= 3 && fabs(energy - prev) <= 1e-13 * energy) break;
-    prev = energy;
-  }
-  // Rayleigh-Ritz: M = Q^T (G Q), padded to even size pp with a zero row/column
+// Rayleigh-Ritz on the block Q [I][p]: M = Q^T G Q (p x p, padded to even
+// size pp with a zero row and column) is diagonalised in LDS by cyclic Jacobi
+// with round-robin ordering (each round rotates pp/2 disjoint pairs); its
+// eigenvectors W rotate the block, Q <- Q W, with the columns ordered by Ritz
+// value, descending (lower index on ties). Returns the sum of the r largest
+// Ritz values (the energy tr(V_r^T G V_r) the leading r Ritz vectors
+// capture). Y is scratch [I][p]; Wm holds W [pp][pp].
+__device__ double rayleigh_ritz(const double* G, double* Q, double* Y, double* Wm, int I, int p, int pp, int r,
+                                double* lds, double* sh, double* red, int* order, double* cs) {
+  const int tid = threadIdx.x;
   gemm_gq(G, Q, Y, I, p, lds);
   __syncthreads();
   gram_ab(Q, Y, lds, I, p);          // lds[a*p+b] = (Q^T G Q)[a][b]
@@ -268,15 +240,13 @@ __global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qal
     for (int o = tid; o < pp * pp; o += LT)
       if (o / pp >= p || o % pp >= p) M[o] = 0.0;
   }
-  for (int o = tid; o < pp * pp; o += LT) W[o] = (o / pp == o % pp) ? 1.0 : 0.0;
+  for (int o = tid; o < pp * pp; o += LT) Wm[o] = (o / pp == o % pp) ? 1.0 : 0.0;
   __syncthreads();
   for (int o = tid; o < pp * pp; o += LT) {          // symmetrise (round-off)
     const int a = o / pp, b = o % pp;
     if (a < b) { const double v = 0.5 * (M[a * pp + b] + M[b * pp + a]); M[a * pp + b] = v; M[b * pp + a] = v; }
   }
   __syncthreads();
-
-  // cyclic Jacobi with round-robin ordering: each round rotates pp/2 disjoint pairs
   for (int sweep = 0; sweep < 40; ++sweep) {
     double off = 0.0, dia = 0.0;
     for (int o = tid; o < pp * pp; o += LT) {
@@ -320,9 +290,9 @@ __global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qal
         const double ma = M[y * pp + a], mb = M[y * pp + b];
         M[y * pp + a] = c * ma - s * mb;
         M[y * pp + b] = s * ma + c * mb;
-        const double wa = W[y * pp + a], wb = W[y * pp + b];
-        W[y * pp + a] = c * wa - s * wb;
-        W[y * pp + b] = s * wa + c * wb;
+        const double wa = Wm[y * pp + a], wb = Wm[y * pp + b];
+        Wm[y * pp + a] = c * wa - s * wb;
+        Wm[y * pp + b] = s * wa + c * wb;
       }
       __syncthreads();
     }
@@ -341,16 +311,71 @@ __global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qal
       }
       order[b + 1] = v;
     }
+    double e = 0.0;
+    for (int l = 0; l < r; ++l) e += M[order[l] * pp + order[l]];
+    sh[0] = e;
   }
   __syncthreads();
-  // V_r = Q W[:, order[0..r)] into Y (I x r, stride r)
+  const double energy = sh[0];
+  // Q <- Q W[:, order], through Y
+  for (int o = tid; o < I * p; o += LT) {
+    const int i = o / p, l = o % p;
+    const int col = order[l];
+    double s = 0.0;
+    for (int a = 0; a < p; ++a) s = fma(Q[(size_t)i * p + a], Wm[a * pp + col], s);
+    Y[o] = s;
+  }
+  __syncthreads();
+  for (int o = tid; o < I * p; o += LT) Q[o] = Y[o];
+  __syncthreads();
+  return energy;
+}
+
+// Block subspace iteration Q <- orth(G Q) with a Rayleigh-Ritz step every
+// kRitzEvery iterations, until the energy the r leading Ritz vectors capture
+// changes by at most 1e-11 of itself between two Rayleigh-Ritz steps (at most
+// `iters` iterations). The leading r columns of the rotated block are then the
+// map's V_r, written to Y with stride r and each column signed so that its
+// largest-magnitude entry is positive (lowest index on ties).
+constexpr int kRitzEvery = 4;
+
+__global__ __launch_bounds__(LT) void k_subspace(const double* Gall, double* Qall, double* Yall,
+                                                 double* Wall, int I, int p, int pp, int r,
+                                                 int iters) {
+  extern __shared__ double lds[];      // GEMM staging / Cholesky factor / Jacobi matrix
+  __shared__ double sh[2];
+  __shared__ double red[LT / 64];
+  __shared__ int order[kMaxRank + 2];
+  __shared__ double cs[4 * (kMaxRank / 2 + 1)];   // per-pair (c, s, a, b) of one Jacobi round
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const double* G = Gall + (size_t)e * I * I;
+  double* Q = Qall + (size_t)e * I * p;
+  double* Y = Yall + (size_t)e * I * p;
+  double* W = Wall + (size_t)e * pp * pp;   // Ritz vectors of M
+
+  for (int o = tid; o < I * p; o += LT) Q[o] = hash_uniform(((uint64_t)e << 40) ^ (uint64_t)o);
+  __syncthreads();
+  cholqr(Q, I, p, lds, sh);
+  cholqr(Q, I, p, lds, sh);
+  double prev = -1.0;
+  for (int it = 1; it <= iters; ++it) {
+    gemm_gq(G, Q, Y, I, p, lds);
+    __syncthreads();
+    cholqr(Y, I, p, lds, sh);
+    cholqr(Y, I, p, lds, sh);
+    for (int o = tid; o < I * p; o += LT) Q[o] = Y[o];
+    __syncthreads();
+    if (it % kRitzEvery == 0 || it == iters) {
+      const double energy = rayleigh_ritz(G, Q, Y, W, I, p, pp, r, lds, sh, red, order, cs);
+      if (fabs(energy - prev) <= 1e-11 * energy) break;
+      prev = energy;
+    }
+  }
+  // V_r = the leading r columns of the rotated block, into Y (I x r, stride r)
   double* Vr = Y;
   for (int o = tid; o < I * r; o += LT) {
     const int i = o / r, l = o % r;
-    const int col = order[l];
-    double s = 0.0;
-    for (int a = 0; a < p; ++a) s = fma(Q[(size_t)i * p + a], W[a * pp + col], s);
-    Vr[o] = s;
+    Vr[o] = Q[(size_t)i * p + l];
   }
   __syncthreads();
   // sign: largest-magnitude entry of each column positive (lowest index on ties)
@@ -429,7 +454,7 @@ LowrankPlan lowrank_plan(int E, int I, int H, int r) {
   int p = std::max(r, std::min(r + 32, 96));
   p = std::min(p, std::min(I, H));
   pl.p = std::max(p, 1);     // p <= 128
-  pl.iters = 200;             // at most; the iteration stops once the captured energy has converged
+  pl.iters = 200;             // at most; the iteration stops once the Ritz energy has converged
   const int pp = (pl.p + 1) & ~1;
   Carve cv;
   pl.off_gram = cv.take((size_t)E * I * I * 8);

@@ -127,9 +127,10 @@ int sketch_build_seeded(const cfm_bf16* w_gate, const cfm_bf16* w_up, int E, int
  * Computes the rank-r truncated SVD W_down ~ A * Bt^T per expert, with
  * A = W_down V_r = U_r diag(s_r) and Bt = V_r (orthonormal columns), both
  * rounded to BF16. Computed on the device in float64: Gram matrix
- * W_down^T W_down, block subspace iteration with oversampling (until the
- * energy the leading r columns capture changes by at most 1e-13 of itself per
- * iteration, at most 200 iterations) and a Rayleigh-Ritz step. Each column of
+ * W_down^T W_down, block subspace iteration with oversampling and a
+ * Rayleigh-Ritz step every 4 iterations (until the energy the r leading Ritz
+ * vectors capture changes by at most 1e-11 of itself between two such steps,
+ * at most 200 iterations). Each column of
  * V_r is signed so that its largest-magnitude entry is positive. Where an
  * expert's W_down has rank below r, the columns past its rank are zero in
  * both A and Bt (they would carry no energy).
