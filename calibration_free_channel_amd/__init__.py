@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     dense_workspace, forward_path, last_error, lowrank_build, lowrank_workspace, moe_dense_forward,
     moe_layer_dense_forward, moe_layer_forward,
     moe_select_forward, moe_select_forward_noalloc, moe_select_forward_threshold, new_workspace, phase_trace, select_workspace,
-    set_forward_path, set_wait_limit, workspace_status,
+    set_forward_path, set_resident_limit, set_wait_limit, workspace_status,
     rotation_signs, sketch_build, sketch_build_seeded, sketch_bytes, timing_enable,
     timing_report, version,
 )

@@ -56,6 +56,7 @@ _SIGS = {
     "cfm_phase_trace": (_i, [_p]),
     "cfm_workspace_status": (_i, [_p, _z, _p]),
     "cfm_set_wait_limit": (_i, [ctypes.c_uint]),
+    "cfm_set_resident_limit": (_i, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -386,6 +387,12 @@ def set_wait_limit(polls: int) -> int:
     """Polls of one exchanged value before a single-launch forward call gives up (default 2^20;
     0: every wait gives up at once, for testing the failure path). Returns the previous value."""
     return int(_lib.cfm_set_wait_limit(int(polls)))
+
+
+def set_resident_limit(workgroups: int) -> int:
+    """Cap on the workgroups a single-launch forward call assumes resident (-1: the device's own count;
+    0: none, so the call is refused). Returns the previous value."""
+    return int(_lib.cfm_set_resident_limit(int(workgroups)))
 
 
 def phase_trace(buf):

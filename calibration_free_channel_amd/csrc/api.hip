@@ -48,6 +48,7 @@ namespace {
 std::mutex g_ws_mu;
 std::unordered_map<uintptr_t, uint64_t> g_ws_sig;    // workspace address -> layout of its last call
 std::atomic<unsigned> g_wait_limit{1u << 20};
+std::atomic<int> g_resident_limit{-1};
 }  // namespace
 
 int prepare_workspace(void* ws, size_t bytes, uint64_t sig, hipStream_t stream) {
@@ -66,6 +67,7 @@ int prepare_workspace(void* ws, size_t bytes, uint64_t sig, hipStream_t stream) 
 }
 
 unsigned wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+int resident_limit() { return g_resident_limit.load(std::memory_order_relaxed); }
 
 void timing_begin(const char* name, hipStream_t s) {
   if (!g_timing) return;
@@ -223,6 +225,8 @@ int cfm_timing_enable(int on) {
 }
 
 int cfm_set_wait_limit(unsigned polls) { return (int)g_wait_limit.exchange(polls); }
+
+int cfm_set_resident_limit(int workgroups) { return g_resident_limit.exchange(workgroups < 0 ? -1 : workgroups); }
 
 int cfm_workspace_status(void* ws, size_t ws_bytes, void* stream) {
   clear_error();

@@ -35,6 +35,9 @@ inline uint64_t layout_signature(std::initializer_list<long> v) {
 // Polls of one exchanged value before a single-launch forward pass gives up
 // (cfm_set_wait_limit; 0: every wait gives up at once).
 unsigned wait_limit();
+// Cap on the workgroups a single-launch forward pass may assume resident at
+// once (cfm_set_resident_limit; -1: none, the device's own count).
+int resident_limit();
 
 // Optional per-kernel event timing (cfm_timing_enable); no-ops while disabled.
 bool timing_on();

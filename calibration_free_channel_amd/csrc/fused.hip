@@ -92,17 +92,19 @@ const void* fused_fn(bool select, int H, bool recx, bool env) {
 
 // How many workgroups of `fn` with `lds` bytes of LDS the current device holds
 // at once (compute units times resident workgroups per unit), capped at the
-// launch sequence slots; cached per (device, kernel, LDS size).
+// launch sequence slots (cached per device, kernel and LDS size) and at the
+// process-wide resident limit when one is set.
 int resident_workgroups(const void* fn, size_t lds, int* out) {
   int dev = 0;
   CFM_HIP_TRY(hipGetDevice(&dev));
   static std::mutex mu;
   static std::map<std::tuple<int, const void*, size_t>, int> cache;
   const auto key = std::make_tuple(dev, fn, lds);
+  const int cap = resident_limit();
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
-    if (it != cache.end()) { *out = it->second; return CFM_OK; }
+    if (it != cache.end()) { *out = cap >= 0 ? std::min(cap, it->second) : it->second; return CFM_OK; }
   }
   if (lds > 65536)
     CFM_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -112,7 +114,7 @@ int resident_workgroups(const void* fn, size_t lds, int* out) {
   const int n = std::min(kSeqSlots, cus * per_cu);
   std::lock_guard<std::mutex> lk(mu);
   cache[key] = n;
-  *out = n;
+  *out = cap >= 0 ? std::min(cap, n) : n;
   return CFM_OK;
 }
 

@@ -146,7 +146,8 @@ __device__ __forceinline__ void await_all(const uint64_t* const (&ptr)[N], uint6
     }
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-    for (int j = 0; j < N; ++j) v[j] = ld_tagged(ptr[j]);
+    for (int j = 0; j < N; ++j)          // only the entries still stale are read again
+      if ((uint32_t)(v[j] >> 32) != tag) v[j] = ld_tagged(ptr[j]);
   }
 }
 __device__ __forceinline__ float tagged_value(uint64_t v) { return __uint_as_float((uint32_t)v); }
@@ -1024,6 +1025,9 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 
     // ---- top-c candidates (identical in every workgroup of the pair)
     phase_stamp(a, 4);
+    const uint64_t* zptr[8];        // (lean instance) the partial recovery sums, awaited after the exact step
+#pragma unroll
+    for (int u = 0; u < 8; ++u) zptr[u] = a.xh + (size_t)p * a.I;
     if (nosk) {
       for (int i = tid; i < a.I; i += NT) {
         L.hh[i] = 0.f;
@@ -1056,15 +1060,27 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           ptr[4 + u] = (zpre && zg < groups && q < nw) ? zp + (size_t)q * r : pb;
         }
 #pragma unroll
-        for (int j = 0; j < 12; ++j) v[j] = ld_tagged(ptr[j]);
-        await_all<12>(ptr, v, tag, a.fail, a.spin);
+        for (int j = 0; j < (LEAN ? 4 : 12); ++j) v[j] = ld_tagged(ptr[j]);
+        if constexpr (LEAN) {
+          // (lean instance) only the sketch activations are waited for here: the
+          // partial sums are published after them and are needed only after
+          // top-k, so they are awaited with the exact activations
+          const uint64_t* const (&p4)[4] = reinterpret_cast<const uint64_t* const (&)[4]>(ptr);
+          uint64_t (&v4)[4] = reinterpret_cast<uint64_t (&)[4]>(v);
+          await_all<4>(p4, v4, tag, a.fail, a.spin);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) zptr[u] = ptr[4 + u];
+        } else {
+          await_all<12>(ptr, v, tag, a.fail, a.spin);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
           if (j < cnt) L.hh[i0 + j] = hv;
           k4[j] = score_key(hv);
         }
-        if (zpre) {
+        if (LEAN) {
+        } else if (zpre) {
           if (zg < groups) {
             float zs = 0.f;
 #pragma unroll
@@ -1091,10 +1107,12 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       }
       if (a.c >= a.I || a.c <= 0) __syncthreads();   // block_topk's early exits skip its barrier
     }
-    for (int l = tid; l < r; l += NT) {
-      float s = 0.f;
-      for (int g = 0; g < groups; ++g) s += L.red[NT + g * r + l];
-      L.zsum[l] = s;
+    if constexpr (!LEAN) {
+      for (int l = tid; l < r; l += NT) {
+        float s = 0.f;
+        for (int g = 0; g < groups; ++g) s += L.red[NT + g * r + l];
+        L.zsum[l] = s;
+      }
     }
     if (w == 0 && a.cand_out)
       for (int i = tid; i < a.c; i += NT) a.cand_out[(size_t)p * a.c + i] = L.candp[i];
@@ -1141,15 +1159,38 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           for (int j = 0; j < 4; ++j) hzc[j] = L.hh[chn[j]];
         }
         const uint64_t* pc = a.xc + (size_t)p * a.c;
-        const uint64_t* ptr[4];
-        uint64_t v[4] = {0, 0, 0, 0};
+        const uint64_t* ptr[12];
+        uint64_t v[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         if (a.c > 0) {     // (unused entries watch the pair's first candidate, which exists)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             ptr[j] = pc + (j < cnt ? i0 + j : 0);
             v[j] = ld_tagged(ptr[j]);
           }
-          await_all<4>(ptr, v, tag, a.fail, a.spin);
+          if constexpr (LEAN) {
+            // with the partial recovery sums (published long before; read
+            // again here rather than carried from the screen, when some of
+            // them were still stale)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              ptr[4 + u] = zptr[u];
+              v[4 + u] = ld_tagged(zptr[u]);
+            }
+            await_all<12>(ptr, v, tag, a.fail, a.spin);
+          } else {
+            const uint64_t* const (&p4)[4] = reinterpret_cast<const uint64_t* const (&)[4]>(ptr);
+            uint64_t (&v4)[4] = reinterpret_cast<uint64_t (&)[4]>(v);
+            await_all<4>(p4, v4, tag, a.fail, a.spin);
+          }
+        }
+        if constexpr (LEAN) {
+          // this thread's share of the pair's partial recovery sums (group zg)
+          if (zg < groups) {
+            float zs = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) zs += zg + groups * u < nw ? tagged_value(v[4 + u]) : 0.f;
+            L.red[NT + zg * r + zl] = zs;
+          }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1270,7 +1311,11 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         }
       }
       __syncthreads();
-      for (int l = tid; l < 64; l += NT) L.zv[l] = L.zsum[l] - (L.red[l] + L.red[64 + l] + L.red[128 + l] + L.red[192 + l]);
+      for (int l = tid; l < 64; l += NT) {
+        float zs = 0.f;
+        for (int g2 = 0; g2 < groups; ++g2) zs += L.red[NT + g2 * r + l];
+        L.zv[l] = zs - (L.red[l] + L.red[64 + l] + L.red[128 + l] + L.red[192 + l]);
+      }
       __syncthreads();
       phase_stamp(a, 12);
 #pragma unroll

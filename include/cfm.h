@@ -406,6 +406,17 @@ int cfm_workspace_status(void* ws, size_t ws_bytes, void* stream);
 int cfm_set_wait_limit(unsigned polls);
 
 /*
+ * cfm_set_resident_limit - caps the number of workgroups a single-launch
+ * forward pass assumes resident at once (process-wide; -1, the default: the
+ * device's compute units times the kernel's occupancy). A smaller grid runs
+ * the routed pairs in rounds of the same launch; 0 stands for a device that
+ * holds none, so that the refusal can be exercised: the call then returns
+ * CFM_EUNSUPPORTED before launching anything. For callers that share the GPU
+ * with other resident work, and for testing. Returns the previous value.
+ */
+int cfm_set_resident_limit(int workgroups);
+
+/*
  * cfm_phase_trace - instrumentation of the single-launch kernels (not part of
  * the method). In the trace build of the library (compiled with
  * CFM_PHASE_TRACE), every later per-pair launch stores, from thread 0 of each

@@ -119,6 +119,36 @@ def test_failure_channel_forced_from_host(cfm):
         assert cfm.workspace_status(ws) == 0
 
 
+def test_resident_limit_rounds_and_refusal(cfm):
+    """A device that holds fewer workgroups than the grid wants: the single launch runs the routed pairs
+    in rounds and gives the same result; one that holds none is refused before anything is launched."""
+    log("resident limit")
+    wl = custom_workload("resident", 8, 8, 768, 2048, 2, 138, 276, 64, 53)
+    L, A, Bt = _layer_and_map(wl)
+    sk = cfm.sketch_build(L.wg, L.wu, L.signs)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        want = down_bf16(cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt,
+                                                wl.k, wl.c, wl.r))
+        dwant = down_bf16(cfm.moe_dense_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd))
+        prev = cfm.set_resident_limit(5)
+        try:
+            got = down_bf16(cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt,
+                                                   wl.k, wl.c, wl.r))
+            dgot = down_bf16(cfm.moe_dense_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd))
+            cfm.set_resident_limit(0)
+            with pytest.raises(cfm.CfmError, match="cannot hold one workgroup"):
+                cfm.moe_select_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd, L.signs, *sk, A, Bt, wl.k, wl.c, wl.r)
+            with pytest.raises(cfm.CfmError, match="cannot hold one workgroup"):
+                cfm.moe_dense_forward(L.x, L.ids, L.w, L.wg, L.wu, L.wd)
+        finally:
+            cfm.set_resident_limit(prev)
+        torch.cuda.synchronize()
+    # the same sets and arithmetic per pair; only the order of the partial sums over slices differs
+    for a, b in ((got, want), (dgot, dwant)):
+        fa, fb = O.bf16_to_f64(a), O.bf16_to_f64(b)
+        assert np.linalg.norm(fa - fb) <= 1e-2 * np.linalg.norm(fb)
+
+
 @pytest.mark.parametrize("which", ["lean", "general"])
 def test_bytes_requested(cfm, which):
     """bytes_requested equals the kept-row count where only kept rows are read (the lean batch-1
