@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="instead of the default line: batch 1, each call timed on its own after a 1 GiB "
                          "cache flush, median / p10 / p90 of the selected and the dense layer")
+    ap.add_argument("--general", action="store_true",
+                    help="with --phase-trace: the general per-pair instance instead of the batch-1 one")
     ap.add_argument("--phase-trace", action="store_true",
                     help="instead of the default line: per-phase timeline of the batch-1 selected and dense "
                          "kernels from in-kernel clock stamps (needs the trace build, CFM_PHASE_TRACE=1)")
@@ -344,6 +346,7 @@ def phase_trace(torch, cfm, args):
         cfm.moe_dense_forward(x[i], ids[i], w[i], wg, wu, wd, out=out[i], ws=ws_d)
 
     res = {}
+    prev_path = cfm.set_forward_path(cfm.FORWARD_PER_PAIR_GENERAL if args.general else cfm.FORWARD_PER_PAIR)
     for name, fn, phases in (("selected", sel, SELECT_PHASES), ("dense", dense, DENSE_PHASES)):
         for i in range(ring):
             fn(i)
@@ -382,7 +385,9 @@ def phase_trace(torch, cfm, args):
         log(f"{name}: " + "; ".join(f"{kk}: {vv['median_wg_us']}/{vv['max_wg_us']}" for kk, vv in table.items()))
         log(f"{name}: XCD start offsets (us) {starts}; passes per select (count of workgroups by passes) {passes}")
     cfm.phase_trace(None)
-    print(json.dumps({"phase_trace": res, "workload": "q18_b1", "ring": ring, "reps": reps}), flush=True)
+    cfm.set_forward_path(prev_path)
+    print(json.dumps({"phase_trace": res, "workload": "q18_b1", "instance": "general" if args.general else "batch-1",
+                      "ring": ring, "reps": reps}), flush=True)
 
 
 def stack(torch, cfm, args):

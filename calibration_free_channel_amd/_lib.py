@@ -333,7 +333,7 @@ def moe_layer_dense_forward(h, norm_w, eps, w_router, K, w_gate, w_up, w_down_t,
     return out
 
 
-FORWARD_AUTO, FORWARD_PER_PAIR, FORWARD_GROUPED = 0, 1, 2
+FORWARD_AUTO, FORWARD_PER_PAIR, FORWARD_GROUPED, FORWARD_PER_PAIR_GENERAL = 0, 1, 2, 3
 
 
 def set_forward_path(path: int) -> int:

@@ -69,6 +69,7 @@ int prepare_workspace(void* ws, size_t bytes, uint64_t sig, hipStream_t stream) 
 unsigned wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 int resident_limit() { return g_resident_limit.load(std::memory_order_relaxed); }
 
+
 void timing_begin(const char* name, hipStream_t s) {
   if (!g_timing) return;
   g_open = name;
@@ -105,7 +106,8 @@ int check_budget(int I, int H, int k, int c, int r) {
   return CFM_OK;
 }
 
-// Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped (process-wide).
+// Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped, 3 per-pair
+// without the batch-1 instance (process-wide).
 std::atomic<int> g_path{0};
 // Automatic choice: the grouped pass from these batch sizes on (measured on the
 // Qwen3-30B-A3B-shaped layer: below them the single-launch per-pair kernels
@@ -133,6 +135,8 @@ int check_tokens(int T, int K) {
 }
 
 }  // namespace
+
+int forward_path() { return g_path.load(std::memory_order_relaxed); }
 
 // ---------------------------------------------------------------- scratch of the no-allocation entry point
 // Device memory of moe_select_forward_noalloc: one copy per GPU, held until
@@ -215,7 +219,7 @@ const char* cfm_last_error(void) { return g_last_error.c_str(); }
 const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
 
 int cfm_set_forward_path(int path) {
-  if (path < 0 || path > 2) return set_error(CFM_EINVAL, "path must be 0, 1 or 2");
+  if (path < 0 || path > 3) return set_error(CFM_EINVAL, "path must be 0, 1, 2 or 3");
   return g_path.exchange(path);
 }
 

@@ -38,6 +38,8 @@ unsigned wait_limit();
 // Cap on the workgroups a single-launch forward pass may assume resident at
 // once (cfm_set_resident_limit; -1: none, the device's own count).
 int resident_limit();
+// The process-wide forward-pass setting (cfm_set_forward_path).
+int forward_path();
 
 // Optional per-kernel event timing (cfm_timing_enable); no-ops while disabled.
 bool timing_on();

@@ -308,7 +308,7 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
     return rc;
   const FusedArgs a = fused_args(s, p);
   if (!a.x) return set_error(CFM_EINVAL, "select forward: no hidden states");
-  const bool lean = lean_fits(p, s);
+  const bool lean = forward_path() != 3 && lean_fits(p, s);
   int rc = launch_fused<true>(a, p.lds, stream, lean);
   if (rc) return rc;
   if (s.stats) {

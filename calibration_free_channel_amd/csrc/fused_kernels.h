@@ -1128,12 +1128,13 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       for (int m = 0; m < CH; ++m) xr[m] = x16(xrow, min(lane + 64 * m, H / 8 - 1));   // past H / 8: times zero rows
       exact_rows<CH>(a, L, e, L.candp, q0, q1, xr, a.xc + (size_t)p * a.c, tag, [] {});
     }
-    // candidate rows for z and the down projection, requested once the exact
-    // rows are in (so they do not share bandwidth with them) and used after
-    // top-k: every candidate's down row for this workgroup's columns and its
-    // Bt row land in LDS while the exact activations are exchanged and the
-    // kept set is selected, so nothing after top-k waits on memory
-    constexpr bool kBtLate = false;
+    // (general instance) candidate rows for the down projection: requested
+    // once the exact rows are in (so they do not share bandwidth with them),
+    // landing in LDS while the exact activations are exchanged and the kept
+    // set is selected; z needs the kept channels' Bt rows, read after top-k
+    // (with the variant, or at the largest hidden width where registers are
+    // short, every candidate's Bt row is prefetched into LDS with them)
+    constexpr bool kBtLate = !RECX && EPT <= 16;
     phase_stamp(a, 7);
     if (!LEAN && a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck, !kBtLate);
     phase_stamp(a, 8);

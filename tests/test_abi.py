@@ -171,7 +171,7 @@ def test_dense_forward_rejects(lib):
 def test_forward_path_switch(lib):
     f = lib.cfm_set_forward_path
     f.restype = ctypes.c_int
-    assert f(3) == EINVAL and f(-1) == EINVAL
+    assert f(4) == EINVAL and f(-1) == EINVAL
     prev = f(2)
     try:
         assert f(2) == 2
@@ -184,6 +184,7 @@ def test_forward_path_switch(lib):
         assert d(FAKE, FAKE, FAKE, 1, 2, FAKE, FAKE, FAKE, 8, 128, 192, FAKE, FAKE, ctypes.c_size_t(16), None) == EWS
         assert f(1) == 2
         assert _sel(lib, r=6, wsb=16) == EWS
+        assert f(3) == 1 and f(1) == 3          # per-pair without the batch-1 instance
     finally:
         f(prev)
 

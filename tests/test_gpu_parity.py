@@ -360,6 +360,18 @@ def test_q18_b1_full_size(cfm, q18_layer):
         _check_lowrank(L.host.w_down_t[e], Ag[e], Bg[e], wl.r, f"q18 expert {e}")
 
 
+def test_q18_b1_full_size_general_instance(cfm, q18_layer):
+    """The batch-1 call through the general per-pair instance (the batch-1 instance switched off)."""
+    L, wl = q18_layer, q18_layer.wl
+    E, I, H = L.host.w_gate.shape
+    used = sorted(set(L.host.ids.reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used, E, I, H)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR_GENERAL):
+        got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
+    compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, what="q18_b1 general instance")
+
+
 def test_q18_b1_full_size_candidates_exact(cfm, q18_layer):
     """The recovery variant (dropped candidates recovered with their exact activation) at full size."""
     L, wl = q18_layer, q18_layer.wl
