@@ -1044,51 +1044,51 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const int per = (a.I + NT - 1) / NT;
       if (LEAN || per <= 4) {
         uint32_t k4[4];
-        // this thread's sketch activations and, when each thread reads at most
-        // 8 of them, its share of the pair's partial recovery sums, awaited
-        // together (unused entries watch the pair's first activation)
-        const bool zpre = EPT <= 16 && r > 0 && a.nw * r <= 8 * NT;
-        const uint64_t* pb = a.xh + (size_t)p * a.I;
-        const uint64_t* zp = a.xz + (size_t)p * a.nw * r + zl;
-        const uint64_t* ptr[12];
-        uint64_t v[12];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ptr[j] = pb + (j < cnt ? i0 + j : 0);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int q = zg + groups * u;
-          ptr[4 + u] = (zpre && zg < groups && q < nw) ? zp + (size_t)q * r : pb;
-        }
-#pragma unroll
-        for (int j = 0; j < (LEAN ? 4 : 12); ++j) v[j] = ld_tagged(ptr[j]);
         if constexpr (LEAN) {
-          // (lean instance) only the sketch activations are waited for here: the
-          // partial sums are published after them and are needed only after
-          // top-k, so they are awaited with the exact activations
-          const uint64_t* const (&p4)[4] = reinterpret_cast<const uint64_t* const (&)[4]>(ptr);
-          uint64_t (&v4)[4] = reinterpret_cast<uint64_t (&)[4]>(v);
-          await_all<4>(p4, v4, tag, a.fail, a.spin);
+          // (lean instance) this thread's sketch activations, awaited together;
+          // the pair's partial recovery sums are published after them and are
+          // needed only after top-k, so they are awaited with the exact
+          // activations (unused entries watch the pair's first activation)
+          const uint64_t* pb = a.xh + (size_t)p * a.I;
+          const uint64_t* zp = a.xz + (size_t)p * a.nw * r + zl;
+          const uint64_t* ptr[4];
+          uint64_t v[4];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) zptr[u] = ptr[4 + u];
-        } else {
-          await_all<12>(ptr, v, tag, a.fail, a.spin);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
-          if (j < cnt) L.hh[i0 + j] = hv;
-          k4[j] = score_key(hv);
-        }
-        if (LEAN) {
-        } else if (zpre) {
-          if (zg < groups) {
-            float zs = 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) zs += zg + groups * u < nw ? tagged_value(v[4 + u]) : 0.f;
-            L.red[NT + zg * r + zl] = zs;
+          for (int j = 0; j < 4; ++j) {
+            ptr[j] = pb + (j < cnt ? i0 + j : 0);
+            v[j] = ld_tagged(ptr[j]);
           }
-        } else if (r > 0) {
-          fetch_zsum(a, L, p, zl, zg, groups, tag);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int q = zg + groups * u;
+            zptr[u] = (zg < groups && q < nw) ? zp + (size_t)q * r : pb;
+          }
+          await_all<4>(ptr, v, tag, a.fail, a.spin);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float hv = j < cnt ? tagged_value(v[j]) : 0.f;
+            if (j < cnt) L.hh[i0 + j] = hv;
+            k4[j] = score_key(hv);
+          }
+        } else {
+          // this thread's sketch activations and, when each thread reads at most
+          // 8 of them, its share of the pair's partial recovery sums, requested
+          // together and then waited for one by one (few registers: this
+          // instance is at its register limit)
+          uint64_t raw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) raw[j] = j < cnt ? ld_tagged(src + j) : 0;
+          const bool zpre = EPT <= 16 && r > 0 && a.nw * r <= 8 * NT;
+          uint64_t zraw[8];
+          if (zpre) zsum_issue(a, p, zl, zg, groups, zraw);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float hv = j < cnt ? await_tagged(src + j, raw[j], tag, a.fail, a.spin) : 0.f;
+            if (j < cnt) L.hh[i0 + j] = hv;
+            k4[j] = score_key(hv);
+          }
+          if (zpre) zsum_finish(a, L, p, zl, zg, groups, zraw, tag);
+          else if (r > 0) fetch_zsum(a, L, p, zl, zg, groups, tag);
         }
         phase_stamp(a, 5);
         wave_stamp(a, 15);
@@ -1160,29 +1160,32 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
           for (int j = 0; j < 4; ++j) hzc[j] = L.hh[chn[j]];
         }
         const uint64_t* pc = a.xc + (size_t)p * a.c;
-        const uint64_t* ptr[12];
         uint64_t v[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        if (a.c > 0) {     // (unused entries watch the pair's first candidate, which exists)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            ptr[j] = pc + (j < cnt ? i0 + j : 0);
-            v[j] = ld_tagged(ptr[j]);
-          }
-          if constexpr (LEAN) {
+        if constexpr (LEAN) {
+          if (a.c > 0) {   // (unused entries watch the pair's first candidate, which exists)
             // with the partial recovery sums (published long before; read
             // again here rather than carried from the screen, when some of
             // them were still stale)
+            const uint64_t* ptr[12];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              ptr[j] = pc + (j < cnt ? i0 + j : 0);
+              v[j] = ld_tagged(ptr[j]);
+            }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
               ptr[4 + u] = zptr[u];
               v[4 + u] = ld_tagged(zptr[u]);
             }
             await_all<12>(ptr, v, tag, a.fail, a.spin);
-          } else {
-            const uint64_t* const (&p4)[4] = reinterpret_cast<const uint64_t* const (&)[4]>(ptr);
-            uint64_t (&v4)[4] = reinterpret_cast<uint64_t (&)[4]>(v);
-            await_all<4>(p4, v4, tag, a.fail, a.spin);
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = j < cnt ? ld_tagged(pc + i0 + j) : 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j < cnt)
+              v[j] = ((uint64_t)tag << 32) | __float_as_uint(await_tagged(pc + i0 + j, v[j], tag, a.fail, a.spin));
         }
         if constexpr (LEAN) {
           // this thread's share of the pair's partial recovery sums (group zg)

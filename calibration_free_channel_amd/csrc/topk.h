@@ -105,17 +105,6 @@ __device__ __forceinline__ int topk_range(int n, int* cnt) {
   return i0;
 }
 
-// Writer of the selected indices: index i0 + j goes to out[pos] (taken) or to
-// a per-thread sink (not taken), without a branch.
-struct IndexEmit {
-  int32_t* out;
-  uint32_t* sink;
-  int i0;
-  __device__ __forceinline__ void operator()(bool take, uint32_t pos, int j) const {
-    *(take ? reinterpret_cast<uint32_t*>(out) + pos : sink + threadIdx.x) = (uint32_t)(i0 + j);
-  }
-};
-
 // Selects the k largest of n keys by (key desc, index asc) and writes their
 // indices in ascending order to out_idx[0..k) (LDS). kr[0..cnt) are this
 // thread's keys for indices [i0, i0 + cnt) as given by topk_range (requires
@@ -225,7 +214,95 @@ __device__ __forceinline__ void block_topk_emit(const uint32_t (&kr)[KPT], int i
 template <int NT, int KPT, typename StepHook>
 __device__ __forceinline__ void block_topk(const uint32_t (&kr)[KPT], int i0, int cnt, int n, int k, int32_t* out_idx,
                                            uint32_t* scratch, StepHook step) {
-  block_topk_emit<NT, KPT>(kr, i0, cnt, n, k, IndexEmit{out_idx, scratch + 3 * 256, i0}, scratch, step);
+  static_assert(NT == 256, "four wavefronts");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += NT) out_idx[i] = i;
+    __syncthreads();
+    return;
+  }
+  uint32_t* hist = scratch;
+  uint32_t* dummy = scratch + 3 * 256;     // sink for the stores of keys not taken
+  uint32_t* red = scratch + 4 * 256;       // [0, 8): per-wave min / max; [8, 12): per-wave totals
+  // keys beyond this thread's range become a sentinel above every real key
+  // (real keys are nonnegative floats, below 2^31), which no pass counts
+  uint32_t kk[KPT];
+  uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    kk[j] = j < cnt ? kr[j] : ~0u;
+    kmin = min(kmin, kk[j]);
+    kmax = max(kmax, j < cnt ? kk[j] : 0u);
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { red[2 * wv] = kmin; red[2 * wv + 1] = kmax; }
+  hist[tid] = 0;
+  __syncthreads();
+  {
+    const uint4 a = *reinterpret_cast<const uint4*>(red);
+    const uint4 b = *reinterpret_cast<const uint4*>(red + 4);
+    kmin = min(min(a.x, a.z), min(b.x, b.z));
+    kmax = max(max(a.y, a.w), max(b.y, b.w));
+  }
+  step(0);
+  int s = kmax == kmin ? 0 : max(0, 24 - __builtin_clz(kmax - kmin));
+  if ((kmax >> s) - (kmin >> s) > 255u) ++s;
+  uint32_t base = kmin >> s;       // digit = (key >> s) - base
+  uint32_t lim = (kmax >> s) - base;   // digits in play: 0 .. lim
+  int S = 32;                      // settled: (key >> S) == V (nothing settled yet)
+  uint32_t V = 0, need = (uint32_t)k, m = 0;
+  for (int pass = 0;; ++pass) {
+    uint32_t* h = hist + 256 * (pass % 3);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      // a key is in play iff its digit lies in 0..lim (keys with other settled
+      // digits, and the sentinel, fall outside); keys out of play add 0 to a
+      // bin of their own lane, so they cause no conflicts
+      const uint32_t d = (kk[j] >> s) - base;
+      const bool in = d <= lim;
+      atomicAdd(&h[in ? d : (uint32_t)lane], in ? 1u : 0u);
+    }
+    hist[256 * ((pass + 1) % 3) + tid] = 0;      // the next pass's histogram
+    __syncthreads();
+    step(1 + pass);
+    V = base + boundary_digit(h, need, &m);
+    S = s;
+    if (m == need || S == 0) break;
+    s = max(S - 8, 0);
+    base = V << (S - s);
+    lim = (1u << (S - s)) - 1u;
+  }
+  uint32_t nd = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t v = kk[j] >> S;       // the sentinel is above V: count it, never write it
+    nd += v > V;
+    ne += v == V;
+  }
+  nd -= (uint32_t)(KPT - cnt);
+  const uint32_t packed = (nd << 16) | ne;
+  const uint32_t incl = wave_incl_scan(packed);
+  if (lane == 63) red[8 + wv] = incl;
+  __syncthreads();
+  step(8);
+  const uint4 wt = *reinterpret_cast<const uint4*>(red + 8);
+  const uint32_t basew = (wv > 0 ? wt.x : 0u) + (wv > 1 ? wt.y : 0u) + (wv > 2 ? wt.z : 0u);
+  const uint32_t ex = basew + incl - packed;
+  uint32_t d = ex >> 16, e = ex & 0xFFFFu;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t v = kk[j] >> S;
+    const bool gt = j < cnt && v > V, eq = v == V;
+    const bool take = gt || (eq && e < need);
+    const uint32_t pos = gt ? d + min(e, need) : d + e;
+    *(take ? reinterpret_cast<uint32_t*>(out_idx) + pos : dummy + tid) = (uint32_t)(i0 + j);
+    d += gt;
+    e += eq;
+  }
+  __syncthreads();
+  step(9);
 }
 
 // The threshold keep rule in place of top-k (abstract: selectors typically
