@@ -372,6 +372,29 @@ def test_q18_b1_full_size_general_instance(cfm, q18_layer):
     compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, what="q18_b1 general instance")
 
 
+@pytest.mark.parametrize("kc", [(1, 2), (23, 46), (138, 276), (160, 768), (100, 700), (140, 141)],
+                         ids=lambda kc: f"k{kc[0]}_c{kc[1]}")
+def test_batch1_instance_against_general_and_oracle(cfm, kc):
+    """The batch-1 instance (H 2048, r 64, 8 pairs) against the general instance on the same inputs (the
+    same candidate and kept sets, bit for bit: both select from identical activations with the same tie
+    rule; outputs within float rounding) and against the oracle, over budgets from 1 to 160 kept
+    channels and up to every channel a candidate."""
+    k, c = kc
+    wl = custom_workload(f"lean_k{k}_c{c}", 8, 8, 768, 2048, 1, k, c, 64, 60 + k)
+    log(f"batch-1 instance {wl.name}")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, sorted(set(L.host.ids.reshape(-1).tolist())), E, I, H)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR):
+        got, cand, keep = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), k, c, wl.r)
+    with cfm.forward_path(cfm.FORWARD_PER_PAIR_GENERAL):
+        got_g, cand_g, keep_g = run_select(cfm, L, sk, up_bf16(A), up_bf16(Bt), k, c, wl.r)
+    assert np.array_equal(cand, cand_g) and np.array_equal(keep, keep_g)
+    assert rel_l2(got[0], got_g[0]) <= 1e-2
+    compare_forward(L, A, Bt, got, cand, keep, k, c, what=wl.name)
+
+
 def test_q18_b1_full_size_candidates_exact(cfm, q18_layer):
     """The recovery variant (dropped candidates recovered with their exact activation) at full size."""
     L, wl = q18_layer, q18_layer.wl
