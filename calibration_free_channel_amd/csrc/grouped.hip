@@ -59,6 +59,7 @@ constexpr int kRowBlk = 64;        // union rows per exact work item (one MFMA r
 constexpr int kKc = 8;             // 32-element steps of one exact load batch (two batches in flight; fewer for H < 256)
 constexpr int kColTile = 64;       // output columns per down work item (16 per wavefront)
 constexpr int kRPad = 128;         // recovery rank padded to whole 32-element steps (r <= 128)
+constexpr int kDP = 17;            // LDS pitch (FP32) of a screen wavefront's D tiles: odd, so the per-row reads hit distinct banks
 constexpr int kExactGrid = 512;    // workgroups of the exact stage (wavefronts loop over its work list)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -116,7 +117,7 @@ struct GArgs {
   int32_t* gpl;       // [P] pairs sorted by expert
   int32_t* gue;       // [E] used experts, ascending
   int32_t* gux;       // [E] used index of each expert (-1: not routed)
-  int32_t* gwork;     // [maxwork] screen work items: used expert << 16 | token group
+  int4* gwork;        // [maxwork] screen work items: {expert, first slot in gpl, pairs, 0}
   int32_t* gexw;      // [maxu nrb] exact work items: used expert << 16 | row block
   uint8_t* xd;        // [T][kPlanes][Hp] digit planes of x~
   int32_t* xf0;       // [T] fixed-point exponents
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(GT) void k_g_prep(GArgs a) {
     if (n > 0) {
       a.gue[uix[e]] = e;
       const uint32_t ng = (n + kTokGroup - 1) / kTokGroup;
-      for (uint32_t g = 0; g < ng; ++g) a.gwork[wof[e] + g] = (int)((uix[e] << 16) | g);
+      for (uint32_t g = 0; g < ng; ++g)
+        a.gwork[wof[e] + g] = make_int4(e, (int)(off[e] + kTokGroup * g), (int)min(n - kTokGroup * g, (uint32_t)kTokGroup), 0);
     }
   }
   if (tid == 0) {
@@ -352,18 +354,16 @@ __device__ __forceinline__ uint4 sketch_item2(const GArgs& a, int e, int jw, int
 // wavefronts never wait for each other.
 template <bool REG>
 __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
-  __shared__ __align__(16) float dsw[4][32 * 16];        // per wavefront: D of its two row tiles
+  __shared__ __align__(16) float dsw[4][32 * kDP];       // per wavefront: D of its two row tiles
   __shared__ __align__(16) float hw[4][2 * 16];          // per wavefront: its activations, two tokens
   __shared__ __align__(16) uint16_t btw[4][16 * kRPad];  // per wavefront: Bt rows of its channels
+  const int4 wd = a.gwork[blockIdx.y];                     // (requested with the item count: one round trip)
   if ((uint32_t)blockIdx.y >= a.meta[1]) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, r = a.r;
   const int Hp = max(H, 256);
   const int nsb = (H + 255) / 256;
-  const int item = a.gwork[blockIdx.y];
-  const int e = a.gue[item >> 16];
-  const int g0 = (item & 0xFFFF) * kTokGroup;
-  const int p0 = a.goff[e], n = min(a.goff[e + 1] - p0 - g0, kTokGroup);
+  const int e = wd.x, q0 = wd.y, n = wd.z;                // expert, its pairs gpl[q0 .. q0 + n - 1]
   const int jw = blockIdx.x * kTile + 16 * wv;             // this wavefront's first channel
   const int cwv = min(16, I - jw);
   if (cwv <= 0) return;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
     }
   }
   for (int q2 = 0; q2 < n; q2 += 2) {
-    const int pa = a.gpl[p0 + g0 + q2], pb = a.gpl[p0 + g0 + min(q2 + 1, n - 1)];
+    const int pa = a.gpl[q0 + q2], pb = a.gpl[q0 + min(q2 + 1, n - 1)];
     const int ta = pa / a.K, tb = pb / a.K;
     const uint8_t* xa = a.xd + (size_t)ta * kPlanes * Hp;
     const uint8_t* xb = a.xd + (size_t)tb * kPlanes * Hp;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * 16 + col] = acc[q][v];
+          for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * kDP + col] = acc[q][v];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -448,10 +448,10 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // lane (row, qe, tk): the row's scale times its exact integer dot for token
     // tk (as in the per-pair screen); gate lanes pair with the up lane 16 above
-    const float* d = myD + (16 * qe + row) * 16 + kPlanes * tk;
+    const float* d = myD + (16 * qe + row) * kDP + kPlanes * tk;
     const long long S = (long long)(int)d[0] + ((long long)(int)d[1] << 4) + ((long long)(int)d[2] << 8) +
                         ((long long)(int)d[3] << 12) + ((long long)(int)d[4] << 16) + ((long long)(int)d[5] << 20) -
-                        ((long long)(int)myD[(16 * qe + row) * 16 + 2 * kPlanes] << 23);
+                        ((long long)(int)myD[(16 * qe + row) * kDP + 2 * kPlanes] << 23);
     const float val = (float)((double)sc * ldexp((double)S, kDShift - F0));
     const float other = __int_as_float(lane_xor<16>(__float_as_int(val)));
     const bool ok = row < cwv && q2 + tk < n;
@@ -491,9 +491,9 @@ __device__ __forceinline__ void stage_load(const GArgs& a, int pa, int pb, int H
   const int ta = pa / a.K, tb = pb / a.K;
 #pragma unroll
   for (int u = 0; u < kStgPieces; ++u) {
-    const int i = tid + GT * u, pl = i / ppl, off = i % ppl;
+    const int i = tid + GT * u, pl = min(i / ppl, 2 * kPlanes - 1), off = i % ppl;   // (pieces past the planes: not stored)
     const uint8_t* src = a.xd + (size_t)(pl < kPlanes ? ta : tb) * kPlanes * Hp + (size_t)(pl % kPlanes) * Hp + 16 * off;
-    v[u] = pl < 2 * kPlanes ? ld16c(src) : make_uint4(0, 0, 0, 0);
+    v[u] = ld16c(src);
   }
 }
 __device__ __forceinline__ void stage_store(uint8_t* buf, int Hp, const uint4 (&v)[kStgPieces]) {
@@ -514,56 +514,74 @@ __device__ __forceinline__ void digit_lds2(const uint8_t* buf, int sb, int m, ui
   hi = *reinterpret_cast<const uint4*>(row + 128);
 }
 
+// The item's pair numbers and their tokens' scale exponents are read once,
+// one per lane, and taken from registers on every pass; every request is
+// unconditional (a wavefront past the last channel requests channels 0 .. 15
+// and does not use them), so no register is cleared while a request to it may
+// be in flight and the planes of the next pass stay in flight while the
+// current pass is multiplied and its activations formed.
 __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
-  __shared__ __align__(16) float dsw[4][32 * 16];
+  __shared__ __align__(16) float dsw[4][32 * kDP];
   __shared__ __align__(16) float hw[4][2 * 16];
   __shared__ __align__(16) uint16_t btw[4][16 * kRPad];
   __shared__ __align__(16) uint8_t stg[2][2 * kPlanes * kStgPS];
+  __shared__ int s_pl[kTokGroup], s_f0[kTokGroup];        // the item's pairs and their tokens' scale exponents
+  const int4 wd = a.gwork[blockIdx.y];                     // (requested with the item count: one round trip)
   if ((uint32_t)blockIdx.y >= a.meta[1]) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, r = a.r;
   const int Hp = max(H, 256);
   const int nsb = (H + 255) / 256;                         // <= kSbReg
-  const int item = a.gwork[blockIdx.y];
-  const int e = a.gue[item >> 16];
-  const int g0 = (item & 0xFFFF) * kTokGroup;
-  const int p0 = a.goff[e], n = min(a.goff[e + 1] - p0 - g0, kTokGroup);
+  const int e = wd.x, q0 = wd.y, n = wd.z;                // expert, its pairs gpl[q0 .. q0 + n - 1] (n <= 16)
   const int jw = blockIdx.x * kTile + 16 * wv;
   const int cwv = min(16, I - jw);
   const bool active = cwv > 0;                             // (inactive wavefronts still stage and join)
+  const int jv = active ? jw : 0, cv = active ? cwv : min(16, I);
   const int zslot = jw / 16;
   const int row = lane & 15, qe = (lane >> 4) & 1, tk = lane >> 5;
   float* myD = dsw[wv];
   float* myH = hw[wv];
   uint16_t* myB = btw[wv];
+  const int pl_l = a.gpl[q0 + min(lane, n - 1)];          // lane i: pair i of the item
   uint4 wa[2][kSbReg];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int s = 0; s < kSbReg; ++s)
-      wa[q][s] = active ? sketch_item2(a, e, jw, cwv, q, min(s, nsb - 1)) : make_uint4(0, 0, 0, 0);
-  const float sc = active ? (qe ? a.su : a.sg)[(size_t)e * I + jw + min(row, cwv - 1)] : 0.f;
-  if (active && r > 0) {
-    const uint4* src4 = reinterpret_cast<const uint4*>(a.Bt + ((size_t)e * I + jw) * r);
-    const int npc = cwv * r / 8;
-    uint4 bv[4];
+    for (int s = 0; s < kSbReg; ++s) wa[q][s] = sketch_item2(a, e, jv, cv, q, min(s, nsb - 1));
+  const float sc = (qe ? a.su : a.sg)[(size_t)e * I + jv + min(row, cv - 1)];
+  uint4 bv[4];
+  if (r > 0) {
+    const uint4* src4 = reinterpret_cast<const uint4*>(a.Bt + ((size_t)e * I + jv) * r);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = ld16c(src4 + min(lane + 64 * i, npc - 1));
+    for (int i = 0; i < 4; ++i) bv[i] = ld16c(src4 + min(lane + 64 * i, cv * r / 8 - 1));
+  }
+  uint4 nx[kStgPieces];
+  stage_load(a, __builtin_amdgcn_readlane(pl_l, 0), __builtin_amdgcn_readlane(pl_l, min(1, n - 1)), Hp, nx);
+  const int f0_l = a.xf0[pl_l / a.K];                      // lane i: the scale exponent of pair i's token
+  if (active && r > 0) {
+    // Bt rows jw .. jw + cwv - 1 (contiguous): 2 r pieces of 16 bytes at most
+    const int npc = cwv * r / 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = lane + 64 * i;
       if (idx < 2 * r) reinterpret_cast<uint4*>(myB)[idx] = idx < npc ? bv[i] : make_uint4(0, 0, 0, 0);
     }
   }
-  uint4 nx[kStgPieces];
-  stage_load(a, a.gpl[p0 + g0], a.gpl[p0 + g0 + min(1, n - 1)], Hp, nx);
+  if (threadIdx.x < kTokGroup) {
+    s_pl[threadIdx.x] = pl_l;
+    s_f0[threadIdx.x] = f0_l;
+  }
   stage_store(stg[0], Hp, nx);
   __syncthreads();
   int buf = 0;
   for (int q2 = 0; q2 < n; q2 += 2) {
-    const int pa = a.gpl[p0 + g0 + q2], pb = a.gpl[p0 + g0 + min(q2 + 1, n - 1)];
+    // (from LDS: reading them waits for no request to memory)
+    const int pa = s_pl[q2], pb = s_pl[min(q2 + 1, n - 1)];
+    const int F0a = s_f0[q2], F0b = s_f0[min(q2 + 1, n - 1)];
     const bool more = q2 + 2 < n;
-    if (more) stage_load(a, a.gpl[p0 + g0 + q2 + 2], a.gpl[p0 + g0 + min(q2 + 3, n - 1)], Hp, nx);
+    // the next pass's planes (the last pass: the first pair's again, not stored)
+    const int qn = more ? q2 + 2 : 0;
+    stage_load(a, s_pl[qn], s_pl[min(qn + 1, n - 1)], Hp, nx);
     if (active) {
       const uint8_t* sb8 = stg[buf];
       v4f acc[2];
@@ -593,17 +611,19 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * 16 + col] = acc[q][v];
+            for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * kDP + col] = acc[q][v];
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int F0 = a.xf0[(tk ? pb : pa) / a.K];
-      const float* d = myD + (16 * qe + row) * 16 + kPlanes * tk;
+      // lane (row, qe, tk): the row's scale times its exact integer dot for
+      // token tk (as in the per-pair screen); gate lanes pair with the up lane 16 above
+      const int F0 = tk ? F0b : F0a;
+      const float* d = myD + (16 * qe + row) * kDP + kPlanes * tk;
       const long long S = (long long)(int)d[0] + ((long long)(int)d[1] << 4) + ((long long)(int)d[2] << 8) +
                           ((long long)(int)d[3] << 12) + ((long long)(int)d[4] << 16) + ((long long)(int)d[5] << 20) -
-                          ((long long)(int)myD[(16 * qe + row) * 16 + 2 * kPlanes] << 23);
+                          ((long long)(int)myD[(16 * qe + row) * kDP + 2 * kPlanes] << 23);
       const float val = (float)((double)sc * ldexp((double)S, kDShift - F0));
       const float other = __int_as_float(lane_xor<16>(__float_as_int(val)));
       const bool ok = row < cwv && q2 + tk < n;
@@ -615,6 +635,7 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // this wavefront's share of the recovery sums: sum_j hhat_j Bt[j][:]
       for (int idx = lane; idx < 2 * r; idx += 64) {
         const int t2 = idx / r, l = idx % r;
         if (q2 + t2 < n) {
@@ -776,18 +797,21 @@ __global__ __launch_bounds__(GT, 2) void k_g_exact(GArgs a) {
       for (int qq = 0; qq < 4; ++qq) { ag[qq] = (v4f){0.f, 0.f, 0.f, 0.f}; au[qq] = ag[qq]; }
       ExactRows<KC> A, B;
       uint4 xv[KC];
-      exact_rows_load(A, wgr, wur, 0, nbat);
+      // x is requested before the rows of the same batch: loads complete in
+      // order, so storing x to LDS waits for x only and the rows stay in
+      // flight across the barrier (two batches of rows outstanding)
       exact_x_load(xv, a, tok, ntk, 0, nbat);
+      exact_rows_load(A, wgr, wur, 0, nbat);
       exact_x_store(xv, xs0);
       __syncthreads();
       for (int kb = 0; kb < nbat; kb += 2) {
-        exact_rows_load(B, wgr, wur, kb + 1, nbat);
         exact_x_load(xv, a, tok, ntk, kb + 1, nbat);
+        exact_rows_load(B, wgr, wur, kb + 1, nbat);
         exact_rows_mul(A, xs0, ngrp, ag, au);
         exact_x_store(xv, xs1);
         __syncthreads();
-        exact_rows_load(A, wgr, wur, kb + 2, nbat);
         exact_x_load(xv, a, tok, ntk, kb + 2, nbat);
+        exact_rows_load(A, wgr, wur, kb + 2, nbat);
         if (kb + 1 < nbat) exact_rows_mul(B, xs1, ngrp, ag, au);
         exact_x_store(xv, xs0);
         __syncthreads();
@@ -949,11 +973,18 @@ __global__ __launch_bounds__(GT) void k_g_topk(GArgs a) {
 // of the expert's tokens, 16 tokens at a time. D = tokens x columns, one MFMA
 // column tile per 16 output columns. Wavefront w takes the 32-row chunks
 // w, w + 4, ... of the expert's kept-union rows (every row when dense): it
-// requests the next chunk, transposes the current one into its own LDS
-// (column-major, so that each lane reads eight consecutive contraction indices)
-// and multiplies, with no barrier; the four partial tiles are summed at the
-// end. The recovery term z A^T of column tile w is computed by wavefront w.
-constexpr int kDnP = 40;           // LDS pitch (BF16) of a wavefront's transposed 32-row chunk
+// requests the next chunk, stores the current one row-major in its own LDS
+// (one 16-byte write per lane) and gathers each lane's eight consecutive
+// contraction indices with 16-bit reads, then multiplies, with no barrier; the
+// four partial tiles are summed at the end. The 16-byte column blocks of row
+// rho sit at block ^ 2 ((rho >> 3) & 3), which keeps both the row writes and
+// the column gathers free of bank conflicts. The recovery term z A^T of column
+// tile w is computed by wavefront w.
+constexpr int kDnP = 40;           // LDS pitch (BF16) of a wavefront's [token][row] activation chunk
+
+__device__ __forceinline__ int dn_swz(int rho, int blk) {      // BF16 offset of block blk of chunk row rho
+  return rho * kColTile + 8 * (blk ^ (2 * ((rho >> 3) & 3)));
+}
 
 struct DownChunk {
   uint4 w[4];        // down-row pieces: row (lane >> 3) + 8 i, columns 8 (lane & 7) .. + 7
@@ -980,7 +1011,7 @@ __device__ __forceinline__ void down_load(DownChunk& d, const GArgs& a, int e, i
 __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* rows = reinterpret_cast<uint16_t*>(smem);          // [IP] kept-union rows (selected layer)
-  __shared__ __align__(16) uint16_t wT[4][kColTile * kDnP];   // per wavefront: [column][row]; then its partial tile
+  __shared__ __align__(16) uint16_t wT[4][32 * kColTile];     // per wavefront: [row][column] (swizzled); then its partial tile
   __shared__ __align__(16) uint16_t hA[4][16 * kDnP];         // per wavefront: [token][row]
   __shared__ int pls[16];
   __shared__ int lastt[16];
@@ -1036,29 +1067,19 @@ __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
       }
     }
     if (wv < nch) {
-      DownChunk cur, nxt;
-      down_load(cur, a, e, c0, rows, pls, 32 * wv, min(32, nU - 32 * wv));
-      for (int ch = wv; ch < nch; ch += 4) {
+      // chunk ch of this wavefront into its LDS (rows past the union: zeros), then multiplied;
+      // the next chunk is requested before the current one is multiplied
+      auto mul_chunk = [&](const DownChunk& d, int ch) {
         const int nr = min(32, nU - 32 * ch);
-        const int cn = ch + 4 < nch ? ch + 4 : ch;          // (past the end: a repeat, not used)
-        down_load(nxt, a, e, c0, rows, pls, 32 * cn, min(32, nU - 32 * cn));
-        // transpose the current chunk into this wavefront's LDS (rows past nr: zeros)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rho = (lane >> 3) + 8 * i, cc = lane & 7;
-          const bool ok = rho < nr;
-          const uint32_t w4[4] = {ok ? cur.w[i].x : 0u, ok ? cur.w[i].y : 0u, ok ? cur.w[i].z : 0u,
-                                  ok ? cur.w[i].w : 0u};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            myT[(8 * cc + 2 * h) * kDnP + rho] = (uint16_t)(w4[h] & 0xFFFFu);
-            myT[(8 * cc + 2 * h + 1) * kDnP + rho] = (uint16_t)(w4[h] >> 16);
-          }
+          const int rho = (lane >> 3) + 8 * i;
+          *reinterpret_cast<uint4*>(myT + dn_swz(rho, lane & 7)) = rho < nr ? d.w[i] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int idx = lane + 64 * i, m = idx >> 5, rho = idx & 31;
-          myA[m * kDnP + rho] = (m < nt && rho < nr) ? cur.h[i] : (uint16_t)0;
+          myA[m * kDnP + rho] = (m < nt && rho < nr) ? d.h[i] : (uint16_t)0;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -1066,12 +1087,24 @@ __global__ __launch_bounds__(GT, 2) void k_g_down(GArgs a) {
         const uint4 av = *reinterpret_cast<const uint4*>(myA + m16 * kDnP + 8 * g);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const uint4 bq = *reinterpret_cast<const uint4*>(myT + (16 * ct + m16) * kDnP + 8 * g);
-          acc[ct] = mfma_bf16(av, bq, acc[ct]);
+          // column 16 ct + m16, rows 8 g .. 8 g + 7
+          const uint16_t* col = myT + dn_swz(8 * g, 2 * ct + (m16 >> 3)) + (m16 & 7);
+          uint32_t b2[4];
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            b2[s2] = (uint32_t)col[2 * s2 * kColTile] | ((uint32_t)col[(2 * s2 + 1) * kColTile] << 16);
+          acc[ct] = mfma_bf16(av, make_uint4(b2[0], b2[1], b2[2], b2[3]), acc[ct]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+      DownChunk cur, nxt;
+      down_load(cur, a, e, c0, rows, pls, 32 * wv, min(32, nU - 32 * wv));
+      for (int ch = wv; ch < nch; ch += 4) {
+        const int cn = ch + 4 < nch ? ch + 4 : ch;          // (past the end: a repeat, not used)
+        down_load(nxt, a, e, c0, rows, pls, 32 * cn, min(32, nU - 32 * cn));
+        mul_chunk(cur, ch);
         cur = nxt;
       }
     }
@@ -1278,7 +1311,7 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   g.off_gpl = cv.take(4 * P);
   g.off_gue = cv.take(4 * (size_t)E);
   g.off_gux = cv.take(4 * (size_t)E);
-  g.off_gwork = cv.take(4 * (size_t)g.maxwork);
+  g.off_gwork = cv.take(16 * (size_t)g.maxwork);
   g.off_gexw = cv.take(dense ? 16 : 4 * U * g.nrb);
   g.off_xf0 = cv.take(4 * (size_t)T);
   g.off_xd = cv.take(dense ? 16 : (size_t)T * kPlanes * Hp);
@@ -1340,7 +1373,7 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.gpl = reinterpret_cast<int32_t*>(ws + g.off_gpl);
   a.gue = reinterpret_cast<int32_t*>(ws + g.off_gue);
   a.gux = reinterpret_cast<int32_t*>(ws + g.off_gux);
-  a.gwork = reinterpret_cast<int32_t*>(ws + g.off_gwork);
+  a.gwork = reinterpret_cast<int4*>(ws + g.off_gwork);
   a.gexw = reinterpret_cast<int32_t*>(ws + g.off_gexw);
   a.xd = reinterpret_cast<uint8_t*>(ws + g.off_xd);
   a.xf0 = reinterpret_cast<int32_t*>(ws + g.off_xf0);
