@@ -504,14 +504,21 @@ __device__ __forceinline__ void stage_store(uint8_t* buf, int Hp, const uint4 (&
     if (pl < 2 * kPlanes) *reinterpret_cast<uint4*>(buf + pl * kStgPS + 16 * off) = v[u];
   }
 }
-// B operand halves of super-block sb, half m, from the staged planes (the layout of digit_load2).
-__device__ __forceinline__ void digit_lds2(const uint8_t* buf, int sb, int m, uint4& lo, uint4& hi) {
+// B operand of super-block sb, half m, from the staged planes (the layout of
+// digit_load2): plane 2 kPlanes of each buffer holds FP8 ones, set once, and
+// columns 13..15 read it too (their sums are not used), so the operand needs
+// no masking.
+__device__ __forceinline__ v8i digit_lds_op(const uint8_t* buf, int sb, int m) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, gB = lane >> 4;
-  const int pl = min(col, 2 * kPlanes - 1);
+  const int pl = min(col, 2 * kPlanes);
   const uint8_t* row = buf + pl * kStgPS + sb * 256 + 64 * (gB >> 1) + 32 * m + 16 * (gB & 1);
-  lo = *reinterpret_cast<const uint4*>(row);
-  hi = *reinterpret_cast<const uint4*>(row + 128);
+  const uint4 lo = *reinterpret_cast<const uint4*>(row);
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + 128);
+  v8i b;
+  b[0] = (int)lo.x; b[1] = (int)lo.y; b[2] = (int)lo.z; b[3] = (int)lo.w;
+  b[4] = (int)hi.x; b[5] = (int)hi.y; b[6] = (int)hi.z; b[7] = (int)hi.w;
+  return b;
 }
 
 // The item's pair numbers and their tokens' scale exponents are read once,
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
   __shared__ __align__(16) float dsw[4][32 * kDP];
   __shared__ __align__(16) float hw[4][2 * 16];
   __shared__ __align__(16) uint16_t btw[4][16 * kRPad];
-  __shared__ __align__(16) uint8_t stg[2][2 * kPlanes * kStgPS];
+  __shared__ __align__(16) uint8_t stg[2][(2 * kPlanes + 1) * kStgPS];
   __shared__ int s_pl[kTokGroup], s_f0[kTokGroup];        // the item's pairs and their tokens' scale exponents
   const int4 wd = a.gwork[blockIdx.y];                     // (requested with the item count: one round trip)
   if ((uint32_t)blockIdx.y >= a.meta[1]) return;
@@ -547,7 +554,16 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int s = 0; s < kSbReg; ++s) wa[q][s] = sketch_item2(a, e, jv, cv, q, min(s, nsb - 1));
+    for (int s = 0; s < kSbReg; ++s) {
+      const uint32_t km = 64 * s + 16 * (lane >> 4) < H / 4 ? ~0u : 0u;   // codes past the row end (H < 256)
+      const uint4 w = sketch_item2(a, e, jv, cv, q, min(s, nsb - 1));
+      wa[q][s] = make_uint4(w.x & km, w.y & km, w.z & km, w.w & km);
+    }
+  // the ones planes of both buffers (FP8 E4M3 1.0)
+  for (int i = threadIdx.x; i < Hp / 16; i += GT) {
+    *reinterpret_cast<uint4*>(stg[0] + 2 * kPlanes * kStgPS + 16 * i) = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);
+    *reinterpret_cast<uint4*>(stg[1] + 2 * kPlanes * kStgPS + 16 * i) = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);
+  }
   const float sc = (qe ? a.su : a.sg)[(size_t)e * I + jv + min(row, cv - 1)];
   uint4 bv[4];
   if (r > 0) {
@@ -590,18 +606,14 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
 #pragma unroll
       for (int s = 0; s < kSbReg; ++s) {
         if (s < nsb) {
-          uint4 lo0, hi0, lo1, hi1;
-          digit_lds2(sb8, s, 0, lo0, hi0);
-          digit_lds2(sb8, s, 1, lo1, hi1);
-          const uint32_t km = 64 * s + 16 * (lane >> 4) < H / 4 ? ~0u : 0u;   // codes past the row end (H < 256)
-          const v8i d0 = digit_operand2(lo0, hi0);
-          const v8i d1 = digit_operand2(lo1, hi1);
+          const v8i d0 = digit_lds_op(sb8, s, 0);
+          const v8i d1 = digit_lds_op(sb8, s, 1);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                trit_operand(wa[q][s].x & km, wa[q][s].y & km), d0, acc[q], 4, 0, 0, 0, 0, 0);
-            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                trit_operand(wa[q][s].z & km, wa[q][s].w & km), d1, acc[q], 4, 0, 0, 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(wa[q][s].x, wa[q][s].y), d0, acc[q],
+                                                                      4, 0, 0, 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(trit_operand(wa[q][s].z, wa[q][s].w), d1, acc[q],
+                                                                      4, 0, 0, 0, 0, 0);
           }
         }
       }
