@@ -486,21 +486,23 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
 constexpr int kStgPS = 2048 + 16;                                  // plane pitch in LDS (bytes)
 constexpr int kStgPieces = 2 * kPlanes * 2048 / 16 / GT;           // 16-byte pieces per thread and pair
 
-__device__ __forceinline__ void stage_load(const GArgs& a, int pa, int pb, int Hp, uint4 (&v)[kStgPieces]) {
-  const int tid = threadIdx.x, ppl = Hp / 16;
-  const int ta = pa / a.K, tb = pb / a.K;
+// (H is a power of two: a plane of Hp bytes is 2^lppl pieces of 16 bytes)
+__device__ __forceinline__ void stage_load(const GArgs& a, int ta, int tb, int Hp, int lppl, uint4 (&v)[kStgPieces]) {
+  const int tid = threadIdx.x;
+  const uint8_t* xa = a.xd + (size_t)ta * kPlanes * Hp;
+  const uint8_t* xb = a.xd + (size_t)tb * kPlanes * Hp;
 #pragma unroll
   for (int u = 0; u < kStgPieces; ++u) {
-    const int i = tid + GT * u, pl = min(i / ppl, 2 * kPlanes - 1), off = i % ppl;   // (pieces past the planes: not stored)
-    const uint8_t* src = a.xd + (size_t)(pl < kPlanes ? ta : tb) * kPlanes * Hp + (size_t)(pl % kPlanes) * Hp + 16 * off;
+    const int i = tid + GT * u, pl = min(i >> lppl, 2 * kPlanes - 1), off = i & ((1 << lppl) - 1);   // (pieces past the planes: not stored)
+    const uint8_t* src = (pl < kPlanes ? xa : xb) + (size_t)(pl % kPlanes) * Hp + 16 * off;
     v[u] = ld16c(src);
   }
 }
-__device__ __forceinline__ void stage_store(uint8_t* buf, int Hp, const uint4 (&v)[kStgPieces]) {
-  const int tid = threadIdx.x, ppl = Hp / 16;
+__device__ __forceinline__ void stage_store(uint8_t* buf, int lppl, const uint4 (&v)[kStgPieces]) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kStgPieces; ++u) {
-    const int i = tid + GT * u, pl = i / ppl, off = i % ppl;
+    const int i = tid + GT * u, pl = i >> lppl, off = i & ((1 << lppl) - 1);
     if (pl < 2 * kPlanes) *reinterpret_cast<uint4*>(buf + pl * kStgPS + 16 * off) = v[u];
   }
 }
@@ -527,18 +529,19 @@ __device__ __forceinline__ v8i digit_lds_op(const uint8_t* buf, int sb, int m) {
 // and does not use them), so no register is cleared while a request to it may
 // be in flight and the planes of the next pass stay in flight while the
 // current pass is multiplied and its activations formed.
-__global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
+__global__ __launch_bounds__(GT, 3) void k_g_screen_lds(GArgs a) {
   __shared__ __align__(16) float dsw[4][32 * kDP];
   __shared__ __align__(16) float hw[4][2 * 16];
   __shared__ __align__(16) uint16_t btw[4][16 * kRPad];
-  __shared__ __align__(16) uint8_t stg[2][(2 * kPlanes + 1) * kStgPS];
-  __shared__ int s_pl[kTokGroup], s_f0[kTokGroup];        // the item's pairs and their tokens' scale exponents
+  __shared__ __align__(16) uint8_t stg[(2 * kPlanes + 1) * kStgPS];
+  __shared__ int s_pl[kTokGroup], s_tk[kTokGroup], s_f0[kTokGroup];   // the item's pairs, their tokens, scale exponents
   const int4 wd = a.gwork[blockIdx.y];                     // (requested with the item count: one round trip)
   if ((uint32_t)blockIdx.y >= a.meta[1]) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, r = a.r;
   const int Hp = max(H, 256);
   const int nsb = (H + 255) / 256;                         // <= kSbReg
+  const int lppl = max(a.log2H, 8) - 4;                    // log2 of the 16-byte pieces of a plane
   const int e = wd.x, q0 = wd.y, n = wd.z;                // expert, its pairs gpl[q0 .. q0 + n - 1] (n <= 16)
   const int jw = blockIdx.x * kTile + 16 * wv;
   const int cwv = min(16, I - jw);
@@ -550,6 +553,7 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
   float* myH = hw[wv];
   uint16_t* myB = btw[wv];
   const int pl_l = a.gpl[q0 + min(lane, n - 1)];          // lane i: pair i of the item
+  const int tk_l = pl_l / a.K;                             // and its token
   uint4 wa[2][kSbReg];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
@@ -559,11 +563,9 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
       const uint4 w = sketch_item2(a, e, jv, cv, q, min(s, nsb - 1));
       wa[q][s] = make_uint4(w.x & km, w.y & km, w.z & km, w.w & km);
     }
-  // the ones planes of both buffers (FP8 E4M3 1.0)
-  for (int i = threadIdx.x; i < Hp / 16; i += GT) {
-    *reinterpret_cast<uint4*>(stg[0] + 2 * kPlanes * kStgPS + 16 * i) = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);
-    *reinterpret_cast<uint4*>(stg[1] + 2 * kPlanes * kStgPS + 16 * i) = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);
-  }
+  // the ones plane (FP8 E4M3 1.0)
+  for (int i = threadIdx.x; i < Hp / 16; i += GT)
+    *reinterpret_cast<uint4*>(stg + 2 * kPlanes * kStgPS + 16 * i) = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);
   const float sc = (qe ? a.su : a.sg)[(size_t)e * I + jv + min(row, cv - 1)];
   uint4 bv[4];
   if (r > 0) {
@@ -572,8 +574,8 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
     for (int i = 0; i < 4; ++i) bv[i] = ld16c(src4 + min(lane + 64 * i, cv * r / 8 - 1));
   }
   uint4 nx[kStgPieces];
-  stage_load(a, __builtin_amdgcn_readlane(pl_l, 0), __builtin_amdgcn_readlane(pl_l, min(1, n - 1)), Hp, nx);
-  const int f0_l = a.xf0[pl_l / a.K];                      // lane i: the scale exponent of pair i's token
+  stage_load(a, __builtin_amdgcn_readlane(tk_l, 0), __builtin_amdgcn_readlane(tk_l, min(1, n - 1)), Hp, lppl, nx);
+  const int f0_l = a.xf0[tk_l];                            // lane i: the scale exponent of pair i's token
   if (active && r > 0) {
     // Bt rows jw .. jw + cwv - 1 (contiguous): 2 r pieces of 16 bytes at most
     const int npc = cwv * r / 8;
@@ -585,21 +587,29 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
   }
   if (threadIdx.x < kTokGroup) {
     s_pl[threadIdx.x] = pl_l;
+    s_tk[threadIdx.x] = tk_l;
     s_f0[threadIdx.x] = f0_l;
   }
-  stage_store(stg[0], Hp, nx);
+  stage_store(stg, lppl, nx);
   __syncthreads();
-  int buf = 0;
   for (int q2 = 0; q2 < n; q2 += 2) {
     // (from LDS: reading them waits for no request to memory)
-    const int pa = s_pl[q2], pb = s_pl[min(q2 + 1, n - 1)];
-    const int F0a = s_f0[q2], F0b = s_f0[min(q2 + 1, n - 1)];
+    const int pa = __builtin_amdgcn_readfirstlane(s_pl[q2]), pb = __builtin_amdgcn_readfirstlane(s_pl[min(q2 + 1, n - 1)]);
+    const int F0a = __builtin_amdgcn_readfirstlane(s_f0[q2]), F0b = __builtin_amdgcn_readfirstlane(s_f0[min(q2 + 1, n - 1)]);
     const bool more = q2 + 2 < n;
     // the next pass's planes (the last pass: the first pair's again, not stored)
     const int qn = more ? q2 + 2 : 0;
-    stage_load(a, s_pl[qn], s_pl[min(qn + 1, n - 1)], Hp, nx);
+    stage_load(a, __builtin_amdgcn_readfirstlane(s_tk[qn]), __builtin_amdgcn_readfirstlane(s_tk[min(qn + 1, n - 1)]), Hp,
+               lppl, nx);
     if (active) {
-      const uint8_t* sb8 = stg[buf];
+      // (the sketch words are opaque to the compiler here: it converts them on
+      // every pass instead of keeping converted copies live across the loop)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int s = 0; s < kSbReg; ++s)
+          asm volatile("" : "+v"(wa[q][s].x), "+v"(wa[q][s].y), "+v"(wa[q][s].z), "+v"(wa[q][s].w));
+      const uint8_t* sb8 = stg;
       v4f acc[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[q] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -626,6 +636,14 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
             for (int v = 0; v < 4; ++v) myD[(16 * q + 4 * (lane >> 4) + v) * kDP + col] = acc[q][v];
         }
       }
+    }
+    // one plane buffer: the next pass's planes go in once every wavefront has
+    // multiplied (the activations below do not read the planes)
+    if (more) {
+      __syncthreads();
+      stage_store(stg, lppl, nx);
+    }
+    if (active) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -648,22 +666,22 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen_lds(GArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // this wavefront's share of the recovery sums: sum_j hhat_j Bt[j][:]
-      for (int idx = lane; idx < 2 * r; idx += 64) {
-        const int t2 = idx / r, l = idx % r;
-        if (q2 + t2 < n) {
-          float z = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 16; ++jj) z += myH[t2 * 16 + jj] * bf16_to_f32(myB[jj * r + l]);
-          a.zp[((size_t)(t2 ? pb : pa) * a.nz + zslot) * r + l] = z;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        if (q2 + t2 < n) {
+          for (int l = lane; l < r; l += 64) {
+            float z = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) z += myH[t2 * 16 + jj] * bf16_to_f32(myB[jj * r + l]);
+            a.zp[((size_t)(t2 ? pb : pa) * a.nz + zslot) * r + l] = z;
+          }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (more) stage_store(stg[buf ^ 1], Hp, nx);
     __syncthreads();
-    buf ^= 1;
   }
 }
 
