@@ -482,7 +482,8 @@ __global__ __launch_bounds__(GT, 2) void k_g_screen(GArgs a) {
 // The same screen for H <= 2048 with each token pair's digit planes staged
 // in LDS once per workgroup (the four wavefronts share them; reading them from
 // L2 in every wavefront made the screen L2-bound): the next pair's planes are
-// requested while the current pair is multiplied, one barrier per pair.
+// requested before the current pair is multiplied and stored after a barrier
+// that follows the multiply (one plane buffer, two barriers per pair).
 constexpr int kStgPS = 2048 + 16;                                  // plane pitch in LDS (bytes)
 constexpr int kStgPieces = 2 * kPlanes * 2048 / 16 / GT;           // 16-byte pieces per thread and pair
 
@@ -507,7 +508,7 @@ __device__ __forceinline__ void stage_store(uint8_t* buf, int lppl, const uint4 
   }
 }
 // B operand of super-block sb, half m, from the staged planes (the layout of
-// digit_load2): plane 2 kPlanes of each buffer holds FP8 ones, set once, and
+// digit_load2): plane 2 kPlanes of the buffer holds FP8 ones, set once, and
 // columns 13..15 read it too (their sums are not used), so the operand needs
 // no masking.
 __device__ __forceinline__ v8i digit_lds_op(const uint8_t* buf, int sb, int m) {
@@ -523,12 +524,12 @@ __device__ __forceinline__ v8i digit_lds_op(const uint8_t* buf, int sb, int m) {
   return b;
 }
 
-// The item's pair numbers and their tokens' scale exponents are read once,
-// one per lane, and taken from registers on every pass; every request is
-// unconditional (a wavefront past the last channel requests channels 0 .. 15
-// and does not use them), so no register is cleared while a request to it may
-// be in flight and the planes of the next pass stay in flight while the
-// current pass is multiplied and its activations formed.
+// The item's pair numbers, tokens and scale exponents are read once, one per
+// lane, and kept in LDS for the passes; every request is unconditional (a
+// wavefront past the last channel requests channels 0 .. 15 and does not use
+// them), so no register is cleared while a request to it may be in flight and
+// the planes of the next pass stay in flight while the current pass is
+// multiplied. Three workgroups fit a CU (160 registers, 52 KB of LDS).
 __global__ __launch_bounds__(GT, 3) void k_g_screen_lds(GArgs a) {
   __shared__ __align__(16) float dsw[4][32 * kDP];
   __shared__ __align__(16) float hw[4][2 * 16];
