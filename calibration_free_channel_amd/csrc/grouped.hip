@@ -194,25 +194,30 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t total, int* 
 
 // Union of the channel bitmaps bm[p][IW] of expert e's pairs: its channels in
 // ascending order into rows_out (global), count returned. U, pc: IW words of
-// LDS each. Called by the whole workgroup.
+// LDS each; U holds the calling pair's own bitmap on entry (a subset of the
+// union). The (pair, word) items are spread over the whole workgroup with four
+// requests in flight per thread, so an expert with many pairs costs a round
+// trip or two, not one per eight pairs. Called by the whole workgroup.
 __device__ __forceinline__ uint32_t expert_union(const GArgs& a, const uint32_t* bm, int e, uint16_t* rows_out,
                                                  uint32_t* U, uint32_t* pc, uint32_t* wtot) {
   const int p0 = a.goff[e], n = a.goff[e + 1] - p0, IW = a.IW;
-  for (int w = threadIdx.x; w < IW; w += GT) {
-    uint32_t u = 0;
-    for (int s0 = 0; s0 < n; s0 += 8) {
-      int pp[8];
-      uint32_t x[8];
+  const int items = n * IW;
+  for (int i0 = threadIdx.x; i0 < items; i0 += 4 * GT) {
+    uint32_t x[4];
+    int wd[4];
 #pragma unroll
-      for (int v = 0; v < 8; ++v) pp[v] = a.gpl[p0 + min(s0 + v, n - 1)];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) x[v] = ld_u(bm + (size_t)pp[v] * IW + w);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) u |= s0 + v < n ? x[v] : 0u;
+    for (int v = 0; v < 4; ++v) {
+      const int it = min(i0 + v * GT, items - 1);
+      const int q = it / IW;
+      wd[v] = it - q * IW;
+      x[v] = ld_u(bm + (size_t)a.gpl[p0 + q] * IW + wd[v]);
     }
-    U[w] = u;
-    pc[w] = __builtin_popcount(u);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (i0 + v * GT < items) atomicOr(&U[wd[v]], x[v]);
   }
+  __syncthreads();
+  for (int w = threadIdx.x; w < IW; w += GT) pc[w] = __builtin_popcount(U[w]);
   __syncthreads();
   const uint32_t nU = block_exscan(pc, IW, wtot);
   for (int w = threadIdx.x; w < IW; w += GT) {
