@@ -65,6 +65,8 @@ def parse():
                          "cache flush, median / p10 / p90 of the selected and the dense layer")
     ap.add_argument("--general", action="store_true",
                     help="with --phase-trace: the general per-pair instance instead of the batch-1 one")
+    ap.add_argument("--trace-batch", type=int, default=1,
+                    help="with --phase-trace: tokens per call (8 and 16 run the general per-pair instance)")
     ap.add_argument("--phase-trace", action="store_true",
                     help="instead of the default line: per-phase timeline of the batch-1 selected and dense "
                          "kernels from in-kernel clock stamps (needs the trace build, CFM_PHASE_TRACE=1)")
@@ -304,8 +306,10 @@ SELECT_PHASES = {
     3: "screen done", 4: "recovery partial sums published", 5: "sketch activations + partial sums in",
     6: "top-c done", 7: "exact rows done (h published)", 8: "candidate-row prefetch issued (general instance)",
     9: "exact activations in", 10: "top-k done",
-    11: "kept down and Bt row loads issued (batch-1 instance) / candidate rows landed (general)",
-    12: "kept Bt rows in, z formed", 13: "pair output slice stored", 14: "combine done",
+    11: "kept down and Bt row loads issued (batch-1 instance) / candidate rows landed (general, one token) / "
+        "z formed (general, several tokens)",
+    12: "kept Bt rows in, z formed / A z formed (general, several tokens)", 13: "pair output slice stored",
+    14: "combine done",
     15: "wave 0 sketch activations in", 16: "wave 1 sketch activations in", 17: "wave 2 sketch activations in",
     18: "wave 3 sketch activations in", 19: "wave 0 exact activations in", 20: "wave 1 exact activations in",
     21: "wave 2 exact activations in", 22: "wave 3 exact activations in", 23: "top-c range known",
@@ -315,8 +319,9 @@ DENSE_PHASES = {0: "start", 20: "exact rows done", 21: "activations in", 22: "do
 
 
 def phase_trace(torch, cfm, args):
-    """Per-phase timeline of the batch-1 kernels from in-kernel clock stamps (100 MHz device clock),
-    taken from the last launch of a ring of back-to-back launches; medians over repetitions."""
+    """Per-phase timeline of the per-pair kernels from in-kernel clock stamps (100 MHz device clock),
+    taken from the last launch of a ring of back-to-back launches; medians over repetitions. Batch 1 by
+    default; --trace-batch 8 or 16 traces the general instance at that batch (one pair slot per workgroup)."""
     import numpy as np
     E, K, I, H = 128, 8, 768, 2048
     k, c, r = 138, 276, 64
@@ -330,10 +335,13 @@ def phase_trace(torch, cfm, args):
         layers.append((wg, wu, wd, signs, sk, A, Bt))
     del lr_ws
     ring, reps = 16, 60
-    x, ids, w = make_tokens(torch, args.seed + 1, ring, 1, E, K, H)
-    ws_s = cfm.new_workspace(cfm.select_workspace(1, K, E, I, H, k, c, r), "cuda")
-    ws_d = cfm.new_workspace(cfm.dense_workspace(1, K, E, I, H), "cuda")
-    out = torch.empty((ring, 1, H), dtype=torch.bfloat16, device="cuda")
+    T = args.trace_batch
+    if T not in (1, 8, 16):
+        raise SystemExit("--trace-batch: 1, 8 or 16 (one pair slot per workgroup of the 256-workgroup grid)")
+    x, ids, w = make_tokens(torch, args.seed + 1, ring, T, E, K, H)
+    ws_s = cfm.new_workspace(cfm.select_workspace(T, K, E, I, H, k, c, r), "cuda")
+    ws_d = cfm.new_workspace(cfm.dense_workspace(T, K, E, I, H), "cuda")
+    out = torch.empty((ring, T, H), dtype=torch.bfloat16, device="cuda")
     buf = torch.zeros(256 * 32, dtype=torch.int64, device="cuda")
     cfm.phase_trace(buf)
 
@@ -386,7 +394,8 @@ def phase_trace(torch, cfm, args):
         log(f"{name}: XCD start offsets (us) {starts}; passes per select (count of workgroups by passes) {passes}")
     cfm.phase_trace(None)
     cfm.set_forward_path(prev_path)
-    print(json.dumps({"phase_trace": res, "workload": "q18_b1", "instance": "general" if args.general else "batch-1",
+    print(json.dumps({"phase_trace": res, "workload": f"q18_b{T}",
+                      "instance": "general" if (args.general or T > 1) else "batch-1",
                       "ring": ring, "reps": reps}), flush=True)
 
 

@@ -739,6 +739,155 @@ __device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p,
   combine_cols(a, t, w, ck0, nck, s_flag, tag, lw);
 }
 
+// Phase C of a workgroup without the candidate-row prefetch (several tokens
+// per launch), with every request that does not wait on another issued before
+// the first wait: the Bt pieces of the recovery coefficients' rows, this
+// workgroup's A pieces and the first batch of its kept down-row pieces; later
+// down batches are requested one batch ahead (two register buffers). The
+// arithmetic and its order are those of the step-by-step form (z, then
+// cols_block): z over the rows in index order per thread, then the groups;
+// each column's down sum over the thread's rows in order, then the threads.
+// Requires nck <= NT and r = 0 or (r % 8 == 0, 64 % (r / 8) == 0). nz rows
+// enter z (the kept rows, or every candidate with the recovery variant).
+template <bool RECX>
+__device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L, int p, int t, int e, int w, int kk,
+                                               int* s_flag, uint32_t tag, const float* lw) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H, r = a.r;
+  const int nck = col_chunks(a), ck0 = w * nck;
+  const bool cols = ck0 < H / 8;
+  // ---- requests
+  const int nz = RECX ? a.c : kk;
+  const int cpr = r > 0 ? r / 8 : 1, ngz = NT / cpr;
+  const int zc = tid % cpr, zgi = tid / cpr;
+  constexpr int ZB = 8, AB = 8, DB = 8;
+  uint4 bz[ZB];
+  float hz[ZB];
+  auto z_issue = [&](int i0) {
+#pragma unroll
+    for (int u = 0; u < ZB; ++u) {
+      const int i = i0 + ngz * u;
+      const int ic = max(min(i, nz - 1), 0);
+      const int j = nz > 0 ? (RECX ? L.candp[ic] : L.keep[ic]) : 0;
+      hz[u] = i < nz ? (RECX ? L.hcl[ic] : L.hh[j]) : 0.f;
+      bz[u] = ld16c(a.Bt + ((size_t)e * a.I + j) * r + 8 * zc);
+    }
+  };
+  const int nitem = 8 * nck * cpr;                  // A pieces of this workgroup's columns
+  const uint16_t* abase = a.A + ((size_t)e * H + 8 * ck0) * r;
+  uint4 av[AB];
+  auto a_issue = [&](int f0) {
+#pragma unroll
+    for (int u = 0; u < AB; ++u) av[u] = ld16(abase + 8 * (size_t)min(f0 + tid + NT * u, nitem - 1));
+  };
+  const int cc = tid % nck, g = tid / nck, ngd = NT / nck;
+  const int n = kk;
+  const uint16_t* dbase = a.wd + (size_t)e * a.I * H + 8 * (ck0 + cc);
+  uint4 dA[DB], dB[DB];
+  float hA[DB], hB[DB];
+  auto d_issue = [&](int m0, uint4 (&wq)[DB], float (&hq)[DB]) {
+#pragma unroll
+    for (int u = 0; u < DB; ++u) {
+      const int mm = m0 + ngd * u, m = max(min(mm, n - 1), 0);
+      wq[u] = ld16(dbase + (size_t)(n > 0 ? L.keep[m] : 0) * H);
+      hq[u] = mm < n ? L.hk[m] : 0.f;
+    }
+  };
+  if (cols && r > 0) z_issue(zgi);
+  // ---- recovery coefficients z = zsum - sum_j coef_j Bt[j] (coef: sketch
+  //      activation of a kept row, or the variant's per-candidate term)
+  float* rec = L.red;                               // [8 nck] recovery term (after z is formed)
+  if (cols && r > 0) {
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    for (int i0 = zgi;;) {
+#pragma unroll
+      for (int u = 0; u < ZB; ++u) fma8(acc, hz[u], bz[u]);
+      i0 += ngz * ZB;
+      if (i0 >= nz) break;
+      z_issue(i0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) L.red[zgi * r + 8 * zc + u] = acc[u];    // ngz r = 8 NT
+  }
+  // the A pieces and the first down batch are in flight during the reduction
+  if (cols && r > 0) a_issue(0);
+  if (cols && n > 0) d_issue(g, dA, hA);
+  __syncthreads();
+  if (cols && r > 0) {
+    for (int l = tid; l < r; l += NT) {
+      float s = 0.f;
+      for (int gg = 0; gg < ngz; ++gg) s += L.red[gg * r + l];
+      L.zv[l] = L.zsum[l] - s;
+    }
+  }
+  __syncthreads();
+  phase_stamp(a, 11);
+  if (!cols) return;
+  // ---- A z over this workgroup's columns
+  if (r > 0) {
+    // every piece of this thread is rank chunk tid % cpr (cpr divides NT)
+    float zq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zq[i] = L.zv[8 * zc + i];
+    for (int f0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < AB; ++u) {
+        const int f = f0 + tid + NT * u;
+        float d = f < nitem ? dot8_f(av[u], zq) : 0.f;
+        d = sum_over_low_lanes(d, cpr);
+        if (f < nitem && f % cpr == 0) rec[f / cpr] = d;
+      }
+      f0 += NT * AB;
+      if (f0 >= nitem) break;
+      a_issue(f0);
+    }
+  }
+  phase_stamp(a, 12);
+  // ---- down projection over the kept rows: two batches in flight
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  if (n > 0) {
+    const int trips = (n + ngd * DB - 1) / (ngd * DB);        // the same for every thread
+    for (int it = 0;;) {
+      d_issue(g + ngd * DB * (it + 1), dB, hB);                // (past the end: row n - 1, weight 0, not used)
+#pragma unroll
+      for (int u = 0; u < DB; ++u) fma8(acc, hA[u], dA[u]);
+      if (++it >= trips) break;
+      d_issue(g + ngd * DB * (it + 1), dA, hA);
+#pragma unroll
+      for (int u = 0; u < DB; ++u) fma8(acc, hB[u], dB[u]);
+      if (++it >= trips) break;
+    }
+  }
+  float* part = L.part;
+  int slot;
+  if (nck < 64) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = sum_over_high_lanes(acc[u], nck);
+    slot = lane < nck ? wv * nck + lane : -1;
+  } else {
+    slot = tid;
+  }
+  if (slot >= 0) {
+    reinterpret_cast<float4*>(part)[2 * slot] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(part)[2 * slot + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  __syncthreads();
+  const int nsrc = nck < 64 ? NT / 64 : ngd;
+  for (int col = tid; col < 8 * nck; col += NT) {
+    const int c8 = col / 8, j = col % 8;
+    float y = r > 0 ? rec[col] : 0.f;
+    for (int q = 0; q < nsrc; ++q) y += part[(q * nck + c8) * 8 + j];
+    st_f(a.ypart + (size_t)p * H + 8 * ck0 + col, y);
+  }
+  __syncthreads();
+  phase_stamp(a, 13);
+  combine_cols(a, t, w, ck0, nck, s_flag, tag, lw);
+  phase_stamp(a, 14);
+}
+
 // ------------------------------------------------------------------ exchange reads
 
 // Partial recovery sums of all nw workgroups of pair p: thread (zl, zg) adds
@@ -1459,6 +1608,13 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
         combine_cols(a, t, w, ck0, nck, &s_flag, tag, ENV ? L.rw : nullptr);
         phase_stamp(a, 14);
       }
+      continue;
+    }
+    // (hidden widths up to 2048 and not in the envelope instances: its
+    // registers would spill in the others)
+    constexpr bool kStream = !ENV && EPT <= 8;
+    if (kStream && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0)) && col_chunks(a) <= NT) {
+      if constexpr (kStream) phase_c_stream<RECX>(a, L, p, t, e, w, kk, &s_flag, tag, nullptr);
       continue;
     }
     if (r > 0) {
