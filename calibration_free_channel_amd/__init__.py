@@ -5,7 +5,8 @@ this package is its ctypes binding. Importing it without the built library
 raises ImportError: there is no CPU fallback.
 """
 from ._lib import (  # noqa: F401
-    FORWARD_AUTO, FORWARD_GROUPED, FORWARD_PER_PAIR, FORWARD_PER_PAIR_GENERAL, RECOVER_CANDIDATES_EXACT, RECOVER_SKETCH, CfmError,
+    FORWARD_AUTO, FORWARD_GROUPED, FORWARD_PER_PAIR, FORWARD_PER_PAIR_GENERAL, FORWARD_PER_PAIR_SINGLE,
+    RECOVER_CANDIDATES_EXACT, RECOVER_SKETCH, CfmError,
     EXPORTED, STATS_BYTES, decode_stats,
     dense_workspace, forward_path, last_error, lowrank_build, lowrank_workspace, moe_dense_forward,
     moe_layer_dense_forward, moe_layer_forward,

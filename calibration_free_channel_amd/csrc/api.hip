@@ -107,7 +107,8 @@ int check_budget(int I, int H, int k, int c, int r) {
 }
 
 // Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped, 3 per-pair
-// without the batch-1 instance (process-wide).
+// without the batch-1 instance, 4 per-pair with the screen inside the single
+// launch (process-wide).
 std::atomic<int> g_path{0};
 // Automatic choice: the grouped pass from these batch sizes on (measured on the
 // Qwen3-30B-A3B-shaped layer: below them the single-launch per-pair kernels
@@ -205,6 +206,7 @@ int select_entry(const cfm_bf16* x, const int32_t* topk_ids, const float* topk_w
   const float tpos = tau == 0.f ? 0.f : tau;             // -0 as +0: every score reaches it
   std::memcpy(&a.tkey, &tpos, sizeof a.tkey);             // |h| >= tau iff bits(|h|) >= bits(tau)
   a.keep_count = thr ? keep_count : nullptr;
+  a.ws_bytes = ws_bytes;
   if (grouped)
     return launch_grouped_forward(a, group_plan(T, K, E, I, H, k, c, r, false, plan.bytes),
                                   static_cast<hipStream_t>(stream));
@@ -219,7 +221,7 @@ const char* cfm_last_error(void) { return g_last_error.c_str(); }
 const char* cfm_version(void) { return "cfm 0.1.0 gfx950"; }
 
 int cfm_set_forward_path(int path) {
-  if (path < 0 || path > 3) return set_error(CFM_EINVAL, "path must be 0, 1, 2 or 3");
+  if (path < 0 || path > 4) return set_error(CFM_EINVAL, "path must be 0, 1, 2, 3 or 4");
   return g_path.exchange(path);
 }
 

@@ -83,6 +83,9 @@ struct SelectArgs {
   int thr;
   uint32_t tkey;
   int32_t* keep_count;
+  // bytes of ws (0: unknown); the per-pair pass puts the expert-grouped screen
+  // in front of its kernel only when the workspace holds that pass's regions
+  size_t ws_bytes;
 };
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 // Phase-timestamp buffer for the single-launch kernels (trace build only).
@@ -108,5 +111,10 @@ struct GroupPlan {
 bool grouped_supported(int T, int K, int E, int I, int H, int r, bool dense);
 GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, bool dense, size_t base);
 int launch_grouped_forward(const SelectArgs& a, const GroupPlan& p, hipStream_t stream);
+// The grouped pass's rotation, grouping and screen stages alone (sketch
+// activations and partial recovery sums into the plan's hs and zp regions),
+// for the per-pair pass with several tokens; the caller prepares the workspace.
+bool grouped_screen_supported(int T, int K, int E, int I, int H, int r);
+int launch_grouped_screen(const SelectArgs& a, const GroupPlan& p, hipStream_t stream);
 
 }  // namespace cfm

@@ -16,6 +16,10 @@ const void* fused_kernel_e8(bool select, bool recx, bool env);
 const void* fused_kernel_e16(bool select, bool recx, bool env);
 const void* fused_kernel_e32(bool select, bool recx, bool env);
 const void* fused_kernel_e8_lean();
+const void* fused_kernel_e0_ps(bool recx);
+const void* fused_kernel_e2_ps(bool recx);
+const void* fused_kernel_e4_ps(bool recx);
+const void* fused_kernel_e8_ps(bool recx);
 
 namespace {
 
@@ -28,7 +32,7 @@ namespace {
 // -1: the kept rows as in bytes_down).
 __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, int c, int r, int T,
                         int K, int select, int exact_step, int sketch_read, const int32_t* kcnt,
-                        int down_req, cfm_stats* st) {
+                        int down_req, int screen_per_expert, cfm_stats* st) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   unsigned used = 0;
   for (int pp = 0; pp < P; ++pp) {
@@ -63,9 +67,13 @@ __global__ void k_stats(const int32_t* ids, int P, int E, int I, int H, int k, i
   }
   s.pad = 0;
   if (select) {
-    const uint64_t per_pair = (sketch_read ? 2ull * I * (H / 4) + 8ull * I : 0) +
-                              (exact_step ? 4ull * H * c : 0) + (r > 0 ? 2ull * H * r + 2ull * I * r : 0);
-    s.bytes_requested = Pu * per_pair + (down_req >= 0 ? Pu * 2ull * H * down_req : s.bytes_down) + s.bytes_io;
+    // the screen's reads (sketch rows and scales, every Bt row for the partial
+    // recovery sums): once per pair, or once per used expert when the grouped
+    // screen ran in front of the per-pair kernel
+    const uint64_t screen = (sketch_read ? 2ull * I * (H / 4) + 8ull * I : 0) + (r > 0 ? 2ull * I * r : 0);
+    const uint64_t per_pair = (exact_step ? 4ull * H * c : 0) + (r > 0 ? 2ull * H * r : 0);
+    s.bytes_requested = (screen_per_expert ? (uint64_t)used : Pu) * screen + Pu * per_pair +
+                        (down_req >= 0 ? Pu * 2ull * H * down_req : s.bytes_down) + s.bytes_io;
   } else {
     s.bytes_requested = Pu * 6ull * I * H + s.bytes_io;
   }
@@ -86,6 +94,16 @@ const void* fused_fn(bool select, int H, bool recx, bool env) {
     case 8: return fused_kernel_e8(select, recx, env);
     case 16: return fused_kernel_e16(select, recx, env);
     case 32: return fused_kernel_e32(select, recx, env);
+    default: return nullptr;
+  }
+}
+
+// The prescreened instance for hidden width H (H <= 2048), or null.
+const void* fused_fn_ps(int H, bool recx) {
+  switch (H >= 1024 ? H / 256 : 0) {
+    case 0: return H == 512 ? fused_kernel_e2_ps(recx) : fused_kernel_e0_ps(recx);
+    case 4: return fused_kernel_e4_ps(recx);
+    case 8: return fused_kernel_e8_ps(recx);
     default: return nullptr;
   }
 }
@@ -130,7 +148,9 @@ bool lean_fits(const ForwardPlan& p, const SelectArgs& s) {
 
 template <bool SELECT>
 int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream, bool lean = false) {
-  const void* fn = lean ? fused_kernel_e8_lean() : fused_fn(SELECT, fa.H, fa.rec_exact != 0, fa.env != 0);
+  const void* fn = lean                     ? fused_kernel_e8_lean()
+                   : (SELECT && fa.hs != nullptr) ? fused_fn_ps(fa.H, fa.rec_exact != 0)
+                                                  : fused_fn(SELECT, fa.H, fa.rec_exact != 0, fa.env != 0);
   if (!fn) return set_error(CFM_EUNSUPPORTED, "hidden width not supported");
   if (lds > 163840) return set_error(CFM_EUNSUPPORTED, "shape needs more LDS than a workgroup has");
   if (lds > 65536)
@@ -299,16 +319,37 @@ int fit_plan(const ForwardPlan& p0, bool recx, ForwardPlan* out) {
   return set_error(CFM_EUNSUPPORTED, "no grid of the forward kernel fits the device");
 }
 
+// Whether the per-pair pass runs the expert-grouped screen before its kernel:
+// with several sub-chunks of channels per workgroup (several tokens), when
+// the screen is needed, the shape suits the grouped screen and the workspace
+// holds its regions (sized from the unrefitted plan, as select_workspace is).
+static bool use_grouped_screen(const SelectArgs& s, const ForwardPlan& p0, const ForwardPlan& p, GroupPlan* g) {
+  if (p.env || forward_path() == 4 || p.cw <= kSubChunk || p.I > 4 * NT || p.H > 2048) return false;
+  if ((s.flags & CFM_RECOVER_CANDIDATES_EXACT) && p.c >= p.I) return false;   // no sketch activation is used
+  if (!grouped_screen_supported(p.T, p.K, p.E, p.I, p.H, p.r)) return false;
+  *g = group_plan(p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, false, p0.bytes);
+  return s.ws_bytes >= g->bytes;
+}
+
 int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_t stream) {
   ForwardPlan p;
   if (int rc = fit_plan<true>(p0, (s.flags & CFM_RECOVER_CANDIDATES_EXACT) != 0, &p)) return rc;
-  if (int rc = prepare_workspace(s.ws, p.bytes,
-                                 layout_signature({1, p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, p.env, p.nw, p.G}),
+  GroupPlan g{};
+  const bool gscreen = use_grouped_screen(s, p0, p, &g);
+  if (int rc = prepare_workspace(s.ws, gscreen ? g.bytes : p.bytes,
+                                 layout_signature({gscreen ? 4 : 1, p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, p.env,
+                                                   p.nw, p.G, gscreen ? (long)g.bytes : 0}),
                                  stream))
     return rc;
-  const FusedArgs a = fused_args(s, p);
+  FusedArgs a = fused_args(s, p);
   if (!a.x) return set_error(CFM_EINVAL, "select forward: no hidden states");
-  const bool lean = forward_path() != 3 && lean_fits(p, s);
+  if (gscreen) {
+    if (int rc = launch_grouped_screen(s, g, stream)) return rc;
+    a.hs = reinterpret_cast<const float*>(s.ws + g.off_hs);
+    a.zp = reinterpret_cast<const float*>(s.ws + g.off_zp);
+    a.nzp = (p.I + 15) / 16;
+  }
+  const bool lean = forward_path() != 3 && forward_path() != 4 && lean_fits(p, s);
   int rc = launch_fused<true>(a, p.lds, stream, lean);
   if (rc) return rc;
   if (s.stats) {
@@ -316,7 +357,7 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
     const int down_req = (p.pre && !lean) ? p.c : -1;
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
                        p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0,
-                       (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr, down_req,
+                       (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr, down_req, gscreen ? 1 : 0,
                        static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
@@ -335,7 +376,7 @@ int launch_dense_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_t
   if (rc) return rc;
   if (s.stats) {
     hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.I, p.I, 0,
-                       p.T, p.K, 0, 1, 0, nullptr, -1, static_cast<cfm_stats*>(s.stats));
+                       p.T, p.K, 0, 1, 0, nullptr, -1, 0, static_cast<cfm_stats*>(s.stats));
     CFM_LAUNCH_CHECK("k_stats");
   }
   return CFM_OK;

@@ -13,4 +13,11 @@ const void* fused_kernel_e0(bool select, bool recx, bool env) {
              : reinterpret_cast<const void*>(&k_select_fused<0, false, false>);
 }
 
+
+// The prescreened instances (several tokens per launch, screen run before it).
+const void* fused_kernel_e0_ps(bool recx) {
+  return recx ? reinterpret_cast<const void*>(&k_select_fused<0, true, false, 0, 0, 1, true>)
+              : reinterpret_cast<const void*>(&k_select_fused<0, false, false, 0, 0, 1, true>);
+}
+
 }  // namespace cfm

@@ -13,4 +13,11 @@ const void* fused_kernel_e4(bool select, bool recx, bool env) {
              : reinterpret_cast<const void*>(&k_select_fused<4, false, false>);
 }
 
+
+// The prescreened instances (several tokens per launch, screen run before it).
+const void* fused_kernel_e4_ps(bool recx) {
+  return recx ? reinterpret_cast<const void*>(&k_select_fused<4, true, false, 0, 0, 1, true>)
+              : reinterpret_cast<const void*>(&k_select_fused<4, false, false, 0, 0, 1, true>);
+}
+
 }  // namespace cfm

@@ -20,4 +20,11 @@ const void* fused_kernel_e8(bool select, bool recx, bool env) {
              : reinterpret_cast<const void*>(&k_select_fused<8, false, false>);
 }
 
+
+// The prescreened instances (several tokens per launch, screen run before it).
+const void* fused_kernel_e8_ps(bool recx) {
+  return recx ? reinterpret_cast<const void*>(&k_select_fused<8, true, false, 0, 0, 1, true>)
+              : reinterpret_cast<const void*>(&k_select_fused<8, false, false, 0, 0, 1, true>);
+}
+
 }  // namespace cfm

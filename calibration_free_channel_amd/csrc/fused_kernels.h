@@ -244,6 +244,12 @@ struct FusedArgs {
   uint16_t* x_out;   // [T][H] (optional)
   uint64_t* trace;   // phase timestamps [G][kTraceSlots] (trace builds only; else unused)
   unsigned spin;     // polls of one exchanged value before the launch fails (0: at once)
+  // prescreened instance (I <= 4 NT): the sketch activations and the partial
+  // recovery sums, computed before the launch by the expert-grouped screen,
+  // which reads each routed expert's sketch once for all of its tokens
+  const float* hs;   // [P][I] sketch activations
+  const float* zp;   // [P][nzp][r] partial recovery sums over 16-channel groups
+  int nzp;
 };
 
 // Phase timestamps (instrumentation, compiled in only with CFM_PHASE_TRACE):
@@ -749,7 +755,7 @@ __device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p,
 // each column's down sum over the thread's rows in order, then the threads.
 // Requires nck <= NT and r = 0 or (r % 8 == 0, 64 % (r / 8) == 0). nz rows
 // enter z (the kept rows, or every candidate with the recovery variant).
-template <bool RECX>
+template <bool RECX, int AB, int DB>
 __device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L, int p, int t, int e, int w, int kk,
                                                int* s_flag, uint32_t tag, const float* lw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H, r = a.r;
@@ -759,7 +765,7 @@ __device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L,
   const int nz = RECX ? a.c : kk;
   const int cpr = r > 0 ? r / 8 : 1, ngz = NT / cpr;
   const int zc = tid % cpr, zgi = tid / cpr;
-  constexpr int ZB = 8, AB = 8, DB = 8;
+  constexpr int ZB = 8;
   uint4 bz[ZB];
   float hz[ZB];
   auto z_issue = [&](int i0) {
@@ -1044,10 +1050,14 @@ __device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) 
 // speculatively: once the kept set is known, each thread loads its LKPT kept
 // rows' 16-byte pieces of the down rows (this workgroup's columns) and of Bt in
 // one batch, so the layer reads exactly the kept rows.
-template <int EPT, bool RECX, bool ENV, int LNCK = 0, int LCPR = 0, int LKPT = 1>
+// PS: the prescreened instance (several tokens per launch, no envelope): the
+// sketch activations and partial recovery sums come from the expert-grouped
+// screen that ran before the launch (a.hs, a.zp), and phase A is not compiled.
+template <int EPT, bool RECX, bool ENV, int LNCK = 0, int LCPR = 0, int LKPT = 1, bool PS = false>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   constexpr bool LEAN = LNCK > 0;
   static_assert(!LEAN || (!RECX && !ENV && LNCK == 8 && LCPR == 8), "lean instance: plain method, 8 chunks, rank 64");
+  static_assert(!PS || (!LEAN && !ENV), "prescreened instance: general, no envelope");
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) uint32_t wred[NT / 64];
   __shared__ __align__(16) int wf0[NT / 64];
@@ -1106,7 +1116,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       }
       e = env_finish(a, L, t, p % a.K, w, tag);
     }
-    if (!nosk) {
+    if (!nosk && !PS) {
       const int cwk0 = min(j1 - j0, kSubChunk);
       // (every prefetch below is issued on every path, so no later wait has to
       //  assume that some of them were skipped; unused ones read valid addresses)
@@ -1184,6 +1194,41 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       }
       for (int i = tid; i < groups * r; i += NT) L.red[NT + i] = 0.f;
       __syncthreads();
+    } else if (PS) {
+      if constexpr (PS) {
+        // this thread's sketch activations and its share of the pair's partial
+        // recovery sums (groups zg, zg + groups, ... of 16 channels), written by
+        // an earlier launch: plain loads, all requested before the first use
+        int cnt;
+        const int i0 = topk_range<NT>(a.I, &cnt);           // (I <= 4 NT)
+        const float* hp = a.hs + (size_t)p * a.I;
+        float hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[j] = hp[j < cnt ? i0 + j : 0];
+        uint32_t k4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < cnt) L.hh[i0 + j] = hv[j];
+          k4[j] = score_key(j < cnt ? hv[j] : 0.f);
+        }
+        phase_stamp(a, 5);
+        block_topk<NT, 4>(k4, i0, cnt, a.I, a.c, L.candp, L.tks, TopkStamp{&a, 23});
+        if (r > 0) {
+          // (all of a batch's loads issued before the first add)
+          constexpr int ZQ = 16;
+          float zs = 0.f;
+          const float* zb = a.zp + (size_t)p * a.nzp * r + zl;
+          for (int q0 = zg; q0 < a.nzp; q0 += groups * ZQ) {
+            float zq[ZQ];
+#pragma unroll
+            for (int u = 0; u < ZQ; ++u) zq[u] = zb[(size_t)min(q0 + groups * u, a.nzp - 1) * r];
+#pragma unroll
+            for (int u = 0; u < ZQ; ++u) zs += q0 + groups * u < a.nzp ? zq[u] : 0.f;
+          }
+          if (zg < groups) L.red[NT + zg * r + zl] = zs;
+        }
+        __syncthreads();
+      }
     } else {
       int cnt;
       const int i0 = topk_range<NT>(a.I, &cnt);
@@ -1614,7 +1659,9 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     // registers would spill in the others)
     constexpr bool kStream = !ENV && EPT <= 8;
     if (kStream && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0)) && col_chunks(a) <= NT) {
-      if constexpr (kStream) phase_c_stream<RECX>(a, L, p, t, e, w, kk, &s_flag, tag, nullptr);
+      // (A pieces and kept-row pieces per request batch: the prescreened
+      // instance has the registers for twice as many)
+      if constexpr (kStream) phase_c_stream<RECX, PS ? 16 : 8, PS ? 16 : 8>(a, L, p, t, e, w, kk, &s_flag, tag, nullptr);
       continue;
     }
     if (r > 0) {

@@ -1372,33 +1372,8 @@ GroupPlan group_plan(int T, int K, int E, int I, int H, int k, int c, int r, boo
   return g;
 }
 
-int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
-  if (int rc = prepare_workspace(s.ws, g.bytes,
-                                 layout_signature({3, g.T, g.K, g.E, g.I, g.H, g.k, g.c, g.r, g.dense ? 1 : 0,
-                                                   s.resid ? 1 : 0, (long)g.bytes}),
-                                 stream))
-    return rc;
-  GArgs a{};
-  a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
-  if (s.resid) {
-    // decode-layer envelope: the router first; the pass then reads the
-    // normalised states and the routing it wrote, and adds the residual
-    RouteArgs ra{};
-    ra.h = s.resid; ra.gamma = s.gamma; ra.wr = s.wr; ra.eps = s.eps; ra.renorm = s.renorm;
-    ra.T = g.T; ra.K = g.K; ra.E = g.E; ra.H = g.H; ra.nb = (g.E + kRouteRows - 1) / kRouteRows;
-    ra.xw = reinterpret_cast<uint16_t*>(s.ws + g.off_xw);
-    ra.lg = reinterpret_cast<float*>(s.ws + g.off_lg);
-    ra.ids = reinterpret_cast<int32_t*>(s.ws + g.off_idw);
-    ra.w = reinterpret_cast<float*>(s.ws + g.off_ww);
-    ra.rctr = reinterpret_cast<uint32_t*>(s.ws + g.off_rctr);
-    ra.ids_out = s.ids_out; ra.w_out = s.w_out; ra.x_out = s.x_out;
-    timing_begin("k_g_route", stream);
-    hipLaunchKernelGGL(k_g_route, dim3(g.T, ra.nb), dim3(GT), 0, stream, ra);
-    timing_end(stream);
-    CFM_LAUNCH_CHECK("k_g_route");
-    a.x = ra.xw; a.ids = ra.ids; a.topk_w = ra.w;
-    a.resid = s.resid;
-  }
+// The pass's arguments from the call and the plan (routing fields aside).
+static void fill_args(GArgs& a, const SelectArgs& s, const GroupPlan& g) {
   a.wg = s.w_gate; a.wu = s.w_up; a.wd = s.w_down_t;
   a.signs = s.signs; a.tg = s.tg; a.tu = s.tu; a.sg = s.sg; a.su = s.su;
   a.A = s.A; a.Bt = s.Bt;
@@ -1440,6 +1415,36 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   a.thr = !g.dense && s.thr ? 1 : 0;
   a.tkey = s.tkey;
   a.keep_count = s.keep_count;
+}
+
+int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
+  if (int rc = prepare_workspace(s.ws, g.bytes,
+                                 layout_signature({3, g.T, g.K, g.E, g.I, g.H, g.k, g.c, g.r, g.dense ? 1 : 0,
+                                                   s.resid ? 1 : 0, (long)g.bytes}),
+                                 stream))
+    return rc;
+  GArgs a{};
+  a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
+  if (s.resid) {
+    // decode-layer envelope: the router first; the pass then reads the
+    // normalised states and the routing it wrote, and adds the residual
+    RouteArgs ra{};
+    ra.h = s.resid; ra.gamma = s.gamma; ra.wr = s.wr; ra.eps = s.eps; ra.renorm = s.renorm;
+    ra.T = g.T; ra.K = g.K; ra.E = g.E; ra.H = g.H; ra.nb = (g.E + kRouteRows - 1) / kRouteRows;
+    ra.xw = reinterpret_cast<uint16_t*>(s.ws + g.off_xw);
+    ra.lg = reinterpret_cast<float*>(s.ws + g.off_lg);
+    ra.ids = reinterpret_cast<int32_t*>(s.ws + g.off_idw);
+    ra.w = reinterpret_cast<float*>(s.ws + g.off_ww);
+    ra.rctr = reinterpret_cast<uint32_t*>(s.ws + g.off_rctr);
+    ra.ids_out = s.ids_out; ra.w_out = s.w_out; ra.x_out = s.x_out;
+    timing_begin("k_g_route", stream);
+    hipLaunchKernelGGL(k_g_route, dim3(g.T, ra.nb), dim3(GT), 0, stream, ra);
+    timing_end(stream);
+    CFM_LAUNCH_CHECK("k_g_route");
+    a.x = ra.xw; a.ids = ra.ids; a.topk_w = ra.w;
+    a.resid = s.resid;
+  }
+  fill_args(a, s, g);
   const int H = g.H;
 
   // 1. rotation + grouping
@@ -1498,6 +1503,33 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
     CFM_LAUNCH_CHECK("k_g_stats");
   }
   return CFM_OK;
+}
+
+// The expert-grouped pass's first two stages only (rotation, grouping and
+// the screen), in front of the per-pair kernel for several tokens: every
+// routed expert's sketch rows are read once for all of its tokens, and the
+// pairs' sketch activations (hs) and partial recovery sums (zp) are left in
+// the workspace for the per-pair kernel. The caller prepares the workspace.
+bool grouped_screen_supported(int T, int K, int E, int I, int H, int r) {
+  return grouped_supported(T, K, E, I, H, r, false) && (H + 255) / 256 <= kSbReg;
+}
+
+int launch_grouped_screen(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
+  GArgs a{};
+  a.x = s.x; a.ids = s.ids; a.topk_w = s.topk_w;
+  fill_args(a, s, g);
+  const int H = g.H;
+  const int ept = H >= 1024 ? H / 256 : 0;
+  const void* fn = nullptr;
+  switch (ept) {
+    case 0: fn = reinterpret_cast<const void*>(&k_g_prep<0>); break;
+    case 4: fn = reinterpret_cast<const void*>(&k_g_prep<4>); break;
+    case 8: fn = reinterpret_cast<const void*>(&k_g_prep<8>); break;
+    default: return set_error(CFM_EUNSUPPORTED, "grouped screen: hidden width not supported");
+  }
+  if (int rc = launch_k("k_g_prep", fn, dim3(g.T + 1), prep_lds(H, g.E), a, stream)) return rc;
+  return launch_k("k_g_screen", reinterpret_cast<const void*>(&k_g_screen_lds), dim3(g.ntile, g.maxwork), 0, a,
+                  stream);
 }
 
 }  // namespace cfm

@@ -356,7 +356,13 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
  *   0 automatic (default): the expert-grouped pass where the shape allows it
  *     and the batch is large (selected layer: 48 tokens or more; dense layer:
  *     32 or more), the per-pair pass otherwise;
- *   1 the per-pair pass (one persistent launch; lowest latency at batch 1);
+ *   1 the per-pair pass (one persistent launch; lowest latency at batch 1).
+ *     With several sub-chunks of channels per workgroup (several tokens per
+ *     call, H <= 2048, I <= 1024, r a multiple of 8, a workspace of
+ *     select_workspace bytes) the expert-grouped pass's screen runs first, as
+ *     two short launches that read each routed expert's sketch once for all
+ *     of its tokens, and the persistent launch starts from its sketch
+ *     activations (the same values the launch would compute itself);
  *   2 the expert-grouped pass (pairs grouped by expert; each weight row an
  *     expert needs is read once for all of its tokens: the larger batches at
  *     which the article, section "Numbers and limits", reports the largest
@@ -365,7 +371,9 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
  *     E <= 4096, and for the selected layer r a multiple of 8;
  *   3 the per-pair pass without its batch-1 instance (the kernel compiled for
  *     the Qwen3-30B-A3B-shaped batch-1 call: H 2048, r 64, at most 8 pairs):
- *     the general instance serves every call, for comparison and testing.
+ *     the general instance serves every call, for comparison and testing;
+ *   4 as 3, with the screen always inside the persistent launch (no grouped
+ *     screen in front), for comparison and testing.
  * Both passes compute the same selections (identical sketch activations, so
  * identical candidate sets; exact activations and outputs agree to float
  * rounding). The workspace sizes returned by select_workspace and

@@ -171,7 +171,10 @@ def test_dense_forward_rejects(lib):
 def test_forward_path_switch(lib):
     f = lib.cfm_set_forward_path
     f.restype = ctypes.c_int
-    assert f(4) == EINVAL and f(-1) == EINVAL
+    assert f(5) == EINVAL and f(-1) == EINVAL
+    prev = f(4)
+    assert f(3) == 4                        # 4: per-pair with the screen inside the single launch
+    f(prev)
     prev = f(2)
     try:
         assert f(2) == 2
