@@ -746,16 +746,18 @@ __device__ __forceinline__ void phase_c(const FusedArgs& a, const Lds& L, int p,
 }
 
 // Phase C of a workgroup without the candidate-row prefetch (several tokens
-// per launch), with every request that does not wait on another issued before
-// the first wait: the Bt pieces of the recovery coefficients' rows, this
-// workgroup's A pieces and the first batch of its kept down-row pieces; later
-// down batches are requested one batch ahead (two register buffers). The
+// per launch), with the requests that wait on nothing else issued early: the
+// Bt pieces of the recovery coefficients' rows first, then this workgroup's
+// A pieces and the first batch of its kept down-row pieces (EARLY: together
+// with the Bt pieces; else once the Bt pieces are used, in flight during the
+// reduction of z); later down batches are requested one batch ahead (two
+// register buffers). AB, DB: A and down pieces per thread and batch. The
 // arithmetic and its order are those of the step-by-step form (z, then
 // cols_block): z over the rows in index order per thread, then the groups;
 // each column's down sum over the thread's rows in order, then the threads.
 // Requires nck <= NT and r = 0 or (r % 8 == 0, 64 % (r / 8) == 0). nz rows
 // enter z (the kept rows, or every candidate with the recovery variant).
-template <bool RECX, int AB, int DB>
+template <bool RECX, int AB, int DB, bool EARLY>
 __device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L, int p, int t, int e, int w, int kk,
                                                int* s_flag, uint32_t tag, const float* lw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, H = a.H, r = a.r;
@@ -799,6 +801,12 @@ __device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L,
     }
   };
   if (cols && r > 0) z_issue(zgi);
+  if constexpr (EARLY) {
+    // (registers to spare) the A pieces and the first down batch are in
+    // flight while z is formed
+    if (cols && r > 0) a_issue(0);
+    if (cols && n > 0) d_issue(g, dA, hA);
+  }
   // ---- recovery coefficients z = zsum - sum_j coef_j Bt[j] (coef: sketch
   //      activation of a kept row, or the variant's per-candidate term)
   float* rec = L.red;                               // [8 nck] recovery term (after z is formed)
@@ -816,9 +824,11 @@ __device__ __forceinline__ void phase_c_stream(const FusedArgs& a, const Lds& L,
 #pragma unroll
     for (int u = 0; u < 8; ++u) L.red[zgi * r + 8 * zc + u] = acc[u];    // ngz r = 8 NT
   }
-  // the A pieces and the first down batch are in flight during the reduction
-  if (cols && r > 0) a_issue(0);
-  if (cols && n > 0) d_issue(g, dA, hA);
+  if constexpr (!EARLY) {
+    // the A pieces and the first down batch are in flight during the reduction
+    if (cols && r > 0) a_issue(0);
+    if (cols && n > 0) d_issue(g, dA, hA);
+  }
   __syncthreads();
   if (cols && r > 0) {
     for (int l = tid; l < r; l += NT) {
@@ -1661,7 +1671,8 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     if (kStream && (r == 0 || (r % 8 == 0 && 64 % (r / 8) == 0)) && col_chunks(a) <= NT) {
       // (A pieces and kept-row pieces per request batch: the prescreened
       // instance has the registers for twice as many)
-      if constexpr (kStream) phase_c_stream<RECX, PS ? 16 : 8, PS ? 16 : 8>(a, L, p, t, e, w, kk, &s_flag, tag, nullptr);
+      if constexpr (kStream)
+        phase_c_stream<RECX, PS ? 16 : 8, PS ? 16 : 8, PS>(a, L, p, t, e, w, kk, &s_flag, tag, nullptr);
       continue;
     }
     if (r > 0) {

@@ -423,6 +423,45 @@ def test_batched_full_size(cfm, name):
         compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=f"{name} path {path}")
 
 
+@pytest.mark.parametrize("spec", [("q18_b8", None), ("q13_b16", None),
+                                  ("ps_small", (16, 4, 256, 512, 16, 46, 92, 8, 33)),
+                                  ("ps_ragged", (6, 3, 101, 128, 40, 17, 33, 8, 34)),
+                                  ("ps_rank0", (16, 4, 256, 512, 16, 46, 92, 0, 35)),
+                                  ("ps_k0_fullrank", (4, 2, 64, 128, 80, 0, 0, 64, 36))],
+                         ids=lambda s: s[0])
+def test_per_pair_screens_agree(cfm, spec):
+    """The per-pair pass with several tokens, its screen run by the expert-grouped screen kernels before
+    the single launch (path 1) against the screen inside the launch (path 4), on the same inputs: the same
+    candidate and kept sets bit for bit (both select from bit-identical sketch activations and the same
+    exact activations), outputs within float rounding (the partial recovery sums are added in another
+    order), and the screen's reads requested once per used expert instead of once per pair. Path 1 is
+    also checked against the oracle on sampled tokens."""
+    name, shape = spec
+    wl = synth.WORKLOADS[name] if shape is None else custom_workload(name, *shape)
+    log(f"per-pair screens {name}")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    T, K = L.host.ids.shape
+    tokens = [0, T // 2, T - 1]
+    used_s = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used_s, E, I, H)
+    Ag, Btg = (up_bf16(A), up_bf16(Bt)) if wl.r > 0 else (None, None)
+    res = {}
+    for path in (cfm.FORWARD_PER_PAIR, cfm.FORWARD_PER_PAIR_SINGLE):
+        with cfm.forward_path(path):
+            res[path] = run_select(cfm, L, sk, Ag, Btg, wl.k, wl.c, wl.r, stats=True)
+    (g1, c1, k1, s1), (g4, c4, k4, s4) = res[cfm.FORWARD_PER_PAIR], res[cfm.FORWARD_PER_PAIR_SINGLE]
+    assert np.array_equal(c1, c4) and np.array_equal(k1, k4)
+    err = max(rel_l2(g1[t], g4[t]) for t in range(T))
+    assert err <= 2e-3, f"{name}: paths 1 and 4 differ by rel L2 {err:.2e}"
+    used = len(set(L.host.ids.reshape(-1).tolist()))
+    screen = 2 * I * (H // 4) + 8 * I + 2 * I * wl.r
+    assert s4["bytes_requested"] - s1["bytes_requested"] == (T * K - used) * screen, (s1, s4)
+    log(f"{name}: paths 1 and 4 agree (max rel L2 {err:.2e}); screen reads {used} experts instead of {T * K} pairs")
+    compare_forward(L, A, Bt, g1, c1, k1, wl.k, wl.c, tokens=tokens, what=f"{name} path 1")
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_qwen_all_candidates_full_size(cfm, T):
     """Qwen3-30B-A3B-shaped layer with every channel a candidate (c = I = 768) and a 53 % budget
