@@ -110,11 +110,14 @@ int check_budget(int I, int H, int k, int c, int r) {
 // without the batch-1 instance, 4 per-pair with the screen inside the single
 // launch (process-wide).
 std::atomic<int> g_path{0};
-// Automatic choice: the grouped pass from these batch sizes on (measured on the
-// Qwen3-30B-A3B-shaped layer: below them the single-launch per-pair kernels
-// are faster; at 64 tokens the grouped selected layer takes 6.0 us/token
-// against 8.2, and the grouped dense layer 5.2 against 11.3).
+// Automatic choice: the grouped pass from these batch sizes on, and for the
+// selected layer also once the routed pairs outnumber the per-pair kernel's
+// resident workgroups (it would serve them in rounds). Measured on the
+// Qwen3-30B-A3B-shaped layer (18 % budget, µs per token, per-pair / grouped):
+// 32 tokens 6.1 / 7.1, 40 tokens 8.0 / 6.0, 64 tokens 5.5 / 4.6; the dense
+// layer at 64 tokens 11.3 / 5.2.
 constexpr int kGroupedMinTokensSelect = 48;
+constexpr int kGroupedMinPairsSelect = 257;
 constexpr int kGroupedMinTokensDense = 32;
 
 // Whether a forward call uses the grouped pass (or an error status).
@@ -122,8 +125,9 @@ int pick_grouped(int T, int K, int E, int I, int H, int r, bool dense, bool* gro
   const bool ok = grouped_supported(T, K, E, I, H, r, dense);
   const int path = g_path.load(std::memory_order_relaxed);
   if (path == 2 && !ok) return set_error(CFM_EUNSUPPORTED, "expert-grouped pass: shape not supported");
-  const int min_tokens = dense ? kGroupedMinTokensDense : kGroupedMinTokensSelect;
-  *grouped = path == 2 || (path == 0 && ok && T >= min_tokens);
+  const bool large = dense ? T >= kGroupedMinTokensDense
+                           : T >= kGroupedMinTokensSelect || (long)T * K >= kGroupedMinPairsSelect;
+  *grouped = path == 2 || (path == 0 && ok && large);
   return CFM_OK;
 }
 

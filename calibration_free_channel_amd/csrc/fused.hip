@@ -319,12 +319,21 @@ int fit_plan(const ForwardPlan& p0, bool recx, ForwardPlan* out) {
   return set_error(CFM_EUNSUPPORTED, "no grid of the forward kernel fits the device");
 }
 
+// Routed pairs from which the per-pair pass puts the grouped screen in front
+// of its kernel (Qwen3-30B-A3B-shaped layer, 18 % budget, µs per token with /
+// without it: 4 tokens 14.9 / 13.9, 6 tokens 11.9 / 13.2, 8 tokens 9.7 / 10.3,
+// 16 tokens 7.3 / 8.8, 32 tokens 6.1 / 8.0).
+constexpr int kGroupedScreenMinPairs = 40;
+
 // Whether the per-pair pass runs the expert-grouped screen before its kernel:
-// with several sub-chunks of channels per workgroup (several tokens), when
-// the screen is needed, the shape suits the grouped screen and the workspace
-// holds its regions (sized from the unrefitted plan, as select_workspace is).
+// from kGroupedScreenMinPairs pairs, with several sub-chunks of channels per
+// workgroup, when the screen is needed, the shape suits the grouped screen and
+// the workspace holds its regions (sized from the unrefitted plan, as
+// select_workspace is).
 static bool use_grouped_screen(const SelectArgs& s, const ForwardPlan& p0, const ForwardPlan& p, GroupPlan* g) {
-  if (p.env || forward_path() == 4 || p.cw <= kSubChunk || p.I > 4 * NT || p.H > 2048) return false;
+  if (p.env || forward_path() == 4 || p.P < kGroupedScreenMinPairs || p.cw <= kSubChunk || p.I > 4 * NT ||
+      p.H > 2048)
+    return false;
   if ((s.flags & CFM_RECOVER_CANDIDATES_EXACT) && p.c >= p.I) return false;   // no sketch activation is used
   if (!grouped_screen_supported(p.T, p.K, p.E, p.I, p.H, p.r)) return false;
   *g = group_plan(p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, false, p0.bytes);

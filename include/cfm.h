@@ -354,8 +354,9 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
  * atomic setting, but a call on one thread changes the pass of concurrent
  * calls on others; returns the previous setting, or CFM_EINVAL).
  *   0 automatic (default): the expert-grouped pass where the shape allows it
- *     and the batch is large (selected layer: 48 tokens or more; dense layer:
- *     32 or more), the per-pair pass otherwise;
+ *     and the batch is large (selected layer: 48 tokens or more, or more than
+ *     256 routed pairs; dense layer: 32 tokens or more), the per-pair pass
+ *     otherwise;
  *   1 the per-pair pass (one persistent launch; lowest latency at batch 1).
  *     With several sub-chunks of channels per workgroup (several tokens per
  *     call, H <= 2048, I <= 1024, r a multiple of 8, a workspace of

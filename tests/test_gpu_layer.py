@@ -8,7 +8,7 @@ Staged comparison, step by step on the device's own intermediate values:
   * the routing (ids_out, w_out) against the oracle's router run on x_out
     (equal, up to near-ties of the logits; weights to float32 rounding);
   * the block on (x_out, ids_out, w_out) through the plain entry point on the
-    same pass as the layer call (per-pair below 48 tokens, grouped from 48),
+    same pass as the layer call (per-pair below 48 tokens and 257 pairs, grouped from there),
     against the oracle with the usual set and output bars;
   * the layer output against that block output plus the residual, one rounding
     each (and the residual must matter).
@@ -98,8 +98,10 @@ def _check_residual(out, h, block):
 
 
 def _layer_pass(cfm, wl, dense=False):
-    """The pass the layer call takes automatically (grouped from 48 tokens, 32 for the dense layer)."""
-    return cfm.FORWARD_GROUPED if wl.T >= (32 if dense else 48) else cfm.FORWARD_PER_PAIR
+    """The pass the layer call takes automatically (grouped from 48 tokens or 257 routed pairs, from 32
+    tokens for the dense layer)."""
+    large = wl.T >= 32 if dense else (wl.T >= 48 or wl.T * wl.shape.K >= 257)
+    return cfm.FORWARD_GROUPED if large else cfm.FORWARD_PER_PAIR
 
 
 def _tokens(wl):
