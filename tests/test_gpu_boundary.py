@@ -56,20 +56,22 @@ def _layer_and_map(wl):
     return L, up_bf16(A), up_bf16(Bt)
 
 
-@pytest.mark.parametrize("path", ["per_pair", "grouped"])
+@pytest.mark.parametrize("path", ["per_pair", "grouped", "per_pair_screened"])
 def test_workspace_reuse_across_shapes(cfm, path):
-    """T = 1, then T = 8, then T = 1 again, then the dense layer, on one workspace: each result equals
-    the same call on a fresh workspace, bit for bit (the calls are deterministic)."""
+    """T = 1, then T = 8 (16 with the per-pair pass's grouped screen in front), then T = 1 again, then
+    the dense layer, on one workspace: each result equals the same call on a fresh workspace, bit for
+    bit (the calls are deterministic)."""
     log(f"workspace reuse {path}")
-    wl8 = custom_workload("reuse8", 16, 4, 256, 512, 8, 46, 92, 8, 31)
+    big = 16 if path == "per_pair_screened" else 8          # 64 routed pairs: the grouped screen runs first
+    wl8 = custom_workload(f"reuse{big}", 16, 4, 256, 512, big, 46, 92, 8, 31)
     L, A, Bt = _layer_and_map(wl8)
     sk = cfm.sketch_build(L.wg, L.wu, L.signs)
     E, I, H = L.host.w_gate.shape
     K = L.host.ids.shape[1]
     k, c, r = wl8.k, wl8.c, wl8.r
-    sizes = [cfm.select_workspace(T, K, E, I, H, k, c, r) for T in (1, 8)] + [cfm.dense_workspace(8, K, E, I, H)]
+    sizes = [cfm.select_workspace(T, K, E, I, H, k, c, r) for T in (1, big)] + [cfm.dense_workspace(big, K, E, I, H)]
     shared = cfm.new_workspace(max(sizes), dev())
-    mode = cfm.FORWARD_PER_PAIR if path == "per_pair" else cfm.FORWARD_GROUPED
+    mode = cfm.FORWARD_GROUPED if path == "grouped" else cfm.FORWARD_PER_PAIR
 
     def sel(T, ws):
         return down_bf16(cfm.moe_select_forward(L.x[:T].contiguous(), L.ids[:T].contiguous(), L.w[:T].contiguous(),
@@ -79,7 +81,7 @@ def test_workspace_reuse_across_shapes(cfm, path):
         return down_bf16(cfm.moe_dense_forward(L.x[:T].contiguous(), L.ids[:T].contiguous(), L.w[:T].contiguous(),
                                                L.wg, L.wu, L.wd, ws=ws))
     with cfm.forward_path(mode):
-        for step, (fn, T) in enumerate([(sel, 1), (sel, 8), (sel, 1), (dense, 8), (sel, 8)]):
+        for step, (fn, T) in enumerate([(sel, 1), (sel, big), (sel, 1), (dense, big), (sel, big)]):
             got = fn(T, shared)
             want = fn(T, None)
             torch.cuda.synchronize()

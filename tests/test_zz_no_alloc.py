@@ -30,11 +30,14 @@ def _run(cfm, L, A, Bt, sk, T, k, c, r, noalloc):
     return down_bf16(out), cand.cpu().numpy(), keep.cpu().numpy()
 
 
-@pytest.mark.parametrize("shape", ["qwen_like", "small"])
+@pytest.mark.parametrize("shape", ["qwen_like", "small", "screened"])
 def test_noalloc_matches_workspace_entry(cfm, shape):
     if shape == "qwen_like":   # H 2048, I 768, 18 %: 4 tokens (16 pairs), then 2 tokens (8 pairs, the lean kernel)
         wl = custom_workload("noalloc_q", 16, 4, 768, 2048, 4, 138, 276, 64, 41)
         sizes = (4, 2)
+    elif shape == "screened":  # 16 tokens (64 pairs), then 10 (40): the grouped screen runs before the launch
+        wl = custom_workload("noalloc_g", 16, 4, 768, 2048, 16, 138, 276, 64, 43)
+        sizes = (16, 10)
     else:
         wl = custom_workload("noalloc_s", 12, 3, 200, 256, 9, 36, 72, 8, 42)
         sizes = (9, 3)
