@@ -337,8 +337,8 @@ FORWARD_AUTO, FORWARD_PER_PAIR, FORWARD_GROUPED, FORWARD_PER_PAIR_GENERAL, FORWA
 
 
 def set_forward_path(path: int) -> int:
-    """Select the forward kernels (0 automatic, 1 per-pair, 2 expert-grouped, 3 per-pair without the batch-1
-    instance, 4 per-pair with the screen always inside the single launch); returns the previous setting."""
+    """Select the forward kernels (0 automatic, 1 per-pair, 2 expert-grouped, 3 per-pair on the general instance
+    only, 4 per-pair with the screen always inside the single launch); returns the previous setting."""
     prev = _lib.cfm_set_forward_path(int(path))
     if prev < 0:
         raise CfmError(prev, "cfm_set_forward_path")

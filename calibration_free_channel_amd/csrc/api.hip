@@ -107,7 +107,7 @@ int check_budget(int I, int H, int k, int c, int r) {
 }
 
 // Forward-pass variant: 0 automatic, 1 per-pair, 2 expert-grouped, 3 per-pair
-// without the batch-1 instance, 4 per-pair with the screen inside the single
+// on the general instance only, 4 per-pair with the screen inside the single
 // launch (process-wide).
 std::atomic<int> g_path{0};
 // Automatic choice: the grouped pass from these batch sizes on, and for the

@@ -20,6 +20,10 @@ const void* fused_kernel_e0_ps(bool recx);
 const void* fused_kernel_e2_ps(bool recx);
 const void* fused_kernel_e4_ps(bool recx);
 const void* fused_kernel_e8_ps(bool recx);
+const void* fused_kernel_e0_ms();
+const void* fused_kernel_e2_ms();
+const void* fused_kernel_e4_ms();
+const void* fused_kernel_e8_ms();
 
 namespace {
 
@@ -108,6 +112,16 @@ const void* fused_fn_ps(int H, bool recx) {
   }
 }
 
+// The multi-sub-chunk instance of the plain method for hidden width H (H <= 2048), or null.
+const void* fused_fn_ms(int H) {
+  switch (H >= 1024 ? H / 256 : 0) {
+    case 0: return H == 512 ? fused_kernel_e2_ms() : fused_kernel_e0_ms();
+    case 4: return fused_kernel_e4_ms();
+    case 8: return fused_kernel_e8_ms();
+    default: return nullptr;
+  }
+}
+
 // How many workgroups of `fn` with `lds` bytes of LDS the current device holds
 // at once (compute units times resident workgroups per unit), capped at the
 // launch sequence slots (cached per device, kernel and LDS size) and at the
@@ -147,9 +161,10 @@ bool lean_fits(const ForwardPlan& p, const SelectArgs& s) {
 }
 
 template <bool SELECT>
-int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream, bool lean = false) {
+int launch_fused(const FusedArgs& fa, size_t lds, hipStream_t stream, bool lean = false, bool ms = false) {
   const void* fn = lean                     ? fused_kernel_e8_lean()
                    : (SELECT && fa.hs != nullptr) ? fused_fn_ps(fa.H, fa.rec_exact != 0)
+                   : (SELECT && ms)               ? fused_fn_ms(fa.H)
                                                   : fused_fn(SELECT, fa.H, fa.rec_exact != 0, fa.env != 0);
   if (!fn) return set_error(CFM_EUNSUPPORTED, "hidden width not supported");
   if (lds > 163840) return set_error(CFM_EUNSUPPORTED, "shape needs more LDS than a workgroup has");
@@ -331,7 +346,7 @@ constexpr int kGroupedScreenMinPairs = 40;
 // the workspace holds its regions (sized from the unrefitted plan, as
 // select_workspace is).
 static bool use_grouped_screen(const SelectArgs& s, const ForwardPlan& p0, const ForwardPlan& p, GroupPlan* g) {
-  if (p.env || forward_path() == 4 || p.P < kGroupedScreenMinPairs || p.cw <= kSubChunk || p.I > 4 * NT ||
+  if (p.env || forward_path() >= 3 || p.P < kGroupedScreenMinPairs || p.cw <= kSubChunk || p.I > 4 * NT ||
       p.H > 2048)
     return false;
   if ((s.flags & CFM_RECOVER_CANDIDATES_EXACT) && p.c >= p.I) return false;   // no sketch activation is used
@@ -359,7 +374,14 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
     a.nzp = (p.I + 15) / 16;
   }
   const bool lean = forward_path() != 3 && forward_path() != 4 && lean_fits(p, s);
-  int rc = launch_fused<true>(a, p.lds, stream, lean);
+  // three or more sub-chunks per workgroup with the screen inside the launch:
+  // the instance that keeps the next sub-chunk's rows in flight (plain method;
+  // Qwen3-30B-A3B-shaped layer, µs per token against the general instance:
+  // 3 tokens 17.7 / 18.0, 4 tokens 13.6 / 14.0; with two sub-chunks, 2 tokens,
+  // 22.3 / 22.1)
+  const bool ms = !lean && !gscreen && forward_path() != 3 && !p.env && !p.pre && p.cw > 2 * kSubChunk &&
+                  p.I <= 4 * NT && p.H <= 2048 && !(s.flags & CFM_RECOVER_CANDIDATES_EXACT);
+  int rc = launch_fused<true>(a, p.lds, stream, lean, ms);
   if (rc) return rc;
   if (s.stats) {
     // the general instances prefetch every candidate's down row (for their columns) when p.pre

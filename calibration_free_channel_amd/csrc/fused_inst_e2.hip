@@ -20,4 +20,10 @@ const void* fused_kernel_e2_ps(bool recx) {
               : reinterpret_cast<const void*>(&k_select_fused<2, false, false, 0, 0, 1, true>);
 }
 
+// The multi-sub-chunk instance of the plain method (several sub-chunks of
+// channels per workgroup, screen inside the launch).
+const void* fused_kernel_e2_ms() {
+  return reinterpret_cast<const void*>(&k_select_fused<2, false, false, 0, 0, 1, false, true>);
+}
+
 }  // namespace cfm

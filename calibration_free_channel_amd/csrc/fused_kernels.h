@@ -961,6 +961,90 @@ __device__ __forceinline__ void screen_and_sum(const FusedArgs& a, const Lds& L,
   __syncthreads();
 }
 
+// Phase A for a slice of more than one sub-chunk (the multi-sub-chunk
+// instance). The sketch rows and scales of the next sub-chunk are requested
+// before the current one is screened, into the other of two register sets
+// that alternate: a copy from one set to the other would wait for the
+// requests still filling it. The slice's sketch activations are kept in L.hh
+// (the exchange later writes the same values there) and its partial recovery
+// sums are formed once, after the last sub-chunk, from the slice's contiguous
+// Bt rows, whose first batch is requested in place of a next sub-chunk.
+// Returns thread (zl, zg)'s share of the slice's partial sum of column zl
+// (with r % 8 = 0 the whole sum sits in zg = 0 and the other groups hold zero).
+template <int EPT>
+__device__ __forceinline__ float screen_slice(const FusedArgs& a, const Lds& L, int p, int e, int j0, int j1, int F0,
+                                              uint4 (&s1)[kSketchPre], float2 sg1, int zl, int zg, int groups,
+                                              uint32_t tag) {
+  const int tid = threadIdx.x, H = a.H, r = a.r;
+  const int nsb = (H + 255) / 256;
+  const int nsub = (j1 - j0 + kSubChunk - 1) / kSubChunk;
+  const bool vec = r > 0 && r % 8 == 0;                       // Bt rows as whole 16-byte pieces
+  const int cpr = vec ? r / 8 : 1;                            // pieces per row (divides NT)
+  const int npc = vec ? (j1 - j0) * cpr : 1;
+  const uint16_t* btb = vec ? a.Bt + ((size_t)e * a.I + j0) * r : a.x;   // (otherwise a valid address, unused)
+  auto request = [&](int i, uint4 (&sk)[kSketchPre], float2& sg) {
+    if (i < nsub) {
+      const int nj0 = j0 + i * kSubChunk, ncwk = min(j1 - nj0, kSubChunk);
+#pragma unroll
+      for (int u = 0; u < kSketchPre; ++u) sk[u] = sketch_item(a, e, nj0, ncwk, min(u, nsb - 1));
+      sg = load_scale(a, e, nj0, ncwk);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSketchPre; ++u) sk[u] = ld16c(btb + 8 * (size_t)min(tid + NT * u, npc - 1));
+    }
+  };
+  auto screen = [&](int i, const uint4 (&sk)[kSketchPre], float2 sg) {
+    const int sj0 = j0 + i * kSubChunk, cwk = min(j1 - sj0, kSubChunk);
+    screen_chunk<(EPT <= kSketchPre)>(a, L, p, e, sj0, cwk, F0, sk, true, sg, tag);
+    if (tid < cwk) L.hh[sj0 + tid] = L.hloc[tid];
+  };
+  // the partial sums from the slice's Bt rows; bt: the first batch of pieces
+  auto bt_sum = [&](uint4 (&bt)[kSketchPre]) -> float {
+    __syncthreads();                                          // the slice's activations are in L.hh
+    float zs = 0.f;
+    if (vec) {
+      // thread tid takes pieces tid + NT u: rank chunk tid % cpr of rows (tid + NT u) / cpr
+      float acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+      for (int f0 = 0;;) {
+#pragma unroll
+        for (int u = 0; u < kSketchPre; ++u) {
+          const int f = f0 + tid + NT * u;
+          const float h = f < npc ? L.hh[j0 + f / cpr] : 0.f;
+          fma8(acc, h, bt[u]);
+        }
+        f0 += NT * kSketchPre;
+        if (f0 >= npc) break;
+#pragma unroll
+        for (int u = 0; u < kSketchPre; ++u) bt[u] = ld16c(btb + 8 * (size_t)min(f0 + tid + NT * u, npc - 1));
+      }
+      const int ng = NT / cpr, c8 = 8 * (tid % cpr);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) L.red[(tid / cpr) * r + c8 + u] = acc[u];    // ng r = 8 NT
+      __syncthreads();
+      if (tid < r)
+        for (int g = 0; g < ng; ++g) zs += L.red[g * r + tid];
+      __syncthreads();
+    } else if (r > 0 && zg < groups) {
+      // any other rank: one Bt value at a time (channels zg, zg + groups, ...)
+      for (int jj = zg; jj < j1 - j0; jj += groups)
+        zs += L.hh[j0 + jj] * bf16_to_f32(a.Bt[((size_t)e * a.I + j0 + jj) * r + zl]);
+    }
+    return zs;
+  };
+  uint4 s2[kSketchPre];
+  float2 sg2 = sg1;
+  for (int i = 0;;) {
+    request(i + 1, s2, sg2);
+    screen(i, s1, sg1);
+    if (++i >= nsub) return bt_sum(s2);
+    request(i + 1, s1, sg1);
+    screen(i, s2, sg2);
+    if (++i >= nsub) return bt_sum(s1);
+  }
+}
+
 // 16-byte piece i of a row of x (in LDS with the envelope, global memory otherwise).
 __device__ __forceinline__ uint4 x16(const uint16_t* row, int i) {
   return ld16c(reinterpret_cast<const uint4*>(row) + i);
@@ -1063,11 +1147,17 @@ __device__ __forceinline__ void finish_launch(const FusedArgs& a, uint32_t tag) 
 // PS: the prescreened instance (several tokens per launch, no envelope): the
 // sketch activations and partial recovery sums come from the expert-grouped
 // screen that ran before the launch (a.hs, a.zp), and phase A is not compiled.
-template <int EPT, bool RECX, bool ENV, int LNCK = 0, int LCPR = 0, int LKPT = 1, bool PS = false>
+// MS: the multi-sub-chunk instance (several sub-chunks of channels per
+// workgroup below the grouped screen's pair count, no envelope, I <= 4 NT, no
+// candidate-row prefetch): the screen keeps the next sub-chunk's rows in
+// flight (screen_slice), which fits in registers only without the general
+// instance's other paths.
+template <int EPT, bool RECX, bool ENV, int LNCK = 0, int LCPR = 0, int LKPT = 1, bool PS = false, bool MS = false>
 __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
   constexpr bool LEAN = LNCK > 0;
   static_assert(!LEAN || (!RECX && !ENV && LNCK == 8 && LCPR == 8), "lean instance: plain method, 8 chunks, rank 64");
   static_assert(!PS || (!LEAN && !ENV), "prescreened instance: general, no envelope");
+  static_assert(!MS || (!LEAN && !ENV && !PS), "multi-sub-chunk instance: general, no envelope");
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) uint32_t wred[NT / 64];
   __shared__ __align__(16) int wf0[NT / 64];
@@ -1148,6 +1238,8 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       float zacc = 0.f;                               // partial recovery sum for (zl, zg)
       if (LEAN || j1 - j0 <= kSubChunk) {
         if (j1 > j0) screen_and_sum<EPT>(a, L, p, e, j0, j1 - j0, F0, spre, sgu, btv, zg, groups, zacc, tag);
+      } else if constexpr (MS) {
+        zacc = screen_slice<EPT>(a, L, p, e, j0, j1, F0, spre, sgu, zl, zg, groups, tag);
       } else {
         // several sub-chunks: the next one's rows are requested before this one is
         // screened (unconditionally inside the loop; the last one is peeled)
@@ -1184,7 +1276,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
 
     // the A rows of this workgroup's columns (prefetched path): requested now, used at the end
     uint4 apre[4];
-    const bool have_apre = a.pre && r > 0 && ck0 < H / 8;
+    const bool have_apre = !MS && a.pre && r > 0 && ck0 < H / 8;
     {
       const uint16_t* abase = have_apre ? a.A + ((size_t)e * H + 8 * ck0) * r : a.x;
       const int nA = have_apre ? nck * r : 1;          // 16-byte pieces (<= 1024)
@@ -1246,7 +1338,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       uint64_t raw[32];
       uint32_t kr[32];
       const int per = (a.I + NT - 1) / NT;
-      if (LEAN || per <= 4) {
+      if (LEAN || MS || per <= 4) {
         uint32_t k4[4];
         if constexpr (LEAN) {
           // (lean instance) this thread's sketch activations, awaited together;
@@ -1340,7 +1432,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
     // short, every candidate's Bt row is prefetched into LDS with them)
     constexpr bool kBtLate = !RECX && EPT <= 16;
     phase_stamp(a, 7);
-    if (!LEAN && a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck, !kBtLate);
+    if (!LEAN && !MS && a.pre && ck0 < H / 8) prefetch_candidate_rows(a, L, e, ck0, nck, !kBtLate);
     phase_stamp(a, 8);
 
     // ---- top-k (or threshold) kept set and recovery coefficients
@@ -1350,7 +1442,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       const int i0 = topk_range<NT>(a.c, &cnt);
       const uint64_t* src = a.xc + (size_t)p * a.c + i0;
       const int per = (a.c + NT - 1) / NT;
-      if (LEAN || per <= 4) {
+      if (LEAN || MS || per <= 4) {
         uint32_t k4[4];
         // (lean instance) this thread's candidates' channels and sketch
         // activations, read before the exchange so that the kept set's
@@ -1572,7 +1664,7 @@ __global__ __launch_bounds__(NT) void k_select_fused(FusedArgs a) {
       }
       phase_stamp(a, 14);
       continue;
-    } else if (a.pre) {
+    } else if (!MS && a.pre) {
       // candidate down rows are in LDS: the down projection of this workgroup's
       // slice needs no further memory reads. z takes the kept channels' Bt rows,
       // requested once the prefetch has landed and in flight while the down

@@ -370,11 +370,14 @@ int moe_layer_dense_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps
  *     gains, peaking at batch 8 or 16). Calls whose
  *     shape it does not cover return CFM_EUNSUPPORTED: it needs T K <= 65535,
  *     E <= 4096, and for the selected layer r a multiple of 8;
- *   3 the per-pair pass without its batch-1 instance (the kernel compiled for
- *     the Qwen3-30B-A3B-shaped batch-1 call: H 2048, r 64, at most 8 pairs):
- *     the general instance serves every call, for comparison and testing;
- *   4 as 3, with the screen always inside the persistent launch (no grouped
- *     screen in front), for comparison and testing.
+ *   3 the per-pair pass on its general instance only: not the batch-1
+ *     instance (compiled for the Qwen3-30B-A3B-shaped batch-1 call: H 2048,
+ *     r 64, at most 8 pairs), not the instance that keeps the next sub-chunk
+ *     of sketch rows in flight (several sub-chunks of channels per workgroup,
+ *     plain method, H <= 2048, I <= 1024), and no grouped screen in front;
+ *     for comparison and testing;
+ *   4 the per-pair pass with the screen always inside the persistent launch
+ *     (no grouped screen in front), for comparison and testing.
  * Both passes compute the same selections (identical sketch activations, so
  * identical candidate sets; exact activations and outputs agree to float
  * rounding). The workspace sizes returned by select_workspace and

@@ -423,6 +423,40 @@ def test_batched_full_size(cfm, name):
         compare_forward(L, A, Bt, got, cand, keep, wl.k, wl.c, tokens=tokens, what=f"{name} path {path}")
 
 
+@pytest.mark.parametrize("spec", [("ms_q18_b4", (128, 8, 768, 2048, 4, 138, 276, 64, 37)),
+                                  ("ms_q18_b3", (128, 8, 768, 2048, 3, 138, 276, 64, 38)),
+                                  ("ms_ragged", (6, 3, 300, 128, 12, 54, 108, 8, 39)),
+                                  ("ms_rank6", (6, 3, 300, 128, 12, 54, 108, 6, 40)),
+                                  ("ms_h512", (16, 4, 640, 512, 8, 115, 230, 16, 44)),
+                                  ("ms_rank0", (16, 4, 640, 512, 8, 115, 230, 0, 45))],
+                         ids=lambda s: s[0])
+def test_multi_subchunk_instance(cfm, spec):
+    """Three or more 32-channel sub-chunks per workgroup below the grouped screen's 40 pairs: the instance that
+    keeps the next sub-chunk's sketch rows in flight (path 1) against the general instance (path 3) on the
+    same inputs (the same candidate and kept sets bit for bit; outputs within float rounding: the partial
+    recovery sums are added in another order), and against the oracle on sampled tokens."""
+    name, shape = spec
+    wl = custom_workload(name, *shape)
+    log(f"multi-sub-chunk instance {name}")
+    L = upload(wl)
+    E, I, H = L.host.w_gate.shape
+    T, K = L.host.ids.shape
+    tokens = sorted({0, T // 2, T - 1})
+    used_s = sorted(set(L.host.ids[tokens].reshape(-1).tolist()))
+    sk = gpu_sketch(cfm, L)
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, used_s, E, I, H)
+    Ag, Btg = (up_bf16(A), up_bf16(Bt)) if wl.r > 0 else (None, None)
+    res = {}
+    for path in (cfm.FORWARD_PER_PAIR, cfm.FORWARD_PER_PAIR_GENERAL):
+        with cfm.forward_path(path):
+            res[path] = run_select(cfm, L, sk, Ag, Btg, wl.k, wl.c, wl.r)
+    (g1, c1, k1), (g3, c3, k3) = res[cfm.FORWARD_PER_PAIR], res[cfm.FORWARD_PER_PAIR_GENERAL]
+    assert np.array_equal(c1, c3) and np.array_equal(k1, k3)
+    err = max(rel_l2(g1[t], g3[t]) for t in range(T))
+    assert err <= 2e-3, f"{name}: the two instances differ by rel L2 {err:.2e}"
+    compare_forward(L, A, Bt, g1, c1, k1, wl.k, wl.c, tokens=tokens, what=f"{name} multi-sub-chunk instance")
+
+
 @pytest.mark.parametrize("spec", [("q18_b8", None), ("q13_b16", None),
                                   ("ps_small", (16, 4, 256, 512, 16, 46, 92, 8, 33)),
                                   ("ps_ragged", (6, 3, 101, 128, 40, 17, 33, 8, 34)),
