@@ -52,6 +52,16 @@ def test_unsigned_scale_mean_is_caught():
         _fails(P.test_twn_scale_is_least_squares_for_its_pattern)
 
 
+def test_swapped_gate_up_in_sketch_build_is_caught(monkeypatch):
+    real = O.sketch_build
+
+    def swapped(wg, wu, d):                         # the up sketch returned as the gate sketch and back
+        tg, tu, sg, su = real(wg, wu, d)
+        return tu, tg, su, sg
+    monkeypatch.setattr(O, "sketch_build", swapped)
+    _fails(P.test_sketch_build_feeds_the_screen_in_gate_up_order)
+
+
 def test_swapped_flag_bits_are_caught(golden_dir):
     with planted("pack_sign_swap"):
         _fails(P.test_pack_golden, golden_dir)

@@ -218,6 +218,28 @@ def test_screen_equals_exact_on_ternary_weights():
     assert np.allclose(O.exact_activations(x, wg, wu), ref, rtol=1e-12, atol=1e-14)
 
 
+def test_sketch_build_feeds_the_screen_in_gate_up_order():
+    """sketch_build's outputs (both matrices of several experts at once) fed straight into the screen give
+    SiLU(W_gate x) * (W_up x) of each expert on exactly ternary rotated rows, against torch: a gate / up
+    swap (SiLU(u) * g), an expert mix-up or a dropped scale in sketch_build fails it."""
+    H, I, E = 64, 40, 3
+    r = _rng(18)
+    d = np.where(r.integers(0, 2, H) == 1, -1, 1).astype(np.int8)
+    wg = np.stack([_ternary_expert(H, I, d, r) for _ in range(E)])
+    wu = np.stack([_ternary_expert(H, I, d, r) for _ in range(E)])
+    tg, tu, sg, su = O.sketch_build(wg, wu, d)
+    x = O.f64_to_bf16(r.standard_normal(H))
+    xt = torch.from_numpy(O.bf16_to_f64(x))
+    for e in range(E):
+        hhat = O.screen_scores(x, tg[e], tu[e], sg[e], su[e], d)
+        g = torch.from_numpy(O.bf16_to_f64(wg[e])) @ xt
+        u = torch.from_numpy(O.bf16_to_f64(wu[e])) @ xt
+        ref = (torch.nn.functional.silu(g) * u).numpy()
+        swapped = (torch.nn.functional.silu(u) * g).numpy()
+        assert np.allclose(hhat, ref, rtol=1e-10, atol=1e-12), f"expert {e}"
+        assert not np.allclose(hhat, swapped, rtol=1e-3, atol=1e-6)
+
+
 # ----------------------------------------------------------------------------- forward
 
 def _small_layer(E=4, I=32, H=64, T=3, K=2, seed=9):
