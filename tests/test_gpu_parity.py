@@ -318,7 +318,8 @@ def test_lowrank_rank_deficient(cfm, IH):
 
 
 def test_lowrank_end_to_end_tiny(cfm):
-    """The library's own map in the forward pass, against the oracle with the oracle's map."""
+    """The library's own map in the forward pass, against the oracle with the oracle's map (full size:
+    test_q18_b1_full_size)."""
     wl = synth.WORKLOADS["tiny"]
     L = upload(wl)
     sk = gpu_sketch(cfm, L)
@@ -358,6 +359,11 @@ def test_q18_b1_full_size(cfm, q18_layer):
     Ag, Bg = down_bf16(Ag), down_bf16(Bg)
     for e in used[:3]:
         _check_lowrank(L.host.w_down_t[e], Ag[e], Bg[e], wl.r, f"q18 expert {e}")
+    # ... and end to end: the forward pass with the library's own map against the oracle with its map
+    # (the map enters only the recovery term, so the sets are the same)
+    got2, cand2, keep2 = run_select(cfm, L, sk, up_bf16(Ag), up_bf16(Bg), wl.k, wl.c, wl.r)
+    assert np.array_equal(cand2, cand) and np.array_equal(keep2, keep)
+    compare_forward(L, A, Bt, got2, cand2, keep2, wl.k, wl.c, what="q18_b1 with the library's own map")
 
 
 def test_q18_b1_full_size_general_instance(cfm, q18_layer):
