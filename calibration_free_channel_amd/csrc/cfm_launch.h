@@ -86,7 +86,14 @@ struct SelectArgs {
   // bytes of ws (0: unknown); the per-pair pass puts the expert-grouped screen
   // in front of its kernel only when the workspace holds that pass's regions
   size_t ws_bytes;
+  // decode-layer envelope served by the per-pair pass with the grouped screen
+  // in front: the grouped pass's router stage runs first (x above unused), and
+  // the residual resid is added by the per-pair kernel's combine
+  int route_first;
 };
+// Whether the per-pair pass for plan p0 (from select_plan) runs the expert-
+// grouped screen in front of its kernel.
+bool select_prescreen_ok(const SelectArgs& a, const ForwardPlan& p0);
 int launch_select_forward(const SelectArgs& a, const ForwardPlan& p, hipStream_t stream);
 // Phase-timestamp buffer for the single-launch kernels (trace build only).
 int set_phase_trace(void* buf);
@@ -116,5 +123,8 @@ int launch_grouped_forward(const SelectArgs& a, const GroupPlan& p, hipStream_t 
 // for the per-pair pass with several tokens; the caller prepares the workspace.
 bool grouped_screen_supported(int T, int K, int E, int I, int H, int r);
 int launch_grouped_screen(const SelectArgs& a, const GroupPlan& p, hipStream_t stream);
+// The grouped pass's router stage alone (decode-layer envelope): RMSNorm and
+// routing into the plan's xw, idw and ww regions, and the optional outputs.
+int launch_grouped_route(const SelectArgs& a, const GroupPlan& p, hipStream_t stream);
 
 }  // namespace cfm

@@ -344,15 +344,20 @@ constexpr int kGroupedScreenMinPairs = 40;
 // from kGroupedScreenMinPairs pairs, with several sub-chunks of channels per
 // workgroup, when the screen is needed, the shape suits the grouped screen and
 // the workspace holds its regions (sized from the unrefitted plan, as
-// select_workspace is).
-static bool use_grouped_screen(const SelectArgs& s, const ForwardPlan& p0, const ForwardPlan& p, GroupPlan* g) {
-  if (p.env || forward_path() >= 3 || p.P < kGroupedScreenMinPairs || p.cw <= kSubChunk || p.I > 4 * NT ||
-      p.H > 2048)
+// select_workspace is). A grid refitted to fewer workgroups only widens the
+// slices, so the decision holds for the launch.
+bool select_prescreen_ok(const SelectArgs& s, const ForwardPlan& p0) {
+  if (forward_path() >= 3 || p0.P < kGroupedScreenMinPairs || p0.cw <= kSubChunk || p0.I > 4 * NT || p0.H > 2048)
     return false;
-  if ((s.flags & CFM_RECOVER_CANDIDATES_EXACT) && p.c >= p.I) return false;   // no sketch activation is used
-  if (!grouped_screen_supported(p.T, p.K, p.E, p.I, p.H, p.r)) return false;
+  if ((s.flags & CFM_RECOVER_CANDIDATES_EXACT) && p0.c >= p0.I) return false;   // no sketch activation is used
+  if (!grouped_screen_supported(p0.T, p0.K, p0.E, p0.I, p0.H, p0.r)) return false;
+  return s.ws_bytes >= group_plan(p0.T, p0.K, p0.E, p0.I, p0.H, p0.k, p0.c, p0.r, false, p0.bytes).bytes;
+}
+
+static bool use_grouped_screen(const SelectArgs& s, const ForwardPlan& p0, const ForwardPlan& p, GroupPlan* g) {
+  if (p.env || !select_prescreen_ok(s, p0)) return false;
   *g = group_plan(p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, false, p0.bytes);
-  return s.ws_bytes >= g->bytes;
+  return true;
 }
 
 int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_t stream) {
@@ -361,14 +366,26 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
   GroupPlan g{};
   const bool gscreen = use_grouped_screen(s, p0, p, &g);
   if (int rc = prepare_workspace(s.ws, gscreen ? g.bytes : p.bytes,
-                                 layout_signature({gscreen ? 4 : 1, p.T, p.K, p.E, p.I, p.H, p.k, p.c, p.r, p.env,
+                                 layout_signature({gscreen ? (s.route_first ? 5 : 4) : 1, p.T, p.K, p.E, p.I, p.H, p.k,
+                                                   p.c, p.r, p.env,
                                                    p.nw, p.G, gscreen ? (long)g.bytes : 0}),
                                  stream))
     return rc;
-  FusedArgs a = fused_args(s, p);
+  // (decode-layer envelope) the grouped pass's router stage first; the pass
+  // then reads the normalised states and the routing it wrote, and the
+  // combine adds the residual
+  SelectArgs sr = s;
+  if (s.route_first) {
+    if (!gscreen) return set_error(CFM_EUNSUPPORTED, "layer forward: the per-pair pass cannot route first here");
+    if (int rc = launch_grouped_route(s, g, stream)) return rc;
+    sr.x = reinterpret_cast<const uint16_t*>(s.ws + g.off_xw);
+    sr.ids = reinterpret_cast<const int32_t*>(s.ws + g.off_idw);
+    sr.topk_w = reinterpret_cast<const float*>(s.ws + g.off_ww);
+  }
+  FusedArgs a = fused_args(sr, p);
   if (!a.x) return set_error(CFM_EINVAL, "select forward: no hidden states");
   if (gscreen) {
-    if (int rc = launch_grouped_screen(s, g, stream)) return rc;
+    if (int rc = launch_grouped_screen(sr, g, stream)) return rc;
     a.hs = reinterpret_cast<const float*>(s.ws + g.off_hs);
     a.zp = reinterpret_cast<const float*>(s.ws + g.off_zp);
     a.nzp = (p.I + 15) / 16;
@@ -386,7 +403,7 @@ int launch_select_forward(const SelectArgs& s, const ForwardPlan& p0, hipStream_
   if (s.stats) {
     // the general instances prefetch every candidate's down row (for their columns) when p.pre
     const int down_req = (p.pre && !lean) ? p.c : -1;
-    hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, s.ids, p.P, p.E, p.I, p.H, p.k, p.c,
+    hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, stream, sr.ids, p.P, p.E, p.I, p.H, p.k, p.c,
                        p.r, p.T, p.K, 1, (p.k > 0 || a.rec_exact) ? 1 : 0,
                        (a.rec_exact && p.c >= p.I) ? 0 : 1, a.thr ? a.kcnt : nullptr, down_req, gscreen ? 1 : 0,
                        static_cast<cfm_stats*>(s.stats));

@@ -728,7 +728,7 @@ __device__ __forceinline__ void combine_cols(const FusedArgs& a, int t, int w, i
       float o = 0.f;
       for (int q = 0; q < a.K; ++q)
         o += (lw ? lw[q] : a.topk_w[(size_t)t * a.K + q]) * ld_f(a.ypart + (size_t)(t * a.K + q) * a.H + col);
-      if (lw) o += bf16_to_f32(a.resid[(size_t)t * a.H + col]);
+      if (a.resid) o += bf16_to_f32(a.resid[(size_t)t * a.H + col]);   // (envelope: the residual)
       a.out[(size_t)t * a.H + col] = bad ? (uint16_t)0x7FC0 : f32_to_bf16(o);
     }
   }

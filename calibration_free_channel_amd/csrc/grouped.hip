@@ -1417,6 +1417,25 @@ static void fill_args(GArgs& a, const SelectArgs& s, const GroupPlan& g) {
   a.keep_count = s.keep_count;
 }
 
+// The router stage of the decode-layer envelope: x = RMSNorm(resid) into the
+// plan's xw region and the routing into idw / ww (and the optional outputs).
+int launch_grouped_route(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
+  RouteArgs ra{};
+  ra.h = s.resid; ra.gamma = s.gamma; ra.wr = s.wr; ra.eps = s.eps; ra.renorm = s.renorm;
+  ra.T = g.T; ra.K = g.K; ra.E = g.E; ra.H = g.H; ra.nb = (g.E + kRouteRows - 1) / kRouteRows;
+  ra.xw = reinterpret_cast<uint16_t*>(s.ws + g.off_xw);
+  ra.lg = reinterpret_cast<float*>(s.ws + g.off_lg);
+  ra.ids = reinterpret_cast<int32_t*>(s.ws + g.off_idw);
+  ra.w = reinterpret_cast<float*>(s.ws + g.off_ww);
+  ra.rctr = reinterpret_cast<uint32_t*>(s.ws + g.off_rctr);
+  ra.ids_out = s.ids_out; ra.w_out = s.w_out; ra.x_out = s.x_out;
+  timing_begin("k_g_route", stream);
+  hipLaunchKernelGGL(k_g_route, dim3(g.T, ra.nb), dim3(GT), 0, stream, ra);
+  timing_end(stream);
+  CFM_LAUNCH_CHECK("k_g_route");
+  return CFM_OK;
+}
+
 int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t stream) {
   if (int rc = prepare_workspace(s.ws, g.bytes,
                                  layout_signature({3, g.T, g.K, g.E, g.I, g.H, g.k, g.c, g.r, g.dense ? 1 : 0,
@@ -1428,20 +1447,10 @@ int launch_grouped_forward(const SelectArgs& s, const GroupPlan& g, hipStream_t 
   if (s.resid) {
     // decode-layer envelope: the router first; the pass then reads the
     // normalised states and the routing it wrote, and adds the residual
-    RouteArgs ra{};
-    ra.h = s.resid; ra.gamma = s.gamma; ra.wr = s.wr; ra.eps = s.eps; ra.renorm = s.renorm;
-    ra.T = g.T; ra.K = g.K; ra.E = g.E; ra.H = g.H; ra.nb = (g.E + kRouteRows - 1) / kRouteRows;
-    ra.xw = reinterpret_cast<uint16_t*>(s.ws + g.off_xw);
-    ra.lg = reinterpret_cast<float*>(s.ws + g.off_lg);
-    ra.ids = reinterpret_cast<int32_t*>(s.ws + g.off_idw);
-    ra.w = reinterpret_cast<float*>(s.ws + g.off_ww);
-    ra.rctr = reinterpret_cast<uint32_t*>(s.ws + g.off_rctr);
-    ra.ids_out = s.ids_out; ra.w_out = s.w_out; ra.x_out = s.x_out;
-    timing_begin("k_g_route", stream);
-    hipLaunchKernelGGL(k_g_route, dim3(g.T, ra.nb), dim3(GT), 0, stream, ra);
-    timing_end(stream);
-    CFM_LAUNCH_CHECK("k_g_route");
-    a.x = ra.xw; a.ids = ra.ids; a.topk_w = ra.w;
+    if (int rc = launch_grouped_route(s, g, stream)) return rc;
+    a.x = reinterpret_cast<const uint16_t*>(s.ws + g.off_xw);
+    a.ids = reinterpret_cast<const int32_t*>(s.ws + g.off_idw);
+    a.topk_w = reinterpret_cast<const float*>(s.ws + g.off_ww);
     a.resid = s.resid;
   }
   fill_args(a, s, g);

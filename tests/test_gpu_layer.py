@@ -115,6 +115,9 @@ CASES = [
     custom_workload("lay_h2048", 32, 8, 96, 2048, 2, 17, 34, 16, 7),
     custom_workload("lay_rounds", 8, 2, 32, 64, 150, 6, 12, 8, 8),    # grouped pass (300 pairs)
     custom_workload("lay_g64", 16, 4, 128, 512, 64, 23, 46, 8, 9),     # grouped pass
+    # per-pair pass routed by the grouped pass's router stage, grouped screen in front (192 to 256 pairs)
+    custom_workload("lay_ps32", 32, 8, 256, 512, 32, 46, 92, 8, 10),
+    custom_workload("lay_ps_h1024", 32, 8, 256, 1024, 24, 46, 92, 16, 12),
 ]
 
 
@@ -136,6 +139,28 @@ def test_layer_forward_staged(cfm, wl, renorm):
         block, cand, keep = run_select(cfm, S, sk, up_bf16(A), up_bf16(Bt), wl.k, wl.c, wl.r)
     compare_forward(S, A, Bt, block, cand, keep, wl.k, wl.c, tokens=_tokens(wl), what=f"{wl.name} block")
     _check_residual(out, h, block)
+
+
+@pytest.mark.parametrize("wl", [CASES[6], CASES[7]], ids=lambda w: w.name)
+def test_layer_route_first_against_fused_envelope(cfm, wl):
+    """Several tokens per layer call: routed by the grouped pass's router stage, screened by the grouped
+    screen and finished by the prescreened per-pair instance, which adds the residual (path 1), against
+    the envelope fused into the single launch (path 4): the same normalised states and routing bit for
+    bit (the same arithmetic on the same values), outputs within float rounding."""
+    log(f"layer route-first {wl.name}")
+    L = upload(wl)
+    sk = gpu_sketch(cfm, L)
+    E, I, H = L.host.w_gate.shape
+    A, Bt = oracle_map(L.host.w_down_t, wl.r, range(E), E, I, H)
+    h, g, wr = _envelope_inputs(wl, 0.1)
+    res = {}
+    for path in (cfm.FORWARD_PER_PAIR, cfm.FORWARD_PER_PAIR_SINGLE):
+        with cfm.forward_path(path):
+            res[path] = _run_layer(cfm, L, sk, h, g, wr, up_bf16(A), up_bf16(Bt), False)
+    (o1, x1, i1, w1), (o4, x4, i4, w4) = res[cfm.FORWARD_PER_PAIR], res[cfm.FORWARD_PER_PAIR_SINGLE]
+    assert np.array_equal(x1, x4) and np.array_equal(i1, i4) and np.array_equal(w1, w4)
+    err = max(rel_l2(o1[t], o4[t]) for t in range(wl.T))
+    assert err <= 2e-3, f"{wl.name}: route-first and fused envelope differ by rel L2 {err:.2e}"
 
 
 def test_layer_forward_candidates_exact(cfm):
