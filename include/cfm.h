@@ -328,7 +328,10 @@ int moe_dense_forward(const cfm_bf16* x, const int32_t* topk_ids, const float* t
  * Supported: as moe_select_forward, and E <= 1024, K <= E. The pass is chosen
  * as for moe_select_forward (cfm_set_forward_path): the per-pair kernel forms
  * the envelope inside its one launch; the expert-grouped pass runs a router
- * step first. Both form the same normalised states and routing.
+ * step first, and so does the per-pair pass from 192 routed pairs (with a
+ * workspace of select_workspace bytes, forward path 0 or 1), followed by the
+ * grouped screen and the per-pair kernel, which adds the residual. All of
+ * them form the same normalised states and routing.
  */
 int moe_layer_forward(const cfm_bf16* h, const cfm_bf16* norm_w, float eps, const cfm_bf16* w_router,
                       int renorm, int T, int K, const cfm_bf16* w_gate, const cfm_bf16* w_up,
